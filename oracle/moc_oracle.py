@@ -1,0 +1,466 @@
+"""Plain CPU oracle of the Mixture-of-Contexts (MoC) attention layer, in IEEE binary64.
+
+TEST INFRASTRUCTURE ONLY. Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg
+may import or call this module. It shares no code with the HIP path (sparse_chunk_routed_amd)
+and imports nothing from it; the only common module is moc_inputs (seeded inputs, no method
+arithmetic).
+
+Sources (page titles; section / equation named, no line numbers):
+  [MoC-S]  "Mixture of Contexts for Long Video Generation | Summary" (greeksharifa.github.io):
+           §3.1 Mixture of Contexts, §3.2 Attention Chunking and Routing, §3.3 Computation
+           Efficiency (Eq. 4, Eq. 5), Appendix A and G.
+  [MoC-W]  jxzklqfsx.com write-up of the MoC paper: sections 上下文混合, 注意力塊劃分與路由
+           (固定的跨模態選擇, 固定的鏡頭內選擇, 稀疏 MoC 中的因果性), 計算效率.
+  [MoC-D]  docswell reading-group slides "Mixture of Contexts for Long Video Generation":
+           slides 11 (Router), 12 (Causal Routing), 13 (Router constraints), 14 (drop-off/in).
+
+What is computed (per batch element b and head h; routing is independent per head, [MoC-S] §3.1):
+  1. Layout: chunks are contiguous token ranges aligned to the caption (text), frames and shots
+     ([MoC-S] §3.2; [MoC-W] 內容對齊的塊劃分). Text chunks form one pseudo-shot.
+  2. Pool: kbar_c = mean of the keys of chunk c ([MoC-D] slide 11; [MoC-S] §3.1). Reading: exact
+     sum, one binary64 division by n_c, round-to-nearest-even to binary32.
+  3. Candidates: chunk c is an optional candidate for query t iff c is not text, c is not in the
+     query's own shot, and (if causal) c < chunk(t). Mandatory links are removed before top-k
+     ([MoC-W] 計算效率: the pre-routing mask); causal masks edges i->j with j >= i ([MoC-S] §3.2).
+  4. Score: s_c = q_t . kbar_c, a plain dot product, no router weights ([MoC-S] §3.1).
+  5. Top-k: the min(k, #candidates) best candidates; an exact tie goes to the lower chunk index.
+  6. Drop-off / drop-in (training noise, [MoC-S] §3.1; [MoC-D] slide 14): see drop_noise().
+  7. Key set: Omega(t) = text tokens U own-shot tokens U tokens of the routed chunks
+     ([MoC-S] §3.1-3.2; [MoC-W] 固定的跨模態選擇 / 固定的鏡頭內選擇).
+  8. Attend: o_t = softmax(q_t K_Omega^T * scale) V_Omega, scale = 1/sqrt(d) by default
+     ([MoC-S] §3.1); lse_t = natural log of the softmax denominator (with the max added back).
+  9. Backward with Omega fixed (top-k is non-differentiable, [MoC-S] §3.1 and Appendix A).
+ 10. Counts: pairs = sum_t |Omega(t)|; FLOPs at 4*d per attended pair ([MoC-S] Eq. 5).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import rng as _rng
+
+TEXT_SHOT = -1  # pseudo-shot id of every text chunk
+
+
+# ---------------------------------------------------------------------------------------------
+# 1. Layout
+# ---------------------------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class Derived:
+    L: int
+    C: int
+    offsets: np.ndarray        # int64 [C+1]
+    sizes: np.ndarray          # int64 [C]
+    shot: np.ndarray           # int64 [C]; TEXT_SHOT for text chunks
+    is_text: np.ndarray        # bool [C]
+    chunk_of: np.ndarray       # int64 [L]
+    text_begin: int
+    text_end: int
+
+
+def derive(layout) -> Derived:
+    """Validate a layout and derive per-token / per-chunk tables."""
+    off = np.asarray(layout.chunk_offsets, dtype=np.int64)
+    shot = np.asarray(layout.chunk_shot, dtype=np.int64)
+    C = len(shot)
+    if len(off) != C + 1 or off[0] != 0 or np.any(np.diff(off) <= 0):
+        raise ValueError("chunk offsets must start at 0 and increase strictly")
+    L = int(off[-1])
+    tb, te = int(layout.text_begin), int(layout.text_end)
+    is_text = np.zeros(C, dtype=bool)
+    for c in range(C):
+        a, b = int(off[c]), int(off[c + 1])
+        inside = tb <= a and b <= te
+        overlap = a < te and tb < b
+        if overlap and not inside:
+            raise ValueError("a chunk straddles the text range")
+        is_text[c] = inside and tb < te
+        if is_text[c] != (shot[c] == TEXT_SHOT):
+            raise ValueError("text chunks must carry shot id -1, and only they")
+    # each shot's chunks are contiguous
+    seen = set()
+    prev = None
+    for c in range(C):
+        s = int(shot[c])
+        if s == TEXT_SHOT:
+            prev = None
+            continue
+        if s != prev:
+            if s in seen:
+                raise ValueError("a shot's chunks must be contiguous")
+            seen.add(s)
+        prev = s
+    if tb < te:
+        # text chunks contiguous (one range)
+        tidx = np.nonzero(is_text)[0]
+        if int(off[tidx[0]]) != tb or int(off[tidx[-1] + 1]) != te:
+            raise ValueError("text range must be a union of whole chunks")
+    chunk_of = np.repeat(np.arange(C, dtype=np.int64), np.diff(off))
+    return Derived(L, C, off, np.diff(off), shot, is_text, chunk_of, tb, te)
+
+
+def shot_of_chunk(D: Derived, c: int) -> int:
+    return int(D.shot[c])
+
+
+def shot_range_tokens(D: Derived, s: int) -> np.ndarray:
+    """All token indices whose chunk belongs to shot s (text tokens for the text pseudo-shot)."""
+    cs = np.nonzero(D.shot == s)[0]
+    return np.concatenate([np.arange(D.offsets[c], D.offsets[c + 1]) for c in cs])
+
+
+def anchor_keys(D: Derived, t: int) -> np.ndarray:
+    """Mandatory keys of query t: all text tokens and all tokens of the query's own shot.
+    A text query's own shot is the text itself, so its anchor set is the text range."""
+    s = int(D.shot[D.chunk_of[t]])
+    own = shot_range_tokens(D, s)
+    text = np.arange(D.text_begin, D.text_end)
+    return np.union1d(text, own)
+
+
+# ---------------------------------------------------------------------------------------------
+# 2. Pool
+# ---------------------------------------------------------------------------------------------
+
+def pool_keys(K, layout) -> np.ndarray:
+    """kbar[b,h,c,:] = RN32( RN64(exact sum of K over chunk c) / n_c ).  float32 [B,H,C,d]."""
+    D = derive(layout)
+    K = np.asarray(_as_f64(K))
+    B, H, L, d = K.shape
+    out = np.zeros((B, H, D.C, d), dtype=np.float32)
+    for b in range(B):
+        for h in range(H):
+            for c in range(D.C):
+                a, e = int(D.offsets[c]), int(D.offsets[c + 1])
+                n = e - a
+                blk = K[b, h, a:e, :]
+                for j in range(d):
+                    s = math.fsum(blk[:, j].tolist())  # exact sum, rounded once to binary64
+                    out[b, h, c, j] = np.float32(s / float(n))
+    return out
+
+
+# ---------------------------------------------------------------------------------------------
+# 3-5. Candidates, scores, top-k
+# ---------------------------------------------------------------------------------------------
+
+def allowed(D: Derived, cq: int, c: int, causal: bool) -> bool:
+    """Is chunk c an optional routing candidate for a query in chunk cq?"""
+    if D.is_text[c]:
+        return False
+    if D.shot[c] == D.shot[cq]:
+        return False
+    if causal and not (c < cq):
+        return False
+    return True
+
+
+def candidates(D: Derived, cq: int, causal: bool) -> np.ndarray:
+    return np.array([c for c in range(D.C) if allowed(D, cq, c, causal)], dtype=np.int64)
+
+
+@dataclass
+class Routing:
+    sel: np.ndarray     # int32 [B,H,L,S]: selected chunk ids ascending, -1 padded
+    nsel: np.ndarray    # int32 [B,H,L]
+    gap_exempt: np.ndarray  # bool [B,H,L]: k-th vs (k+1)-th score gap < 1e-4 relative
+    k_eff: int
+
+
+def scores(Q, kbar) -> np.ndarray:
+    """s[b,h,t,c] = q_t . kbar_c in binary64 (bf16/fp32 inputs widen exactly)."""
+    Q = _as_f64(Q)
+    kb = np.asarray(kbar, dtype=np.float64)
+    return np.einsum("bhtd,bhcd->bhtc", Q, kb, optimize=True)
+
+
+TIE_REL = 1e-4
+
+
+def route(Q, kbar, layout, top_k: int, causal: bool) -> Routing:
+    """Top-min(k, #candidates) chunks per (b, h, t), stored ascending by chunk id."""
+    D = derive(layout)
+    s_all = scores(Q, kbar)
+    B, H, L, C = s_all.shape
+    k_eff = min(int(top_k), C)
+    sel = np.full((B, H, L, k_eff), -1, dtype=np.int32)
+    nsel = np.zeros((B, H, L), dtype=np.int32)
+    exempt = np.zeros((B, H, L), dtype=bool)
+    for cq in range(C):
+        toks = np.arange(D.offsets[cq], D.offsets[cq + 1])
+        cand = candidates(D, cq, causal)
+        n = min(k_eff, len(cand))
+        if n == 0:
+            continue
+        for b in range(B):
+            for h in range(H):
+                sc = s_all[b, h][np.ix_(toks, cand)]           # [nt, ncand]
+                # order by (-score, chunk id): cand is ascending and the sort is stable
+                order = np.argsort(-sc, axis=1, kind="stable")
+                top = cand[order[:, :n]]
+                sel[b, h, toks, :n] = np.sort(top, axis=1)
+                nsel[b, h, toks] = n
+                if len(cand) > n:
+                    sk = np.take_along_axis(sc, order[:, n - 1:n], axis=1)[:, 0]
+                    sk1 = np.take_along_axis(sc, order[:, n:n + 1], axis=1)[:, 0]
+                    exempt[b, h, toks] = (sk - sk1) < TIE_REL * np.maximum(np.abs(sk), np.abs(sk1))
+    return Routing(sel, nsel, exempt, k_eff)
+
+
+# ---------------------------------------------------------------------------------------------
+# 6. Context drop-off and drop-in
+# ---------------------------------------------------------------------------------------------
+
+def drop_noise_row(D: Derived, top: Sequence[int], b: int, h: int, t: int, H: int,
+                   k_eff: int, causal: bool, p_max: float, lam: float, m_cap: int,
+                   seed: int, thr: Optional[List[int]]) -> List[int]:
+    """Training-time routing noise for one query ([MoC-S] §3.1; [MoC-D] slide 14).
+
+    Readings: drop-off removes min(floor(p*k), |T|) chunks from the routed top-k set T only
+    (never the mandatory anchors), with p = u * p_max, u the top 24 bits of an H32 word;
+    drop-in then adds min(m, |pool|) chunks from pool = candidates(t) minus T, with
+    m ~ Poisson(lam) truncated at m_cap. Picks are uniform without replacement via
+    idx = (H32 * remaining) >> 32 over the ascending list of what remains."""
+    L = D.L
+    T = sorted(int(c) for c in top)
+    kept = list(T)
+    if p_max > 0.0:
+        r = _rng.h32(seed, _rng.counter(b, h, t, _rng.STREAM_DROP_P, 0, H, L))
+        u = float(r >> 8) * (2.0 ** -24)
+        p = u * float(np.float32(p_max))
+        nd = min(int(math.floor(p * float(k_eff))), len(kept))
+        for j in range(nd):
+            w = _rng.h32(seed, _rng.counter(b, h, t, _rng.STREAM_DROP_PICK, j, H, L))
+            idx = (w * (len(kept))) >> 32
+            kept.pop(idx)
+    added: List[int] = []
+    if lam > 0.0:
+        r = _rng.h32(seed, _rng.counter(b, h, t, _rng.STREAM_IN_COUNT, 0, H, L))
+        m = _rng.poisson_from_word(r, thr, m_cap)
+        cq = int(D.chunk_of[t])
+        pool = [int(c) for c in candidates(D, cq, causal) if int(c) not in T]
+        for j in range(min(m, len(pool))):
+            w = _rng.h32(seed, _rng.counter(b, h, t, _rng.STREAM_IN_PICK, j, H, L))
+            idx = (w * len(pool)) >> 32
+            added.append(pool.pop(idx))
+    return sorted(kept + added)
+
+
+def drop_noise(routing: Routing, layout, causal: bool, p_max: float, lam: float,
+               m_cap: int, seed: int, rows: Optional[Iterable[Tuple[int, int, int]]] = None
+               ) -> Tuple[np.ndarray, np.ndarray]:
+    """Apply drop-off then drop-in. Returns (sel [B,H,L,S], nsel [B,H,L]) with
+    S = k_eff + (m_cap if lam > 0 else 0). With `rows`, only those (b,h,t) are computed and
+    the other rows are left at -1 / 0."""
+    D = derive(layout)
+    B, H, L, _ = routing.sel.shape
+    k_eff = routing.k_eff
+    S = k_eff + (m_cap if lam > 0.0 else 0)
+    thr = _rng.poisson_thresholds(float(np.float32(lam)), m_cap) if lam > 0.0 else None
+    sel = np.full((B, H, L, S), -1, dtype=np.int32)
+    nsel = np.zeros((B, H, L), dtype=np.int32)
+    it = rows if rows is not None else ((b, h, t) for b in range(B) for h in range(H)
+                                        for t in range(L))
+    for (b, h, t) in it:
+        n = int(routing.nsel[b, h, t])
+        top = routing.sel[b, h, t, :n]
+        out = drop_noise_row(D, top, b, h, t, H, k_eff, causal, p_max, lam, m_cap, seed, thr)
+        sel[b, h, t, :len(out)] = out
+        nsel[b, h, t] = len(out)
+    return sel, nsel
+
+
+# ---------------------------------------------------------------------------------------------
+# 7-8. Key sets and attention
+# ---------------------------------------------------------------------------------------------
+
+def key_set(D: Derived, t: int, sel_row: Sequence[int]) -> np.ndarray:
+    """Omega(t) as a sorted array of key indices (a set: no key counted twice)."""
+    parts = [anchor_keys(D, t)]
+    for c in sel_row:
+        c = int(c)
+        if c < 0:
+            continue
+        parts.append(np.arange(D.offsets[c], D.offsets[c + 1]))
+    return np.unique(np.concatenate(parts))
+
+
+def attend_row(q: np.ndarray, Kbh: np.ndarray, Vbh: np.ndarray, keys: np.ndarray,
+               scale: float) -> Tuple[np.ndarray, float]:
+    x = (Kbh[keys] @ q) * scale
+    m = float(np.max(x))
+    w = np.exp(x - m)
+    z = float(np.sum(w))
+    o = (w @ Vbh[keys]) / z
+    return o, m + math.log(z)
+
+
+def attend(Q, K, V, layout, sel, scale: Optional[float] = None,
+           rows: Optional[Sequence[Tuple[int, int, int]]] = None):
+    """Forward attention over Omega. Full: returns (O [B,H,L,d] fp64, lse [B,H,L] fp64).
+    With `rows` (a list of (b,h,t)): returns (O [n,d], lse [n]) for those rows."""
+    D = derive(layout)
+    Q = _as_f64(Q)
+    K = _as_f64(K)
+    V = _as_f64(V)
+    B, H, L, d = Q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    sel = np.asarray(sel)
+    if rows is None:
+        O = np.zeros((B, H, L, d))
+        lse = np.zeros((B, H, L))
+        for b in range(B):
+            for h in range(H):
+                for t in range(L):
+                    keys = key_set(D, t, sel[b, h, t])
+                    O[b, h, t], lse[b, h, t] = attend_row(Q[b, h, t], K[b, h], V[b, h], keys, scale)
+        return O, lse
+    rows = list(rows)
+    O = np.zeros((len(rows), d))
+    lse = np.zeros(len(rows))
+    for i, (b, h, t) in enumerate(rows):
+        keys = key_set(D, t, sel[b, h, t])
+        O[i], lse[i] = attend_row(Q[b, h, t], K[b, h], V[b, h], keys, scale)
+    return O, lse
+
+
+# ---------------------------------------------------------------------------------------------
+# 9. Backward with Omega fixed
+# ---------------------------------------------------------------------------------------------
+
+def attend_bwd(Q, K, V, dO, layout, sel, scale: Optional[float] = None):
+    """Gradients of sum(O * dO) w.r.t. Q, K, V with the routed sets held fixed.
+
+    Per query t with P = softmax(x), x_j = q_t.k_j*scale over j in Omega(t):
+      dV_j += P_j dO_t;  dP_j = dO_t . v_j;  dS_j = P_j (dP_j - sum_i P_i dP_i);
+      dQ_t = scale * sum_j dS_j k_j;  dK_j += scale * dS_j q_t."""
+    D = derive(layout)
+    Q = _as_f64(Q)
+    K = _as_f64(K)
+    V = _as_f64(V)
+    dO = _as_f64(dO)
+    B, H, L, d = Q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    sel = np.asarray(sel)
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    for b in range(B):
+        for h in range(H):
+            Kbh, Vbh = K[b, h], V[b, h]
+            for t in range(L):
+                keys = key_set(D, t, sel[b, h, t])
+                x = (Kbh[keys] @ Q[b, h, t]) * scale
+                p = np.exp(x - np.max(x))
+                p /= np.sum(p)
+                g = dO[b, h, t]
+                dV[b, h, keys] += np.outer(p, g)
+                dp = Vbh[keys] @ g
+                ds = p * (dp - np.dot(p, dp))
+                dQ[b, h, t] = scale * (ds @ Kbh[keys])
+                dK[b, h, keys] += scale * np.outer(ds, Q[b, h, t])
+    return dQ, dK, dV
+
+
+# ---------------------------------------------------------------------------------------------
+# 10. Counts and invariants
+# ---------------------------------------------------------------------------------------------
+
+def pair_counts(layout, sel) -> np.ndarray:
+    """int64 [B,H]: sum over queries of |Omega(t)| = |Anch(t)| + sum of routed chunk sizes
+    (routed chunks are never text or own-shot chunks, so the two parts are disjoint)."""
+    D = derive(layout)
+    sel = np.asarray(sel)
+    B, H, L, _ = sel.shape
+    anch = np.zeros(D.C, dtype=np.int64)
+    for c in range(D.C):
+        anch[c] = len(anchor_keys(D, int(D.offsets[c])))
+    anchor_total = int(anch[D.chunk_of].sum())
+    out = np.zeros((B, H), dtype=np.int64)
+    for b in range(B):
+        for h in range(H):
+            s = sel[b, h]
+            out[b, h] = anchor_total + int(D.sizes[s[s >= 0]].sum())
+    return out
+
+
+def attention_flops(pairs: int, d: int) -> int:
+    """Forward attention FLOPs at 4*d per attended (query, key) pair ([MoC-S] Eq. 5)."""
+    return 4 * d * int(pairs)
+
+
+def dense_flops(L: int, d: int) -> int:
+    """FLOPs_dense = 4 L^2 d for one head ([MoC-S] Eq. 5)."""
+    return 4 * L * L * d
+
+
+def routed_edges(layout, sel) -> set:
+    """Chunk interaction edges (chunk(t) -> c) for every routed selection."""
+    D = derive(layout)
+    sel = np.asarray(sel)
+    E = set()
+    B, H, L, S = sel.shape
+    for b in range(B):
+        for h in range(H):
+            for t in range(L):
+                for c in sel[b, h, t]:
+                    if c >= 0:
+                        E.add((int(D.chunk_of[t]), int(c)))
+    return E
+
+
+def is_dag(C: int, edges: Iterable[Tuple[int, int]]) -> bool:
+    """Kahn's topological sort over chunk nodes."""
+    out = {i: set() for i in range(C)}
+    indeg = [0] * C
+    for (a, b) in edges:
+        if b not in out[a]:
+            out[a].add(b)
+            indeg[b] += 1
+    stack = [i for i in range(C) if indeg[i] == 0]
+    seen = 0
+    while stack:
+        n = stack.pop()
+        seen += 1
+        for m in out[n]:
+            indeg[m] -= 1
+            if indeg[m] == 0:
+                stack.append(m)
+    return seen == C
+
+
+def check_routing(layout, sel, nsel, top_k: int, causal: bool, exact_count: bool = True) -> None:
+    """Raise AssertionError unless every selection is a legal candidate, ascending and unique,
+    and (exact_count) there are exactly min(k, #candidates) of them."""
+    D = derive(layout)
+    sel = np.asarray(sel)
+    B, H, L, S = sel.shape
+    for cq in range(D.C):
+        cand = set(int(c) for c in candidates(D, cq, causal))
+        need = min(int(top_k), D.C, len(cand))
+        for t in range(int(D.offsets[cq]), int(D.offsets[cq + 1])):
+            for b in range(B):
+                for h in range(H):
+                    n = int(nsel[b, h, t])
+                    row = [int(c) for c in sel[b, h, t, :n]]
+                    assert all(c in cand for c in row), (b, h, t, row)
+                    assert row == sorted(set(row)), (b, h, t, row)
+                    assert all(int(c) == -1 for c in sel[b, h, t, n:]), (b, h, t)
+                    if exact_count:
+                        assert n == need, (b, h, t, n, need)
+
+
+def _as_f64(x) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return x.detach().to(torch.float64).cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(x, dtype=np.float64)
