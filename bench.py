@@ -1,0 +1,192 @@
+"""Benchmark of the MoC attention layer on one MI355X.
+
+One step = one pass of the whole layer (pool -> route -> index inversion -> attention forward;
+plus the backward for --workload train) over one batch of seeded synthetic input already
+resident in HBM. Prints ONE JSON line.
+
+value = effective TFLOP/s on attended pairs over the whole layer: 4*d FLOPs per attended
+(query, key) pair (the dense-attention convention of the MoC summary, Eq. 5), pairs counted
+exactly by the index inversion, divided by the layer time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoC layer ms + effective TFLOP/s on attended pairs at ~175k tokens, 1 MI355X"
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}  # MI355X dense MFMA (bf16), fp32
+PEAK_HBM_GBS = 8000.0
+
+
+def parse(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="headline",
+                    choices=["headline", "mid", "short", "tiny", "train", "headline_uniform"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=192,
+                    help="query rows of the oracle attention sample (one head)")
+    return ap.parse_args(argv)
+
+
+def cpu_baseline(w, Q, K, V, rows_n: int):
+    """The oracle timed on a bounded sample of the same workload, extrapolated linearly."""
+    import numpy as np
+    from oracle import moc_oracle as mo
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    hs = min(2, w.H)
+    t0 = time.perf_counter()
+    kb = mo.pool_keys(K[:, :hs], w.layout)
+    t_pool = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    r = mo.route(Q[:, :hs], kb, w.layout, w.top_k, w.causal)
+    t_route = time.perf_counter() - t0
+    rng = np.random.default_rng(w.seed)
+    ts = sorted(rng.choice(w.L, size=min(rows_n, w.L), replace=False).tolist())
+    rows = [(0, 0, int(t)) for t in ts]
+    t0 = time.perf_counter()
+    mo.attend(Q[:, :1], K[:, :1], V[:, :1], w.layout, r.sel[:, :1], rows=rows)
+    t_att = time.perf_counter() - t0
+    measured = t_pool + t_route + t_att
+    full = (t_pool + t_route) * (w.B * w.H / (w.B * hs)) + t_att * (w.B * w.H * w.L / len(rows))
+    pairs = int(mo.pair_counts(w.layout, r.sel[:, :1])[0, 0]) * w.B * w.H
+    flops = 4 * w.d * pairs
+    return {
+        "value": flops / full / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"fp64 numpy oracle: pool+route on {hs} of {w.H} heads, attention on "
+                   f"{len(rows)} query rows of head 0; measured {measured:.1f} s, extrapolated "
+                   f"linearly to the full layer = {full:.1f} s"),
+        "measured_s": measured, "extrapolated_full_layer_s": full,
+    }
+
+
+def main(argv=None) -> int:
+    a = parse(argv)
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        return 2
+    import torch
+
+    import moc_inputs as mi
+    import sparse_chunk_routed_amd as moc
+
+    dev = torch.device("cuda:0")
+    w = mi.WORKLOADS[a.workload](a.seed)
+    with_bwd = a.workload == "train"
+    print(f"[bench] workload {w.name}: {w.description}; B={w.B} H={w.H} L={w.L} d={w.d} "
+          f"C={w.C} k={w.top_k}", file=sys.stderr, flush=True)
+    tensors = mi.make_qkv(w, with_dout=with_bwd)
+    Q, K, V = tensors[:3]
+    Qd, Kd, Vd = (x.to(dev) for x in (Q, K, V))
+    dOd = tensors[3].to(dev) if with_bwd else None
+    lay = moc.DeviceLayout.from_layout(w.layout, dev)
+    cfg = moc.RouteCfg(w.top_k, w.causal, w.p_max, w.lam, w.max_drop_in, w.seed)
+    fwd_ws = torch.empty(moc.workspace_bytes(lay, w.B, w.H, w.d, Qd.dtype, cfg, 2),
+                         dtype=torch.uint8, device=dev)
+
+    names = ["pool", "route", "varlen", "attend_fwd"] + (["attend_bwd"] if with_bwd else [])
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        kbar = moc.pool_keys(Kd, lay)
+        mark(1)
+        sel, nsel = moc.route(Qd, kbar, lay, cfg)
+        mark(2)
+        vl = moc.build_varlen(sel, nsel, lay, cfg, w.d, Qd.dtype)
+        mark(3)
+        O, lse = moc.attend_fwd(Qd, Kd, Vd, lay, vl, ws=fwd_ws)
+        mark(4)
+        if with_bwd:
+            moc.attend_bwd(Qd, Kd, Vd, O, lse, dOd, lay, vl)
+            mark(5)
+        return vl
+
+    for _ in range(a.warmup):
+        vl = step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({a.warmup} steps)", file=sys.stderr, flush=True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(a.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(a.steps):
+        vl = step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms = total_ms / a.steps
+    stage = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / a.steps
+             for j, n in enumerate(names)}
+    pairs = int(vl.pair_count.sum().item())
+    fwd_flops = 4 * w.d * pairs
+    bwd_flops = 10 * w.d * pairs if with_bwd else 0
+    flops = fwd_flops + bwd_flops
+    s_in = 2 if w.dtype == "bf16" else 4
+    BHLd = w.B * w.H * w.L * w.d
+    S = moc.sel_width(cfg, w.C)
+    pool_bytes = BHLd * s_in + w.B * w.H * w.C * w.d * 4
+    route_bytes = BHLd * s_in + w.B * w.H * w.C * w.d * 4 + w.B * w.H * w.L * (S + 1) * 4
+    peak = PEAK_TFLOPS[w.dtype]
+    att_tf = fwd_flops / (stage["attend_fwd"] * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": flops / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded normal Q/V, chunk-clustered K; no trained activations)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "C": w.C,
+                   "top_k": w.top_k, "causal": w.causal, "p_max": w.p_max, "lambda": w.lam,
+                   "seed": w.seed, "layout": w.description},
+        "layer_ms": ms,
+        "stages_ms": stage,
+        "pairs": pairs,
+        "pruned_fraction": 1.0 - pairs / (w.B * w.H * w.L * w.L),
+        "attention_tflops": att_tf,
+        "pool_gbs": pool_bytes / (stage["pool"] * 1e-3) / 1e9,
+        "route_gbs": route_bytes / (stage["route"] * 1e-3) / 1e9,
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attention forward (routed + anchor kernels of moc_attend_fwd)",
+            "achieved": att_tf, "peak": peak, "unit": "TFLOP/s", "frac": att_tf / peak,
+            "traffic": None,
+        },
+        "cpu_baseline": None,
+    }
+    if with_bwd:
+        out["backward_tflops"] = bwd_flops / (stage["attend_bwd"] * 1e-3) / 1e12
+    if not a.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, Q, K, V, a.cpu_rows)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,209 @@
+/*
+ * moc.h - C ABI of libmoc, a Mixture-of-Contexts (MoC) attention layer for AMD MI355X (gfx950).
+ *
+ * The layer replaces dense self-attention: keys are mean-pooled per content-aligned chunk
+ * (caption, frame, shot), every query scores the chunk descriptors by dot product, optional
+ * retrieval is limited to earlier chunks by the causal routing mask, the top-k chunks are
+ * picked, and exact softmax attention runs over the mandatory anchors (all caption tokens and
+ * the query's own shot) plus the routed chunks.
+ *   Source: "Mixture of Contexts for Long Video Generation | Summary" (greeksharifa.github.io),
+ *   §3.1 Mixture of Contexts, §3.2 Attention Chunking and Routing, §3.3 Computation Efficiency;
+ *   jxzklqfsx.com write-up of the paper, sections 注意力塊劃分與路由 and 計算效率.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, except the moc_layout /
+ *     moc_route_cfg / moc_varlen structs themselves, which are host structs read during the
+ *     call only. The library never allocates or frees device memory and keeps no state between
+ *     calls (beyond loaded kernels and a thread-local error string).
+ *   - Q, K, V, O, dO, dQ, dK, dV are [B, H, L, d] contiguous (head-major: each head's tokens
+ *     are contiguous rows of d elements), in the layout's dtype.
+ *   - Calls only enqueue work on `stream` (a hipStream_t passed as void*; NULL = default
+ *     stream) and return without synchronising. All argument checks run on the host before
+ *     anything is enqueued, so a non-OK status means nothing ran.
+ *   - Workspaces are sized with moc_workspace_bytes(). Distinct workspaces allow concurrent
+ *     calls on distinct streams; calls sharing a workspace must be ordered by the caller.
+ *   - Layout arrays live on the device, so their content (monotone offsets, contiguous shots,
+ *     text on chunk boundaries) is a precondition, not checked here; the Python binding checks
+ *     it on a host copy.
+ */
+#ifndef MOC_H_
+#define MOC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOC_OK = 0,
+  MOC_EINVAL = 1,       /* null pointer, negative size, bad flag, aliasing */
+  MOC_ESHAPE = 2,       /* a size outside the supported limits */
+  MOC_EDTYPE = 3,       /* unknown dtype */
+  MOC_EWORKSPACE = 4,   /* workspace pointer null or smaller than moc_workspace_bytes() */
+  MOC_EUNSUPPORTED = 5, /* a valid request this build does not implement */
+  MOC_EHIP = 6,         /* a HIP launch or runtime call failed */
+  MOC_EINTERNAL = 7     /* unexpected internal error (no C++ exception crosses the ABI) */
+} moc_status;
+
+typedef enum { MOC_F32 = 0, MOC_BF16 = 1 } moc_dtype;
+
+/* Workspace kinds for moc_workspace_bytes(). */
+enum { MOC_OP_ROUTE = 0, MOC_OP_VARLEN = 1, MOC_OP_FWD = 2, MOC_OP_BWD = 3 };
+
+/* Hard limits of this build. */
+#define MOC_MAX_C 1024        /* chunks per sequence */
+#define MOC_MAX_TOPK 32       /* min(top_k, C) */
+#define MOC_MAX_DROP_IN 16    /* max_drop_in */
+
+/*
+ * Token layout (shared by all batch elements and heads). Chunks are content-aligned token
+ * ranges (summary §3.2; write-up 內容對齊的塊劃分): chunk c is [chunk_offsets[c],
+ * chunk_offsets[c+1]).
+ *   chunk_offsets: device int32 [C+1], 0 = off[0] < off[1] < ... < off[C] = L (cu_seqlens style).
+ *   chunk_shot:    device int32 [C], the shot id of each chunk; a shot's chunks are contiguous;
+ *                  every text chunk carries -1, and no other chunk does.
+ *   [text_begin, text_end): the caption tokens, a union of whole chunks; may be empty.
+ *   dtype: MOC_F32 or MOC_BF16; d in {64, 128}; 1 <= C <= min(L, MOC_MAX_C).
+ */
+typedef struct {
+  int32_t B, H, L, d;
+  int32_t dtype;
+  int32_t C;
+  const int32_t *chunk_offsets;
+  const int32_t *chunk_shot;
+  int32_t text_begin, text_end;
+} moc_layout;
+
+/*
+ * Routing configuration (summary §3.1-3.2; slides "Mixture of Contexts for Long Video
+ * Generation", slides 11-14).
+ *   top_k:  >= 0; the routed budget per query is min(top_k, #candidates).
+ *           min(top_k, C) must not exceed MOC_MAX_TOPK.
+ *   causal: 1 = an optional candidate chunk c must come before the query's chunk (c < chunk(t)).
+ *   p_max:  context drop-off, in [0, 1]; 0 disables. p = u * p_max with u ~ U[0,1) and
+ *           min(floor(p * min(top_k, C)), |T|) routed chunks are removed at random.
+ *   lambda: context drop-in, >= 0; 0 disables. m ~ Poisson(lambda) truncated at max_drop_in
+ *           extra chunks are added at random from the candidates not already routed.
+ *   max_drop_in: in [0, MOC_MAX_DROP_IN] (used only when lambda > 0).
+ *   seed:   key of the counter-based generator (SplitMix64, Steele-Lea-Flood 2014), so a
+ *           draw depends only on (seed, b, h, t, stream, j).
+ */
+typedef struct {
+  int32_t top_k;
+  int32_t causal;
+  float p_max;
+  float lambda;
+  int32_t max_drop_in;
+  int32_t reserved;
+  uint64_t seed;
+} moc_route_cfg;
+
+/*
+ * Result of the index inversion (moc_build_varlen). All pointers point into the caller's
+ * VARLEN workspace and stay valid while that workspace is not reused. Filled by
+ * moc_build_varlen on the host side (pointers, sizes) and on the device (contents).
+ *   S:          selection width, = min(top_k, C) + (lambda > 0 ? max_drop_in : 0).
+ *   bucket_off: [B*H*C + 1] exclusive prefix of the number of queries that routed to each
+ *               (b, h, chunk) bucket; bucket_off[B*H*C] = total routed selections.
+ *   bucket_q:   [B*H*L*S] the query token ids of each bucket, ascending within a bucket.
+ *   slot:       [B*H*L*S] for selection j of query (b,h,t): its position in bucket_q (the row
+ *               of that (query, chunk) partial result), -1 for padding.
+ *   rtiles:     [max_rtiles][2] routed work tiles (bucket id, first position in the bucket),
+ *               n_rtiles[0] of them valid; each tile covers up to tile_rows queries.
+ *   atiles:     [max_atiles][6] anchor work tiles (q0, q1, key range 1 [a0,a1), key range 2
+ *               [b0,b1)), n_atiles[0] valid, shared by every (b, h).
+ */
+typedef struct {
+  int32_t S;
+  int32_t tile_rows;
+  int32_t max_rtiles;
+  int32_t max_atiles;
+  int32_t *bucket_off;
+  int32_t *bucket_q;
+  int32_t *slot;
+  int32_t *rtiles;
+  int32_t *n_rtiles;
+  int32_t *atiles;
+  int32_t *n_atiles;
+  int32_t *scratch;     /* internal: per-tile counts and offsets of the inversion */
+} moc_varlen;
+
+/* Selection width S for a route configuration and chunk count (see moc_varlen.S). */
+int32_t moc_sel_width(const moc_route_cfg *cfg, int32_t C);
+
+/* Bytes of device workspace needed by the entry point `op` (MOC_OP_*); 0 on invalid
+ * arguments (see moc_last_error()). */
+size_t moc_workspace_bytes(const moc_layout *lay, const moc_route_cfg *cfg, int32_t op);
+
+/*
+ * Mean-pooled chunk keys (summary §3.1: each chunk is represented by the mean of its keys;
+ * slides, slide 11; write-up 計算效率: on-the-fly segmented mean).
+ *   kbar[b,h,c,:] = RN32( RN64(sum_{t in chunk c} K[b,h,t,:]) / n_c ): the sum is accumulated
+ *   in double-double (exact for every bf16 input and for fp32 inputs whose exponents span
+ *   < ~80 binades), divided once in binary64 and rounded to nearest-even binary32.
+ *   K: [B,H,L,d] layout dtype. kbar: device float [B,H,C,d], fully overwritten.
+ */
+moc_status moc_pool_keys(const moc_layout *lay, const void *K, float *kbar, void *stream);
+
+/*
+ * Routing (summary §3.1-3.2; write-up 計算效率: mandatory links are masked before top-k).
+ * For each (b,h,t): candidates are chunks c that are not text, not in the query's own shot,
+ * and (causal) c < chunk(t); score s_c = q_t . kbar_c (binary32 accumulation of exact
+ * products); the min(top_k, #candidates) highest scores are kept (an exact tie keeps the
+ * lower chunk id); then drop-off and drop-in are applied when enabled.
+ *   sel:  device int32 [B,H,L,S], chunk ids ascending, -1 padded; nsel: int32 [B,H,L].
+ *   ws:   MOC_OP_ROUTE workspace (may be NULL when its size is 0).
+ */
+moc_status moc_route(const moc_layout *lay, const moc_route_cfg *cfg, const void *Q,
+                     const float *kbar, int32_t *sel, int32_t *nsel, void *ws, size_t ws_bytes,
+                     void *stream);
+
+/*
+ * Index inversion (write-up 計算效率: packing the (query, key-group) pairs into one
+ * variable-length attention problem). Turns per-query chunk lists into per-(b,h,chunk) query
+ * buckets (stable: ascending query id), the slot map, routed and anchor work tiles, and
+ *   pair_count[b,h] = sum_t |Omega(t)| (int64, device), Omega = text U own shot U routed chunks.
+ * `out` is filled with pointers into ws (MOC_OP_VARLEN workspace).
+ */
+moc_status moc_build_varlen(const moc_layout *lay, const moc_route_cfg *cfg, const int32_t *sel,
+                            const int32_t *nsel, moc_varlen *out, int64_t *pair_count, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/*
+ * Attention forward over the routed key sets (summary §3.1: Attn(q_i) =
+ * softmax(q_i K_Omega^T / sqrt(d)) V_Omega; no token-level causal mask inside Omega).
+ *   O:   [B,H,L,d] layout dtype; lse: device float [B,H,L], natural-log softmax denominator.
+ *   softmax_scale: > 0 (usually 1/sqrt(d)).
+ *   ws:  MOC_OP_FWD workspace: per-(query, routed chunk) partial results in fp32.
+ *   O and lse must not alias Q, K or V.
+ */
+moc_status moc_attend_fwd(const moc_layout *lay, const moc_varlen *vl, const void *Q,
+                          const void *K, const void *V, float softmax_scale, void *O, float *lse,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Attention backward with the routed sets held fixed (summary §3.1 and Appendix A: top-k is
+ * not differentiable; gradients reach the selected keys and values only).
+ *   Inputs: Q, K, V, O, lse from moc_attend_fwd, dO. Outputs dQ, dK, dV [B,H,L,d] in the
+ *   layout dtype, fully overwritten. ws: MOC_OP_BWD workspace (fp32 accumulators).
+ */
+moc_status moc_attend_bwd(const moc_layout *lay, const moc_varlen *vl, const void *Q,
+                          const void *K, const void *V, const void *O, const float *lse,
+                          const void *dO, float softmax_scale, void *dQ, void *dK, void *dV,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/* Host-side helper: the drop-in Poisson thresholds the routing kernel uses,
+ * thr[i] = min(2^32, floor(2^32 * P(m <= i))) for i < max_drop_in (binary64, C library exp). */
+moc_status moc_poisson_thresholds(float lambda, int32_t max_drop_in, uint64_t *thr);
+
+const char *moc_status_string(moc_status s);
+/* Message of the last non-OK status returned on the calling thread. */
+const char *moc_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOC_H_ */

@@ -1,0 +1,17 @@
+"""Mixture-of-Contexts (MoC) attention layer for AMD MI355X (gfx950).
+
+The layer's steps run in hand-written HIP kernels behind the C ABI of libmoc.so
+(include/moc.h); this package loads that library and exposes the same entry points for torch
+tensors. Importing it fails if libmoc.so has not been built.
+"""
+from . import _lib
+from ._lib import MocError, load
+from .api import (DeviceLayout, ForwardResult, MoCAttention, RouteCfg, Varlen, attend_bwd,
+                  attend_fwd, build_varlen, forward, pool_keys, route, sel_width, validate_layout,
+                  workspace_bytes)
+
+load()
+
+__all__ = ["DeviceLayout", "ForwardResult", "MoCAttention", "MocError", "RouteCfg", "Varlen",
+           "attend_bwd", "attend_fwd", "build_varlen", "forward", "pool_keys", "route",
+           "sel_width", "validate_layout", "workspace_bytes"]

@@ -1,0 +1,94 @@
+"""ctypes view of libmoc.so (include/moc.h). Marshalling only: no arithmetic of the layer here."""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_uint64, c_void_p
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoc.so")
+
+MOC_OK, MOC_EINVAL, MOC_ESHAPE, MOC_EDTYPE, MOC_EWORKSPACE, MOC_EUNSUPPORTED, MOC_EHIP, \
+    MOC_EINTERNAL = range(8)
+MOC_F32, MOC_BF16 = 0, 1
+MOC_OP_ROUTE, MOC_OP_VARLEN, MOC_OP_FWD, MOC_OP_BWD = range(4)
+MOC_MAX_C, MOC_MAX_TOPK, MOC_MAX_DROP_IN = 1024, 32, 16
+
+# every function include/moc.h declares
+EXPORTS = (
+    "moc_sel_width", "moc_workspace_bytes", "moc_pool_keys", "moc_route", "moc_build_varlen",
+    "moc_attend_fwd", "moc_attend_bwd", "moc_poisson_thresholds", "moc_status_string",
+    "moc_last_error",
+)
+
+
+class MocLayout(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("H", c_int32), ("L", c_int32), ("d", c_int32),
+                ("dtype", c_int32), ("C", c_int32), ("chunk_offsets", c_void_p),
+                ("chunk_shot", c_void_p), ("text_begin", c_int32), ("text_end", c_int32)]
+
+
+class MocRouteCfg(ctypes.Structure):
+    _fields_ = [("top_k", c_int32), ("causal", c_int32), ("p_max", c_float), ("lambda_", c_float),
+                ("max_drop_in", c_int32), ("reserved", c_int32), ("seed", c_uint64)]
+
+
+class MocVarlen(ctypes.Structure):
+    _fields_ = [("S", c_int32), ("tile_rows", c_int32), ("max_rtiles", c_int32),
+                ("max_atiles", c_int32), ("bucket_off", c_void_p), ("bucket_q", c_void_p),
+                ("slot", c_void_p), ("rtiles", c_void_p), ("n_rtiles", c_void_p),
+                ("atiles", c_void_p), ("n_atiles", c_void_p), ("scratch", c_void_p)]
+
+
+class MocError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libmoc.so (built in-tree by `python -m sparse_chunk_routed_amd.build`). There is no
+    fallback: a missing library is an error."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing; build it with "
+                          "`python -m sparse_chunk_routed_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = POINTER
+    lib.moc_sel_width.argtypes = [P(MocRouteCfg), c_int32]
+    lib.moc_sel_width.restype = c_int32
+    lib.moc_workspace_bytes.argtypes = [P(MocLayout), P(MocRouteCfg), c_int32]
+    lib.moc_workspace_bytes.restype = c_size_t
+    lib.moc_pool_keys.argtypes = [P(MocLayout), c_void_p, c_void_p, c_void_p]
+    lib.moc_pool_keys.restype = c_int32
+    lib.moc_route.argtypes = [P(MocLayout), P(MocRouteCfg), c_void_p, c_void_p, c_void_p,
+                              c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.moc_route.restype = c_int32
+    lib.moc_build_varlen.argtypes = [P(MocLayout), P(MocRouteCfg), c_void_p, c_void_p,
+                                     P(MocVarlen), c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.moc_build_varlen.restype = c_int32
+    lib.moc_attend_fwd.argtypes = [P(MocLayout), P(MocVarlen), c_void_p, c_void_p, c_void_p,
+                                   c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.moc_attend_fwd.restype = c_int32
+    lib.moc_attend_bwd.argtypes = [P(MocLayout), P(MocVarlen), c_void_p, c_void_p, c_void_p,
+                                   c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p,
+                                   c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.moc_attend_bwd.restype = c_int32
+    lib.moc_poisson_thresholds.argtypes = [c_float, c_int32, P(c_uint64)]
+    lib.moc_poisson_thresholds.restype = c_int32
+    lib.moc_status_string.argtypes = [c_int32]
+    lib.moc_status_string.restype = c_char_p
+    lib.moc_last_error.argtypes = []
+    lib.moc_last_error.restype = c_char_p
+    _lib = lib
+    return lib
+
+
+def check(status: int) -> None:
+    if status != MOC_OK:
+        lib = load()
+        raise MocError(status, lib.moc_last_error().decode(errors="replace"))

@@ -1,0 +1,295 @@
+"""Python surface of libmoc: the C-ABI entry points with the same names, taking torch tensors.
+
+torch supplies device memory and the current HIP stream; every step of the layer runs in the
+library's HIP kernels. Nothing here computes any part of the layer.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return L.MOC_BF16
+    if dt == torch.float32:
+        return L.MOC_F32
+    raise TypeError(f"unsupported dtype {dt} (bfloat16 or float32)")
+
+
+class DeviceLayout:
+    """A token layout resident on the device: chunk offsets [C+1], chunk shot ids [C]
+    (-1 = text) and the text range. The content is validated here on the host copy, since the
+    library treats it as a precondition."""
+
+    def __init__(self, chunk_offsets: Sequence[int], chunk_shot: Sequence[int], text_begin: int,
+                 text_end: int, device="cuda"):
+        off = np.asarray(chunk_offsets, dtype=np.int64)
+        shot = np.asarray(chunk_shot, dtype=np.int64)
+        validate_layout(off, shot, int(text_begin), int(text_end))
+        self.C = int(len(shot))
+        self.L = int(off[-1])
+        self.text_begin, self.text_end = int(text_begin), int(text_end)
+        self.offsets_host = off.astype(np.int32)
+        self.shot_host = shot.astype(np.int32)
+        self.offsets = torch.from_numpy(self.offsets_host.copy()).to(device)
+        self.shot = torch.from_numpy(self.shot_host.copy()).to(device)
+
+    @classmethod
+    def from_layout(cls, lay, device="cuda") -> "DeviceLayout":
+        return cls(lay.chunk_offsets, lay.chunk_shot, lay.text_begin, lay.text_end, device)
+
+    def struct(self, B: int, H: int, d: int, dtype: torch.dtype) -> L.MocLayout:
+        return L.MocLayout(B, H, self.L, d, _dtype_code(dtype), self.C, self.offsets.data_ptr(),
+                           self.shot.data_ptr(), self.text_begin, self.text_end)
+
+
+def validate_layout(off: np.ndarray, shot: np.ndarray, tb: int, te: int) -> None:
+    C = len(shot)
+    if C < 1 or len(off) != C + 1 or off[0] != 0 or np.any(np.diff(off) <= 0):
+        raise ValueError("chunk offsets must be 0 = off[0] < off[1] < ... < off[C]")
+    if C > L.MOC_MAX_C:
+        raise ValueError(f"at most {L.MOC_MAX_C} chunks")
+    Ltot = int(off[-1])
+    if not (0 <= tb <= te <= Ltot):
+        raise ValueError("text range outside the sequence")
+    seen, prev = set(), None
+    for c in range(C):
+        a, b = int(off[c]), int(off[c + 1])
+        in_text = tb <= a and b <= te and tb < te
+        if (a < te and tb < b) and not in_text:
+            raise ValueError(f"chunk {c} straddles the text range")
+        if in_text != (shot[c] == -1):
+            raise ValueError(f"chunk {c}: text chunks carry shot -1, and only they")
+        s = int(shot[c])
+        if s == -1:
+            prev = None
+            continue
+        if s < 0:
+            raise ValueError("shot ids must be >= 0 (or -1 for text)")
+        if s != prev:
+            if s in seen:
+                raise ValueError(f"shot {s} is not contiguous")
+            seen.add(s)
+        prev = s
+    if tb < te:
+        idx = np.nonzero(shot == -1)[0]
+        if int(off[idx[0]]) != tb or int(off[idx[-1] + 1]) != te:
+            raise ValueError("text range must be a union of whole chunks")
+
+
+@dataclass
+class RouteCfg:
+    top_k: int
+    causal: bool = True
+    p_max: float = 0.0
+    lam: float = 0.0
+    max_drop_in: int = 8
+    seed: int = 0
+
+    def struct(self) -> L.MocRouteCfg:
+        return L.MocRouteCfg(int(self.top_k), 1 if self.causal else 0, float(self.p_max),
+                             float(self.lam), int(self.max_drop_in), 0,
+                             int(self.seed) & ((1 << 64) - 1))
+
+
+def _check_qkv(*ts: torch.Tensor) -> None:
+    t0 = ts[0]
+    for t in ts:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B,H,L,d]")
+        if t.shape != t0.shape or t.dtype != t0.dtype:
+            raise ValueError("Q/K/V-like tensors must share shape and dtype")
+
+
+def sel_width(cfg: RouteCfg, C: int) -> int:
+    lib = L.load()
+    return int(lib.moc_sel_width(ctypes.byref(cfg.struct()), C))
+
+
+def workspace_bytes(lay: DeviceLayout, B: int, H: int, d: int, dtype: torch.dtype,
+                    cfg: RouteCfg, op: int) -> int:
+    lib = L.load()
+    s = lay.struct(B, H, d, dtype)
+    n = int(lib.moc_workspace_bytes(ctypes.byref(s), ctypes.byref(cfg.struct()), op))
+    if n == 0 and op != L.MOC_OP_ROUTE:
+        raise L.MocError(L.MOC_EINVAL, lib.moc_last_error().decode())
+    return n
+
+
+def pool_keys(K: torch.Tensor, lay: DeviceLayout) -> torch.Tensor:
+    """kbar [B,H,C,d] fp32: the mean of each chunk's keys."""
+    _check_qkv(K)
+    B, H, Lq, d = K.shape
+    kbar = torch.empty((B, H, lay.C, d), dtype=torch.float32, device=K.device)
+    s = lay.struct(B, H, d, K.dtype)
+    lib = L.load()
+    L.check(lib.moc_pool_keys(ctypes.byref(s), _ptr(K), _ptr(kbar), _stream(K.device)))
+    return kbar
+
+
+def route(Q: torch.Tensor, kbar: torch.Tensor, lay: DeviceLayout, cfg: RouteCfg):
+    """(sel [B,H,L,S] int32 ascending, -1 padded; nsel [B,H,L] int32)."""
+    _check_qkv(Q)
+    B, H, Lq, d = Q.shape
+    S = sel_width(cfg, lay.C)
+    sel = torch.empty((B, H, Lq, S), dtype=torch.int32, device=Q.device)
+    nsel = torch.empty((B, H, Lq), dtype=torch.int32, device=Q.device)
+    s = lay.struct(B, H, d, Q.dtype)
+    lib = L.load()
+    L.check(lib.moc_route(ctypes.byref(s), ctypes.byref(cfg.struct()), _ptr(Q), _ptr(kbar),
+                          _ptr(sel) if S > 0 else None, _ptr(nsel), None, 0, _stream(Q.device)))
+    return sel, nsel
+
+
+class Varlen:
+    """The inverted index (per-chunk query buckets, slots, work tiles) and its workspace."""
+
+    def __init__(self, struct: L.MocVarlen, ws: torch.Tensor, pair_count: torch.Tensor,
+                 cfg: RouteCfg, lay: DeviceLayout, B: int, H: int):
+        self.struct = struct
+        self.ws = ws
+        self.pair_count = pair_count
+        self.cfg = cfg
+        self.layout = lay
+        self.B, self.H = B, H
+
+    @property
+    def S(self) -> int:
+        return int(self.struct.S)
+
+    def _view(self, addr: int, n: int) -> torch.Tensor:
+        base = self.ws.data_ptr()
+        off = addr - base
+        assert off % 4 == 0 and 0 <= off and off + 4 * n <= self.ws.numel()
+        return self.ws[off:off + 4 * n].view(torch.int32)
+
+    def bucket_off(self) -> torch.Tensor:
+        return self._view(self.struct.bucket_off, self.B * self.H * self.layout.C + 1)
+
+    def bucket_q(self, total: int) -> torch.Tensor:
+        return self._view(self.struct.bucket_q, total)
+
+    def slot(self, Lq: int) -> torch.Tensor:
+        S = self.S
+        return self._view(self.struct.slot, self.B * self.H * Lq * S).view(self.B, self.H, Lq, S)
+
+    def n_rtiles(self) -> int:
+        return int(self._view(self.struct.n_rtiles, 1).item())
+
+    def n_atiles(self) -> int:
+        return int(self._view(self.struct.n_atiles, 1).item())
+
+
+def build_varlen(sel: torch.Tensor, nsel: torch.Tensor, lay: DeviceLayout, cfg: RouteCfg,
+                 d: int, dtype: torch.dtype) -> Varlen:
+    B, H, Lq = nsel.shape
+    ws_n = workspace_bytes(lay, B, H, d, dtype, cfg, L.MOC_OP_VARLEN)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=nsel.device)
+    pair = torch.empty((B, H), dtype=torch.int64, device=nsel.device)
+    vs = L.MocVarlen()
+    s = lay.struct(B, H, d, dtype)
+    lib = L.load()
+    S = sel_width(cfg, lay.C)
+    L.check(lib.moc_build_varlen(ctypes.byref(s), ctypes.byref(cfg.struct()),
+                                 _ptr(sel) if S > 0 else None, _ptr(nsel), ctypes.byref(vs),
+                                 _ptr(pair), _ptr(ws), ws_n, _stream(nsel.device)))
+    return Varlen(vs, ws, pair, cfg, lay, B, H)
+
+
+def attend_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, lay: DeviceLayout,
+               vl: Varlen, scale: Optional[float] = None, ws: Optional[torch.Tensor] = None):
+    """(O [B,H,L,d] in the input dtype, lse [B,H,L] fp32, natural log)."""
+    _check_qkv(Q, K, V)
+    B, H, Lq, d = Q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    O = torch.empty_like(Q)
+    lse = torch.empty((B, H, Lq), dtype=torch.float32, device=Q.device)
+    need = workspace_bytes(lay, B, H, d, Q.dtype, vl.cfg, L.MOC_OP_FWD)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    s = lay.struct(B, H, d, Q.dtype)
+    lib = L.load()
+    L.check(lib.moc_attend_fwd(ctypes.byref(s), ctypes.byref(vl.struct), _ptr(Q), _ptr(K), _ptr(V),
+                               float(scale), _ptr(O), _ptr(lse), _ptr(ws), ws.numel(),
+                               _stream(Q.device)))
+    return O, lse
+
+
+def attend_bwd(Q, K, V, O, lse, dO, lay: DeviceLayout, vl: Varlen, scale: Optional[float] = None,
+               ws: Optional[torch.Tensor] = None):
+    """(dQ, dK, dV) in the input dtype."""
+    _check_qkv(Q, K, V, O, dO)
+    B, H, Lq, d = Q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dQ = torch.empty_like(Q)
+    dK = torch.empty_like(K)
+    dV = torch.empty_like(V)
+    need = workspace_bytes(lay, B, H, d, Q.dtype, vl.cfg, L.MOC_OP_BWD)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    s = lay.struct(B, H, d, Q.dtype)
+    lib = L.load()
+    L.check(lib.moc_attend_bwd(ctypes.byref(s), ctypes.byref(vl.struct), _ptr(Q), _ptr(K), _ptr(V),
+                               _ptr(O), _ptr(lse), _ptr(dO), float(scale), _ptr(dQ), _ptr(dK),
+                               _ptr(dV), _ptr(ws), ws.numel(), _stream(Q.device)))
+    return dQ, dK, dV
+
+
+@dataclass
+class ForwardResult:
+    O: torch.Tensor
+    lse: torch.Tensor
+    kbar: torch.Tensor
+    sel: torch.Tensor
+    nsel: torch.Tensor
+    varlen: Varlen
+
+
+def forward(Q, K, V, lay: DeviceLayout, cfg: RouteCfg, scale: Optional[float] = None
+            ) -> ForwardResult:
+    """The whole layer: pool -> route -> index inversion -> attention."""
+    kbar = pool_keys(K, lay)
+    sel, nsel = route(Q, kbar, lay, cfg)
+    vl = build_varlen(sel, nsel, lay, cfg, Q.shape[-1], Q.dtype)
+    O, lse = attend_fwd(Q, K, V, lay, vl, scale)
+    return ForwardResult(O, lse, kbar, sel, nsel, vl)
+
+
+class MoCAttention(torch.autograd.Function):
+    """Autograd wrapper: routing is a discrete choice (no gradient); gradients flow to Q, K, V
+    through the attention over the selected keys and values."""
+
+    @staticmethod
+    def forward(ctx, Q, K, V, lay: DeviceLayout, cfg: RouteCfg, scale: Optional[float] = None):
+        r = forward(Q, K, V, lay, cfg, scale)
+        ctx.save_for_backward(Q, K, V, r.O, r.lse)
+        ctx.lay, ctx.vl, ctx.scale = lay, r.varlen, scale
+        return r.O
+
+    @staticmethod
+    def backward(ctx, dO):
+        Q, K, V, O, lse = ctx.saved_tensors
+        dQ, dK, dV = attend_bwd(Q, K, V, O, lse, dO.contiguous(), ctx.lay, ctx.vl, ctx.scale)
+        return dQ, dK, dV, None, None, None

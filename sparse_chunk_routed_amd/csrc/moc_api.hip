@@ -1,0 +1,357 @@
+// Host side of the libmoc C ABI: argument validation, workspace sizing and carving, launches.
+// Every check runs before anything is enqueued; no C++ exception crosses the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "moc.h"
+#include "moc_params.h"
+
+
+namespace moc_host {
+hipError_t launch_pool(const moc_layout* lay, const void* K, float* kbar, hipStream_t st);
+hipError_t launch_route(const moc_layout* lay, const moc::RouteParams& p, const void* Q,
+                        const float* kbar, int32_t* sel, int32_t* nsel, hipStream_t st);
+hipError_t launch_varlen(const moc_layout* lay, const moc::VarlenParams& p, const int32_t* sel,
+                         const int32_t* nsel, int32_t* counts, int32_t* totals,
+                         int32_t* tile_base, const moc_varlen* out, int64_t* pair_count,
+                         hipStream_t st);
+hipError_t launch_attn_fwd(const moc_layout* lay, const moc_varlen* vl, const void* Q,
+                           const void* K, const void* V, float scale, void* O, float* lse,
+                           float* pO, float* plse, hipStream_t st);
+hipError_t launch_attn_bwd(const moc_layout* lay, const moc_varlen* vl, const void* Q,
+                           const void* K, const void* V, const void* O, const float* lse,
+                           const void* dO, float scale, void* dQ, void* dK, void* dV,
+                           void* ws, size_t ws_bytes, hipStream_t st);
+size_t attn_bwd_workspace(const moc_layout* lay, int S);
+}  // namespace moc_host
+
+namespace {
+
+constexpr int kTileRows = 128;   // queries per attention work tile
+constexpr int kInvTile = 256;    // queries per inversion tile
+constexpr size_t kAlign = 256;
+
+thread_local std::string g_last_error;
+
+moc_status fail(moc_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = std::string(moc_status_string(s)) + ": " + buf;
+  return s;
+}
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+moc_status check_layout(const moc_layout* lay) {
+  if (!lay) return fail(MOC_EINVAL, "layout is NULL");
+  if (lay->dtype != MOC_F32 && lay->dtype != MOC_BF16)
+    return fail(MOC_EDTYPE, "dtype %d is neither MOC_F32 nor MOC_BF16", lay->dtype);
+  if (lay->B < 1 || lay->H < 1 || lay->L < 1)
+    return fail(MOC_ESHAPE, "B, H, L must be >= 1 (got %d, %d, %d)", lay->B, lay->H, lay->L);
+  if (lay->d != 64 && lay->d != 128) return fail(MOC_ESHAPE, "d must be 64 or 128 (got %d)", lay->d);
+  if (lay->C < 1 || lay->C > MOC_MAX_C || lay->C > lay->L)
+    return fail(MOC_ESHAPE, "C must be in [1, min(L, %d)] (got %d)", MOC_MAX_C, lay->C);
+  if (!lay->chunk_offsets || !lay->chunk_shot) return fail(MOC_EINVAL, "layout arrays are NULL");
+  if (lay->text_begin < 0 || lay->text_end < lay->text_begin || lay->text_end > lay->L)
+    return fail(MOC_EINVAL, "text range [%d, %d) outside [0, %d]", lay->text_begin, lay->text_end,
+                lay->L);
+  const int64_t elems = static_cast<int64_t>(lay->B) * lay->H * lay->L * lay->d;
+  if (elems >= (int64_t(1) << 40)) return fail(MOC_ESHAPE, "tensor too large");
+  return MOC_OK;
+}
+
+int k_eff_of(const moc_route_cfg* cfg, int C) { return cfg->top_k < C ? cfg->top_k : C; }
+
+moc_status check_cfg(const moc_layout* lay, const moc_route_cfg* cfg) {
+  if (!cfg) return fail(MOC_EINVAL, "route cfg is NULL");
+  if (cfg->top_k < 0) return fail(MOC_EINVAL, "top_k must be >= 0 (got %d)", cfg->top_k);
+  if (cfg->causal != 0 && cfg->causal != 1) return fail(MOC_EINVAL, "causal must be 0 or 1");
+  if (k_eff_of(cfg, lay->C) > MOC_MAX_TOPK)
+    return fail(MOC_ESHAPE, "min(top_k, C) = %d exceeds %d", k_eff_of(cfg, lay->C), MOC_MAX_TOPK);
+  if (!(cfg->p_max >= 0.f && cfg->p_max <= 1.f))
+    return fail(MOC_EINVAL, "p_max must be in [0, 1]");
+  if (!(cfg->lambda >= 0.f) || !std::isfinite(cfg->lambda))
+    return fail(MOC_EINVAL, "lambda must be finite and >= 0");
+  if (cfg->max_drop_in < 0 || cfg->max_drop_in > MOC_MAX_DROP_IN)
+    return fail(MOC_ESHAPE, "max_drop_in must be in [0, %d]", MOC_MAX_DROP_IN);
+  const int S = moc_sel_width(cfg, lay->C);
+  const int64_t rows = static_cast<int64_t>(lay->B) * lay->H * lay->L * (S > 0 ? S : 1);
+  if (rows >= (int64_t(1) << 31)) return fail(MOC_ESHAPE, "B*H*L*S must be < 2^31");
+  return MOC_OK;
+}
+
+struct VarlenSizes {
+  size_t counts, totals, tile_base, bucket_off, bucket_q, slot, rtiles, n_rtiles, atiles, n_atiles;
+  int max_rtiles, max_atiles, nqt;
+  size_t total() const {
+    return counts + totals + tile_base + bucket_off + bucket_q + slot + rtiles + n_rtiles + atiles +
+           n_atiles;
+  }
+};
+
+VarlenSizes varlen_sizes(const moc_layout* lay, int S) {
+  VarlenSizes z;
+  const int64_t BH = static_cast<int64_t>(lay->B) * lay->H;
+  const int64_t NB = BH * lay->C;
+  const int64_t sel = BH * lay->L * S;
+  z.nqt = (lay->L + kInvTile - 1) / kInvTile;
+  z.max_rtiles = static_cast<int>((sel + kTileRows - 1) / kTileRows + NB);
+  z.max_atiles = (lay->L + kTileRows - 1) / kTileRows + lay->C + 1;
+  z.counts = align_up(sizeof(int32_t) * NB * z.nqt);
+  z.totals = align_up(sizeof(int32_t) * NB);
+  z.tile_base = align_up(sizeof(int32_t) * NB);
+  z.bucket_off = align_up(sizeof(int32_t) * (NB + 1));
+  z.bucket_q = align_up(sizeof(int32_t) * (sel > 0 ? sel : 1));
+  z.slot = align_up(sizeof(int32_t) * (sel > 0 ? sel : 1));
+  z.rtiles = align_up(sizeof(int32_t) * 2 * z.max_rtiles);
+  z.n_rtiles = kAlign;
+  z.atiles = align_up(sizeof(int32_t) * 6 * z.max_atiles);
+  z.n_atiles = kAlign;
+  return z;
+}
+
+size_t fwd_bytes(const moc_layout* lay, int S) {
+  const int64_t rows = static_cast<int64_t>(lay->B) * lay->H * lay->L * S;
+  const int64_t r = rows > 0 ? rows : 1;
+  return align_up(sizeof(float) * r * lay->d) + align_up(sizeof(float) * r);
+}
+
+moc_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOC_OK;
+  return fail(MOC_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moc_status_string(moc_status s) {
+  switch (s) {
+    case MOC_OK: return "MOC_OK";
+    case MOC_EINVAL: return "MOC_EINVAL";
+    case MOC_ESHAPE: return "MOC_ESHAPE";
+    case MOC_EDTYPE: return "MOC_EDTYPE";
+    case MOC_EWORKSPACE: return "MOC_EWORKSPACE";
+    case MOC_EUNSUPPORTED: return "MOC_EUNSUPPORTED";
+    case MOC_EHIP: return "MOC_EHIP";
+    case MOC_EINTERNAL: return "MOC_EINTERNAL";
+  }
+  return "MOC_UNKNOWN";
+}
+
+const char* moc_last_error(void) { return g_last_error.c_str(); }
+
+int32_t moc_sel_width(const moc_route_cfg* cfg, int32_t C) {
+  if (!cfg || C < 1) return 0;
+  const int k = cfg->top_k < 0 ? 0 : (cfg->top_k < C ? cfg->top_k : C);
+  return k + (cfg->lambda > 0.f ? cfg->max_drop_in : 0);
+}
+
+moc_status moc_poisson_thresholds(float lambda, int32_t max_drop_in, uint64_t* thr) {
+  if (!thr) return fail(MOC_EINVAL, "thr is NULL");
+  if (max_drop_in < 0 || max_drop_in > MOC_MAX_DROP_IN)
+    return fail(MOC_ESHAPE, "max_drop_in must be in [0, %d]", MOC_MAX_DROP_IN);
+  if (!(lambda >= 0.f) || !std::isfinite(lambda)) return fail(MOC_EINVAL, "bad lambda");
+  // CDF of Poisson(lambda) accumulated term by term in binary64, in the order written.
+  const double lam = static_cast<double>(lambda);
+  double term = std::exp(-lam);
+  double cdf = term;
+  for (int i = 0; i < max_drop_in; ++i) {
+    if (i > 0) {
+      term = term * lam / static_cast<double>(i);
+      cdf = cdf + term;
+    }
+    double v = std::floor(cdf * 4294967296.0);
+    uint64_t u = static_cast<uint64_t>(v);
+    thr[i] = u > (uint64_t(1) << 32) ? (uint64_t(1) << 32) : u;
+  }
+  return MOC_OK;
+}
+
+size_t moc_workspace_bytes(const moc_layout* lay, const moc_route_cfg* cfg, int32_t op) {
+  if (check_layout(lay) != MOC_OK) return 0;
+  if (check_cfg(lay, cfg) != MOC_OK) return 0;
+  const int S = moc_sel_width(cfg, lay->C);
+  switch (op) {
+    case MOC_OP_ROUTE: return 0;
+    case MOC_OP_VARLEN: return varlen_sizes(lay, S).total();
+    case MOC_OP_FWD: return fwd_bytes(lay, S);
+    case MOC_OP_BWD: return moc_host::attn_bwd_workspace(lay, S);
+    default: fail(MOC_EINVAL, "unknown op %d", op); return 0;
+  }
+}
+
+moc_status moc_pool_keys(const moc_layout* lay, const void* K, float* kbar, void* stream) {
+  try {
+    moc_status s = check_layout(lay);
+    if (s != MOC_OK) return s;
+    if (!K || !kbar) return fail(MOC_EINVAL, "K or kbar is NULL");
+    if (static_cast<const void*>(kbar) == K) return fail(MOC_EINVAL, "kbar aliases K");
+    return hip_status(moc_host::launch_pool(lay, K, kbar, static_cast<hipStream_t>(stream)),
+                      "pool launch");
+  } catch (...) {
+    return fail(MOC_EINTERNAL, "exception in moc_pool_keys");
+  }
+}
+
+moc_status moc_route(const moc_layout* lay, const moc_route_cfg* cfg, const void* Q,
+                     const float* kbar, int32_t* sel, int32_t* nsel, void* ws, size_t ws_bytes,
+                     void* stream) {
+  try {
+    moc_status s = check_layout(lay);
+    if (s != MOC_OK) return s;
+    s = check_cfg(lay, cfg);
+    if (s != MOC_OK) return s;
+    const int S = moc_sel_width(cfg, lay->C);
+    if (!Q || !kbar || !nsel || (S > 0 && !sel)) return fail(MOC_EINVAL, "NULL tensor argument");
+    if (static_cast<void*>(sel) == static_cast<void*>(nsel) && S > 0)
+      return fail(MOC_EINVAL, "sel aliases nsel");
+    (void)ws;
+    (void)ws_bytes;
+    moc::RouteParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.B = lay->B; p.H = lay->H; p.L = lay->L; p.C = lay->C; p.S = S;
+    p.k_eff = k_eff_of(cfg, lay->C);
+    p.causal = cfg->causal;
+    p.drop_off = cfg->p_max > 0.f ? 1 : 0;
+    p.drop_in = cfg->lambda > 0.f ? 1 : 0;
+    p.m_cap = p.drop_in ? cfg->max_drop_in : 0;
+    p.p_max = cfg->p_max;
+    p.seed = cfg->seed;
+    if (p.drop_in) {
+      s = moc_poisson_thresholds(cfg->lambda, cfg->max_drop_in, p.thr);
+      if (s != MOC_OK) return s;
+    }
+    return hip_status(moc_host::launch_route(lay, p, Q, kbar, sel, nsel,
+                                             static_cast<hipStream_t>(stream)),
+                      "route launch");
+  } catch (...) {
+    return fail(MOC_EINTERNAL, "exception in moc_route");
+  }
+}
+
+moc_status moc_build_varlen(const moc_layout* lay, const moc_route_cfg* cfg, const int32_t* sel,
+                            const int32_t* nsel, moc_varlen* out, int64_t* pair_count, void* ws,
+                            size_t ws_bytes, void* stream) {
+  try {
+    moc_status s = check_layout(lay);
+    if (s != MOC_OK) return s;
+    s = check_cfg(lay, cfg);
+    if (s != MOC_OK) return s;
+    const int S = moc_sel_width(cfg, lay->C);
+    if (!nsel || !out || !pair_count || (S > 0 && !sel))
+      return fail(MOC_EINVAL, "NULL argument");
+    const VarlenSizes z = varlen_sizes(lay, S);
+    if (!ws || ws_bytes < z.total())
+      return fail(MOC_EWORKSPACE, "VARLEN workspace needs %zu bytes (got %zu)", z.total(),
+                  ws ? ws_bytes : size_t(0));
+    char* w = static_cast<char*>(ws);
+    int32_t* counts = reinterpret_cast<int32_t*>(w); w += z.counts;
+    int32_t* totals = reinterpret_cast<int32_t*>(w); w += z.totals;
+    int32_t* tile_base = reinterpret_cast<int32_t*>(w); w += z.tile_base;
+    out->bucket_off = reinterpret_cast<int32_t*>(w); w += z.bucket_off;
+    out->bucket_q = reinterpret_cast<int32_t*>(w); w += z.bucket_q;
+    out->slot = reinterpret_cast<int32_t*>(w); w += z.slot;
+    out->rtiles = reinterpret_cast<int32_t*>(w); w += z.rtiles;
+    out->n_rtiles = reinterpret_cast<int32_t*>(w); w += z.n_rtiles;
+    out->atiles = reinterpret_cast<int32_t*>(w); w += z.atiles;
+    out->n_atiles = reinterpret_cast<int32_t*>(w); w += z.n_atiles;
+    out->scratch = counts;
+    out->S = S;
+    out->tile_rows = kTileRows;
+    out->max_rtiles = z.max_rtiles;
+    out->max_atiles = z.max_atiles;
+    moc::VarlenParams p;
+    p.B = lay->B; p.H = lay->H; p.L = lay->L; p.C = lay->C; p.S = S; p.nqt = z.nqt;
+    p.tile_rows = kTileRows; p.max_rtiles = z.max_rtiles; p.max_atiles = z.max_atiles;
+    p.text_begin = lay->text_begin; p.text_end = lay->text_end;
+    return hip_status(moc_host::launch_varlen(lay, p, sel, nsel, counts, totals, tile_base, out,
+                                              pair_count, static_cast<hipStream_t>(stream)),
+                      "varlen launch");
+  } catch (...) {
+    return fail(MOC_EINTERNAL, "exception in moc_build_varlen");
+  }
+}
+
+static moc_status check_varlen(const moc_layout* lay, const moc_varlen* vl) {
+  if (!vl) return fail(MOC_EINVAL, "varlen is NULL");
+  if (vl->S < 0 || vl->tile_rows != kTileRows || !vl->bucket_off || !vl->bucket_q || !vl->slot ||
+      !vl->rtiles || !vl->n_rtiles || !vl->atiles || !vl->n_atiles)
+    return fail(MOC_EINVAL, "varlen struct not filled by moc_build_varlen");
+  const VarlenSizes z = varlen_sizes(lay, vl->S);
+  if (vl->max_rtiles != z.max_rtiles || vl->max_atiles != z.max_atiles)
+    return fail(MOC_EINVAL, "varlen struct built for another layout");
+  return MOC_OK;
+}
+
+moc_status moc_attend_fwd(const moc_layout* lay, const moc_varlen* vl, const void* Q,
+                          const void* K, const void* V, float softmax_scale, void* O, float* lse,
+                          void* ws, size_t ws_bytes, void* stream) {
+  try {
+    moc_status s = check_layout(lay);
+    if (s != MOC_OK) return s;
+    s = check_varlen(lay, vl);
+    if (s != MOC_OK) return s;
+    if (!Q || !K || !V || !O || !lse) return fail(MOC_EINVAL, "NULL tensor argument");
+    if (O == Q || O == K || O == V || static_cast<const void*>(lse) == Q ||
+        static_cast<const void*>(lse) == K || static_cast<const void*>(lse) == V)
+      return fail(MOC_EINVAL, "outputs alias inputs");
+    if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+      return fail(MOC_EINVAL, "softmax_scale must be finite and > 0");
+    const size_t need = fwd_bytes(lay, vl->S);
+    if (!ws || ws_bytes < need)
+      return fail(MOC_EWORKSPACE, "FWD workspace needs %zu bytes (got %zu)", need,
+                  ws ? ws_bytes : size_t(0));
+    const int64_t rows = static_cast<int64_t>(lay->B) * lay->H * lay->L * vl->S;
+    float* pO = static_cast<float*>(ws);
+    float* plse = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                           align_up(sizeof(float) * (rows > 0 ? rows : 1) * lay->d));
+    return hip_status(moc_host::launch_attn_fwd(lay, vl, Q, K, V, softmax_scale, O, lse, pO, plse,
+                                                static_cast<hipStream_t>(stream)),
+                      "attention forward launch");
+  } catch (...) {
+    return fail(MOC_EINTERNAL, "exception in moc_attend_fwd");
+  }
+}
+
+moc_status moc_attend_bwd(const moc_layout* lay, const moc_varlen* vl, const void* Q,
+                          const void* K, const void* V, const void* O, const float* lse,
+                          const void* dO, float softmax_scale, void* dQ, void* dK, void* dV,
+                          void* ws, size_t ws_bytes, void* stream) {
+  try {
+    moc_status s = check_layout(lay);
+    if (s != MOC_OK) return s;
+    s = check_varlen(lay, vl);
+    if (s != MOC_OK) return s;
+    if (!Q || !K || !V || !O || !lse || !dO || !dQ || !dK || !dV)
+      return fail(MOC_EINVAL, "NULL tensor argument");
+    const void* ins[] = {Q, K, V, O, lse, dO};
+    const void* outs[] = {dQ, dK, dV};
+    for (const void* a : outs)
+      for (const void* b : ins)
+        if (a == b) return fail(MOC_EINVAL, "outputs alias inputs");
+    if (dQ == dK || dQ == dV || dK == dV) return fail(MOC_EINVAL, "gradient outputs alias");
+    if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+      return fail(MOC_EINVAL, "softmax_scale must be finite and > 0");
+    const size_t need = moc_host::attn_bwd_workspace(lay, vl->S);
+    if (!ws || ws_bytes < need)
+      return fail(MOC_EWORKSPACE, "BWD workspace needs %zu bytes (got %zu)", need,
+                  ws ? ws_bytes : size_t(0));
+    hipError_t e = moc_host::launch_attn_bwd(lay, vl, Q, K, V, O, lse, dO, softmax_scale, dQ, dK,
+                                             dV, ws, ws_bytes, static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported) return fail(MOC_EUNSUPPORTED, "backward not available");
+    return hip_status(e, "attention backward launch");
+  } catch (...) {
+    return fail(MOC_EINTERNAL, "exception in moc_attend_bwd");
+  }
+}
+
+}  // extern "C"

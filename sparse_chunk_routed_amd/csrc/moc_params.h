@@ -1,0 +1,23 @@
+// Kernel parameter blocks shared by the host API and the kernels (passed by value).
+#pragma once
+
+#include <stdint.h>
+
+#include "moc.h"
+
+namespace moc {
+
+struct RouteParams {
+  int B, H, L, C, S, k_eff, causal, m_cap;
+  int drop_off, drop_in;
+  float p_max;
+  uint64_t seed;
+  uint64_t thr[MOC_MAX_DROP_IN];  // drop-in Poisson CDF thresholds (x 2^32)
+};
+
+struct VarlenParams {
+  int B, H, L, C, S, nqt, tile_rows, max_rtiles, max_atiles;
+  int text_begin, text_end;
+};
+
+}  // namespace moc
