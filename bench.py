@@ -37,7 +37,23 @@ def parse(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=192,
                     help="query rows of the oracle attention sample (one head)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (calibrates the HBM "
+                         "byte counters of a profiler against a known traffic)")
     return ap.parse_args(argv)
+
+
+def copy_calibration() -> int:
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                      "launches": 3}), flush=True)
+    return 0
 
 
 def cpu_baseline(w, Q, K, V, rows_n: int):
@@ -77,6 +93,8 @@ def cpu_baseline(w, Q, K, V, rows_n: int):
 
 def main(argv=None) -> int:
     a = parse(argv)
+    if a.copy_calibration:
+        return copy_calibration()
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         return 2

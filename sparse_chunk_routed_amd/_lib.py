@@ -5,7 +5,8 @@ import ctypes
 import os
 from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_uint64, c_void_p
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoc.so")
+LIB_PATH = os.environ.get("MOC_LIB_PATH") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libmoc.so")
 
 MOC_OK, MOC_EINVAL, MOC_ESHAPE, MOC_EDTYPE, MOC_EWORKSPACE, MOC_EUNSUPPORTED, MOC_EHIP, \
     MOC_EINTERNAL = range(8)

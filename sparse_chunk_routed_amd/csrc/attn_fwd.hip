@@ -9,19 +9,30 @@
 //
 // Omega(t) = text range U own-shot range U routed chunks, which are disjoint, so the softmax
 // over Omega is the log-sum-exp merge of independent partial softmaxes:
-//   K4a (routed): one workgroup per tile of <= 128 queries gathered from one (b, h, chunk)
+//   K4a (routed): one workgroup per tile of <= 256 queries gathered from one (b, h, chunk)
 //        bucket; the chunk's K/V are streamed once per tile; writes a normalised partial
-//        output row and its LSE for each (query, routed chunk) into the workspace.
-//   K4b (anchor): one workgroup per tile of <= 128 consecutive queries of one shot (or the
+//        output row and its base-2 LSE for each (query, routed chunk) into the workspace.
+//   K4b (anchor): one workgroup per tile of <= 256 consecutive queries of one shot (or the
 //        text); streams text keys then own-shot keys; the epilogue merges the query's routed
 //        partials in ascending chunk order (deterministic) and writes O and LSE.
-// Both are exp2-domain online-softmax flash loops on MFMA (see attn_common.h), 4 waves x 32
-// queries, 64-key tiles staged through LDS with the next tile's global loads in flight.
+// Both are exp2-domain online-softmax flash loops on MFMA (see attn_common.h): 4 waves x 64
+// queries (two 32-query MFMA blocks per wave), 64-key tiles in a double-buffered LDS ring with
+// the global loads issued two tiles ahead (one barrier per tile), and lazy rescaling of the
+// running max (only when it grows by more than 2^8).
 #include "attn_common.h"
 
 namespace moc {
 
-constexpr int kBM = 128;  // queries per workgroup
+#ifndef MOC_ATTN_QB
+#define MOC_ATTN_QB 1
+#endif
+#ifndef MOC_ATTN_NW
+#define MOC_ATTN_NW 8
+#endif
+constexpr int kQB = MOC_ATTN_QB;       // 32-query blocks per wave
+constexpr int kNW = MOC_ATTN_NW;       // waves per workgroup
+constexpr int kNT = 64 * kNW;          // threads per workgroup
+constexpr int kBM = kNW * 32 * kQB;    // queries per workgroup
 
 struct AttnParams {
   int B, H, L, C, S;
@@ -32,17 +43,16 @@ struct AttnParams {
 enum { MODE_ANCHOR = 0, MODE_ROUTED = 1 };
 
 template <typename T, int D, int MODE>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(
+__global__ __launch_bounds__(kNT) void attn_fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int32_t* __restrict__ off, AttnParams p, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ bucket_off,
     const int32_t* __restrict__ bucket_q, const int32_t* __restrict__ slot,
     float* __restrict__ pO, float* __restrict__ plse, T* __restrict__ O,
     float* __restrict__ lse) {
-  using TL = Tiles<T, D>;
-  __shared__ __attribute__((aligned(16))) T lds[TL::LDS_ELEMS];
-  T* Ks = lds;
-  T* Vt = lds + kBN * TL::KSTR;
+  using TL = Tiles<T, D, kNT>;
+  constexpr int QB = kQB;
+  __shared__ __attribute__((aligned(16))) T lds[2 * TL::STAGE];
 
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   int bh, q_lo, nq;            // tile queries: bucket positions or consecutive tokens
@@ -71,149 +81,188 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int ql = lane & 31, g = lane >> 5;
-  const int r = wv * 32 + ql;   // query row within the tile
-  const bool valid = r < nq;
-  int t;
-  if constexpr (MODE == MODE_ANCHOR) {
-    t = q_lo + (valid ? r : nq - 1);
-  } else {
-    t = bucket_q[bstart + (valid ? r : nq - 1)];
+  int rows[QB];
+  int tok[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    rows[qb] = wv * 32 * QB + qb * 32 + ql;
+    const int rr = rows[qb] < nq ? rows[qb] : nq - 1;
+    if constexpr (MODE == MODE_ANCHOR) tok[qb] = q_lo + rr;
+    else tok[qb] = bucket_q[bstart + rr];
   }
 
   const size_t bh_off = static_cast<size_t>(bh) * p.L * D;
   const T* Kbh = K + bh_off;
   const T* Vbh = V + bh_off;
-  QFrag<T, D> qf;
-  qf.load(Q + bh_off + static_cast<size_t>(t) * D, g);
-
-  f32x16 acc[D / 32];
+  QFrag<T, D> qf[QB];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
-  float m = -__builtin_inff();
-  float lsum = 0.f;
+  for (int qb = 0; qb < QB; ++qb) qf[qb].load(Q + bh_off + static_cast<size_t>(tok[qb]) * D, g);
+
+  f32x16 acc[QB][D / 32];
+  float m_ref[QB], lsum[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) acc[qb][db] = f32x16{};
+    m_ref[qb] = -__builtin_inff();
+    lsum[qb] = 0.f;
+  }
+  const float c2 = p.scale_log2;
 
   const int n1 = (r1b - r1a + kBN - 1) / kBN;
   const int n2 = (r2b - r2a + kBN - 1) / kBN;
   const int ntot = n1 + n2;
-
-  TileRegs<T, D> regs;
   auto tile_pos = [&](int j, int& key0, int& kend) {
     if (j < n1) { key0 = r1a + j * kBN; kend = r1b; }
     else { key0 = r2a + (j - n1) * kBN; kend = r2b; }
   };
+
+  TileRegs<T, D, kNT> regs;
   {
     int key0, kend;
     tile_pos(0, key0, kend);
     regs.load(Kbh, Vbh, key0, kend);
-    regs.store(Ks, Vt);
+    regs.store(lds, lds + kBN * TL::KSTR);
+    if (ntot > 1) {
+      tile_pos(1, key0, kend);
+      regs.load(Kbh, Vbh, key0, kend);
+    }
   }
   __syncthreads();
 
   for (int j = 0; j < ntot; ++j) {
+    T* cur = lds + (j & 1) * TL::STAGE;
+    if (j + 1 < ntot) {
+      T* nxt = lds + ((j + 1) & 1) * TL::STAGE;
+      regs.store(nxt, nxt + kBN * TL::KSTR);
+    }
+    if (j + 2 < ntot) {
+      int key0, kend;
+      tile_pos(j + 2, key0, kend);
+      regs.load(Kbh, Vbh, key0, kend);
+    }
+    const T* Ks = cur;
+    const T* Vt = cur + kBN * TL::KSTR;
+
+    f32x16 s[QB][2];
+    {
+      f32x16 s0[QB], s1[QB];
+      score_blocks<D, QB>(Ks, qf, 0, ql, g, s0);
+      score_blocks<D, QB>(Ks, qf, 1, ql, g, s1);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) { s[qb][0] = s0[qb]; s[qb][1] = s1[qb]; }
+    }
     int key0, kend;
     tile_pos(j, key0, kend);
-    const bool has_next = j + 1 < ntot;
-    if (has_next) {
-      int nk0, nke;
-      tile_pos(j + 1, nk0, nke);
-      regs.load(Kbh, Vbh, nk0, nke);
+    const int nvalid = kend - key0;
+    if (nvalid < kBN) {  // ragged last tile of a range: mask keys past its end
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (key_of(kb, i, g) >= nvalid) s[qb][kb][i] = -__builtin_inff();
     }
-    f32x16 s[2];
-    s[0] = score_block<D>(Ks, qf, 0, ql, g);
-    s[1] = score_block<D>(Ks, qf, 1, ql, g);
-    const int nvalid = kend - key0;  // keys at or beyond nvalid are masked
-    float mx = -__builtin_inff();
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = s[qb][0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+      // move the reference max only when this tile exceeds it by more than 2^kRescale
+      if (__builtin_amdgcn_ballot_w64(mx > m_ref[qb] + kRescale)) {
+        const float m_new = fmaxf(m_ref[qb], mx);
+        const float alpha = fast_exp2(m_ref[qb] - m_new);
+        m_ref[qb] = m_new;
+        lsum[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) acc[qb][db] *= alpha;
+      }
+      const float neg = -m_ref[qb];
+      float l0 = 0.f, l1 = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float x = s[kb][i] * p.scale_log2;
-        x = key_of(kb, i, g) < nvalid ? x : -__builtin_inff();
-        s[kb][i] = x;
-        mx = fmaxf(mx, x);
+        const float p0 = fast_exp2(__builtin_fmaf(s[qb][0][i], c2, neg));
+        const float p1 = fast_exp2(__builtin_fmaf(s[qb][1][i], c2, neg));
+        s[qb][0][i] = p0;
+        s[qb][1][i] = p1;
+        l0 += p0;
+        l1 += p1;
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - m_new);
-    m = m_new;
-    lsum *= alpha;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = fast_exp2(s[kb][i] - m);
-        s[kb][i] = pv;
-        lsum += pv;
-      }
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
-    pv_accumulate<D>(Vt, s, acc, ql, g);
+      lsum[qb] += l0 + l1;
+    }
+    pv_accumulate<D, QB>(Vt, s, acc, ql, g);
     __syncthreads();
-    if (has_next) {
-      regs.store(Ks, Vt);
-      __syncthreads();
-    }
   }
 
-  const float ltot = lsum + __shfl_xor(lsum, 32);
-  const float inv = 1.f / ltot;
-  float lse2 = m + fast_log2(ltot);  // base-2 log-sum-exp of the scaled scores
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) acc[db] *= inv;
-
-  if (!valid) return;
-  if constexpr (MODE == MODE_ROUTED) {
-    const size_t pos = static_cast<size_t>(bstart) + r;
-    float* prow = pO + pos * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        f32x4 v = {acc[db][4 * jj + 0], acc[db][4 * jj + 1], acc[db][4 * jj + 2], acc[db][4 * jj + 3]};
-        *reinterpret_cast<f32x4*>(prow + db * 32 + 8 * jj + 4 * g) = v;
-      }
-    if (g == 0) plse[pos] = lse2;  // kept in base 2 inside the workspace
-  } else {
-    const size_t row = static_cast<size_t>(bh) * p.L + t;
-    const int32_t* sl = slot + row * p.S;
-    float M = lse2, wsum = 1.f;
-    for (int j = 0; j < p.S; ++j) {
-      const int pos = sl[j];
-      if (pos < 0) break;
-      const float lj = plse[pos];
-      const float Mn = fmaxf(M, lj);
-      const float so = fast_exp2(M - Mn), sn = fast_exp2(lj - Mn);
-      const float* prow = pO + static_cast<size_t>(pos) * D;
+  for (int qb = 0; qb < QB; ++qb) {
+    const float ltot = lsum[qb] + __shfl_xor(lsum[qb], 32);
+    const float inv = 1.f / ltot;
+    const float lse2 = m_ref[qb] + fast_log2(ltot);  // base-2 log-sum-exp of the scaled scores
+    const int r = rows[qb];
+    if (r >= nq) continue;
+    if constexpr (MODE == MODE_ROUTED) {
+      const size_t pos = static_cast<size_t>(bstart) + r;
+      float* prow = pO + pos * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(prow + db * 32 + 8 * jj + 4 * g);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[db][4 * jj + e] = acc[db][4 * jj + e] * so + v[e] * sn;
+          const f32x4 v = {acc[qb][db][4 * jj + 0] * inv, acc[qb][db][4 * jj + 1] * inv,
+                           acc[qb][db][4 * jj + 2] * inv, acc[qb][db][4 * jj + 3] * inv};
+          *reinterpret_cast<f32x4*>(prow + db * 32 + 8 * jj + 4 * g) = v;
         }
-      wsum = wsum * so + sn;
-      M = Mn;
-    }
-    const float winv = 1.f / wsum;
-    T* orow = O + row * D;
+      if (g == 0) plse[pos] = lse2;  // kept in base 2 inside the workspace
+    } else {
+      const int t = tok[qb];
+      const size_t row = static_cast<size_t>(bh) * p.L + t;
+      const int32_t* sl = slot + row * p.S;
+      f32x16 (&o)[D / 32] = acc[qb];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db) o[db] *= inv;
+      float M = lse2, wsum = 1.f;
+      for (int jsl = 0; jsl < p.S; ++jsl) {
+        const int pos = sl[jsl];
+        if (pos < 0) break;
+        const float lj = plse[pos];
+        const float Mn = fmaxf(M, lj);
+        const float so = fast_exp2(M - Mn), sn = fast_exp2(lj - Mn);
+        const float* prow = pO + static_cast<size_t>(pos) * D;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        T* dst = orow + db * 32 + 8 * jj + 4 * g;
-        if constexpr (sizeof(T) == 2) {
-          uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(acc[db][4 * jj + 0] * winv)) |
-                        (static_cast<uint32_t>(f32_to_bf16(acc[db][4 * jj + 1] * winv)) << 16);
-          uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(acc[db][4 * jj + 2] * winv)) |
-                        (static_cast<uint32_t>(f32_to_bf16(acc[db][4 * jj + 3] * winv)) << 16);
-          *reinterpret_cast<u32x2*>(dst) = u32x2{w0, w1};
-        } else {
-          *reinterpret_cast<f32x4*>(dst) = f32x4{acc[db][4 * jj + 0] * winv, acc[db][4 * jj + 1] * winv,
-                                                 acc[db][4 * jj + 2] * winv, acc[db][4 * jj + 3] * winv};
-        }
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(prow + db * 32 + 8 * jj + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[db][4 * jj + e] = o[db][4 * jj + e] * so + v[e] * sn;
+          }
+        wsum = wsum * so + sn;
+        M = Mn;
       }
-    if (g == 0) lse[row] = (M + fast_log2(wsum)) * kLn2;
+      const float winv = 1.f / wsum;
+      T* orow = O + row * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          T* dst = orow + db * 32 + 8 * jj + 4 * g;
+          if constexpr (sizeof(T) == 2) {
+            const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(o[db][4 * jj + 0] * winv)) |
+                                (static_cast<uint32_t>(f32_to_bf16(o[db][4 * jj + 1] * winv)) << 16);
+            const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(o[db][4 * jj + 2] * winv)) |
+                                (static_cast<uint32_t>(f32_to_bf16(o[db][4 * jj + 3] * winv)) << 16);
+            *reinterpret_cast<u32x2*>(dst) = u32x2{w0, w1};
+          } else {
+            *reinterpret_cast<f32x4*>(dst) = f32x4{o[db][4 * jj + 0] * winv, o[db][4 * jj + 1] * winv,
+                                                   o[db][4 * jj + 2] * winv, o[db][4 * jj + 3] * winv};
+          }
+        }
+      if (g == 0) lse[row] = (M + fast_log2(wsum)) * kLn2;
+    }
   }
 }
 
@@ -222,6 +271,8 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
 namespace moc_host {
 
 using moc::AttnParams;
+
+int attn_tile_rows() { return moc::kBM; }
 
 template <typename T, int D>
 static hipError_t launch_fwd_t(const moc_layout* lay, const moc_varlen* vl, const void* Q,
@@ -236,7 +287,7 @@ static hipError_t launch_fwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   if (vl->S > 0 && vl->max_rtiles > 0) {
     p.max_tiles = vl->max_rtiles;
     hipLaunchKernelGGL((moc::attn_fwd_kernel<T, D, moc::MODE_ROUTED>), dim3(vl->max_rtiles),
-                       dim3(256), 0, st, q, k, v, lay->chunk_offsets, p, vl->rtiles,
+                       dim3(moc::kNT), 0, st, q, k, v, lay->chunk_offsets, p, vl->rtiles,
                        vl->n_rtiles, vl->bucket_off, vl->bucket_q, vl->slot, pO, plse,
                        static_cast<T*>(O), lse);
     hipError_t e = hipGetLastError();
@@ -244,7 +295,7 @@ static hipError_t launch_fwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   }
   p.max_tiles = vl->max_atiles;
   hipLaunchKernelGGL((moc::attn_fwd_kernel<T, D, moc::MODE_ANCHOR>),
-                     dim3(vl->max_atiles * lay->B * lay->H), dim3(256), 0, st, q, k, v,
+                     dim3(vl->max_atiles * lay->B * lay->H), dim3(moc::kNT), 0, st, q, k, v,
                      lay->chunk_offsets, p, vl->atiles, vl->n_atiles, vl->bucket_off,
                      vl->bucket_q, vl->slot, pO, plse, static_cast<T*>(O), lse);
   return hipGetLastError();

@@ -28,11 +28,11 @@ hipError_t launch_attn_bwd(const moc_layout* lay, const moc_varlen* vl, const vo
                            const void* dO, float scale, void* dQ, void* dK, void* dV,
                            void* ws, size_t ws_bytes, hipStream_t st);
 size_t attn_bwd_workspace(const moc_layout* lay, int S);
+int attn_tile_rows();
 }  // namespace moc_host
 
 namespace {
 
-constexpr int kTileRows = 128;   // queries per attention work tile
 constexpr int kInvTile = 256;    // queries per inversion tile
 constexpr size_t kAlign = 256;
 
@@ -103,8 +103,8 @@ VarlenSizes varlen_sizes(const moc_layout* lay, int S) {
   const int64_t NB = BH * lay->C;
   const int64_t sel = BH * lay->L * S;
   z.nqt = (lay->L + kInvTile - 1) / kInvTile;
-  z.max_rtiles = static_cast<int>((sel + kTileRows - 1) / kTileRows + NB);
-  z.max_atiles = (lay->L + kTileRows - 1) / kTileRows + lay->C + 1;
+  z.max_rtiles = static_cast<int>((sel + moc_host::attn_tile_rows() - 1) / moc_host::attn_tile_rows() + NB);
+  z.max_atiles = (lay->L + moc_host::attn_tile_rows() - 1) / moc_host::attn_tile_rows() + lay->C + 1;
   z.counts = align_up(sizeof(int32_t) * NB * z.nqt);
   z.totals = align_up(sizeof(int32_t) * NB);
   z.tile_base = align_up(sizeof(int32_t) * NB);
@@ -266,12 +266,12 @@ moc_status moc_build_varlen(const moc_layout* lay, const moc_route_cfg* cfg, con
     out->n_atiles = reinterpret_cast<int32_t*>(w); w += z.n_atiles;
     out->scratch = counts;
     out->S = S;
-    out->tile_rows = kTileRows;
+    out->tile_rows = moc_host::attn_tile_rows();
     out->max_rtiles = z.max_rtiles;
     out->max_atiles = z.max_atiles;
     moc::VarlenParams p;
     p.B = lay->B; p.H = lay->H; p.L = lay->L; p.C = lay->C; p.S = S; p.nqt = z.nqt;
-    p.tile_rows = kTileRows; p.max_rtiles = z.max_rtiles; p.max_atiles = z.max_atiles;
+    p.tile_rows = moc_host::attn_tile_rows(); p.max_rtiles = z.max_rtiles; p.max_atiles = z.max_atiles;
     p.text_begin = lay->text_begin; p.text_end = lay->text_end;
     return hip_status(moc_host::launch_varlen(lay, p, sel, nsel, counts, totals, tile_base, out,
                                               pair_count, static_cast<hipStream_t>(stream)),
@@ -283,7 +283,7 @@ moc_status moc_build_varlen(const moc_layout* lay, const moc_route_cfg* cfg, con
 
 static moc_status check_varlen(const moc_layout* lay, const moc_varlen* vl) {
   if (!vl) return fail(MOC_EINVAL, "varlen is NULL");
-  if (vl->S < 0 || vl->tile_rows != kTileRows || !vl->bucket_off || !vl->bucket_q || !vl->slot ||
+  if (vl->S < 0 || vl->tile_rows != moc_host::attn_tile_rows() || !vl->bucket_off || !vl->bucket_q || !vl->slot ||
       !vl->rtiles || !vl->n_rtiles || !vl->atiles || !vl->n_atiles)
     return fail(MOC_EINVAL, "varlen struct not filled by moc_build_varlen");
   const VarlenSizes z = varlen_sizes(lay, vl->S);

@@ -178,7 +178,8 @@ def test_varlen_tiny(tiny_run):
     ref = mo.pair_counts(w.layout, run.h_sel)
     assert np.array_equal(run.h_pairs, ref)
     assert int(run.h_pairs[0, 0]) == 6_307_840  # closed form for this layout (k=2, causal)
-    assert run.vl.n_atiles() == math.ceil(128 / 128) + 4 * math.ceil(1024 / 128)
+    bm = run.vl.struct.tile_rows
+    assert run.vl.n_atiles() == math.ceil(128 / bm) + 4 * math.ceil(1024 / bm)
 
 
 def test_attend_tiny_full(tiny_run):
