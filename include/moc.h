@@ -114,6 +114,10 @@ typedef struct {
  *               n_rtiles[0] of them valid; each tile covers up to tile_rows queries.
  *   atiles:     [max_atiles][6] anchor work tiles (q0, q1, key range 1 [a0,a1), key range 2
  *               [b0,b1)), n_atiles[0] valid, shared by every (b, h).
+ *   ktiles:     [max_ktiles][6] key tiles of the backward (k0, k1, chunk or -1 for text,
+ *               anchor query range q0, q1, text split index), n_ktiles[0] valid, shared by every
+ *               (b, h). A key tile never straddles a chunk; text keys, which every query
+ *               attends, are split into n_text_split query ranges.
  */
 typedef struct {
   int32_t S;
@@ -128,6 +132,10 @@ typedef struct {
   int32_t *atiles;
   int32_t *n_atiles;
   int32_t *scratch;     /* internal: per-tile counts and offsets of the inversion */
+  int32_t max_ktiles;
+  int32_t n_text_split;
+  int32_t *ktiles;
+  int32_t *n_ktiles;
 } moc_varlen;
 
 /* Selection width S for a route configuration and chunk count (see moc_varlen.S). */
@@ -187,7 +195,10 @@ moc_status moc_attend_fwd(const moc_layout *lay, const moc_varlen *vl, const voi
  * Attention backward with the routed sets held fixed (summary §3.1 and Appendix A: top-k is
  * not differentiable; gradients reach the selected keys and values only).
  *   Inputs: Q, K, V, O, lse from moc_attend_fwd, dO. Outputs dQ, dK, dV [B,H,L,d] in the
- *   layout dtype, fully overwritten. ws: MOC_OP_BWD workspace (fp32 accumulators).
+ *   layout dtype, fully overwritten. ws: MOC_OP_BWD workspace (fp32 row statistics,
+ *   per-(query, routed chunk) dQ partials and text-key partials). Deterministic: no float
+ *   atomics; partial results are merged in a fixed order. bf16 layouts only (an fp32 layout
+ *   returns MOC_EUNSUPPORTED).
  */
 moc_status moc_attend_bwd(const moc_layout *lay, const moc_varlen *vl, const void *Q,
                           const void *K, const void *V, const void *O, const float *lse,

@@ -37,7 +37,9 @@ class MocVarlen(ctypes.Structure):
     _fields_ = [("S", c_int32), ("tile_rows", c_int32), ("max_rtiles", c_int32),
                 ("max_atiles", c_int32), ("bucket_off", c_void_p), ("bucket_q", c_void_p),
                 ("slot", c_void_p), ("rtiles", c_void_p), ("n_rtiles", c_void_p),
-                ("atiles", c_void_p), ("n_atiles", c_void_p), ("scratch", c_void_p)]
+                ("atiles", c_void_p), ("n_atiles", c_void_p), ("scratch", c_void_p),
+                ("max_ktiles", c_int32), ("n_text_split", c_int32), ("ktiles", c_void_p),
+                ("n_ktiles", c_void_p)]
 
 
 class MocError(RuntimeError):

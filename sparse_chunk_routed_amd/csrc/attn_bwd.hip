@@ -1,18 +1,507 @@
-// K5: MoC attention backward (placeholder until the kernels land).
+// K5: MoC attention backward with the routed sets held fixed.
+//
+// Source: "Mixture of Contexts for Long Video Generation | Summary" §3.1 and Appendix A (top-k is
+// a discrete, non-differentiable choice; gradients reach the keys/values that were selected,
+// and the pages' implementation wraps the attention in a custom autograd function).
+//
+// For every attended pair (t, j), with x_tj = scale q_t.k_j and P_tj = exp(x_tj - lse_t):
+//   dV_j += P_tj dO_t;  dP_tj = dO_t.v_j;  dS_tj = P_tj (dP_tj - D_t) with D_t = dO_t.O_t;
+//   dQ_t += scale dS_tj k_j;  dK_j += scale dS_tj q_t.
+// Pairs come in the same blocks as the forward: anchor (a query tile x text U own-shot keys)
+// and routed (a bucket of gathered queries x one chunk). The kernels:
+//   prep      D_t and the base-2 LSE per query row.
+//   dq        query-centric, like the forward (S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T):
+//             routed tiles write fp32 partial rows per (query, routed chunk); anchor tiles
+//             merge those partials in ascending chunk order and write dQ.
+//   dkdv      key-centric: a workgroup owns 128 keys of one chunk (4 waves x 32), streams 32-query
+//             tiles of the chunk's shot (anchor) and then of the chunk's routed bucket, and
+//             accumulates dV^T += dO^T P and dK^T += Q^T dS in registers (S = Q K^T).
+//   text      text keys are attended by every query: their key tiles are split over query
+//             ranges into fp32 partials, summed here in a fixed order.
+// No float atomics anywhere, so the result is deterministic. The separate dQ and dK/dV passes
+// recompute S and dP (7 GEMM-units per pair instead of 5).
 #include "attn_common.h"
+
+namespace moc {
+
+constexpr int kBwdQNW = 8;                 // dq: waves (32 queries each) per workgroup
+constexpr int kBwdQNT = 64 * kBwdQNW;
+constexpr int kBwdQBM = 32 * kBwdQNW;      // queries per dq workgroup (= varlen tile rows)
+constexpr int kBwdKNW = 4;                 // dkdv: waves (32 keys each) per workgroup
+constexpr int kBwdKNT = 64 * kBwdKNW;
+constexpr int kBwdKR = 32 * kBwdKNW;       // keys per key tile
+constexpr int kBwdQT = 32;                 // queries per dkdv step
+constexpr int kTextSplitRows = 16384;      // queries per text-key split
+
+struct BwdParams {
+  int B, H, L, C, S, max_tiles;
+  int text_begin, text_len, n_split;
+  float scale_log2;  // softmax_scale * log2(e)
+  float scale;
+};
+
+enum { BMODE_ANCHOR = 0, BMODE_ROUTED = 1 };
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// D_t = sum_d dO[t,d] O[t,d]; lse2_t = lse_t * log2(e)
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16_t* __restrict__ O,
+                                                       const bf16_t* __restrict__ dO,
+                                                       const float* __restrict__ lse,
+                                                       float* __restrict__ Dq,
+                                                       float* __restrict__ lse2, int64_t rows) {
+  constexpr int TPR = D / 8;
+  constexpr int RPB = 256 / TPR;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  float s = 0.f;
+  if (row < rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(O + row * D + c * 8);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(dO + row * D + c * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) s += bf_lo(a[w]) * bf_lo(b[w]) + bf_hi(a[w]) * bf_hi(b[w]);
+  }
+#pragma unroll
+  for (int o = TPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (row < rows && c == 0) {
+    Dq[row] = s;
+    lse2[row] = lse[row] * kLog2e;
+  }
+}
+
+template <int D, int MODE>
+__global__ __launch_bounds__(kBwdQNT) void bwd_dq_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const bf16_t* __restrict__ dO, const float* __restrict__ Dq, const float* __restrict__ lse2,
+    const int32_t* __restrict__ off, BwdParams p, const int32_t* __restrict__ tiles,
+    const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ bucket_off,
+    const int32_t* __restrict__ bucket_q, const int32_t* __restrict__ slot,
+    float* __restrict__ dQp, bf16_t* __restrict__ dQ) {
+  constexpr int KSTR = D + 8, TSTR = kBN + 4;
+  constexpr int STAGE = 2 * kBN * KSTR + D * TSTR;  // K rows, V rows, K^T
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * STAGE];
+
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  int bh, q_lo, nq, r1a, r1b, r2a, r2b, bstart = 0;
+  if constexpr (MODE == BMODE_ANCHOR) {
+    bh = lid / p.max_tiles;
+    const int tile = lid % p.max_tiles;
+    if (tile >= n_tiles[0]) return;
+    const int32_t* a = tiles + 6 * tile;
+    q_lo = a[0]; nq = a[1] - a[0];
+    r1a = a[2]; r1b = a[3]; r2a = a[4]; r2b = a[5];
+  } else {
+    if (lid >= n_tiles[0]) return;
+    const int bucket = tiles[2 * lid];
+    const int start = tiles[2 * lid + 1];
+    bh = bucket / p.C;
+    const int c = bucket % p.C;
+    bstart = bucket_off[bucket] + start;
+    const int rem = bucket_off[bucket + 1] - bstart;
+    nq = rem < kBwdQBM ? rem : kBwdQBM;
+    q_lo = 0;
+    r1a = off[c]; r1b = off[c + 1]; r2a = 0; r2b = 0;
+  }
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int ql = lane & 31, g = lane >> 5;
+  const int r = wv * 32 + ql;
+  const int rr = r < nq ? r : nq - 1;
+  int t;
+  if constexpr (MODE == BMODE_ANCHOR) t = q_lo + rr;
+  else t = bucket_q[bstart + rr];
+
+  const size_t bh_off = static_cast<size_t>(bh) * p.L * D;
+  const bf16_t* Kbh = K + bh_off;
+  const bf16_t* Vbh = V + bh_off;
+  QFrag<bf16_t, D> qf, dof;
+  qf.load(Q + bh_off + static_cast<size_t>(t) * D, g);
+  dof.load(dO + bh_off + static_cast<size_t>(t) * D, g);
+  const size_t trow = static_cast<size_t>(bh) * p.L + t;
+  const float l2 = lse2[trow];
+  const float dd = Dq[trow];
+  const float c2 = p.scale_log2;
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+
+  const int n1 = (r1b - r1a + kBN - 1) / kBN;
+  const int n2 = (r2b - r2a + kBN - 1) / kBN;
+  const int ntot = n1 + n2;
+  auto tile_pos = [&](int j, int& key0, int& kend) {
+    if (j < n1) { key0 = r1a + j * kBN; kend = r1b; }
+    else { key0 = r2a + (j - n1) * kBN; kend = r2b; }
+  };
+  PairTile<D, kBN, kBwdQNT> kt, vt;
+  auto load = [&](int j) {
+    int key0, kend;
+    tile_pos(j, key0, kend);
+    auto row_of = [&](int i) { return key0 + i < kend ? key0 + i : -1; };
+    kt.load(Kbh, row_of);
+    vt.load(Vbh, row_of);
+  };
+  auto store = [&](bf16_t* st) {
+    kt.template store_rows<KSTR>(st);
+    vt.template store_rows<KSTR>(st + kBN * KSTR);
+    kt.template store_transposed<TSTR>(st + 2 * kBN * KSTR);
+  };
+  load(0);
+  store(lds);
+  if (ntot > 1) load(1);
+  __syncthreads();
+
+  for (int j = 0; j < ntot; ++j) {
+    const bf16_t* cur = lds + (j & 1) * STAGE;
+    if (j + 1 < ntot) store(lds + ((j + 1) & 1) * STAGE);
+    if (j + 2 < ntot) load(j + 2);
+    const bf16_t* Ks = cur;
+    const bf16_t* Vs = cur + kBN * KSTR;
+    const bf16_t* Kt = cur + 2 * kBN * KSTR;
+    f32x16 s[2], dp[2];
+    s[0] = mma_nt<D, KSTR>(Ks, 0, qf, ql, g);
+    s[1] = mma_nt<D, KSTR>(Ks, 32, qf, ql, g);
+    dp[0] = mma_nt<D, KSTR>(Vs, 0, dof, ql, g);
+    dp[1] = mma_nt<D, KSTR>(Vs, 32, dof, ql, g);
+    int key0, kend;
+    tile_pos(j, key0, kend);
+    const int nvalid = kend - key0;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float pr = fast_exp2(__builtin_fmaf(s[kb][i], c2, -l2));
+        if (nvalid < kBN && key_of(kb, i, g) >= nvalid) pr = 0.f;
+        s[kb][i] = pr * (dp[kb][i] - dd);  // dS^T
+      }
+    mma_tn<D, 2, TSTR>(Kt, s, acc, ql, g);  // dQ^T += K^T dS^T
+    __syncthreads();
+  }
+
+  if (r >= nq) return;
+  if constexpr (MODE == BMODE_ROUTED) {
+    float* prow = dQp + (static_cast<size_t>(bstart) + r) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        *reinterpret_cast<f32x4*>(prow + db * 32 + 8 * jj + 4 * g) =
+            f32x4{acc[db][4 * jj], acc[db][4 * jj + 1], acc[db][4 * jj + 2], acc[db][4 * jj + 3]};
+  } else {
+    const int32_t* sl = slot + trow * p.S;
+    for (int js = 0; js < p.S; ++js) {
+      const int pos = sl[js];
+      if (pos < 0) break;
+      const float* prow = dQp + static_cast<size_t>(pos) * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(prow + db * 32 + 8 * jj + 4 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[db][4 * jj + e] += v[e];
+        }
+    }
+    bf16_t* orow = dQ + trow * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(acc[db][4 * jj + 0] * p.scale)) |
+                            (static_cast<uint32_t>(f32_to_bf16(acc[db][4 * jj + 1] * p.scale)) << 16);
+        const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(acc[db][4 * jj + 2] * p.scale)) |
+                            (static_cast<uint32_t>(f32_to_bf16(acc[db][4 * jj + 3] * p.scale)) << 16);
+        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * jj + 4 * g) = u32x2{w0, w1};
+      }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kBwdKNT) void bwd_dkdv_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const bf16_t* __restrict__ dO, const float* __restrict__ Dq, const float* __restrict__ lse2,
+    BwdParams p, const int32_t* __restrict__ ktiles, const int32_t* __restrict__ n_ktiles,
+    const int32_t* __restrict__ bucket_off, const int32_t* __restrict__ bucket_q,
+    float* __restrict__ textK, float* __restrict__ textV, bf16_t* __restrict__ dK,
+    bf16_t* __restrict__ dV) {
+  constexpr int KSTR = D + 8, TSTR = kBwdQT + 4;
+  constexpr int MAT = 2 * kBwdQT * KSTR + 2 * D * TSTR;  // Q rows, dO rows, Q^T, dO^T
+  constexpr int STAGE = MAT + 4 * kBwdQT;                // + lse2[32], D[32] as floats
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * STAGE];
+
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lid / p.max_tiles;
+  const int tile = lid % p.max_tiles;
+  if (tile >= n_ktiles[0]) return;
+  const int32_t* kt6 = ktiles + 6 * tile;
+  const int k0 = kt6[0], k1 = kt6[1], c = kt6[2], q0 = kt6[3], q1 = kt6[4], sp = kt6[5];
+
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int ql = lane & 31, g = lane >> 5;
+  const int key = k0 + wv * 32 + ql;
+  const int kl = key < k1 ? key : k1 - 1;
+  const size_t bh_off = static_cast<size_t>(bh) * p.L * D;
+  QFrag<bf16_t, D> kf, vf;
+  kf.load(K + bh_off + static_cast<size_t>(kl) * D, g);
+  vf.load(V + bh_off + static_cast<size_t>(kl) * D, g);
+  const float c2 = p.scale_log2;
+
+  const int na = q1 - q0;
+  int nb = 0, bstart = 0;
+  if (c >= 0) {
+    const int bucket = bh * p.C + c;
+    bstart = bucket_off[bucket];
+    nb = bucket_off[bucket + 1] - bstart;
+  }
+  const int nta = (na + kBwdQT - 1) / kBwdQT;
+  const int ntb = (nb + kBwdQT - 1) / kBwdQT;
+  const int ntot = nta + ntb;
+  const float* l2bh = lse2 + static_cast<size_t>(bh) * p.L;
+  const float* Dbh = Dq + static_cast<size_t>(bh) * p.L;
+
+  f32x16 accK[D / 32], accV[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) { accK[db] = f32x16{}; accV[db] = f32x16{}; }
+
+  auto row_token = [&](int j, int i) -> int {
+    if (j < nta) {
+      const int tq = q0 + j * kBwdQT + i;
+      return tq < q1 ? tq : -1;
+    }
+    const int idx = (j - nta) * kBwdQT + i;
+    return idx < nb ? bucket_q[bstart + idx] : -1;
+  };
+  PairTile<D, kBwdQT, kBwdKNT> qt, dt;
+  float st_l2 = 0.f, st_d = 0.f;  // row statistics staged by threads 0..31
+  auto load = [&](int j) {
+    auto row_of = [&](int i) { return row_token(j, i); };
+    qt.load(Q + bh_off, row_of);
+    dt.load(dO + bh_off, row_of);
+    if (threadIdx.x < kBwdQT) {
+      const int tq = row_token(j, threadIdx.x);
+      st_l2 = tq >= 0 ? l2bh[tq] : __builtin_inff();  // an absent row gets P = 0
+      st_d = tq >= 0 ? Dbh[tq] : 0.f;
+    }
+  };
+  auto store = [&](bf16_t* st) {
+    qt.template store_rows<KSTR>(st);
+    dt.template store_rows<KSTR>(st + kBwdQT * KSTR);
+    qt.template store_transposed<TSTR>(st + 2 * kBwdQT * KSTR);
+    dt.template store_transposed<TSTR>(st + 2 * kBwdQT * KSTR + D * TSTR);
+    float* stats = reinterpret_cast<float*>(st + MAT);
+    if (threadIdx.x < kBwdQT) {
+      stats[threadIdx.x] = st_l2;
+      stats[kBwdQT + threadIdx.x] = st_d;
+    }
+  };
+  if (ntot > 0) {
+    load(0);
+    store(lds);
+    if (ntot > 1) load(1);
+  }
+  __syncthreads();
+
+  for (int j = 0; j < ntot; ++j) {
+    const bf16_t* cur = lds + (j & 1) * STAGE;
+    if (j + 1 < ntot) store(lds + ((j + 1) & 1) * STAGE);
+    if (j + 2 < ntot) load(j + 2);
+    const bf16_t* Qs = cur;
+    const bf16_t* dOs = cur + kBwdQT * KSTR;
+    const bf16_t* Qt = cur + 2 * kBwdQT * KSTR;
+    const bf16_t* dOt = Qt + D * TSTR;
+    const float* sl2 = reinterpret_cast<const float*>(cur + MAT);
+    const float* sD = sl2 + kBwdQT;
+    f32x16 s[1], dp;
+    s[0] = mma_nt<D, KSTR>(Qs, 0, kf, ql, g);   // S[q][key]: lane = key, 16 queries
+    dp = mma_nt<D, KSTR>(dOs, 0, vf, ql, g);    // dP[q][key]
+    f32x16 ds[1];
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl2 + 8 * i4 + 4 * g);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(sD + 8 * i4 + 4 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * i4 + e;
+        const float pr = fast_exp2(__builtin_fmaf(s[0][i], c2, -l4[e]));
+        s[0][i] = pr;
+        ds[0][i] = pr * (dp[i] - d4[e]);
+      }
+    }
+    mma_tn<D, 1, TSTR>(dOt, s, accV, ql, g);   // dV^T += dO^T P
+    mma_tn<D, 1, TSTR>(Qt, ds, accK, ql, g);   // dK^T += Q^T dS
+    __syncthreads();
+  }
+
+  if (key >= k1) return;
+  if (c >= 0) {
+    bf16_t* kr = dK + bh_off + static_cast<size_t>(key) * D;
+    bf16_t* vr = dV + bh_off + static_cast<size_t>(key) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d0 = db * 32 + 8 * jj + 4 * g;
+        const uint32_t k0w = static_cast<uint32_t>(f32_to_bf16(accK[db][4 * jj] * p.scale)) |
+                             (static_cast<uint32_t>(f32_to_bf16(accK[db][4 * jj + 1] * p.scale)) << 16);
+        const uint32_t k1w = static_cast<uint32_t>(f32_to_bf16(accK[db][4 * jj + 2] * p.scale)) |
+                             (static_cast<uint32_t>(f32_to_bf16(accK[db][4 * jj + 3] * p.scale)) << 16);
+        *reinterpret_cast<u32x2*>(kr + d0) = u32x2{k0w, k1w};
+        const uint32_t v0w = static_cast<uint32_t>(f32_to_bf16(accV[db][4 * jj])) |
+                             (static_cast<uint32_t>(f32_to_bf16(accV[db][4 * jj + 1])) << 16);
+        const uint32_t v1w = static_cast<uint32_t>(f32_to_bf16(accV[db][4 * jj + 2])) |
+                             (static_cast<uint32_t>(f32_to_bf16(accV[db][4 * jj + 3])) << 16);
+        *reinterpret_cast<u32x2*>(vr + d0) = u32x2{v0w, v1w};
+      }
+  } else {
+    const size_t prow = ((static_cast<size_t>(bh) * p.n_split + sp) * p.text_len +
+                         (key - p.text_begin)) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d0 = db * 32 + 8 * jj + 4 * g;
+        *reinterpret_cast<f32x4*>(textK + prow + d0) =
+            f32x4{accK[db][4 * jj], accK[db][4 * jj + 1], accK[db][4 * jj + 2], accK[db][4 * jj + 3]};
+        *reinterpret_cast<f32x4*>(textV + prow + d0) =
+            f32x4{accV[db][4 * jj], accV[db][4 * jj + 1], accV[db][4 * jj + 2], accV[db][4 * jj + 3]};
+      }
+  }
+}
+
+// Text keys: dK, dV = the sum of the per-split partials, in split order.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_text_reduce_kernel(const float* __restrict__ textK,
+                                                              const float* __restrict__ textV,
+                                                              BwdParams p,
+                                                              bf16_t* __restrict__ dK,
+                                                              bf16_t* __restrict__ dV) {
+  const int64_t n = static_cast<int64_t>(p.B) * p.H * p.text_len * D;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  const int dim = static_cast<int>(e % D);
+  const int64_t rt = e / D;
+  const int tk = static_cast<int>(rt % p.text_len);
+  const int64_t bh = rt / p.text_len;
+  float sk = 0.f, sv = 0.f;
+  for (int s = 0; s < p.n_split; ++s) {
+    const size_t idx = ((static_cast<size_t>(bh) * p.n_split + s) * p.text_len + tk) * D + dim;
+    sk += textK[idx];
+    sv += textV[idx];
+  }
+  const size_t out = (static_cast<size_t>(bh) * p.L + p.text_begin + tk) * D + dim;
+  dK[out] = f32_to_bf16(sk * p.scale);
+  dV[out] = f32_to_bf16(sv);
+}
+
+}  // namespace moc
 
 namespace moc_host {
 
-size_t attn_bwd_workspace(const moc_layout* lay, int S) {
-  (void)lay;
-  (void)S;
-  return 256;
+using moc::BwdParams;
+
+int attn_bwd_key_rows() { return moc::kBwdKR; }
+
+int attn_bwd_text_split(int L) {
+  const int n = (L + moc::kTextSplitRows - 1) / moc::kTextSplitRows;
+  return n < 1 ? 1 : n;
 }
 
-hipError_t launch_attn_bwd(const moc_layout*, const moc_varlen*, const void*, const void*,
-                           const void*, const void*, const float*, const void*, float, void*,
-                           void*, void*, void*, size_t, hipStream_t) {
-  return hipErrorNotSupported;
+namespace {
+struct BwdSizes {
+  size_t dq, l2, dqp, textk, textv;
+  size_t total() const { return dq + l2 + dqp + textk + textv; }
+};
+size_t al(size_t x) { return (x + 255) / 256 * 256; }
+BwdSizes bwd_sizes(const moc_layout* lay, int S) {
+  BwdSizes z;
+  const size_t rows = static_cast<size_t>(lay->B) * lay->H * lay->L;
+  const size_t sel = rows * static_cast<size_t>(S);
+  const size_t text = static_cast<size_t>(lay->text_end - lay->text_begin);
+  const size_t ns = static_cast<size_t>(attn_bwd_text_split(lay->L));
+  z.dq = al(sizeof(float) * rows);
+  z.l2 = al(sizeof(float) * rows);
+  z.dqp = al(sizeof(float) * (sel > 0 ? sel : 1) * lay->d);
+  const size_t tp = static_cast<size_t>(lay->B) * lay->H * ns * (text > 0 ? text : 1) * lay->d;
+  z.textk = al(sizeof(float) * tp);
+  z.textv = al(sizeof(float) * tp);
+  return z;
+}
+}  // namespace
+
+size_t attn_bwd_workspace(const moc_layout* lay, int S) { return bwd_sizes(lay, S).total(); }
+
+template <int D>
+static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, const void* Q,
+                               const void* K, const void* V, const void* O, const float* lse,
+                               const void* dO, float scale, void* dQ, void* dK, void* dV,
+                               void* ws, hipStream_t st) {
+  using moc::bf16_t;
+  const BwdSizes z = bwd_sizes(lay, vl->S);
+  char* w = static_cast<char*>(ws);
+  float* Dq = reinterpret_cast<float*>(w); w += z.dq;
+  float* l2 = reinterpret_cast<float*>(w); w += z.l2;
+  float* dqp = reinterpret_cast<float*>(w); w += z.dqp;
+  float* textK = reinterpret_cast<float*>(w); w += z.textk;
+  float* textV = reinterpret_cast<float*>(w); w += z.textv;
+
+  const bf16_t* q = static_cast<const bf16_t*>(Q);
+  const bf16_t* k = static_cast<const bf16_t*>(K);
+  const bf16_t* v = static_cast<const bf16_t*>(V);
+  const bf16_t* o = static_cast<const bf16_t*>(O);
+  const bf16_t* g = static_cast<const bf16_t*>(dO);
+  const int64_t rows = static_cast<int64_t>(lay->B) * lay->H * lay->L;
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL((moc::bwd_prep_kernel<D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, st,
+                     o, g, lse, Dq, l2, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  BwdParams p;
+  p.B = lay->B; p.H = lay->H; p.L = lay->L; p.C = lay->C; p.S = vl->S;
+  p.text_begin = lay->text_begin;
+  p.text_len = lay->text_end - lay->text_begin;
+  p.n_split = vl->n_text_split;
+  p.scale_log2 = scale * moc::kLog2e;
+  p.scale = scale;
+  if (vl->S > 0 && vl->max_rtiles > 0) {
+    p.max_tiles = vl->max_rtiles;
+    hipLaunchKernelGGL((moc::bwd_dq_kernel<D, moc::BMODE_ROUTED>), dim3(vl->max_rtiles),
+                       dim3(moc::kBwdQNT), 0, st, q, k, v, g, Dq, l2, lay->chunk_offsets, p,
+                       vl->rtiles, vl->n_rtiles, vl->bucket_off, vl->bucket_q, vl->slot, dqp,
+                       static_cast<bf16_t*>(dQ));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  p.max_tiles = vl->max_atiles;
+  hipLaunchKernelGGL((moc::bwd_dq_kernel<D, moc::BMODE_ANCHOR>),
+                     dim3(vl->max_atiles * lay->B * lay->H), dim3(moc::kBwdQNT), 0, st, q, k, v, g,
+                     Dq, l2, lay->chunk_offsets, p, vl->atiles, vl->n_atiles, vl->bucket_off,
+                     vl->bucket_q, vl->slot, dqp, static_cast<bf16_t*>(dQ));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  p.max_tiles = vl->max_ktiles;
+  hipLaunchKernelGGL((moc::bwd_dkdv_kernel<D>), dim3(vl->max_ktiles * lay->B * lay->H),
+                     dim3(moc::kBwdKNT), 0, st, q, k, v, g, Dq, l2, p, vl->ktiles, vl->n_ktiles,
+                     vl->bucket_off, vl->bucket_q, textK, textV, static_cast<bf16_t*>(dK),
+                     static_cast<bf16_t*>(dV));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (p.text_len > 0) {
+    const int64_t n = static_cast<int64_t>(lay->B) * lay->H * p.text_len * D;
+    hipLaunchKernelGGL((moc::bwd_text_reduce_kernel<D>), dim3((n + 255) / 256), dim3(256), 0, st,
+                       textK, textV, p, static_cast<bf16_t*>(dK), static_cast<bf16_t*>(dV));
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+hipError_t launch_attn_bwd(const moc_layout* lay, const moc_varlen* vl, const void* Q,
+                           const void* K, const void* V, const void* O, const float* lse,
+                           const void* dO, float scale, void* dQ, void* dK, void* dV, void* ws,
+                           size_t ws_bytes, hipStream_t st) {
+  (void)ws_bytes;
+  if (lay->dtype != MOC_BF16) return hipErrorNotSupported;
+  if (vl->tile_rows != moc::kBwdQBM) return hipErrorInvalidValue;
+  return lay->d == 128 ? launch_bwd_t<128>(lay, vl, Q, K, V, O, lse, dO, scale, dQ, dK, dV, ws, st)
+                       : launch_bwd_t<64>(lay, vl, Q, K, V, O, lse, dO, scale, dQ, dK, dV, ws, st);
 }
 
 }  // namespace moc_host

@@ -29,6 +29,8 @@ hipError_t launch_attn_bwd(const moc_layout* lay, const moc_varlen* vl, const vo
                            void* ws, size_t ws_bytes, hipStream_t st);
 size_t attn_bwd_workspace(const moc_layout* lay, int S);
 int attn_tile_rows();
+int attn_bwd_key_rows();
+int attn_bwd_text_split(int L);
 }  // namespace moc_host
 
 namespace {
@@ -89,11 +91,12 @@ moc_status check_cfg(const moc_layout* lay, const moc_route_cfg* cfg) {
 }
 
 struct VarlenSizes {
-  size_t counts, totals, tile_base, bucket_off, bucket_q, slot, rtiles, n_rtiles, atiles, n_atiles;
-  int max_rtiles, max_atiles, nqt;
+  size_t counts, totals, tile_base, bucket_off, bucket_q, slot, rtiles, n_rtiles, atiles, n_atiles,
+      ktiles, n_ktiles;
+  int max_rtiles, max_atiles, max_ktiles, n_text_split, nqt;
   size_t total() const {
     return counts + totals + tile_base + bucket_off + bucket_q + slot + rtiles + n_rtiles + atiles +
-           n_atiles;
+           n_atiles + ktiles + n_ktiles;
   }
 };
 
@@ -115,6 +118,12 @@ VarlenSizes varlen_sizes(const moc_layout* lay, int S) {
   z.n_rtiles = kAlign;
   z.atiles = align_up(sizeof(int32_t) * 6 * z.max_atiles);
   z.n_atiles = kAlign;
+  const int KR = moc_host::attn_bwd_key_rows();
+  const int text = lay->text_end - lay->text_begin;
+  z.n_text_split = moc_host::attn_bwd_text_split(lay->L);
+  z.max_ktiles = (lay->L + KR - 1) / KR + lay->C + (text + KR - 1) / KR * z.n_text_split;
+  z.ktiles = align_up(sizeof(int32_t) * 6 * z.max_ktiles);
+  z.n_ktiles = kAlign;
   return z;
 }
 
@@ -264,6 +273,10 @@ moc_status moc_build_varlen(const moc_layout* lay, const moc_route_cfg* cfg, con
     out->n_rtiles = reinterpret_cast<int32_t*>(w); w += z.n_rtiles;
     out->atiles = reinterpret_cast<int32_t*>(w); w += z.atiles;
     out->n_atiles = reinterpret_cast<int32_t*>(w); w += z.n_atiles;
+    out->ktiles = reinterpret_cast<int32_t*>(w); w += z.ktiles;
+    out->n_ktiles = reinterpret_cast<int32_t*>(w); w += z.n_ktiles;
+    out->max_ktiles = z.max_ktiles;
+    out->n_text_split = z.n_text_split;
     out->scratch = counts;
     out->S = S;
     out->tile_rows = moc_host::attn_tile_rows();
@@ -273,6 +286,8 @@ moc_status moc_build_varlen(const moc_layout* lay, const moc_route_cfg* cfg, con
     p.B = lay->B; p.H = lay->H; p.L = lay->L; p.C = lay->C; p.S = S; p.nqt = z.nqt;
     p.tile_rows = moc_host::attn_tile_rows(); p.max_rtiles = z.max_rtiles; p.max_atiles = z.max_atiles;
     p.text_begin = lay->text_begin; p.text_end = lay->text_end;
+    p.key_rows = moc_host::attn_bwd_key_rows(); p.max_ktiles = z.max_ktiles;
+    p.n_text_split = z.n_text_split;
     return hip_status(moc_host::launch_varlen(lay, p, sel, nsel, counts, totals, tile_base, out,
                                               pair_count, static_cast<hipStream_t>(stream)),
                       "varlen launch");
@@ -287,7 +302,9 @@ static moc_status check_varlen(const moc_layout* lay, const moc_varlen* vl) {
       !vl->rtiles || !vl->n_rtiles || !vl->atiles || !vl->n_atiles)
     return fail(MOC_EINVAL, "varlen struct not filled by moc_build_varlen");
   const VarlenSizes z = varlen_sizes(lay, vl->S);
-  if (vl->max_rtiles != z.max_rtiles || vl->max_atiles != z.max_atiles)
+  if (vl->max_rtiles != z.max_rtiles || vl->max_atiles != z.max_atiles ||
+      vl->max_ktiles != z.max_ktiles || vl->n_text_split != z.n_text_split || !vl->ktiles ||
+      !vl->n_ktiles)
     return fail(MOC_EINVAL, "varlen struct built for another layout");
   return MOC_OK;
 }

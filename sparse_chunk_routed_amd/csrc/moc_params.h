@@ -18,6 +18,7 @@ struct RouteParams {
 struct VarlenParams {
   int B, H, L, C, S, nqt, tile_rows, max_rtiles, max_atiles;
   int text_begin, text_end;
+  int key_rows, max_ktiles, n_text_split;  // backward key tiles
 };
 
 }  // namespace moc

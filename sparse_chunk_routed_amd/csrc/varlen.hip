@@ -117,8 +117,8 @@ __global__ __launch_bounds__(1024) void inv_global_kernel(
     const int32_t* __restrict__ totals, const int32_t* __restrict__ off,
     const int32_t* __restrict__ shot, VarlenParams p, int32_t* __restrict__ bucket_off,
     int32_t* __restrict__ tile_base, int32_t* __restrict__ rtiles, int32_t* __restrict__ n_rtiles,
-    int32_t* __restrict__ atiles, int32_t* __restrict__ n_atiles,
-    int64_t* __restrict__ pair_count) {
+    int32_t* __restrict__ atiles, int32_t* __restrict__ n_atiles, int32_t* __restrict__ ktiles,
+    int32_t* __restrict__ n_ktiles, int64_t* __restrict__ pair_count) {
   __shared__ int64_t part[1024];
   __shared__ int64_t s_anchor;
   const int NB = p.B * p.H * p.C;
@@ -172,6 +172,37 @@ __global__ __launch_bounds__(1024) void inv_global_kernel(
     }
     n_atiles[0] = n;
     s_anchor = anchor;
+    // backward key tiles: text keys x query splits, then every video chunk's keys with its
+    // shot as the anchor query range (a tile never straddles a chunk)
+    const int KR = p.key_rows;
+    int nk = 0;
+    if (nt_txt > 0) {
+      const int qs = (p.L + p.n_text_split - 1) / p.n_text_split;
+      for (int k0 = tb; k0 < te; k0 += KR)
+        for (int sp = 0; sp < p.n_text_split; ++sp) {
+          const int qa = sp * qs;
+          const int qb = qa + qs < p.L ? qa + qs : p.L;
+          if (qa >= qb) continue;
+          int32_t* a = ktiles + 6 * nk++;
+          a[0] = k0; a[1] = k0 + KR < te ? k0 + KR : te;
+          a[2] = -1; a[3] = qa; a[4] = qb; a[5] = sp;
+        }
+    }
+    c = 0;
+    while (c < p.C) {
+      const int s = shot[c];
+      if (s < 0) { ++c; continue; }
+      const int c0 = c;
+      while (c < p.C && shot[c] == s) ++c;
+      const int q0 = off[c0], q1 = off[c];
+      for (int cc = c0; cc < c; ++cc)
+        for (int k0 = off[cc]; k0 < off[cc + 1]; k0 += KR) {
+          int32_t* a = ktiles + 6 * nk++;
+          a[0] = k0; a[1] = k0 + KR < off[cc + 1] ? k0 + KR : off[cc + 1];
+          a[2] = cc; a[3] = q0; a[4] = q1; a[5] = -1;
+        }
+    }
+    n_ktiles[0] = nk;
   }
   __syncthreads();
   // pair counts: anchor pairs + routed chunk sizes
@@ -240,7 +271,8 @@ hipError_t launch_varlen(const moc_layout* lay, const VarlenParams& p, const int
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(moc::inv_global_kernel, dim3(1), dim3(1024), 0, st, totals,
                      lay->chunk_offsets, lay->chunk_shot, p, out->bucket_off, tile_base,
-                     out->rtiles, out->n_rtiles, out->atiles, out->n_atiles, pair_count);
+                     out->rtiles, out->n_rtiles, out->atiles, out->n_atiles, out->ktiles,
+                     out->n_ktiles, pair_count);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(moc::inv_scatter_kernel, dim3(p.nqt, BH), dim3(256), 0, st, sel, nsel,

@@ -1,0 +1,114 @@
+"""GPU parity of the training path: drop-off / drop-in routing noise (bit-exact generator words,
+set parity with the tie exemption) and the attention backward (dQ, dK, dV against the oracle's
+fp64 backward over the same routed sets, max-abs 1e-2 for bf16)."""
+import numpy as np
+import pytest
+import torch
+
+import moc_inputs as mi
+from oracle import moc_oracle as mo
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+
+def _say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def _run(w: mi.Workload, backward: bool):
+    import sparse_chunk_routed_amd as moc
+    assert torch.cuda.is_available()
+    dev = torch.device("cuda:0")
+    _say(f"workload {w.name} L={w.L} C={w.C} B={w.B} H={w.H} d={w.d} k={w.top_k} "
+         f"p_max={w.p_max} lam={w.lam}")
+    Q, K, V, dO = mi.make_qkv(w, with_dout=True)
+    lay = moc.DeviceLayout.from_layout(w.layout, dev)
+    cfg = moc.RouteCfg(w.top_k, w.causal, w.p_max, w.lam, w.max_drop_in, w.seed)
+    Qd, Kd, Vd, dOd = (x.to(dev) for x in (Q, K, V, dO))
+    r = moc.forward(Qd, Kd, Vd, lay, cfg)
+    out = {"Q": Q, "K": K, "V": V, "dO": dO, "sel": r.sel.cpu().numpy(),
+           "nsel": r.nsel.cpu().numpy(), "O": r.O.float().cpu().numpy(),
+           "pairs": r.varlen.pair_count.cpu().numpy()}
+    if backward:
+        dQ, dK, dV = moc.attend_bwd(Qd, Kd, Vd, r.O, r.lse, dOd, lay, r.varlen)
+        torch.cuda.synchronize()
+        out.update(dQ=dQ.float().cpu().numpy(), dK=dK.float().cpu().numpy(),
+                   dV=dV.float().cpu().numpy())
+    torch.cuda.synchronize()
+    _say("gpu path done")
+    return out
+
+
+def _check_noise(w, g):
+    """GPU selections vs oracle route + drop noise; exempt (near-tie) queries only need legal,
+    correctly sized sets."""
+    kb = mo.pool_keys(g["K"], w.layout)
+    r = mo.route(g["Q"], kb, w.layout, w.top_k, w.causal)
+    sel, nsel = mo.drop_noise(r, w.layout, w.causal, w.p_max, w.lam, w.max_drop_in, w.seed)
+    same = np.all(g["sel"] == sel, axis=-1) & (g["nsel"] == nsel)
+    bad = ~same & ~r.gap_exempt
+    assert not bad.any(), f"{int(bad.sum())} noisy selections differ: {np.argwhere(bad)[:5]}"
+    _say(f"noise parity: {int(same.sum())}/{same.size} identical, "
+         f"{int((~same).sum())} tie-exempt")
+    # the causal DAG survives the noise (drop-in only draws causal candidates)
+    if w.causal:
+        assert mo.is_dag(w.C, mo.routed_edges(w.layout, g["sel"]))
+    assert np.array_equal(g["pairs"], mo.pair_counts(w.layout, g["sel"]))
+    return int((nsel != r.nsel).sum())
+
+
+def _check_grads(w, g):
+    dQ, dK, dV = mo.attend_bwd(g["Q"], g["K"], g["V"], g["dO"], w.layout, g["sel"])
+    for name, a, b in (("dQ", g["dQ"], dQ), ("dK", g["dK"], dK), ("dV", g["dV"], dV)):
+        err = float(np.max(np.abs(a - b)))
+        rel = err / max(1e-30, float(np.max(np.abs(b))))
+        _say(f"{name}: max|err|={err:.3e} (max|ref|={np.max(np.abs(b)):.3e}, rel {rel:.2e})")
+        assert err <= TOL, (name, err)
+        assert rel <= 2e-2, (name, rel)
+
+
+@pytest.mark.parametrize("k", [2, 4])
+def test_noise_and_backward_slice(k):
+    """The 4,224-token gradient slice at the headline head shape; k=4 so drop-off fires."""
+    w = mi.grad_slice(top_k=k)
+    g = _run(w, backward=True)
+    changed = _check_noise(w, g)
+    assert changed > 0  # drop-in (lambda=1) changes many selections
+    _check_grads(w, g)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_backward_random_layouts(seed):
+    rng = np.random.default_rng(500 + seed)
+    lay = mi.make_random_layout(rng, max_shots=4, max_frames=3, max_chunk=200,
+                                frame_is_shot=(seed == 2))
+    w = mi.Workload(f"bwd{seed}", 2, 2, [64, 128, 64][seed], "bf16", lay,
+                    top_k=[1, 3, 2][seed], causal=bool(seed != 1), clustered_keys=True,
+                    p_max=[0.0, 0.5, 0.3][seed], lam=[0.0, 2.0, 1.0][seed], seed=seed)
+    g = _run(w, backward=True)
+    _check_noise(w, g)
+    _check_grads(w, g)
+
+
+def test_noise_headline_sampled():
+    """Training-noise routing at the headline size (the train workload), checked on every query
+    against the oracle's route plus noise."""
+    w = mi.train()
+    g = _run(w, backward=False)
+    kb = mo.pool_keys(g["K"], w.layout)
+    r = mo.route(g["Q"], kb, w.layout, w.top_k, w.causal)
+    rng = np.random.default_rng(0)
+    rows = [(0, h, int(t)) for h in range(w.H) for t in rng.choice(w.L, 400, replace=False)]
+    sel, nsel = mo.drop_noise(r, w.layout, w.causal, w.p_max, w.lam, w.max_drop_in, w.seed,
+                              rows=rows)
+    n_ex = 0
+    for (b, h, t) in rows:
+        a = list(g["sel"][b, h, t])
+        o = list(sel[b, h, t])
+        if a != o:
+            assert r.gap_exempt[b, h, t], (b, h, t, a, o)
+            n_ex += 1
+    _say(f"headline noise: {len(rows)} rows, {n_ex} tie-exempt differences")
+    assert np.array_equal(g["pairs"], mo.pair_counts(w.layout, g["sel"]))
