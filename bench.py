@@ -43,6 +43,32 @@ def parse(argv=None):
     return ap.parse_args(argv)
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_fwd_headline_traffic.txt")
+TRAFFIC_SOURCES = ["sparse_chunk_routed_amd/csrc/attn_fwd.hip",
+                   "sparse_chunk_routed_amd/csrc/attn_common.h",
+                   "sparse_chunk_routed_amd/csrc/moc_common.h"]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per attention-forward call from the committed rocprofv3 counter summary, or
+    None when the workload differs or the kernel sources changed since the counters were
+    taken."""
+    import hashlib
+    if workload != "headline" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = {}
+    for line in open(TRAFFIC_FILE):
+        if line.strip() and not line.startswith("#"):
+            k, v = line.split()
+            rec[k] = v
+    h = hashlib.sha256()
+    for src in TRAFFIC_SOURCES:
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    if h.hexdigest() != rec.get("kernel_sources_sha256"):
+        return None
+    return int(rec["fetch_bytes_per_launch"]) + int(rec["write_bytes_per_launch"])
+
+
 def copy_calibration() -> int:
     import torch
     n = 1 << 30
@@ -193,7 +219,9 @@ def main(argv=None) -> int:
             "bound": "mfma",
             "kernel": "attention forward (routed + anchor kernels of moc_attend_fwd)",
             "achieved": att_tf, "peak": peak, "unit": "TFLOP/s", "frac": att_tf / peak,
-            "traffic": None,
+            "traffic": recorded_traffic(a.workload if a.seed == 0 else ""),
+            "traffic_unit": "HBM bytes per moc_attend_fwd call (rocprofv3 FETCH_SIZE+WRITE_SIZE, "
+                            "copy-calibrated)",
         },
         "cpu_baseline": None,
     }
