@@ -83,17 +83,23 @@ __global__ __launch_bounds__(kBwdQNT) void bwd_dq_kernel(
   constexpr int STAGE = 2 * kBN * KSTR + D * TSTR;  // K rows, V rows, K^T
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * STAGE];
 
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  // upper-bound grid: blocks past the device-side work count exit; the rest are remapped so
+  // each XCD takes a contiguous range of the real work items
   int bh, q_lo, nq, r1a, r1b, r2a, r2b, bstart = 0;
   if constexpr (MODE == BMODE_ANCHOR) {
-    bh = lid / p.max_tiles;
-    const int tile = lid % p.max_tiles;
-    if (tile >= n_tiles[0]) return;
+    const int nt = n_tiles[0];
+    const int nwork = nt * p.B * p.H;
+    if (static_cast<int>(blockIdx.x) >= nwork) return;
+    const int lid = xcd_remap(blockIdx.x, nwork);
+    bh = lid / nt;
+    const int tile = lid % nt;
     const int32_t* a = tiles + 6 * tile;
     q_lo = a[0]; nq = a[1] - a[0];
     r1a = a[2]; r1b = a[3]; r2a = a[4]; r2b = a[5];
   } else {
-    if (lid >= n_tiles[0]) return;
+    const int nwork = n_tiles[0];
+    if (static_cast<int>(blockIdx.x) >= nwork) return;
+    const int lid = xcd_remap(blockIdx.x, nwork);
     const int bucket = tiles[2 * lid];
     const int start = tiles[2 * lid + 1];
     bh = bucket / p.C;
@@ -167,12 +173,18 @@ __global__ __launch_bounds__(kBwdQNT) void bwd_dq_kernel(
     int key0, kend;
     tile_pos(j, key0, kend);
     const int nvalid = kend - key0;
+    if (nvalid < kBN) {  // ragged last tile of a range: keys past its end get P = 0
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (key_of(kb, i, g) >= nvalid) s[kb][i] = -__builtin_inff();
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float pr = fast_exp2(__builtin_fmaf(s[kb][i], c2, -l2));
-        if (nvalid < kBN && key_of(kb, i, g) >= nvalid) pr = 0.f;
+        const float pr = fast_exp2(__builtin_fmaf(s[kb][i], c2, -l2));
         s[kb][i] = pr * (dp[kb][i] - dd);  // dS^T
       }
     mma_tn<D, 2, TSTR>(Kt, s, acc, ql, g);  // dQ^T += K^T dS^T
@@ -230,10 +242,12 @@ __global__ __launch_bounds__(kBwdKNT) void bwd_dkdv_kernel(
   constexpr int STAGE = MAT + 4 * kBwdQT;                // + lse2[32], D[32] as floats
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * STAGE];
 
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = lid / p.max_tiles;
-  const int tile = lid % p.max_tiles;
-  if (tile >= n_ktiles[0]) return;
+  const int nt = n_ktiles[0];
+  const int nwork = nt * p.B * p.H;
+  if (static_cast<int>(blockIdx.x) >= nwork) return;
+  const int lid = xcd_remap(blockIdx.x, nwork);
+  const int bh = lid / nt;
+  const int tile = lid % nt;
   const int32_t* kt6 = ktiles + 6 * tile;
   const int k0 = kt6[0], k1 = kt6[1], c = kt6[2], q0 = kt6[3], q1 = kt6[4], sp = kt6[5];
 

@@ -54,20 +54,27 @@ __global__ __launch_bounds__(kNT) void attn_fwd_kernel(
   constexpr int QB = kQB;
   __shared__ __attribute__((aligned(16))) T lds[2 * TL::STAGE];
 
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  // The grid is an upper bound of the work list (its length lives on the device): blocks
+  // past the real count exit, and the rest are remapped so that each XCD takes a contiguous
+  // range of the real work items.
   int bh, q_lo, nq;            // tile queries: bucket positions or consecutive tokens
   int r1a, r1b, r2a, r2b;      // key ranges
   int bstart = 0;
   if constexpr (MODE == MODE_ANCHOR) {
-    bh = lid / p.max_tiles;
-    const int tile = lid % p.max_tiles;
-    if (tile >= n_tiles[0]) return;
+    const int nt = n_tiles[0];
+    const int nwork = nt * p.B * p.H;
+    if (static_cast<int>(blockIdx.x) >= nwork) return;
+    const int lid = xcd_remap(blockIdx.x, nwork);
+    bh = lid / nt;
+    const int tile = lid % nt;
     const int32_t* a = tiles + 6 * tile;
     q_lo = a[0];
     nq = a[1] - a[0];
     r1a = a[2]; r1b = a[3]; r2a = a[4]; r2b = a[5];
   } else {
-    if (lid >= n_tiles[0]) return;
+    const int nwork = n_tiles[0];
+    if (static_cast<int>(blockIdx.x) >= nwork) return;
+    const int lid = xcd_remap(blockIdx.x, nwork);
     const int bucket = tiles[2 * lid];
     const int start = tiles[2 * lid + 1];
     bh = bucket / p.C;

@@ -114,13 +114,19 @@ __device__ int64_t block_exclusive_scan(int n, Get get, Put put, int64_t* part) 
 }
 
 __global__ __launch_bounds__(1024) void inv_global_kernel(
-    const int32_t* __restrict__ totals, const int32_t* __restrict__ off,
-    const int32_t* __restrict__ shot, VarlenParams p, int32_t* __restrict__ bucket_off,
+    const int32_t* __restrict__ totals, const int32_t* __restrict__ off_g,
+    const int32_t* __restrict__ shot_g, VarlenParams p, int32_t* __restrict__ bucket_off,
     int32_t* __restrict__ tile_base, int32_t* __restrict__ rtiles, int32_t* __restrict__ n_rtiles,
     int32_t* __restrict__ atiles, int32_t* __restrict__ n_atiles, int32_t* __restrict__ ktiles,
     int32_t* __restrict__ n_ktiles, int64_t* __restrict__ pair_count) {
   __shared__ int64_t part[1024];
   __shared__ int64_t s_anchor;
+  __shared__ int32_t off[MOC_MAX_C + 1];
+  __shared__ int32_t shot[MOC_MAX_C];
+  // the serial tile emission below walks the layout: keep it in LDS, not in global memory
+  for (int i = threadIdx.x; i <= p.C; i += blockDim.x) off[i] = off_g[i];
+  for (int i = threadIdx.x; i < p.C; i += blockDim.x) shot[i] = shot_g[i];
+  __syncthreads();
   const int NB = p.B * p.H * p.C;
   const int BM = p.tile_rows;
   // bucket offsets
