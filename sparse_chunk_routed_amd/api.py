@@ -147,7 +147,8 @@ def pool_keys(K: torch.Tensor, lay: DeviceLayout) -> torch.Tensor:
     return kbar
 
 
-def route(Q: torch.Tensor, kbar: torch.Tensor, lay: DeviceLayout, cfg: RouteCfg):
+def route(Q: torch.Tensor, kbar: torch.Tensor, lay: DeviceLayout, cfg: RouteCfg,
+          ws: Optional[torch.Tensor] = None):
     """(sel [B,H,L,S] int32 ascending, -1 padded; nsel [B,H,L] int32)."""
     _check_qkv(Q)
     B, H, Lq, d = Q.shape
@@ -156,8 +157,13 @@ def route(Q: torch.Tensor, kbar: torch.Tensor, lay: DeviceLayout, cfg: RouteCfg)
     nsel = torch.empty((B, H, Lq), dtype=torch.int32, device=Q.device)
     s = lay.struct(B, H, d, Q.dtype)
     lib = L.load()
+    need = workspace_bytes(lay, B, H, d, Q.dtype, cfg, L.MOC_OP_ROUTE)
+    if need > 0 and (ws is None or ws.numel() < need):
+        ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
     L.check(lib.moc_route(ctypes.byref(s), ctypes.byref(cfg.struct()), _ptr(Q), _ptr(kbar),
-                          _ptr(sel) if S > 0 else None, _ptr(nsel), None, 0, _stream(Q.device)))
+                          _ptr(sel) if S > 0 else None, _ptr(nsel),
+                          _ptr(ws) if need > 0 else None, ws.numel() if need > 0 else 0,
+                          _stream(Q.device)))
     return sel, nsel
 
 

@@ -20,6 +20,7 @@
 // the global loads issued two tiles ahead (one barrier per tile), and lazy rescaling of the
 // running max (only when it grows by more than 2^8).
 #include "attn_common.h"
+#include "attn_fwd_lds.h"
 
 namespace moc {
 
@@ -273,6 +274,244 @@ __global__ __launch_bounds__(kNT) void attn_fwd_kernel(
   }
 }
 
+
+// V [B*H][L][D] -> V^T [B*H][D][Lp] (Lp = L rounded up to 64, zero padded), so that attention
+// tiles of 64 aligned keys read each dim's 64 keys as 128 contiguous bytes.
+template <int D>
+__global__ __launch_bounds__(256) void transpose_v_kernel(const bf16_t* __restrict__ V,
+                                                          bf16_t* __restrict__ Vt, int L, int Lp) {
+  __shared__ __attribute__((aligned(16))) bf16_t tile[kBN * (D + 8)];
+  const int bh = blockIdx.y;
+  const int k0 = blockIdx.x * kBN;
+  for (int e = threadIdx.x; e < kBN * D / 8; e += blockDim.x) {
+    const int r = e / (D / 8), c = e % (D / 8);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (k0 + r < L) v = *reinterpret_cast<const u32x4*>(V + (static_cast<size_t>(bh) * L + k0 + r) * D + c * 8);
+    *reinterpret_cast<u32x4*>(tile + r * (D + 8) + c * 8) = v;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < D * (kBN / 8); e += blockDim.x) {
+    const int d = e / (kBN / 8), c = e % (kBN / 8);
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(tile[(c * 8 + 2 * i) * (D + 8) + d]) |
+             (static_cast<uint32_t>(tile[(c * 8 + 2 * i + 1) * (D + 8) + d]) << 16);
+    *reinterpret_cast<u32x4*>(Vt + (static_cast<size_t>(bh) * D + d) * Lp + k0 + c * 8) =
+        u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// bf16 attention forward: same work decomposition and epilogue as attn_fwd_kernel, with K and
+// V^T tiles staged by direct-to-LDS copies into swizzled 64-key-aligned tiles (two stages, one
+// barrier per tile) and the permuted key order of attn_fwd_lds.h.
+template <int D, int MODE>
+__global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ Vt,
+    int Lp, const int32_t* __restrict__ off, AttnParams p, const int32_t* __restrict__ tiles,
+    const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ bucket_off,
+    const int32_t* __restrict__ bucket_q, const int32_t* __restrict__ slot,
+    float* __restrict__ pO, float* __restrict__ plse, bf16_t* __restrict__ O,
+    float* __restrict__ lse) {
+  using LT = LdsTiles<D>;
+  // three stage buffers as distinct objects, so that the compiler can tell the LDS written by
+  // the in-flight direct-to-LDS copies from the stage being read (no forced wait between them)
+  __shared__ __attribute__((aligned(1024))) char st0[LT::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[LT::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[LT::STAGE];
+  constexpr int LOADS = (LT::KBYTES / 1024 + LT::VBYTES / 1024) / kNW;  // copies per wave per tile
+  // s_waitcnt vmcnt(LOADS) lgkmcnt(0): only the newest tile's copies may still be in flight
+  constexpr int WAIT_ALL_BUT_ONE_TILE = 0x0070 | LOADS;
+
+  int bh, q_lo, nq, r1a, r1b, r2a, r2b, bstart = 0;
+  if constexpr (MODE == MODE_ANCHOR) {
+    const int nt = n_tiles[0];
+    const int nwork = nt * p.B * p.H;
+    if (static_cast<int>(blockIdx.x) >= nwork) return;
+    const int lid = xcd_remap(blockIdx.x, nwork);
+    bh = lid / nt;
+    const int32_t* a = tiles + 6 * (lid % nt);
+    q_lo = a[0];
+    nq = a[1] - a[0];
+    r1a = a[2]; r1b = a[3]; r2a = a[4]; r2b = a[5];
+  } else {
+    const int nwork = n_tiles[0];
+    if (static_cast<int>(blockIdx.x) >= nwork) return;
+    const int lid = xcd_remap(blockIdx.x, nwork);
+    const int bucket = tiles[2 * lid];
+    const int start = tiles[2 * lid + 1];
+    bh = bucket / p.C;
+    const int c = bucket % p.C;
+    bstart = bucket_off[bucket] + start;
+    const int rem = bucket_off[bucket + 1] - bstart;
+    nq = rem < kBM ? rem : kBM;
+    q_lo = 0;
+    r1a = off[c]; r1b = off[c + 1]; r2a = 0; r2b = 0;
+  }
+
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int ql = lane & 31, g = lane >> 5;
+  const int row = wv * 32 + ql;
+  int tok;
+  {
+    const int rr = row < nq ? row : nq - 1;
+    if constexpr (MODE == MODE_ANCHOR) tok = q_lo + rr;
+    else tok = bucket_q[bstart + rr];
+  }
+  const size_t bh_off = static_cast<size_t>(bh) * p.L * D;
+  const bf16_t* Kbh = K + bh_off;
+  const bf16_t* Vtbh = Vt + static_cast<size_t>(bh) * D * Lp;
+  QFrag<bf16_t, D> qf;
+  qf.load(Q + bh_off + static_cast<size_t>(tok) * D, g);
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+  float m_ref = -__builtin_inff();
+  float lsum = 0.f;
+  const float c2 = p.scale_log2;
+
+  // 64-aligned tiles covering [r1a, r1b) then [r2a, r2b)
+  const int m1a = r1a >> 6, n1 = r1b > r1a ? ((r1b - 1) >> 6) - m1a + 1 : 0;
+  const int m2a = r2a >> 6, n2 = r2b > r2a ? ((r2b - 1) >> 6) - m2a + 1 : 0;
+  const int ntot = n1 + n2;
+  auto tile_of = [&](int j, int& base, int& lo, int& hi) {
+    int ra, rb;
+    if (j < n1) { base = (m1a + j) * kBN; ra = r1a; rb = r1b; }
+    else { base = (m2a + j - n1) * kBN; ra = r2a; rb = r2b; }
+    lo = ra > base ? ra - base : 0;
+    hi = rb - base < kBN ? rb - base : kBN;
+  };
+  const int kmax = p.L - 1;
+  auto stage_load = [&](int j, char* st) {
+    int base, lo, hi;
+    tile_of(j, base, lo, hi);
+    stage_tile_async<D, kNW>(st, Kbh, Vtbh, Lp, base, kmax);
+  };
+  // prologue: tiles 0 and 1 in flight; wait for tile 0
+  stage_load(0, st0);
+  if (ntot > 1) {
+    stage_load(1, st1);
+    __builtin_amdgcn_s_waitcnt(WAIT_ALL_BUT_ONE_TILE);
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  __syncthreads();
+
+  // step j: copies for tile j+2 go out first, tile j is consumed, then tile j+1 must have
+  // landed before the barrier (the copies of tile j+2 stay in flight)
+  auto step = [&](int j, const char* cur, char* nxt2) {
+    if (j + 2 < ntot) stage_load(j + 2, nxt2);
+    f32x16 s[2];
+    s[0] = score_block_swz<D>(cur, qf, 0, ql, g);
+    s[1] = score_block_swz<D>(cur, qf, 1, ql, g);
+    int base, lo, hi;
+    tile_of(j, base, lo, hi);
+    if (lo > 0 || hi < kBN) {  // partial tile at a range edge: mask keys outside [lo, hi)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int k = key_of_perm(kb, i, g);
+          if (k < lo || k >= hi) s[kb][i] = -__builtin_inff();
+        }
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+    if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescale)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = fast_exp2(m_ref - m_new);
+      m_ref = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+    }
+    const float neg = -m_ref;
+    float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p0 = fast_exp2(__builtin_fmaf(s[0][i], c2, neg));
+      const float p1 = fast_exp2(__builtin_fmaf(s[1][i], c2, neg));
+      s[0][i] = p0;
+      s[1][i] = p1;
+      l0 += p0;
+      l1 += p1;
+    }
+    lsum += l0 + l1;
+    pv_swz<D>(cur, s, acc, ql, g);
+    // All LDS reads of this stage are done (lgkmcnt 0) and tile j+1 has landed; tile j+2's
+    // copies stay in flight across the barrier (a fenced __syncthreads would drain them).
+    if (j + 2 < ntot) __builtin_amdgcn_s_waitcnt(WAIT_ALL_BUT_ONE_TILE);
+    else __builtin_amdgcn_s_waitcnt(0x0070);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  for (int j = 0; j < ntot; j += 3) {
+    step(j, st0, st2);
+    if (j + 1 < ntot) step(j + 1, st1, st0);
+    if (j + 2 < ntot) step(j + 2, st2, st1);
+  }
+
+  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float inv = 1.f / ltot;
+  const float lse2 = m_ref + fast_log2(ltot);
+  if (row >= nq) return;
+  if constexpr (MODE == MODE_ROUTED) {
+    const size_t pos = static_cast<size_t>(bstart) + row;
+    float* prow = pO + pos * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        *reinterpret_cast<f32x4*>(prow + db * 32 + 8 * jj + 4 * g) =
+            f32x4{acc[db][4 * jj] * inv, acc[db][4 * jj + 1] * inv, acc[db][4 * jj + 2] * inv,
+                  acc[db][4 * jj + 3] * inv};
+    if (g == 0) plse[pos] = lse2;
+  } else {
+    const size_t trow = static_cast<size_t>(bh) * p.L + tok;
+    const int32_t* sl = slot + trow * p.S;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) acc[db] *= inv;
+    float M = lse2, wsum = 1.f;
+    for (int jsl = 0; jsl < p.S; ++jsl) {
+      const int pos = sl[jsl];
+      if (pos < 0) break;
+      const float lj = plse[pos];
+      const float Mn = fmaxf(M, lj);
+      const float so = fast_exp2(M - Mn), sn = fast_exp2(lj - Mn);
+      const float* prow = pO + static_cast<size_t>(pos) * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(prow + db * 32 + 8 * jj + 4 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[db][4 * jj + e] = acc[db][4 * jj + e] * so + v[e] * sn;
+        }
+      wsum = wsum * so + sn;
+      M = Mn;
+    }
+    const float winv = 1.f / wsum;
+    bf16_t* orow = O + trow * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(acc[db][4 * jj + 0] * winv)) |
+                            (static_cast<uint32_t>(f32_to_bf16(acc[db][4 * jj + 1] * winv)) << 16);
+        const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(acc[db][4 * jj + 2] * winv)) |
+                            (static_cast<uint32_t>(f32_to_bf16(acc[db][4 * jj + 3] * winv)) << 16);
+        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * jj + 4 * g) = u32x2{w0, w1};
+      }
+    if (g == 0) lse[trow] = (M + fast_log2(wsum)) * kLn2;
+  }
+}
+
 }  // namespace moc
 
 namespace moc_host {
@@ -280,6 +519,14 @@ namespace moc_host {
 using moc::AttnParams;
 
 int attn_tile_rows() { return moc::kBM; }
+
+// rows of the transposed V copy: L rounded up to the 64-key tile
+int attn_vt_rows(int L) { return (L + moc::kBN - 1) / moc::kBN * moc::kBN; }
+
+size_t attn_fwd_vt_bytes(const moc_layout* lay) {
+  if (lay->dtype != MOC_BF16) return 0;
+  return static_cast<size_t>(lay->B) * lay->H * lay->d * attn_vt_rows(lay->L) * 2;
+}
 
 template <typename T, int D>
 static hipError_t launch_fwd_t(const moc_layout* lay, const moc_varlen* vl, const void* Q,
@@ -308,12 +555,44 @@ static hipError_t launch_fwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   return hipGetLastError();
 }
 
+template <int D>
+static hipError_t launch_fwd_bf16(const moc_layout* lay, const moc_varlen* vl, const void* Q,
+                                  const void* K, const void* V, float scale, void* O, float* lse,
+                                  float* pO, float* plse, void* vt_ws, hipStream_t st) {
+  using moc::bf16_t;
+  AttnParams p;
+  p.B = lay->B; p.H = lay->H; p.L = lay->L; p.C = lay->C; p.S = vl->S;
+  p.scale_log2 = scale * moc::kLog2e;
+  const int Lp = attn_vt_rows(lay->L);
+  bf16_t* Vt = static_cast<bf16_t*>(vt_ws);
+  hipLaunchKernelGGL((moc::transpose_v_kernel<D>), dim3(Lp / moc::kBN, lay->B * lay->H),
+                     dim3(256), 0, st, static_cast<const bf16_t*>(V), Vt, lay->L, Lp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const bf16_t* q = static_cast<const bf16_t*>(Q);
+  const bf16_t* k = static_cast<const bf16_t*>(K);
+  if (vl->S > 0 && vl->max_rtiles > 0) {
+    p.max_tiles = vl->max_rtiles;
+    hipLaunchKernelGGL((moc::attn_fwd_bf16_kernel<D, moc::MODE_ROUTED>), dim3(vl->max_rtiles),
+                       dim3(moc::kNT), 0, st, q, k, Vt, Lp, lay->chunk_offsets, p, vl->rtiles,
+                       vl->n_rtiles, vl->bucket_off, vl->bucket_q, vl->slot, pO, plse,
+                       static_cast<bf16_t*>(O), lse);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  p.max_tiles = vl->max_atiles;
+  hipLaunchKernelGGL((moc::attn_fwd_bf16_kernel<D, moc::MODE_ANCHOR>),
+                     dim3(vl->max_atiles * lay->B * lay->H), dim3(moc::kNT), 0, st, q, k, Vt, Lp,
+                     lay->chunk_offsets, p, vl->atiles, vl->n_atiles, vl->bucket_off,
+                     vl->bucket_q, vl->slot, pO, plse, static_cast<bf16_t*>(O), lse);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_fwd(const moc_layout* lay, const moc_varlen* vl, const void* Q,
                            const void* K, const void* V, float scale, void* O, float* lse,
-                           float* pO, float* plse, hipStream_t st) {
+                           float* pO, float* plse, void* vt_ws, hipStream_t st) {
   if (lay->dtype == MOC_BF16)
-    return lay->d == 128 ? launch_fwd_t<moc::bf16_t, 128>(lay, vl, Q, K, V, scale, O, lse, pO, plse, st)
-                         : launch_fwd_t<moc::bf16_t, 64>(lay, vl, Q, K, V, scale, O, lse, pO, plse, st);
+    return lay->d == 128 ? launch_fwd_bf16<128>(lay, vl, Q, K, V, scale, O, lse, pO, plse, vt_ws, st)
+                         : launch_fwd_bf16<64>(lay, vl, Q, K, V, scale, O, lse, pO, plse, vt_ws, st);
   return lay->d == 128 ? launch_fwd_t<float, 128>(lay, vl, Q, K, V, scale, O, lse, pO, plse, st)
                        : launch_fwd_t<float, 64>(lay, vl, Q, K, V, scale, O, lse, pO, plse, st);
 }

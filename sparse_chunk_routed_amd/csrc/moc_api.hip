@@ -15,14 +15,16 @@
 namespace moc_host {
 hipError_t launch_pool(const moc_layout* lay, const void* K, float* kbar, hipStream_t st);
 hipError_t launch_route(const moc_layout* lay, const moc::RouteParams& p, const void* Q,
-                        const float* kbar, int32_t* sel, int32_t* nsel, hipStream_t st);
+                        const float* kbar, int32_t* sel, int32_t* nsel, void* ws, hipStream_t st);
+size_t route_workspace(const moc_layout* lay);
 hipError_t launch_varlen(const moc_layout* lay, const moc::VarlenParams& p, const int32_t* sel,
                          const int32_t* nsel, int32_t* counts, int32_t* totals,
                          int32_t* tile_base, const moc_varlen* out, int64_t* pair_count,
                          hipStream_t st);
 hipError_t launch_attn_fwd(const moc_layout* lay, const moc_varlen* vl, const void* Q,
                            const void* K, const void* V, float scale, void* O, float* lse,
-                           float* pO, float* plse, hipStream_t st);
+                           float* pO, float* plse, void* vt_ws, hipStream_t st);
+size_t attn_fwd_vt_bytes(const moc_layout* lay);
 hipError_t launch_attn_bwd(const moc_layout* lay, const moc_varlen* vl, const void* Q,
                            const void* K, const void* V, const void* O, const float* lse,
                            const void* dO, float scale, void* dQ, void* dK, void* dV,
@@ -130,7 +132,8 @@ VarlenSizes varlen_sizes(const moc_layout* lay, int S) {
 size_t fwd_bytes(const moc_layout* lay, int S) {
   const int64_t rows = static_cast<int64_t>(lay->B) * lay->H * lay->L * S;
   const int64_t r = rows > 0 ? rows : 1;
-  return align_up(sizeof(float) * r * lay->d) + align_up(sizeof(float) * r);
+  return align_up(sizeof(float) * r * lay->d) + align_up(sizeof(float) * r) +
+         align_up(moc_host::attn_fwd_vt_bytes(lay));
 }
 
 moc_status hip_status(hipError_t e, const char* what) {
@@ -190,7 +193,7 @@ size_t moc_workspace_bytes(const moc_layout* lay, const moc_route_cfg* cfg, int3
   if (check_cfg(lay, cfg) != MOC_OK) return 0;
   const int S = moc_sel_width(cfg, lay->C);
   switch (op) {
-    case MOC_OP_ROUTE: return 0;
+    case MOC_OP_ROUTE: return moc_host::route_workspace(lay);
     case MOC_OP_VARLEN: return varlen_sizes(lay, S).total();
     case MOC_OP_FWD: return fwd_bytes(lay, S);
     case MOC_OP_BWD: return moc_host::attn_bwd_workspace(lay, S);
@@ -223,8 +226,10 @@ moc_status moc_route(const moc_layout* lay, const moc_route_cfg* cfg, const void
     if (!Q || !kbar || !nsel || (S > 0 && !sel)) return fail(MOC_EINVAL, "NULL tensor argument");
     if (static_cast<void*>(sel) == static_cast<void*>(nsel) && S > 0)
       return fail(MOC_EINVAL, "sel aliases nsel");
-    (void)ws;
-    (void)ws_bytes;
+    const size_t need = moc_host::route_workspace(lay);
+    if (need > 0 && (!ws || ws_bytes < need))
+      return fail(MOC_EWORKSPACE, "ROUTE workspace needs %zu bytes (got %zu)", need,
+                  ws ? ws_bytes : size_t(0));
     moc::RouteParams p;
     std::memset(&p, 0, sizeof(p));
     p.B = lay->B; p.H = lay->H; p.L = lay->L; p.C = lay->C; p.S = S;
@@ -239,7 +244,7 @@ moc_status moc_route(const moc_layout* lay, const moc_route_cfg* cfg, const void
       s = moc_poisson_thresholds(cfg->lambda, cfg->max_drop_in, p.thr);
       if (s != MOC_OK) return s;
     }
-    return hip_status(moc_host::launch_route(lay, p, Q, kbar, sel, nsel,
+    return hip_status(moc_host::launch_route(lay, p, Q, kbar, sel, nsel, ws,
                                              static_cast<hipStream_t>(stream)),
                       "route launch");
   } catch (...) {
@@ -328,11 +333,14 @@ moc_status moc_attend_fwd(const moc_layout* lay, const moc_varlen* vl, const voi
       return fail(MOC_EWORKSPACE, "FWD workspace needs %zu bytes (got %zu)", need,
                   ws ? ws_bytes : size_t(0));
     const int64_t rows = static_cast<int64_t>(lay->B) * lay->H * lay->L * vl->S;
-    float* pO = static_cast<float*>(ws);
-    float* plse = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                           align_up(sizeof(float) * (rows > 0 ? rows : 1) * lay->d));
+    char* w = static_cast<char*>(ws);
+    float* pO = reinterpret_cast<float*>(w);
+    w += align_up(sizeof(float) * (rows > 0 ? rows : 1) * lay->d);
+    float* plse = reinterpret_cast<float*>(w);
+    w += align_up(sizeof(float) * (rows > 0 ? rows : 1));
+    void* vt = w;  // transposed V (bf16 layouts)
     return hip_status(moc_host::launch_attn_fwd(lay, vl, Q, K, V, softmax_scale, O, lse, pO, plse,
-                                                static_cast<hipStream_t>(stream)),
+                                                vt, static_cast<hipStream_t>(stream)),
                       "attention forward launch");
   } catch (...) {
     return fail(MOC_EINTERNAL, "exception in moc_attend_fwd");

@@ -20,7 +20,7 @@
 //
 // Work decomposition: one thread per query, 256 queries per workgroup, one (b,h) per
 // grid row; kbar for the (b,h) is staged through LDS in blocks of chunks and read by broadcast.
-#include "moc_common.h"
+#include "attn_common.h"
 #include "moc_params.h"
 
 namespace moc {
@@ -36,98 +36,17 @@ __device__ __forceinline__ uint32_t h32(uint64_t seed, int bh, int L, int t, int
   return static_cast<uint32_t>(mix64(seed + (ctr + 1) * 0x9E3779B97F4A7C15ull) >> 32);
 }
 
-template <typename T, int D, int KMAX, bool NOISE>
-__global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ Q,
-                                                    const float* __restrict__ kbar,
-                                                    const int32_t* __restrict__ off_g,
-                                                    const int32_t* __restrict__ shot_g,
-                                                    RouteParams p, int32_t* __restrict__ sel,
-                                                    int32_t* __restrict__ nsel) {
-  constexpr int CB = 16384 / D;  // chunks per LDS block (64 KB of fp32)
+// Final selection of one query: T = the first min(k_eff, n_allowed) entries of the sorted
+// top list (bs descending, ties by lower chunk id), drop-off / drop-in, ascending write-out.
+template <int KMAX, bool NOISE>
+__device__ __forceinline__ void finish_query(const float (&bs)[KMAX], const int (&bc)[KMAX],
+                                             int n_allowed, const RouteParams& p, int bh, int t,
+                                             int cq, int sq, const int32_t* s_shot,
+                                             int32_t* __restrict__ sel,
+                                             int32_t* __restrict__ nsel) {
   constexpr int MC = NOISE ? MOC_MAX_DROP_IN : 0;
-  __shared__ float kb[CB * D];
-  __shared__ int32_t s_off[MOC_MAX_C + 1];
-  __shared__ int32_t s_shot[MOC_MAX_C];
-
   const int L = p.L, C = p.C;
-  const int bh = blockIdx.y;
-  const int t0 = blockIdx.x * 256;
-  const int t = t0 + threadIdx.x;
-  const bool live = t < L;
-
-  for (int i = threadIdx.x; i <= C; i += 256) s_off[i] = off_g[i];
-  for (int i = threadIdx.x; i < C; i += 256) s_shot[i] = shot_g[i];
-  __syncthreads();
-
-  const int tq = live ? t : L - 1;
-  const int cq = chunk_of(s_off, C, tq);
-  const int sq = s_shot[cq];
-  // highest chunk any thread of this block may need
-  int c_end = C;
-  if (p.causal) {
-    int tl = t0 + 255 < L ? t0 + 255 : L - 1;
-    c_end = chunk_of(s_off, C, tl);  // candidates satisfy c < chunk(t) <= chunk(tl)
-  }
-
-  float q[D];
-  {
-    typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-    constexpr int VEC = 16 / sizeof(T);
-    const u32x4* qr = reinterpret_cast<const u32x4*>(Q + (static_cast<size_t>(bh) * L + tq) * D);
-#pragma unroll
-    for (int v = 0; v < D / VEC; ++v) {
-      u32x4 raw = qr[v];
-      const T* e = reinterpret_cast<const T*>(&raw);
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) q[v * VEC + i] = to_f32<T>(e[i]);
-    }
-  }
-
-  float bs[KMAX];
-  int bc[KMAX];
-#pragma unroll
-  for (int i = 0; i < KMAX; ++i) { bs[i] = -__builtin_inff(); bc[i] = -1; }
-  int n_allowed = 0;
-
-  const float* kbh = kbar + static_cast<size_t>(bh) * C * D;
-  for (int cb0 = 0; cb0 < c_end; cb0 += CB) {
-    const int ncb = (c_end - cb0) < CB ? (c_end - cb0) : CB;
-    __syncthreads();
-    for (int i = threadIdx.x; i < ncb * D / 4; i += 256)
-      reinterpret_cast<f32x4*>(kb)[i] = reinterpret_cast<const f32x4*>(kbh + static_cast<size_t>(cb0) * D)[i];
-    __syncthreads();
-    for (int cc = 0; cc < ncb; ++cc) {
-      const int c = cb0 + cc;
-      const int sc = s_shot[c];
-      const bool ok = live && sc >= 0 && sc != sq && (!p.causal || c < cq);
-      if (!__builtin_amdgcn_ballot_w64(ok)) continue;
-      const f32x4* kr = reinterpret_cast<const f32x4*>(kb + cc * D);
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-      for (int j = 0; j < D / 4; ++j) {
-        f32x4 kv = kr[j];
-        a0 = __builtin_fmaf(q[4 * j + 0], kv.x, a0);
-        a1 = __builtin_fmaf(q[4 * j + 1], kv.y, a1);
-        a2 = __builtin_fmaf(q[4 * j + 2], kv.z, a2);
-        a3 = __builtin_fmaf(q[4 * j + 3], kv.w, a3);
-      }
-      if (!ok) continue;
-      ++n_allowed;
-      float cs = (a0 + a1) + (a2 + a3);
-      int ci = c;
-#pragma unroll
-      for (int i = 0; i < KMAX; ++i) {  // strict '>' keeps earlier (lower-id) chunks ahead on ties
-        const bool take = cs > bs[i];
-        const float ts = take ? bs[i] : cs;
-        const int tc = take ? bc[i] : ci;
-        bs[i] = take ? cs : bs[i];
-        bc[i] = take ? ci : bc[i];
-        cs = ts;
-        ci = tc;
-      }
-    }
-  }
-  if (!live) return;
+  (void)bs;
 
   // T = the first min(k_eff, n_allowed) entries; make everything else invalid.
   const int nT = p.k_eff < n_allowed ? p.k_eff : n_allowed;
@@ -215,6 +134,264 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ Q,
   nsel[static_cast<size_t>(bh) * L + t] = nout;
 }
 
+template <typename T, int D, int KMAX, bool NOISE>
+__global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ Q,
+                                                    const float* __restrict__ kbar,
+                                                    const int32_t* __restrict__ off_g,
+                                                    const int32_t* __restrict__ shot_g,
+                                                    RouteParams p, int32_t* __restrict__ sel,
+                                                    int32_t* __restrict__ nsel) {
+  constexpr int CB = 16384 / D;  // chunks per LDS block (64 KB of fp32)
+  __shared__ float kb[CB * D];
+  __shared__ int32_t s_off[MOC_MAX_C + 1];
+  __shared__ int32_t s_shot[MOC_MAX_C];
+
+  const int L = p.L, C = p.C;
+  const int bh = blockIdx.y;
+  const int t0 = blockIdx.x * 256;
+  const int t = t0 + threadIdx.x;
+  const bool live = t < L;
+
+  for (int i = threadIdx.x; i <= C; i += 256) s_off[i] = off_g[i];
+  for (int i = threadIdx.x; i < C; i += 256) s_shot[i] = shot_g[i];
+  __syncthreads();
+
+  const int tq = live ? t : L - 1;
+  const int cq = chunk_of(s_off, C, tq);
+  const int sq = s_shot[cq];
+  // highest chunk any thread of this block may need
+  int c_end = C;
+  if (p.causal) {
+    int tl = t0 + 255 < L ? t0 + 255 : L - 1;
+    c_end = chunk_of(s_off, C, tl);  // candidates satisfy c < chunk(t) <= chunk(tl)
+  }
+
+  float q[D];
+  {
+    typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+    constexpr int VEC = 16 / sizeof(T);
+    const u32x4* qr = reinterpret_cast<const u32x4*>(Q + (static_cast<size_t>(bh) * L + tq) * D);
+#pragma unroll
+    for (int v = 0; v < D / VEC; ++v) {
+      u32x4 raw = qr[v];
+      const T* e = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) q[v * VEC + i] = to_f32<T>(e[i]);
+    }
+  }
+
+  float bs[KMAX];
+  int bc[KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) { bs[i] = -__builtin_inff(); bc[i] = -1; }
+  int n_allowed = 0;
+
+  const float* kbh = kbar + static_cast<size_t>(bh) * C * D;
+  for (int cb0 = 0; cb0 < c_end; cb0 += CB) {
+    const int ncb = (c_end - cb0) < CB ? (c_end - cb0) : CB;
+    __syncthreads();
+    for (int i = threadIdx.x; i < ncb * D / 4; i += 256)
+      reinterpret_cast<f32x4*>(kb)[i] = reinterpret_cast<const f32x4*>(kbh + static_cast<size_t>(cb0) * D)[i];
+    __syncthreads();
+    for (int cc = 0; cc < ncb; ++cc) {
+      const int c = cb0 + cc;
+      const int sc = s_shot[c];
+      const bool ok = live && sc >= 0 && sc != sq && (!p.causal || c < cq);
+      if (!__builtin_amdgcn_ballot_w64(ok)) continue;
+      const f32x4* kr = reinterpret_cast<const f32x4*>(kb + cc * D);
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+      for (int j = 0; j < D / 4; ++j) {
+        f32x4 kv = kr[j];
+        a0 = __builtin_fmaf(q[4 * j + 0], kv.x, a0);
+        a1 = __builtin_fmaf(q[4 * j + 1], kv.y, a1);
+        a2 = __builtin_fmaf(q[4 * j + 2], kv.z, a2);
+        a3 = __builtin_fmaf(q[4 * j + 3], kv.w, a3);
+      }
+      if (!ok) continue;
+      ++n_allowed;
+      float cs = (a0 + a1) + (a2 + a3);
+      int ci = c;
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i) {  // strict '>' keeps earlier (lower-id) chunks ahead on ties
+        const bool take = cs > bs[i];
+        const float ts = take ? bs[i] : cs;
+        const int tc = take ? bc[i] : ci;
+        bs[i] = take ? cs : bs[i];
+        bc[i] = take ? ci : bc[i];
+        cs = ts;
+        ci = tc;
+      }
+    }
+  }
+  if (!live) return;
+  finish_query<KMAX, NOISE>(bs, bc, n_allowed, p, bh, t, cq, sq, s_shot, sel, nsel);
+}
+
+
+// kbar (fp32) -> three bf16 terms hi + mid + lo per element (each the round-to-nearest-even of
+// what the previous terms leave), laid out [B*H][3][C][D]. With bf16 queries every product
+// q * term is exact in fp32, so the three MFMA passes score against kbar to about 2^-25.
+template <int D>
+__global__ __launch_bounds__(256) void route_split_kernel(const float* __restrict__ kbar,
+                                                          bf16_t* __restrict__ split, int C,
+                                                          int64_t n) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= n) return;
+  const int64_t per = static_cast<int64_t>(C) * D;
+  const int64_t bh = e / per;
+  const int64_t r = e % per;
+  const float x = kbar[e];
+  const bf16_t hi = f32_to_bf16(x);
+  const float r1 = x - bf16_to_f32(hi);
+  const bf16_t mid = f32_to_bf16(r1);
+  const float r2 = r1 - bf16_to_f32(mid);
+  const bf16_t lo = f32_to_bf16(r2);
+  bf16_t* o = split + bh * 3 * per + r;
+  o[0] = hi;
+  o[per] = mid;
+  o[2 * per] = lo;
+}
+
+// Routing for bf16 queries on MFMA: each wave scores 32 queries against 32-chunk blocks,
+// S^T = kbar_block Q^T summed over the three bf16 terms (fp32 accumulation). In the 32x32
+// output layout a lane holds one query and 16 chunks of the block (lanes l and l^32 split the
+// block), visited in ascending chunk order; each lane keeps its own top list, then the two
+// lists of a query are merged (ties by lower chunk id) and the even half-wave finishes.
+template <int D, int KMAX, bool NOISE>
+__global__ __launch_bounds__(512) void route_mfma_kernel(const bf16_t* __restrict__ Q,
+                                                         const bf16_t* __restrict__ split,
+                                                         const int32_t* __restrict__ off_g,
+                                                         const int32_t* __restrict__ shot_g,
+                                                         RouteParams p, int32_t* __restrict__ sel,
+                                                         int32_t* __restrict__ nsel) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  constexpr int NW = 8;
+  constexpr int QPB = 32 * NW;
+  constexpr int CB = 128;            // chunks per LDS stage
+  constexpr int KSTR = D + 8;
+  __shared__ __attribute__((aligned(16))) bf16_t ks[3 * CB * KSTR];
+  __shared__ int32_t s_off[MOC_MAX_C + 1];
+  __shared__ int32_t s_shot[MOC_MAX_C];
+
+  const int L = p.L, C = p.C;
+  const int bh = blockIdx.y;
+  const int t0 = blockIdx.x * QPB;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int ql = lane & 31, g = lane >> 5;
+  const int t = t0 + wv * 32 + ql;
+  const bool live = t < L;
+  const int tq = live ? t : L - 1;
+
+  for (int i = threadIdx.x; i <= C; i += blockDim.x) s_off[i] = off_g[i];
+  for (int i = threadIdx.x; i < C; i += blockDim.x) s_shot[i] = shot_g[i];
+  __syncthreads();
+  const int cq = chunk_of(s_off, C, tq);
+  const int sq = s_shot[cq];
+  // chunk limits: candidates satisfy c < chunk(t) <= chunk(last query) under causal routing
+  int c_blk = C, c_wave = C;
+  if (p.causal) {
+    const int tb = t0 + QPB - 1 < L ? t0 + QPB - 1 : L - 1;
+    const int tw = t0 + wv * 32 + 31 < L ? t0 + wv * 32 + 31 : L - 1;
+    c_blk = chunk_of(s_off, C, tb);
+    c_wave = chunk_of(s_off, C, tw);
+  }
+
+  QFrag<bf16_t, D> qf;
+  qf.load(Q + (static_cast<size_t>(bh) * L + tq) * D, g);
+
+  // Candidate test as index ranges: the query's own shot is the chunk range [s0, s1) (shots
+  // are contiguous) and the text chunks are [x0, x1); under causal routing c < chunk(t) and
+  // not in the own shot means c < s0.
+  int s0 = cq, s1 = cq + 1;
+  while (s0 > 0 && s_shot[s0 - 1] == sq) --s0;
+  while (s1 < C && s_shot[s1] == sq) ++s1;
+  int x0 = C, x1 = C;
+  for (int c = 0; c < C; ++c)
+    if (s_shot[c] < 0) { x0 = c; break; }
+  for (int c = x0; c < C && s_shot[c] < 0; ++c) x1 = c + 1;
+  const int lim = live ? (p.causal ? s0 : C) : 0;
+
+  float bs[KMAX];
+  int bc[KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) { bs[i] = -__builtin_inff(); bc[i] = -1; }
+  int n_allowed = 0;
+
+  const size_t per = static_cast<size_t>(C) * D;
+  const bf16_t* sp = split + static_cast<size_t>(bh) * 3 * per;
+  for (int cb0 = 0; cb0 < c_blk; cb0 += CB) {
+    const int ncb = (c_blk - cb0) < CB ? (c_blk - cb0) : CB;
+    __syncthreads();
+    constexpr int VPR = D / 8;  // 16-byte vectors per row
+    for (int v = threadIdx.x; v < 3 * ncb * VPR; v += blockDim.x) {
+      const int term = v / (ncb * VPR);
+      const int rem = v % (ncb * VPR);
+      const int c = rem / VPR, col = rem % VPR;
+      *reinterpret_cast<u32x4*>(ks + (term * CB + c) * KSTR + col * 8) =
+          *reinterpret_cast<const u32x4*>(sp + term * per + static_cast<size_t>(cb0 + c) * D + col * 8);
+    }
+    __syncthreads();
+    for (int b32 = 0; b32 < ncb; b32 += 32) {
+      if (cb0 + b32 >= c_wave) break;  // wave-uniform: no candidate of this wave beyond here
+      f32x16 acc = {};
+#pragma unroll
+      for (int term = 0; term < 3; ++term) {
+        const bf16_t* kr = ks + (term * CB + b32 + ql) * KSTR + 8 * g;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kr + 16 * kk));
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf.q[kk], acc, 0, 0, 0);
+        }
+      }
+      const int cend = lim < cb0 + ncb ? lim : cb0 + ncb;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int c = cb0 + b32 + 8 * (i >> 2) + 4 * g + (i & 3);
+        const bool ok = c < cend && (c < x0 || c >= x1) && (c < s0 || c >= s1);
+        n_allowed += ok ? 1 : 0;
+        if (!(ok && acc[i] > bs[KMAX - 1])) continue;  // cannot enter the top list
+        float cs = acc[i];
+        int ci = c;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {  // strict '>' keeps earlier (lower-id) chunks ahead
+          const bool take = cs > bs[k];
+          const float ts = take ? bs[k] : cs;
+          const int tc = take ? bc[k] : ci;
+          bs[k] = take ? cs : bs[k];
+          bc[k] = take ? ci : bc[k];
+          cs = ts;
+          ci = tc;
+        }
+      }
+    }
+  }
+  // merge the partner lane's list (disjoint chunk sets: ties go to the lower chunk id)
+  const int n_all = n_allowed + __shfl_xor(n_allowed, 32);
+  float ps[KMAX];
+  int pc[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) { ps[k] = __shfl_xor(bs[k], 32); pc[k] = __shfl_xor(bc[k], 32); }
+#pragma unroll
+  for (int m = 0; m < KMAX; ++m) {
+    float cs = ps[m];
+    int ci = pc[m];
+    if (ci < 0) continue;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      const bool take = cs > bs[k] || (cs == bs[k] && (bc[k] < 0 || ci < bc[k]));
+      const float ts = take ? bs[k] : cs;
+      const int tc = take ? bc[k] : ci;
+      bs[k] = take ? cs : bs[k];
+      bc[k] = take ? ci : bc[k];
+      cs = ts;
+      ci = tc;
+    }
+  }
+  if (!live || g != 0) return;
+  finish_query<KMAX, NOISE>(bs, bc, n_all, p, bh, t, cq, sq, s_shot, sel, nsel);
+}
+
 }  // namespace moc
 
 namespace moc_host {
@@ -223,42 +400,60 @@ using moc::RouteParams;
 
 template <typename T, int D, int KMAX, bool NOISE>
 static hipError_t launch_route_t(const moc_layout* lay, const RouteParams& p, const void* Q,
-                                 const float* kbar, int32_t* sel, int32_t* nsel,
+                                 const float* kbar, int32_t* sel, int32_t* nsel, void* ws,
                                  hipStream_t st) {
-  dim3 grid((lay->L + 255) / 256, lay->B * lay->H);
-  hipLaunchKernelGGL((moc::route_kernel<T, D, KMAX, NOISE>), grid, dim3(256), 0, st,
-                     static_cast<const T*>(Q), kbar, lay->chunk_offsets, lay->chunk_shot, p,
-                     sel, nsel);
+  if constexpr (sizeof(T) == 2) {
+    // bf16 queries: split kbar into the workspace, then score on MFMA
+    moc::bf16_t* split = static_cast<moc::bf16_t*>(ws);
+    const int64_t n = static_cast<int64_t>(lay->B) * lay->H * lay->C * D;
+    hipLaunchKernelGGL((moc::route_split_kernel<D>), dim3((n + 255) / 256), dim3(256), 0, st,
+                       kbar, split, lay->C, n);
+    dim3 grid((lay->L + 255) / 256, lay->B * lay->H);
+    hipLaunchKernelGGL((moc::route_mfma_kernel<D, KMAX, NOISE>), grid, dim3(512), 0, st,
+                       static_cast<const moc::bf16_t*>(Q), split, lay->chunk_offsets,
+                       lay->chunk_shot, p, sel, nsel);
+  } else {
+    (void)ws;
+    dim3 grid((lay->L + 255) / 256, lay->B * lay->H);
+    hipLaunchKernelGGL((moc::route_kernel<T, D, KMAX, NOISE>), grid, dim3(256), 0, st,
+                       static_cast<const T*>(Q), kbar, lay->chunk_offsets, lay->chunk_shot, p,
+                       sel, nsel);
+  }
   return hipGetLastError();
 }
 
 template <typename T, int D, bool NOISE>
 static hipError_t launch_route_k(const moc_layout* lay, const RouteParams& p, const void* Q,
-                                 const float* kbar, int32_t* sel, int32_t* nsel,
+                                 const float* kbar, int32_t* sel, int32_t* nsel, void* ws,
                                  hipStream_t st) {
-  if (p.k_eff <= 2) return launch_route_t<T, D, 2, NOISE>(lay, p, Q, kbar, sel, nsel, st);
-  if (p.k_eff <= 4) return launch_route_t<T, D, 4, NOISE>(lay, p, Q, kbar, sel, nsel, st);
-  if (p.k_eff <= 8) return launch_route_t<T, D, 8, NOISE>(lay, p, Q, kbar, sel, nsel, st);
-  if (p.k_eff <= 16) return launch_route_t<T, D, 16, NOISE>(lay, p, Q, kbar, sel, nsel, st);
-  return launch_route_t<T, D, 32, NOISE>(lay, p, Q, kbar, sel, nsel, st);
+  if (p.k_eff <= 2) return launch_route_t<T, D, 2, NOISE>(lay, p, Q, kbar, sel, nsel, ws, st);
+  if (p.k_eff <= 4) return launch_route_t<T, D, 4, NOISE>(lay, p, Q, kbar, sel, nsel, ws, st);
+  if (p.k_eff <= 8) return launch_route_t<T, D, 8, NOISE>(lay, p, Q, kbar, sel, nsel, ws, st);
+  if (p.k_eff <= 16) return launch_route_t<T, D, 16, NOISE>(lay, p, Q, kbar, sel, nsel, ws, st);
+  return launch_route_t<T, D, 32, NOISE>(lay, p, Q, kbar, sel, nsel, ws, st);
 }
 
 template <typename T, int D>
 static hipError_t launch_route_n(const moc_layout* lay, const RouteParams& p, const void* Q,
-                                 const float* kbar, int32_t* sel, int32_t* nsel,
+                                 const float* kbar, int32_t* sel, int32_t* nsel, void* ws,
                                  hipStream_t st) {
-  if (p.drop_off || p.drop_in) return launch_route_k<T, D, true>(lay, p, Q, kbar, sel, nsel, st);
-  return launch_route_k<T, D, false>(lay, p, Q, kbar, sel, nsel, st);
+  if (p.drop_off || p.drop_in) return launch_route_k<T, D, true>(lay, p, Q, kbar, sel, nsel, ws, st);
+  return launch_route_k<T, D, false>(lay, p, Q, kbar, sel, nsel, ws, st);
+}
+
+size_t route_workspace(const moc_layout* lay) {
+  if (lay->dtype != MOC_BF16) return 0;
+  return static_cast<size_t>(lay->B) * lay->H * lay->C * lay->d * 3 * sizeof(moc::bf16_t);
 }
 
 hipError_t launch_route(const moc_layout* lay, const RouteParams& p, const void* Q,
-                        const float* kbar, int32_t* sel, int32_t* nsel, hipStream_t st) {
+                        const float* kbar, int32_t* sel, int32_t* nsel, void* ws, hipStream_t st) {
   if (lay->dtype == MOC_BF16) {
-    return lay->d == 128 ? launch_route_n<moc::bf16_t, 128>(lay, p, Q, kbar, sel, nsel, st)
-                         : launch_route_n<moc::bf16_t, 64>(lay, p, Q, kbar, sel, nsel, st);
+    return lay->d == 128 ? launch_route_n<moc::bf16_t, 128>(lay, p, Q, kbar, sel, nsel, ws, st)
+                         : launch_route_n<moc::bf16_t, 64>(lay, p, Q, kbar, sel, nsel, ws, st);
   }
-  return lay->d == 128 ? launch_route_n<float, 128>(lay, p, Q, kbar, sel, nsel, st)
-                       : launch_route_n<float, 64>(lay, p, Q, kbar, sel, nsel, st);
+  return lay->d == 128 ? launch_route_n<float, 128>(lay, p, Q, kbar, sel, nsel, ws, st)
+                       : launch_route_n<float, 64>(lay, p, Q, kbar, sel, nsel, ws, st);
 }
 
 }  // namespace moc_host
