@@ -34,6 +34,10 @@ constexpr int kQB = MOC_ATTN_QB;       // 32-query blocks per wave
 constexpr int kNW = MOC_ATTN_NW;       // waves per workgroup
 constexpr int kNT = 64 * kNW;          // threads per workgroup
 constexpr int kBM = kNW * 32 * kQB;    // queries per workgroup
+#ifndef MOC_ATTN_RA
+#define MOC_ATTN_RA 4
+#endif
+constexpr int kReadAhead = MOC_ATTN_RA;  // LDS operand reads in flight ahead of the MFMAs
 
 struct AttnParams {
   int B, H, L, C, S;
@@ -314,14 +318,12 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
     float* __restrict__ pO, float* __restrict__ plse, bf16_t* __restrict__ O,
     float* __restrict__ lse) {
   using LT = LdsTiles<D>;
+  static_assert(kNW == 8, "two groups of four waves");
   // three stage buffers as distinct objects, so that the compiler can tell the LDS written by
   // the in-flight direct-to-LDS copies from the stage being read (no forced wait between them)
   __shared__ __attribute__((aligned(1024))) char st0[LT::STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[LT::STAGE];
   __shared__ __attribute__((aligned(1024))) char st2[LT::STAGE];
-  constexpr int LOADS = (LT::KBYTES / 1024 + LT::VBYTES / 1024) / kNW;  // copies per wave per tile
-  // s_waitcnt vmcnt(LOADS) lgkmcnt(0): only the newest tile's copies may still be in flight
-  constexpr int WAIT_ALL_BUT_ONE_TILE = 0x0070 | LOADS;
 
   int bh, q_lo, nq, r1a, r1b, r2a, r2b, bstart = 0;
   if constexpr (MODE == MODE_ANCHOR) {
@@ -349,7 +351,8 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
     r1a = off[c]; r1b = off[c + 1]; r2a = 0; r2b = 0;
   }
 
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int ql = lane & 31, g = lane >> 5;
   const int row = wv * 32 + ql;
   int tok;
@@ -358,6 +361,17 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
     if constexpr (MODE == MODE_ANCHOR) tok = q_lo + rr;
     else tok = bucket_q[bstart + rr];
   }
+  // s_waitcnt vmcnt(n) lgkmcnt(0), n = this wave's copies of one stage: all but the newest
+  // stage's copies have landed
+  StageCopier<D, kNW> cp;
+  cp.init(wv, lane, Lp);
+  const int ncopy = cp.count();
+  auto wait_but_newest = [&]() {
+    constexpr int NB = LT::KBLK / kNW + LT::VBLK / kNW;
+    if (ncopy == NB) __builtin_amdgcn_s_waitcnt(0x0070 | NB);
+    else if (ncopy == NB + 1) __builtin_amdgcn_s_waitcnt(0x0070 | (NB + 1));
+    else __builtin_amdgcn_s_waitcnt(0x0070 | (NB + 2));
+  };
   const size_t bh_off = static_cast<size_t>(bh) * p.L * D;
   const bf16_t* Kbh = K + bh_off;
   const bf16_t* Vtbh = Vt + static_cast<size_t>(bh) * D * Lp;
@@ -383,28 +397,50 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
     hi = rb - base < kBN ? rb - base : kBN;
   };
   const int kmax = p.L - 1;
-  auto stage_load = [&](int j, char* st) {
-    int base, lo, hi;
-    tile_of(j, base, lo, hi);
-    stage_tile_async<D, kNW>(st, Kbh, Vtbh, Lp, base, kmax);
+  auto tile_base = [&](int j) { return j < n1 ? (m1a + j) * kBN : (m2a + j - n1) * kBN; };
+  // Skewed stage j (0 <= j <= ntot) holds K of tile j and V^T of tile j-1: both are read in the
+  // same pair of half-steps (see below). Indices past the ends are clamped; those halves are
+  // loaded but never read, so every wave issues the same number of copies per stage.
+  const uint32_t lds0 = lds_addr(st0), lds1 = lds_addr(st1), lds2 = lds_addr(st2);
+  auto issue = [&](int j, uint32_t lds) {
+    if (j > ntot || ntot == 0) return;
+    cp.issue(lds, Kbh, tile_base(j < ntot ? j : ntot - 1), kmax, Vtbh,
+             tile_base(j > 0 ? j - 1 : 0));
   };
-  // prologue: tiles 0 and 1 in flight; wait for tile 0
-  stage_load(0, st0);
-  if (ntot > 1) {
-    stage_load(1, st1);
-    __builtin_amdgcn_s_waitcnt(WAIT_ALL_BUT_ONE_TILE);
-  } else {
-    __builtin_amdgcn_s_waitcnt(0);
-  }
-  __syncthreads();
 
-  // step j: copies for tile j+2 go out first, tile j is consumed, then tile j+1 must have
-  // landed before the barrier (the copies of tile j+2 stay in flight)
-  auto step = [&](int j, const char* cur, char* nxt2) {
-    if (j + 2 < ntot) stage_load(j + 2, nxt2);
-    f32x16 s[2];
-    s[0] = score_block_swz<D>(cur, qf, 0, ql, g);
-    s[1] = score_block_swz<D>(cur, qf, 1, ql, g);
+  // Two wave groups (waves 0-3 and 4-7; wave w and w+4 run on the same SIMD) work on the same
+  // key tiles half a step apart: in every half-step one group issues MFMAs (O += V P of the
+  // previous tile, then S of the current one) while the other runs the softmax of its current
+  // tile on the VALU, so the matrix cores of each SIMD stay busy during the exp / max / sum
+  // work. Half-step t ends with a workgroup barrier; group 0 runs MFMAs on even t, group 1 on
+  // odd t. Skewed stage j is read in half-steps 2j (group 0) and 2j+1 (group 1); its copies
+  // are issued in half-step 2j-4 (group 1) or 2j-3 (group 0) into the buffer freed by stage
+  // j-3, so three LDS buffers give every copy at least three half-steps to land.
+  f32x16 s[2];
+  bf16x8 pb[4];  // P^T of the previous tile, packed for the four 16-key MFMA steps
+  auto scores = [&](const char* st) { score_tile_swz<D>(st, qf, s, ql, g); };
+  // steady MFMA half-step: O += V P of tile j-1, then S of tile j, both from stage j
+  auto mfma_full = [&](const char* st) {
+    pv_swz_packed<D>(st, pb, acc, ql, g);
+    scores(st);
+    // operand reads run kReadAhead ahead of the MFMAs that use them (bounded registers)
+    constexpr int NM = 4 * (D / 32) + 2 * (D / 16);
+    __builtin_amdgcn_sched_group_barrier(0x100, kReadAhead, 0);
+#pragma unroll
+    for (int i = 0; i < NM - kReadAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kReadAhead, 0);
+  };
+  // last MFMA half-step: O += V P of the last tile, from stage ntot
+  auto mfma_last = [&]() {
+    const int r = ntot % 3;
+    if (r == 0) pv_swz_packed<D>(st0, pb, acc, ql, g);
+    else if (r == 1) pv_swz_packed<D>(st1, pb, acc, ql, g);
+    else pv_swz_packed<D>(st2, pb, acc, ql, g);
+  };
+  auto valu_half = [&](int j) {
     int base, lo, hi;
     tile_of(j, base, lo, hi);
     if (lo > 0 || hi < kBN) {  // partial tile at a range edge: mask keys outside [lo, hi)
@@ -436,25 +472,88 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
     for (int i = 0; i < 16; ++i) {
       const float p0 = fast_exp2(__builtin_fmaf(s[0][i], c2, neg));
       const float p1 = fast_exp2(__builtin_fmaf(s[1][i], c2, neg));
-      s[0][i] = p0;
-      s[1][i] = p1;
+      pb[i >> 3][i & 7] = static_cast<__bf16>(p0);
+      pb[2 + (i >> 3)][i & 7] = static_cast<__bf16>(p1);
       l0 += p0;
       l1 += p1;
     }
     lsum += l0 + l1;
-    pv_swz<D>(cur, s, acc, ql, g);
-    // All LDS reads of this stage are done (lgkmcnt 0) and tile j+1 has landed; tile j+2's
-    // copies stay in flight across the barrier (a fenced __syncthreads would drain them).
-    if (j + 2 < ntot) __builtin_amdgcn_s_waitcnt(WAIT_ALL_BUT_ONE_TILE);
-    else __builtin_amdgcn_s_waitcnt(0x0070);
+  };
+  // workgroup barrier that no instruction is scheduled across; copies in flight stay in flight
+  // (a fenced __syncthreads would wait for them)
+  auto bar = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
   };
-  for (int j = 0; j < ntot; j += 3) {
-    step(j, st0, st2);
-    if (j + 1 < ntot) step(j + 1, st1, st0);
-    if (j + 2 < ntot) step(j + 2, st2, st1);
+  // end of half-step 2i+1: stage i+1 must have landed; stage i+2 (issued at 2i) may stay in flight
+  auto wait_next = [&](int i) {
+    if (i + 2 <= ntot) wait_but_newest();
+    else __builtin_amdgcn_s_waitcnt(0x0070);
+  };
+
+  if (ntot > 0) {
+    // prologue: stages 0 and 1 in flight (stage 1 exists since ntot >= 1), wait for stage 0
+    issue(0, lds0);
+    issue(1, lds1);
+    wait_but_newest();
+    bar();
+    if (wv < 4) {
+      // group 0: half-step 2j = MFMAs of stage j, 2j+1 = softmax of tile j. Its copies of stage
+      // j+2 go out at the start of half-step 2j+1 (the buffer was last read in 2j-1), where the
+      // wave has slack, and not together with group 1's copies.
+      scores(st0);
+      bar();
+      issue(2, lds2);
+      valu_half(0);
+      wait_next(0);
+      bar();
+      auto step = [&](int j, const char* cur, uint32_t nxt2) {
+        mfma_full(cur);
+        bar();
+        issue(j + 2, nxt2);
+        valu_half(j);
+        wait_next(j);
+        bar();
+      };
+      for (int j = 1; j < ntot; j += 3) {
+        step(j, st1, lds0);
+        if (j + 1 < ntot) step(j + 1, st2, lds1);
+        if (j + 2 < ntot) step(j + 2, st0, lds2);
+      }
+      mfma_last();  // half-step 2 ntot
+      bar();
+      wait_next(ntot);  // idle half-step 2 ntot + 1
+      bar();
+    } else {
+      // group 1: idle half-step 0, then 2j+1 = MFMAs of stage j, 2j+2 = softmax of tile j
+      issue(2, lds2);
+      bar();
+      scores(st0);
+      wait_next(0);
+      bar();
+      issue(3, lds0);
+      valu_half(0);
+      bar();
+      auto step = [&](int j, const char* cur, uint32_t cur_lds) {
+        mfma_full(cur);
+        wait_next(j);
+        bar();
+        issue(j + 3, cur_lds);  // stage j+3 reuses stage j's buffer, read for the last time above
+        valu_half(j);
+        bar();
+      };
+      for (int j = 1; j < ntot; j += 3) {
+        step(j, st1, lds1);
+        if (j + 1 < ntot) step(j + 1, st2, lds2);
+        if (j + 2 < ntot) step(j + 2, st0, lds0);
+      }
+      mfma_last();  // half-step 2 ntot + 1
+      wait_next(ntot);
+      bar();
+    }
   }
 
   const float ltot = lsum + __shfl_xor(lsum, 32);

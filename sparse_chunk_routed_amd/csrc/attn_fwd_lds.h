@@ -1,12 +1,14 @@
-// Direct-to-LDS staging and swizzled MFMA operand reads for the bf16 attention kernels.
+// Direct-to-LDS staging and MFMA operand reads for the bf16 attention kernels.
 //
 // Tiles cover 64 keys on 64-aligned positions of the (b, h) key axis. K rows (D bf16 each) and
 // V^T rows (64 keys of one dim, from a transposed copy of V) are copied global -> LDS with
 // 16-byte global_load_lds (lane l of a wave lands at base + 16 l), so staging uses no VGPRs
-// and no VALU. Both tiles use an XOR swizzle of 16-byte chunks instead of padding:
-//   K   [64][D]:  chunk c of row r is stored at chunk c ^ (r & (D/8 - 1))
-//   V^T [D][64]:  chunk c of row d is stored at chunk c ^ ((d >> 1) & 7)
-// which keeps the MFMA operand reads below free of bank conflicts.
+// and no VALU. Both tiles are stored row-major with one spare 16-byte chunk per row:
+//   K   [64][D/8 + 1] chunks,   V^T [D][9] chunks
+// With these odd row pitches (in chunks), the 16 lanes that one LDS read pass serves land on 16
+// different 16-byte bank slots, and every operand read of a lane is one base address plus a
+// compile-time offset (no per-step address registers). The copy of a 1 KB block walks the
+// padded positions in order; a position that is padding copies a valid chunk that is never read.
 //
 // Key order: S^T = K Q^T is computed with lane m of the A operand reading K row pi(m),
 //   pi(8a + 4b + c) = 16 (a >> 1) + 8 b + 4 (a & 1) + c,   (a = 0..3, b = 0..1, c = 0..3)
@@ -22,9 +24,24 @@ namespace moc {
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
-// 16-byte global -> LDS copy; lane l lands at lds_base + 16 l (lds_base is wave-uniform)
-__device__ __forceinline__ void copy16_to_lds(const void* src, char* lds_base) {
-  __builtin_amdgcn_global_load_lds((gbl_ptr_t)const_cast<void*>(src), (lds_ptr_t)lds_base, 16, 0, 0);
+// 16-byte global -> LDS copy: lane l reads gbase + voff (voff per lane, gbase wave-uniform)
+// and lands at LDS byte address lds + 16 l (lds wave-uniform). Issued as inline asm so that
+// the compiler adds no waits for it (its alias tracking of these copies is too coarse and would
+// drain copies meant to stay in flight); the asm has no register outputs, and the callers wait
+// for completion with an explicit s_waitcnt vmcnt and a barrier before any wave reads the stage.
+__device__ __forceinline__ void copy16_to_lds(const void* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(gbase), "s"(lds)
+      : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)const_cast<void*>(p)));
 }
 
 __device__ __forceinline__ int kperm(int m) {
@@ -38,82 +55,110 @@ __device__ __forceinline__ int key_of_perm(int kb, int i, int g) {
 
 template <int D>
 struct LdsTiles {
-  static constexpr int KBYTES = kBN * D * 2;        // K tile
-  static constexpr int VBYTES = D * kBN * 2;        // V^T tile
-  static constexpr int STAGE = KBYTES + VBYTES;     // bytes per stage
-  static constexpr int KCH = D / 8;                 // 16-byte chunks per K row
+  static constexpr int KCH = D / 8;                       // 16-byte chunks of one K row
+  static constexpr int KROW = KCH + 1;                    // padded K row pitch (chunks)
+  static constexpr int VROW = kBN / 8 + 1;                // padded V^T row pitch (chunks)
+  static constexpr int KBLK = (kBN * KROW + 63) / 64;     // 1 KB copy blocks of the K tile
+  static constexpr int VBLK = (D * VROW + 63) / 64;       // 1 KB copy blocks of the V^T tile
+  static constexpr int KBYTES = KBLK * 1024;
+  static constexpr int VBYTES = VBLK * 1024;
+  static constexpr int STAGE = KBYTES + VBYTES;           // bytes per stage
 };
 
-// Issue the direct-to-LDS copies of one (K, V^T) tile. NW waves; every wave issues
-// (64*KCH + D*8) / (64 * NW) 16-byte loads per lane. K rows past `kmax` are clamped to it
-// (their scores are masked), V^T reads stay inside the padded transposed copy.
+// Direct-to-LDS copies of one wave for one stage. The wave copies blocks w, w + NW, ... of the
+// K tile and of the V^T tile (1 KB each, one 16-byte chunk per lane); the per-lane source
+// offsets are computed once, so issuing a stage costs a few scalar instructions per copy.
 template <int D, int NW>
-__device__ __forceinline__ void stage_tile_async(char* stage, const bf16_t* __restrict__ Kbh,
-                                                 const bf16_t* __restrict__ Vtbh, int Lp,
-                                                 int tbase, int kmax) {
+struct StageCopier {
   using LT = LdsTiles<D>;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  constexpr int KBLK = LT::KBYTES / 1024;  // 1 KB blocks of the K tile
-  constexpr int VBLK = LT::VBYTES / 1024;
-  static_assert(KBLK % NW == 0 && VBLK % NW == 0, "tile split over waves");
-#pragma unroll
-  for (int j = 0; j < KBLK / NW; ++j) {
-    const int blk = wv * (KBLK / NW) + j;
-    const int e = blk * 64 + lane;             // 16-byte chunk index within the tile
-    const int r = e / LT::KCH, c = e % LT::KCH;
-    const int cg = c ^ (r & (LT::KCH - 1));    // global chunk stored at this LDS chunk
-    int key = tbase + r;
-    key = key < kmax ? key : kmax;
-    const bf16_t* src = Kbh + static_cast<size_t>(key) * D + cg * 8;
-    copy16_to_lds(src, stage + blk * 1024);
-  }
-#pragma unroll
-  for (int j = 0; j < VBLK / NW; ++j) {
-    const int blk = wv * (VBLK / NW) + j;
-    const int e = blk * 64 + lane;
-    const int d = e >> 3, c = e & 7;
-    const int cg = c ^ ((d >> 1) & 7);
-    const bf16_t* src = Vtbh + static_cast<size_t>(d) * Lp + tbase + cg * 8;
-    copy16_to_lds(src, stage + LT::KBYTES + blk * 1024);
-  }
-}
+  static constexpr int KI = (LT::KBLK + NW - 1) / NW;  // most K blocks per wave
+  static constexpr int VI = (LT::VBLK + NW - 1) / NW;  // most V^T blocks per wave
+  int wv;
+  uint32_t krow[KI];   // tile row (key) of this lane's chunk
+  uint32_t kcol[KI];   // byte offset of the chunk within the row (padding chunks copy chunk 0)
+  uint32_t voff[VI];   // byte offset within the V^T tile of this (b, h): d * Lp * 2 + chunk * 16
 
-// S^T block kb (32 keys x 32 queries) with the permuted key order.
+  __device__ __forceinline__ void init(int wave, int lane, int Lp) {
+    wv = wave;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int pos = (wv + i * NW) * 64 + lane;  // padded chunk position
+      int r = pos / LT::KROW, c = pos % LT::KROW;
+      if (c >= LT::KCH) c = 0;
+      if (r >= kBN) r = kBN - 1;
+      krow[i] = r;
+      kcol[i] = c * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int pos = (wv + i * NW) * 64 + lane;
+      int d = pos / LT::VROW, c = pos % LT::VROW;
+      if (c >= kBN / 8) c = 0;
+      if (d >= D) d = D - 1;
+      voff[i] = static_cast<uint32_t>(d) * Lp * 2 + c * 16;
+    }
+  }
+
+  // this wave's copies per stage
+  __device__ __forceinline__ int count() const {
+    return LT::KBLK / NW + (wv < LT::KBLK % NW) + LT::VBLK / NW + (wv < LT::VBLK % NW);
+  }
+
+  // Copy K rows kbase .. kbase+63 (rows past kmax are clamped to it; their scores are masked)
+  // and V^T keys vbase .. vbase+63 into the stage at LDS byte address `lds`.
+  __device__ __forceinline__ void issue(uint32_t lds, const bf16_t* Kbh, int kbase, int kmax,
+                                        const bf16_t* Vtbh, int vbase) const {
+    const bf16_t* kb = Kbh + static_cast<size_t>(kbase) * D;
+    const uint32_t lim = static_cast<uint32_t>(kmax - kbase);  // >= 0: kbase <= kmax
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      if (i * NW + NW > LT::KBLK && wv + i * NW >= LT::KBLK) break;
+      const uint32_t r = krow[i] < lim ? krow[i] : lim;
+      copy16_to_lds(kb, r * (D * 2) + kcol[i], lds + (wv + i * NW) * 1024);
+    }
+    const bf16_t* vb = Vtbh + vbase;
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      if (i * NW + NW > LT::VBLK && wv + i * NW >= LT::VBLK) break;
+      copy16_to_lds(vb, voff[i], lds + LT::KBYTES + (wv + i * NW) * 1024);
+    }
+  }
+};
+
+// S^T of one 64-key tile: blocks kb = 0, 1 (32 keys x 32 queries each) with the permuted key
+// order. The two accumulation chains are interleaved so that consecutive MFMAs never depend on
+// each other.
 template <int D>
-__device__ __forceinline__ f32x16 score_block_swz(const char* stage, const QFrag<bf16_t, D>& qf,
-                                                  int kb, int ql, int g) {
-  f32x16 acc = {};
-  const int r = kb * 32 + kperm(ql);
-  const char* row = stage + r * (D * 2);
-  const int sw = r & (D / 8 - 1);
+__device__ __forceinline__ void score_tile_swz(const char* stage, const QFrag<bf16_t, D>& qf,
+                                               f32x16 (&s)[2], int ql, int g) {
+  using LT = LdsTiles<D>;
+  const char* row0 = stage + (LT::KROW * kperm(ql) + g) * 16;
+  const char* row1 = row0 + LT::KROW * 32 * 16;
+  s[0] = f32x16{};
+  s[1] = f32x16{};
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
-    const int ch = (2 * kk + g) ^ sw;
-    const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + ch * 16));
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf.q[kk], acc, 0, 0, 0);
+    const bf16x8 a0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row0 + kk * 32));
+    const bf16x8 a1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row1 + kk * 32));
+    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf.q[kk], s[0], 0, 0, 0);
+    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf.q[kk], s[1], 0, 0, 0);
   }
-  return acc;
 }
 
-// O^T[db] += V^T P^T for one 64-key tile (P^T in the permuted output layout, fp32).
+// O^T[db] += V^T P^T for one 64-key tile, P^T packed to bf16 in the permuted output layout:
+// pb[ks] holds values 8 (ks & 1) .. 8 (ks & 1) + 7 of S^T block ks >> 1.
 template <int D>
-__device__ __forceinline__ void pv_swz(const char* stage, const f32x16 (&p)[2],
-                                       f32x16 (&acc)[D / 32], int ql, int g) {
+__device__ __forceinline__ void pv_swz_packed(const char* stage, const bf16x8 (&pb)[4],
+                                              f32x16 (&acc)[D / 32], int ql, int g) {
   using LT = LdsTiles<D>;
-  const char* vt = stage + LT::KBYTES;
+  const char* vt = stage + LT::KBYTES + (LT::VROW * ql + g) * 16;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const int kb = ks >> 1, hh = ks & 1;
-    bf16x8 pb;
-#pragma unroll
-    for (int ii = 0; ii < 8; ++ii) pb[ii] = static_cast<__bf16>(p[kb][8 * hh + ii]);
-    const int c = 4 * kb + 2 * hh + g;  // 8-key chunk of this lane group
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const int d = db * 32 + ql;
-      const int ch = c ^ ((d >> 1) & 7);
-      const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vt + d * 128 + ch * 16));
-      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[db], 0, 0, 0);
+      const bf16x8 a = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(vt + (db * 32 * LT::VROW + 2 * ks) * 16));
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], acc[db], 0, 0, 0);
     }
   }
 }
