@@ -45,6 +45,7 @@ def parse(argv=None):
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_fwd_headline_traffic.txt")
 TRAFFIC_SOURCES = ["sparse_chunk_routed_amd/csrc/attn_fwd.hip",
+                   "sparse_chunk_routed_amd/csrc/attn_fwd_lds.h",
                    "sparse_chunk_routed_amd/csrc/attn_common.h",
                    "sparse_chunk_routed_amd/csrc/moc_common.h"]
 
