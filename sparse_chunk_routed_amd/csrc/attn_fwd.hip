@@ -15,10 +15,12 @@
 //   K4b (anchor): one workgroup per tile of <= 256 consecutive queries of one shot (or the
 //        text); streams text keys then own-shot keys; the epilogue merges the query's routed
 //        partials in ascending chunk order (deterministic) and writes O and LSE.
-// Both are exp2-domain online-softmax flash loops on MFMA (see attn_common.h): 4 waves x 64
-// queries (two 32-query MFMA blocks per wave), 64-key tiles in a double-buffered LDS ring with
-// the global loads issued two tiles ahead (one barrier per tile), and lazy rescaling of the
-// running max (only when it grows by more than 2^8).
+// Both are exp2-domain online-softmax flash loops on MFMA (S^T = K Q^T, O^T += V^T P^T; a lane
+// owns one query), 8 waves x 32 queries per workgroup, 64-key tiles, lazy rescaling of the
+// running max (only when it grows by more than 2^8). The bf16 kernel runs its two wave groups
+// half a tile apart so that one group's MFMAs overlap the other group's softmax, with K and
+// V^T tiles copied global -> LDS without registers (attn_fwd_lds.h); the fp32 kernel stages
+// tiles through registers into a double-buffered LDS ring.
 #include "attn_common.h"
 #include "attn_fwd_lds.h"
 

@@ -18,8 +18,10 @@
 // first i with word < Thr_i (Poisson CDF thresholds, truncated at m_cap); picks from the
 // ascending candidates not in the original top-k, the same way.
 //
-// Work decomposition: one thread per query, 256 queries per workgroup, one (b,h) per
-// grid row; kbar for the (b,h) is staged through LDS in blocks of chunks and read by broadcast.
+// Work decomposition: bf16 queries are scored on MFMA (route_mfma_kernel: 32 queries per wave
+// against 32-chunk blocks of kbar split into three bf16 terms). fp32 queries use route_kernel:
+// one thread per query, 256 queries per workgroup, one (b,h) per grid row; kbar for the (b,h)
+// is staged through LDS in blocks of chunks and read by broadcast.
 #include "attn_common.h"
 #include "moc_params.h"
 
