@@ -32,11 +32,17 @@ def parse(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="headline",
-                    choices=["headline", "mid", "short", "tiny", "train", "headline_uniform"])
+                    choices=["headline", "mid", "short", "tiny", "train", "headline_uniform",
+                             "single_shot_c64", "single_shot_c128", "single_shot_c256",
+                             "single_shot_c512", "single_shot_c1024"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=192,
                     help="query rows of the oracle attention sample (one head)")
+    ap.add_argument("--sweep", default="",
+                    help="comma-separated shot counts: instead of the one-line benchmark, time "
+                         "the MoC layer on n shots of 21,840 tokens (+512 text) against dense "
+                         "attention over the same tokens, one JSON line per n")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates the HBM "
                          "byte counters of a profiler against a known traffic)")
@@ -118,10 +124,80 @@ def cpu_baseline(w, Q, K, V, rows_n: int):
     }
 
 
+def sweep(a) -> int:
+    """MoC layer vs dense attention over the same tokens, for several shot counts."""
+    import torch
+
+    import moc_inputs as mi
+    import sparse_chunk_routed_amd as moc
+
+    dev = torch.device("cuda:0")
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    for n in [int(x) for x in a.sweep.split(",") if x]:
+        w = mi.shots(a.seed, n_shots=n)
+        wd = mi.dense(a.seed, n_shots=n)
+        print(f"[bench] sweep: {n} shots, L={w.L}", file=sys.stderr, flush=True)
+        Qd, Kd, Vd = (x.to(dev) for x in mi.make_qkv(w))
+        lay = moc.DeviceLayout.from_layout(w.layout, dev)
+        cfg = moc.RouteCfg(w.top_k, w.causal, w.p_max, w.lam, w.max_drop_in, w.seed)
+        ws = torch.empty(moc.workspace_bytes(lay, w.B, w.H, w.d, Qd.dtype, cfg, 2),
+                         dtype=torch.uint8, device=dev)
+        box = {}
+
+        def layer():
+            kbar = moc.pool_keys(Kd, lay)
+            sel, nsel = moc.route(Qd, kbar, lay, cfg)
+            box["vl"] = moc.build_varlen(sel, nsel, lay, cfg, w.d, Qd.dtype)
+            moc.attend_fwd(Qd, Kd, Vd, lay, box["vl"], ws=ws)
+
+        moc_ms = timed(layer, a.steps, a.warmup)
+        pairs = int(box["vl"].pair_count.sum().item())
+        del ws, box
+        lay_d = moc.DeviceLayout.from_layout(wd.layout, dev)
+        cfg_d = moc.RouteCfg(0, True, 0.0, 0.0, 8, wd.seed)
+        kbar = moc.pool_keys(Kd, lay_d)
+        sel, nsel = moc.route(Qd, kbar, lay_d, cfg_d)
+        vl_d = moc.build_varlen(sel, nsel, lay_d, cfg_d, wd.d, Qd.dtype)
+        dpairs = int(vl_d.pair_count.sum().item())
+        assert dpairs == wd.B * wd.H * wd.L * wd.L
+        ws_d = torch.empty(moc.workspace_bytes(lay_d, wd.B, wd.H, wd.d, Qd.dtype, cfg_d, 2),
+                           dtype=torch.uint8, device=dev)
+        dense_ms = timed(lambda: moc.attend_fwd(Qd, Kd, Vd, lay_d, vl_d, ws=ws_d),
+                         max(1, a.steps // 2), 1)
+        print(json.dumps({
+            "sweep": "shots", "n_shots": n, "L": w.L, "B": w.B, "H": w.H, "d": w.d,
+            "moc_layer_ms": moc_ms, "dense_attention_ms": dense_ms,
+            "speedup": dense_ms / moc_ms, "pairs": pairs, "dense_pairs": dpairs,
+            "pruned_fraction": 1.0 - pairs / dpairs,
+            "moc_tflops": 4 * w.d * pairs / (moc_ms * 1e-3) / 1e12,
+            "dense_tflops": 4 * wd.d * dpairs / (dense_ms * 1e-3) / 1e12}), flush=True)
+        del Qd, Kd, Vd, ws_d, vl_d, sel, nsel, kbar
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main(argv=None) -> int:
     a = parse(argv)
     if a.copy_calibration:
         return copy_calibration()
+    if a.sweep:
+        if a.gpus != 1:
+            print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+            return 2
+        return sweep(a)
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         return 2

@@ -223,8 +223,62 @@ def grad_slice(seed: int = 0, **kw) -> Workload:
     return replace(w, **kw)
 
 
+def fixed_chunk_layout(text_tokens: int, visual_tokens: int, chunk: int) -> Layout:
+    """Text chunk plus fixed-size visual chunks that ignore frame boundaries (the last one is
+    ragged). Every visual chunk carries its own shot id, so a query's mandatory local link is its
+    own chunk (the single-shot recipe: mandatory intra-chunk and text links, Mixture of Contexts
+    summary, Appendix F)."""
+    n = -(-int(visual_tokens) // int(chunk))
+    sizes = ([int(text_tokens)] if text_tokens > 0 else []) + \
+        [min(int(chunk), int(visual_tokens) - i * int(chunk)) for i in range(n)]
+    shots = ([-1] if text_tokens > 0 else []) + list(range(n))
+    return layout_from_chunks(sizes, shots)
+
+
+SINGLE_SHOT_FRAMES = 24        # 8 s at 12 fps, 4x temporal latent compression
+SINGLE_SHOT_FRAME_TOKENS = 252  # 320 x 192 clip: 256 text + 24 x 252 = 6,304 tokens (~6,300)
+
+
+def single_shot(seed: int = 0, chunk: int = 256, **kw) -> Workload:
+    """Single-shot short clip with fixed-size chunks (Mixture of Contexts summary, Appendix E-G
+    and Table 3: about 6,300 tokens, chunk size 256, top-k 3, intra-chunk and text links, no
+    causal routing; Table 3 sweeps chunk sizes 64 to 1024). bf16, B=1 H=12 d=128."""
+    lay = fixed_chunk_layout(256, SINGLE_SHOT_FRAMES * SINGLE_SHOT_FRAME_TOKENS, chunk)
+    w = Workload(f"single_shot_c{chunk}", 1, 12, 128, "bf16", lay, top_k=3, causal=False,
+                 clustered_keys=True, seed=seed,
+                 description=(f"256 text + 24 frames x 252 tokens in fixed {chunk}-token chunks, "
+                              "chunk = shot, non-causal"))
+    return replace(w, **kw)
+
+
+def shots(seed: int = 0, n_shots: int = 8, frames_per_shot: int = 14, **kw) -> Workload:
+    """Multi-shot sequence for the length sweep: 512 text + n_shots x frames_per_shot frames of
+    1,560 tokens (14 frames = 21,840 tokens, the headline's mean shot), top_k=2, causal."""
+    lay = build_layout(512, [frames_per_shot] * n_shots, FRAME_TOKENS)
+    w = Workload(f"shots{n_shots}", 1, 12, 128, "bf16", lay, top_k=2, causal=True,
+                 clustered_keys=True, seed=seed,
+                 description=f"512 text + {n_shots} shots x {frames_per_shot} frames x 1560 tokens")
+    return replace(w, **kw)
+
+
+def dense(seed: int = 0, n_shots: int = 8, frames_per_shot: int = 14, **kw) -> Workload:
+    """Dense attention over the same token count as shots(n_shots): one shot holding every token
+    and no text range, so every query attends every key (no routing, top_k=0)."""
+    L = 512 + n_shots * frames_per_shot * FRAME_TOKENS
+    sizes = [512] + [FRAME_TOKENS] * (n_shots * frames_per_shot)
+    lay = layout_from_chunks(sizes, [0] * len(sizes))
+    assert lay.L == L
+    w = Workload(f"dense{n_shots}", 1, 12, 128, "bf16", lay, top_k=0, causal=True,
+                 clustered_keys=True, seed=seed,
+                 description=f"dense attention over {L} tokens (one shot, no routing)")
+    return replace(w, **kw)
+
+
 WORKLOADS = {"tiny": tiny, "mid": mid, "headline": headline, "short": short, "train": train,
-             "slice": grad_slice, "headline_uniform": headline_uniform}
+             "slice": grad_slice, "headline_uniform": headline_uniform,
+             "single_shot": single_shot}
+for _c in (64, 128, 256, 512, 1024):
+    WORKLOADS[f"single_shot_c{_c}"] = (lambda c: lambda seed=0, **kw: single_shot(seed, c, **kw))(_c)
 
 
 # ---------------------------------------------------------------------------------------------
