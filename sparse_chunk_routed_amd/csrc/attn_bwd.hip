@@ -21,6 +21,7 @@
 // No float atomics anywhere, so the result is deterministic. The separate dQ and dK/dV passes
 // recompute S and dP (7 GEMM-units per pair instead of 5).
 #include "attn_common.h"
+#include "attn_fwd_lds.h"
 
 namespace moc {
 
@@ -71,17 +72,28 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16_t* __restrict_
   }
 }
 
+// Query-centric dQ (bf16), built like the forward kernel: 8 waves x 32 queries, 64-key aligned
+// tiles of K rows, V rows and K^T copied global -> LDS without registers (K^T from a transposed
+// copy of K), two wave groups half a tile apart. Per tile a wave computes S^T = K Q^T and
+// dP^T = V dO^T (lane = query, 16 keys), the VALU forms dS^T = P (dP - D) with
+// P = exp2(S scale log2(e) - lse2), and dQ^T += K^T dS^T accumulates in registers. Skewed stage
+// j holds K and V of tile j and K^T of tile j-1: a group's MFMA half-step runs dQ of tile j-1
+// and S, dP of tile j, while the other group computes dS of its current tile.
 template <int D, int MODE>
 __global__ __launch_bounds__(kBwdQNT) void bwd_dq_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const bf16_t* __restrict__ dO, const float* __restrict__ Dq, const float* __restrict__ lse2,
+    const bf16_t* __restrict__ Kt, int Lp, const bf16_t* __restrict__ dO,
+    const float* __restrict__ Dq, const float* __restrict__ lse2,
     const int32_t* __restrict__ off, BwdParams p, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ bucket_off,
     const int32_t* __restrict__ bucket_q, const int32_t* __restrict__ slot,
     float* __restrict__ dQp, bf16_t* __restrict__ dQ) {
-  constexpr int KSTR = D + 8, TSTR = kBN + 4;
-  constexpr int STAGE = 2 * kBN * KSTR + D * TSTR;  // K rows, V rows, K^T
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * STAGE];
+  static_assert(kBwdQNW == 8, "two groups of four waves");
+  using LT = LdsTiles<D>;
+  using CP = RowsTCopier<D, kBwdQNW, 2>;
+  __shared__ __attribute__((aligned(1024))) char st0[CP::BYTES];
+  __shared__ __attribute__((aligned(1024))) char st1[CP::BYTES];
+  __shared__ __attribute__((aligned(1024))) char st2[CP::BYTES];
 
   // upper-bound grid: blocks past the device-side work count exit; the rest are remapped so
   // each XCD takes a contiguous range of the real work items
@@ -92,8 +104,7 @@ __global__ __launch_bounds__(kBwdQNT) void bwd_dq_kernel(
     if (static_cast<int>(blockIdx.x) >= nwork) return;
     const int lid = xcd_remap(blockIdx.x, nwork);
     bh = lid / nt;
-    const int tile = lid % nt;
-    const int32_t* a = tiles + 6 * tile;
+    const int32_t* a = tiles + 6 * (lid % nt);
     q_lo = a[0]; nq = a[1] - a[0];
     r1a = a[2]; r1b = a[3]; r2a = a[4]; r2b = a[5];
   } else {
@@ -110,7 +121,8 @@ __global__ __launch_bounds__(kBwdQNT) void bwd_dq_kernel(
     q_lo = 0;
     r1a = off[c]; r1b = off[c + 1]; r2a = 0; r2b = 0;
   }
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int ql = lane & 31, g = lane >> 5;
   const int r = wv * 32 + ql;
   const int rr = r < nq ? r : nq - 1;
@@ -118,9 +130,18 @@ __global__ __launch_bounds__(kBwdQNT) void bwd_dq_kernel(
   if constexpr (MODE == BMODE_ANCHOR) t = q_lo + rr;
   else t = bucket_q[bstart + rr];
 
+  CP cp;
+  cp.init(wv, lane, Lp);
+  const int ncopy = cp.count();
+  auto wait_but_newest = [&]() __attribute__((always_inline)) {
+    constexpr int NB = CP::NBLK / kBwdQNW;
+    if (ncopy == NB) __builtin_amdgcn_s_waitcnt(0x0070 | NB);
+    else __builtin_amdgcn_s_waitcnt(0x0070 | (NB + 1));
+  };
   const size_t bh_off = static_cast<size_t>(bh) * p.L * D;
   const bf16_t* Kbh = K + bh_off;
   const bf16_t* Vbh = V + bh_off;
+  const bf16_t* Ktbh = Kt + static_cast<size_t>(bh) * D * Lp;
   QFrag<bf16_t, D> qf, dof;
   qf.load(Q + bh_off + static_cast<size_t>(t) * D, g);
   dof.load(dO + bh_off + static_cast<size_t>(t) * D, g);
@@ -133,62 +154,141 @@ __global__ __launch_bounds__(kBwdQNT) void bwd_dq_kernel(
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
 
-  const int n1 = (r1b - r1a + kBN - 1) / kBN;
-  const int n2 = (r2b - r2a + kBN - 1) / kBN;
+  const int m1a = r1a >> 6, n1 = r1b > r1a ? ((r1b - 1) >> 6) - m1a + 1 : 0;
+  const int m2a = r2a >> 6, n2 = r2b > r2a ? ((r2b - 1) >> 6) - m2a + 1 : 0;
   const int ntot = n1 + n2;
-  auto tile_pos = [&](int j, int& key0, int& kend) {
-    if (j < n1) { key0 = r1a + j * kBN; kend = r1b; }
-    else { key0 = r2a + (j - n1) * kBN; kend = r2b; }
+  auto tile_base = [&](int j) __attribute__((always_inline)) { return j < n1 ? (m1a + j) * kBN : (m2a + j - n1) * kBN; };
+  auto tile_of = [&](int j, int& lo, int& hi) __attribute__((always_inline)) {
+    int base, ra, rb;
+    if (j < n1) { base = (m1a + j) * kBN; ra = r1a; rb = r1b; }
+    else { base = (m2a + j - n1) * kBN; ra = r2a; rb = r2b; }
+    lo = ra > base ? ra - base : 0;
+    hi = rb - base < kBN ? rb - base : kBN;
   };
-  PairTile<D, kBN, kBwdQNT> kt, vt;
-  auto load = [&](int j) {
-    int key0, kend;
-    tile_pos(j, key0, kend);
-    auto row_of = [&](int i) { return key0 + i < kend ? key0 + i : -1; };
-    kt.load(Kbh, row_of);
-    vt.load(Vbh, row_of);
+  const int kmax = p.L - 1;
+  const uint32_t lds0 = lds_addr(st0), lds1 = lds_addr(st1), lds2 = lds_addr(st2);
+  auto issue = [&](int j, uint32_t lds) __attribute__((always_inline)) {
+    if (j > ntot || ntot == 0) return;
+    cp.issue(lds, Kbh, Vbh, tile_base(j < ntot ? j : ntot - 1), kmax, Ktbh,
+             tile_base(j > 0 ? j - 1 : 0));
   };
-  auto store = [&](bf16_t* st) {
-    kt.template store_rows<KSTR>(st);
-    vt.template store_rows<KSTR>(st + kBN * KSTR);
-    kt.template store_transposed<TSTR>(st + 2 * kBN * KSTR);
-  };
-  load(0);
-  store(lds);
-  if (ntot > 1) load(1);
-  __syncthreads();
 
-  for (int j = 0; j < ntot; ++j) {
-    const bf16_t* cur = lds + (j & 1) * STAGE;
-    if (j + 1 < ntot) store(lds + ((j + 1) & 1) * STAGE);
-    if (j + 2 < ntot) load(j + 2);
-    const bf16_t* Ks = cur;
-    const bf16_t* Vs = cur + kBN * KSTR;
-    const bf16_t* Kt = cur + 2 * kBN * KSTR;
-    f32x16 s[2], dp[2];
-    s[0] = mma_nt<D, KSTR>(Ks, 0, qf, ql, g);
-    s[1] = mma_nt<D, KSTR>(Ks, 32, qf, ql, g);
-    dp[0] = mma_nt<D, KSTR>(Vs, 0, dof, ql, g);
-    dp[1] = mma_nt<D, KSTR>(Vs, 32, dof, ql, g);
-    int key0, kend;
-    tile_pos(j, key0, kend);
-    const int nvalid = kend - key0;
-    if (nvalid < kBN) {  // ragged last tile of a range: keys past its end get P = 0
+  f32x16 s[2], dp[2];
+  bf16x8 dsb[4];  // dS^T of the previous tile, packed for the four 16-key MFMA steps
+  auto sdp = [&](const char* st) __attribute__((always_inline)) {
+    score_tile_swz<D>(st, qf, s, ql, g);
+    score_tile_swz<D>(st + LT::KBYTES, dof, dp, ql, g);
+  };
+  auto mfma_full = [&](const char* st) __attribute__((always_inline)) {
+    // dQ^T += K^T dS^T: the K^T tile sits after the two row tiles, in the V^T position of a
+    // forward stage whose K tile starts one row tile later
+    pv_swz_packed<D>(st + LT::KBYTES, dsb, acc, ql, g);
+    sdp(st);
+    // operand reads run two ahead of their MFMAs (bounded registers)
+    constexpr int NM = 4 * (D / 32) + 4 * (D / 16);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < NM - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  };
+  auto mfma_last = [&]() __attribute__((always_inline)) {
+    const int rl = ntot % 3;
+    if (rl == 0) pv_swz_packed<D>(st0 + LT::KBYTES, dsb, acc, ql, g);
+    else if (rl == 1) pv_swz_packed<D>(st1 + LT::KBYTES, dsb, acc, ql, g);
+    else pv_swz_packed<D>(st2 + LT::KBYTES, dsb, acc, ql, g);
+  };
+  auto valu_half = [&](int j) __attribute__((always_inline)) {
+    int lo, hi;
+    tile_of(j, lo, hi);
+    if (lo > 0 || hi < kBN) {  // partial tile at a range edge: keys outside [lo, hi) get P = 0
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (key_of(kb, i, g) >= nvalid) s[kb][i] = -__builtin_inff();
+        for (int i = 0; i < 16; ++i) {
+          const int k = key_of_perm(kb, i, g);
+          if (k < lo || k >= hi) s[kb][i] = -__builtin_inff();
+        }
     }
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pr = fast_exp2(__builtin_fmaf(s[kb][i], c2, -l2));
-        s[kb][i] = pr * (dp[kb][i] - dd);  // dS^T
+    for (int i = 0; i < 16; ++i) {
+      const float p0 = fast_exp2(__builtin_fmaf(s[0][i], c2, -l2));
+      const float p1 = fast_exp2(__builtin_fmaf(s[1][i], c2, -l2));
+      dsb[i >> 3][i & 7] = static_cast<__bf16>(p0 * (dp[0][i] - dd));
+      dsb[2 + (i >> 3)][i & 7] = static_cast<__bf16>(p1 * (dp[1][i] - dd));
+    }
+  };
+  auto bar = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto wait_next = [&](int i) __attribute__((always_inline)) {
+    if (i + 2 <= ntot) wait_but_newest();
+    else __builtin_amdgcn_s_waitcnt(0x0070);
+  };
+
+  if (ntot > 0) {
+    issue(0, lds0);
+    issue(1, lds1);
+    wait_but_newest();
+    bar();
+    if (wv < 4) {
+      // group 0: half-step 2j = MFMAs of stage j, 2j+1 = dS of tile j (+ copies of stage j+2)
+      sdp(st0);
+      bar();
+      issue(2, lds2);
+      valu_half(0);
+      wait_next(0);
+      bar();
+      auto step = [&](int j, const char* cur, uint32_t nxt2) __attribute__((always_inline)) {
+        mfma_full(cur);
+        bar();
+        issue(j + 2, nxt2);
+        valu_half(j);
+        wait_next(j);
+        bar();
+      };
+      for (int j = 1; j < ntot; j += 3) {
+        step(j, st1, lds0);
+        if (j + 1 < ntot) step(j + 1, st2, lds1);
+        if (j + 2 < ntot) step(j + 2, st0, lds2);
       }
-    mma_tn<D, 2, TSTR>(Kt, s, acc, ql, g);  // dQ^T += K^T dS^T
-    __syncthreads();
+      mfma_last();
+      bar();
+      wait_next(ntot);
+      bar();
+    } else {
+      // group 1: idle half-step 0, then 2j+1 = MFMAs of stage j, 2j+2 = dS of tile j
+      issue(2, lds2);
+      bar();
+      sdp(st0);
+      wait_next(0);
+      bar();
+      issue(3, lds0);
+      valu_half(0);
+      bar();
+      auto step = [&](int j, const char* cur, uint32_t cur_lds) __attribute__((always_inline)) {
+        mfma_full(cur);
+        wait_next(j);
+        bar();
+        issue(j + 3, cur_lds);
+        valu_half(j);
+        bar();
+      };
+      for (int j = 1; j < ntot; j += 3) {
+        step(j, st1, lds1);
+        if (j + 1 < ntot) step(j + 1, st2, lds2);
+        if (j + 2 < ntot) step(j + 2, st0, lds0);
+      }
+      mfma_last();
+      wait_next(ntot);
+      bar();
+    }
   }
 
   if (r >= nq) return;
@@ -278,7 +378,7 @@ __global__ __launch_bounds__(kBwdKNT) void bwd_dkdv_kernel(
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) { accK[db] = f32x16{}; accV[db] = f32x16{}; }
 
-  auto row_token = [&](int j, int i) -> int {
+  auto row_token = [&](int j, int i) __attribute__((always_inline)) -> int {
     if (j < nta) {
       const int tq = q0 + j * kBwdQT + i;
       return tq < q1 ? tq : -1;
@@ -288,8 +388,8 @@ __global__ __launch_bounds__(kBwdKNT) void bwd_dkdv_kernel(
   };
   PairTile<D, kBwdQT, kBwdKNT> qt, dt;
   float st_l2 = 0.f, st_d = 0.f;  // row statistics staged by threads 0..31
-  auto load = [&](int j) {
-    auto row_of = [&](int i) { return row_token(j, i); };
+  auto load = [&](int j) __attribute__((always_inline)) {
+    auto row_of = [&](int i) __attribute__((always_inline)) { return row_token(j, i); };
     qt.load(Q + bh_off, row_of);
     dt.load(dO + bh_off, row_of);
     if (threadIdx.x < kBwdQT) {
@@ -298,7 +398,7 @@ __global__ __launch_bounds__(kBwdKNT) void bwd_dkdv_kernel(
       st_d = tq >= 0 ? Dbh[tq] : 0.f;
     }
   };
-  auto store = [&](bf16_t* st) {
+  auto store = [&](bf16_t* st) __attribute__((always_inline)) {
     qt.template store_rows<KSTR>(st);
     dt.template store_rows<KSTR>(st + kBwdQT * KSTR);
     qt.template store_transposed<TSTR>(st + 2 * kBwdQT * KSTR);
@@ -414,6 +514,9 @@ namespace moc_host {
 
 using moc::BwdParams;
 
+hipError_t launch_transpose_rows(const void* X, void* Xt, int BH, int L, int Lp, int d,
+                                 hipStream_t st);  // attn_fwd.hip
+
 int attn_bwd_key_rows() { return moc::kBwdKR; }
 
 int attn_bwd_text_split(int L) {
@@ -423,9 +526,10 @@ int attn_bwd_text_split(int L) {
 
 namespace {
 struct BwdSizes {
-  size_t dq, l2, dqp, textk, textv;
-  size_t total() const { return dq + l2 + dqp + textk + textv; }
+  size_t dq, l2, dqp, textk, textv, kt;
+  size_t total() const { return dq + l2 + dqp + textk + textv + kt; }
 };
+int kt_rows(int L) { return (L + moc::kBN - 1) / moc::kBN * moc::kBN; }
 size_t al(size_t x) { return (x + 255) / 256 * 256; }
 BwdSizes bwd_sizes(const moc_layout* lay, int S) {
   BwdSizes z;
@@ -439,6 +543,8 @@ BwdSizes bwd_sizes(const moc_layout* lay, int S) {
   const size_t tp = static_cast<size_t>(lay->B) * lay->H * ns * (text > 0 ? text : 1) * lay->d;
   z.textk = al(sizeof(float) * tp);
   z.textv = al(sizeof(float) * tp);
+  // transposed copy of K, [B*H][d][Lp] bf16, for the dQ kernel's K^T tiles
+  z.kt = al(static_cast<size_t>(lay->B) * lay->H * lay->d * kt_rows(lay->L) * 2);
   return z;
 }
 }  // namespace
@@ -458,6 +564,8 @@ static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   float* dqp = reinterpret_cast<float*>(w); w += z.dqp;
   float* textK = reinterpret_cast<float*>(w); w += z.textk;
   float* textV = reinterpret_cast<float*>(w); w += z.textv;
+  bf16_t* Kt = reinterpret_cast<bf16_t*>(w); w += z.kt;
+  const int Lp = kt_rows(lay->L);
 
   const bf16_t* q = static_cast<const bf16_t*>(Q);
   const bf16_t* k = static_cast<const bf16_t*>(K);
@@ -478,19 +586,21 @@ static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   p.n_split = vl->n_text_split;
   p.scale_log2 = scale * moc::kLog2e;
   p.scale = scale;
+  if ((e = launch_transpose_rows(k, Kt, lay->B * lay->H, lay->L, Lp, D, st)) != hipSuccess)
+    return e;
   if (vl->S > 0 && vl->max_rtiles > 0) {
     p.max_tiles = vl->max_rtiles;
     hipLaunchKernelGGL((moc::bwd_dq_kernel<D, moc::BMODE_ROUTED>), dim3(vl->max_rtiles),
-                       dim3(moc::kBwdQNT), 0, st, q, k, v, g, Dq, l2, lay->chunk_offsets, p,
-                       vl->rtiles, vl->n_rtiles, vl->bucket_off, vl->bucket_q, vl->slot, dqp,
+                       dim3(moc::kBwdQNT), 0, st, q, k, v, Kt, Lp, g, Dq, l2, lay->chunk_offsets,
+                       p, vl->rtiles, vl->n_rtiles, vl->bucket_off, vl->bucket_q, vl->slot, dqp,
                        static_cast<bf16_t*>(dQ));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   p.max_tiles = vl->max_atiles;
   hipLaunchKernelGGL((moc::bwd_dq_kernel<D, moc::BMODE_ANCHOR>),
-                     dim3(vl->max_atiles * lay->B * lay->H), dim3(moc::kBwdQNT), 0, st, q, k, v, g,
-                     Dq, l2, lay->chunk_offsets, p, vl->atiles, vl->n_atiles, vl->bucket_off,
-                     vl->bucket_q, vl->slot, dqp, static_cast<bf16_t*>(dQ));
+                     dim3(vl->max_atiles * lay->B * lay->H), dim3(moc::kBwdQNT), 0, st, q, k, v,
+                     Kt, Lp, g, Dq, l2, lay->chunk_offsets, p, vl->atiles, vl->n_atiles,
+                     vl->bucket_off, vl->bucket_q, vl->slot, dqp, static_cast<bf16_t*>(dQ));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   p.max_tiles = vl->max_ktiles;
   hipLaunchKernelGGL((moc::bwd_dkdv_kernel<D>), dim3(vl->max_ktiles * lay->B * lay->H),

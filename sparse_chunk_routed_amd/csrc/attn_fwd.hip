@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kNT) void attn_fwd_kernel(
   const int n1 = (r1b - r1a + kBN - 1) / kBN;
   const int n2 = (r2b - r2a + kBN - 1) / kBN;
   const int ntot = n1 + n2;
-  auto tile_pos = [&](int j, int& key0, int& kend) {
+  auto tile_pos = [&](int j, int& key0, int& kend) __attribute__((always_inline)) {
     if (j < n1) { key0 = r1a + j * kBN; kend = r1b; }
     else { key0 = r2a + (j - n1) * kBN; kend = r2b; }
   };
@@ -281,36 +281,9 @@ __global__ __launch_bounds__(kNT) void attn_fwd_kernel(
 }
 
 
-// V [B*H][L][D] -> V^T [B*H][D][Lp] (Lp = L rounded up to 64, zero padded), so that attention
-// tiles of 64 aligned keys read each dim's 64 keys as 128 contiguous bytes.
-template <int D>
-__global__ __launch_bounds__(256) void transpose_v_kernel(const bf16_t* __restrict__ V,
-                                                          bf16_t* __restrict__ Vt, int L, int Lp) {
-  __shared__ __attribute__((aligned(16))) bf16_t tile[kBN * (D + 8)];
-  const int bh = blockIdx.y;
-  const int k0 = blockIdx.x * kBN;
-  for (int e = threadIdx.x; e < kBN * D / 8; e += blockDim.x) {
-    const int r = e / (D / 8), c = e % (D / 8);
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (k0 + r < L) v = *reinterpret_cast<const u32x4*>(V + (static_cast<size_t>(bh) * L + k0 + r) * D + c * 8);
-    *reinterpret_cast<u32x4*>(tile + r * (D + 8) + c * 8) = v;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < D * (kBN / 8); e += blockDim.x) {
-    const int d = e / (kBN / 8), c = e % (kBN / 8);
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = static_cast<uint32_t>(tile[(c * 8 + 2 * i) * (D + 8) + d]) |
-             (static_cast<uint32_t>(tile[(c * 8 + 2 * i + 1) * (D + 8) + d]) << 16);
-    *reinterpret_cast<u32x4*>(Vt + (static_cast<size_t>(bh) * D + d) * Lp + k0 + c * 8) =
-        u32x4{w[0], w[1], w[2], w[3]};
-  }
-}
-
-// bf16 attention forward: same work decomposition and epilogue as attn_fwd_kernel, with K and
-// V^T tiles staged by direct-to-LDS copies into swizzled 64-key-aligned tiles (two stages, one
-// barrier per tile) and the permuted key order of attn_fwd_lds.h.
+// bf16 attention forward: same work decomposition and epilogue as attn_fwd_kernel; two wave
+// groups half a tile apart, K and V^T tiles staged by direct-to-LDS copies into padded
+// 64-key-aligned tiles (three skewed stages) and the permuted key order of attn_fwd_lds.h.
 template <int D, int MODE>
 __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ Vt,
@@ -368,7 +341,7 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
   StageCopier<D, kNW> cp;
   cp.init(wv, lane, Lp);
   const int ncopy = cp.count();
-  auto wait_but_newest = [&]() {
+  auto wait_but_newest = [&]() __attribute__((always_inline)) {
     constexpr int NB = LT::KBLK / kNW + LT::VBLK / kNW;
     if (ncopy == NB) __builtin_amdgcn_s_waitcnt(0x0070 | NB);
     else if (ncopy == NB + 1) __builtin_amdgcn_s_waitcnt(0x0070 | (NB + 1));
@@ -391,7 +364,7 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
   const int m1a = r1a >> 6, n1 = r1b > r1a ? ((r1b - 1) >> 6) - m1a + 1 : 0;
   const int m2a = r2a >> 6, n2 = r2b > r2a ? ((r2b - 1) >> 6) - m2a + 1 : 0;
   const int ntot = n1 + n2;
-  auto tile_of = [&](int j, int& base, int& lo, int& hi) {
+  auto tile_of = [&](int j, int& base, int& lo, int& hi) __attribute__((always_inline)) {
     int ra, rb;
     if (j < n1) { base = (m1a + j) * kBN; ra = r1a; rb = r1b; }
     else { base = (m2a + j - n1) * kBN; ra = r2a; rb = r2b; }
@@ -399,12 +372,12 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
     hi = rb - base < kBN ? rb - base : kBN;
   };
   const int kmax = p.L - 1;
-  auto tile_base = [&](int j) { return j < n1 ? (m1a + j) * kBN : (m2a + j - n1) * kBN; };
+  auto tile_base = [&](int j) __attribute__((always_inline)) { return j < n1 ? (m1a + j) * kBN : (m2a + j - n1) * kBN; };
   // Skewed stage j (0 <= j <= ntot) holds K of tile j and V^T of tile j-1: both are read in the
   // same pair of half-steps (see below). Indices past the ends are clamped; those halves are
   // loaded but never read, so every wave issues the same number of copies per stage.
   const uint32_t lds0 = lds_addr(st0), lds1 = lds_addr(st1), lds2 = lds_addr(st2);
-  auto issue = [&](int j, uint32_t lds) {
+  auto issue = [&](int j, uint32_t lds) __attribute__((always_inline)) {
     if (j > ntot || ntot == 0) return;
     cp.issue(lds, Kbh, tile_base(j < ntot ? j : ntot - 1), kmax, Vtbh,
              tile_base(j > 0 ? j - 1 : 0));
@@ -420,9 +393,9 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
   // j-3, so three LDS buffers give every copy at least three half-steps to land.
   f32x16 s[2];
   bf16x8 pb[4];  // P^T of the previous tile, packed for the four 16-key MFMA steps
-  auto scores = [&](const char* st) { score_tile_swz<D>(st, qf, s, ql, g); };
+  auto scores = [&](const char* st) __attribute__((always_inline)) { score_tile_swz<D>(st, qf, s, ql, g); };
   // steady MFMA half-step: O += V P of tile j-1, then S of tile j, both from stage j
-  auto mfma_full = [&](const char* st) {
+  auto mfma_full = [&](const char* st) __attribute__((always_inline)) {
     pv_swz_packed<D>(st, pb, acc, ql, g);
     scores(st);
     // operand reads run kReadAhead ahead of the MFMAs that use them (bounded registers)
@@ -436,13 +409,13 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
     __builtin_amdgcn_sched_group_barrier(0x008, kReadAhead, 0);
   };
   // last MFMA half-step: O += V P of the last tile, from stage ntot
-  auto mfma_last = [&]() {
+  auto mfma_last = [&]() __attribute__((always_inline)) {
     const int r = ntot % 3;
     if (r == 0) pv_swz_packed<D>(st0, pb, acc, ql, g);
     else if (r == 1) pv_swz_packed<D>(st1, pb, acc, ql, g);
     else pv_swz_packed<D>(st2, pb, acc, ql, g);
   };
-  auto valu_half = [&](int j) {
+  auto valu_half = [&](int j) __attribute__((always_inline)) {
     int base, lo, hi;
     tile_of(j, base, lo, hi);
     if (lo > 0 || hi < kBN) {  // partial tile at a range edge: mask keys outside [lo, hi)
@@ -483,7 +456,7 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
   };
   // workgroup barrier that no instruction is scheduled across; copies in flight stay in flight
   // (a fenced __syncthreads would wait for them)
-  auto bar = [&]() {
+  auto bar = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -491,7 +464,7 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
     __builtin_amdgcn_sched_barrier(0);
   };
   // end of half-step 2i+1: stage i+1 must have landed; stage i+2 (issued at 2i) may stay in flight
-  auto wait_next = [&](int i) {
+  auto wait_next = [&](int i) __attribute__((always_inline)) {
     if (i + 2 <= ntot) wait_but_newest();
     else __builtin_amdgcn_s_waitcnt(0x0070);
   };
@@ -512,7 +485,7 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
       valu_half(0);
       wait_next(0);
       bar();
-      auto step = [&](int j, const char* cur, uint32_t nxt2) {
+      auto step = [&](int j, const char* cur, uint32_t nxt2) __attribute__((always_inline)) {
         mfma_full(cur);
         bar();
         issue(j + 2, nxt2);
@@ -539,7 +512,7 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
       issue(3, lds0);
       valu_half(0);
       bar();
-      auto step = [&](int j, const char* cur, uint32_t cur_lds) {
+      auto step = [&](int j, const char* cur, uint32_t cur_lds) __attribute__((always_inline)) {
         mfma_full(cur);
         wait_next(j);
         bar();
@@ -624,6 +597,19 @@ int attn_tile_rows() { return moc::kBM; }
 // rows of the transposed V copy: L rounded up to the 64-key tile
 int attn_vt_rows(int L) { return (L + moc::kBN - 1) / moc::kBN * moc::kBN; }
 
+// X [BH][L][d] -> X^T [BH][d][Lp] (bf16), the only instantiation of the transpose kernel
+hipError_t launch_transpose_rows(const void* X, void* Xt, int BH, int L, int Lp, int d,
+                                 hipStream_t st) {
+  using moc::bf16_t;
+  if (d == 128)
+    hipLaunchKernelGGL((moc::transpose_rows_kernel<128>), dim3(Lp / moc::kBN, BH), dim3(256), 0,
+                       st, static_cast<const bf16_t*>(X), static_cast<bf16_t*>(Xt), L, Lp);
+  else
+    hipLaunchKernelGGL((moc::transpose_rows_kernel<64>), dim3(Lp / moc::kBN, BH), dim3(256), 0,
+                       st, static_cast<const bf16_t*>(X), static_cast<bf16_t*>(Xt), L, Lp);
+  return hipGetLastError();
+}
+
 size_t attn_fwd_vt_bytes(const moc_layout* lay) {
   if (lay->dtype != MOC_BF16) return 0;
   return static_cast<size_t>(lay->B) * lay->H * lay->d * attn_vt_rows(lay->L) * 2;
@@ -666,9 +652,7 @@ static hipError_t launch_fwd_bf16(const moc_layout* lay, const moc_varlen* vl, c
   p.scale_log2 = scale * moc::kLog2e;
   const int Lp = attn_vt_rows(lay->L);
   bf16_t* Vt = static_cast<bf16_t*>(vt_ws);
-  hipLaunchKernelGGL((moc::transpose_v_kernel<D>), dim3(Lp / moc::kBN, lay->B * lay->H),
-                     dim3(256), 0, st, static_cast<const bf16_t*>(V), Vt, lay->L, Lp);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_transpose_rows(V, Vt, lay->B * lay->H, lay->L, Lp, D, st);
   if (e != hipSuccess) return e;
   const bf16_t* q = static_cast<const bf16_t*>(Q);
   const bf16_t* k = static_cast<const bf16_t*>(K);

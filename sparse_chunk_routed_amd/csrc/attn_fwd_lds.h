@@ -30,6 +30,14 @@ typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 // drain copies meant to stay in flight); the asm has no register outputs, and the callers wait
 // for completion with an explicit s_waitcnt vmcnt and a barrier before any wave reads the stage.
 __device__ __forceinline__ void copy16_to_lds(const void* gbase, uint32_t voff, uint32_t lds) {
+  // the base and the LDS address are wave-uniform; make that visible (a no-op for values the
+  // compiler already keeps in scalar registers)
+  // (readfirstlane returns a signed int: both halves go through uint32_t, no sign extension)
+  const uint64_t gb = reinterpret_cast<uint64_t>(gbase);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(gb)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(gb >> 32)));
+  gbase = reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  lds = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(lds)));
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
@@ -121,6 +129,91 @@ struct StageCopier {
     for (int i = 0; i < VI; ++i) {
       if (i * NW + NW > LT::VBLK && wv + i * NW >= LT::VBLK) break;
       copy16_to_lds(vb, voff[i], lds + LT::KBYTES + (wv + i * NW) * 1024);
+    }
+  }
+};
+
+// X [B*H][L][D] -> X^T [B*H][D][Lp] (Lp = L rounded up to 64, zero padded), so that tiles of 64
+// aligned keys read each dim's 64 keys as 128 contiguous bytes (V for the forward, K for the
+// backward's dQ). One workgroup per 64-row tile of one (b, h).
+template <int D>
+__global__ __launch_bounds__(256) void transpose_rows_kernel(const bf16_t* __restrict__ V,
+                                                             bf16_t* __restrict__ Vt, int L,
+                                                             int Lp) {
+  __shared__ __attribute__((aligned(16))) bf16_t tile[kBN * (D + 8)];
+  const int bh = blockIdx.y;
+  const int k0 = blockIdx.x * kBN;
+  for (int e = threadIdx.x; e < kBN * D / 8; e += blockDim.x) {
+    const int r = e / (D / 8), c = e % (D / 8);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (k0 + r < L) v = *reinterpret_cast<const u32x4*>(V + (static_cast<size_t>(bh) * L + k0 + r) * D + c * 8);
+    *reinterpret_cast<u32x4*>(tile + r * (D + 8) + c * 8) = v;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < D * (kBN / 8); e += blockDim.x) {
+    const int d = e / (kBN / 8), c = e % (kBN / 8);
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(tile[(c * 8 + 2 * i) * (D + 8) + d]) |
+             (static_cast<uint32_t>(tile[(c * 8 + 2 * i + 1) * (D + 8) + d]) << 16);
+    *reinterpret_cast<u32x4*>(Vt + (static_cast<size_t>(bh) * D + d) * Lp + k0 + c * 8) =
+        u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// Direct-to-LDS copies of one wave for a stage made of NROW row tiles (64 rows of D bf16 each,
+// pitch KROW chunks, rows past kmax clamped) followed by one transposed tile (D rows of 64 keys,
+// pitch VROW chunks). The stage's 1 KB blocks are numbered in that order; wave w copies blocks
+// w, w + NW, ... The per-lane source offsets are recomputed at every issue (a few VALU per
+// copy) so that they hold no registers across the kernel's main loop.
+template <int D, int NW, int NROW>
+struct RowsTCopier {
+  using LT = LdsTiles<D>;
+  static constexpr int NBLK = NROW * LT::KBLK + LT::VBLK;
+  static constexpr int SLOTS = (NBLK + NW - 1) / NW;
+  static constexpr int BYTES = NBLK * 1024;  // LDS bytes of one stage
+  int wv, lane, Lp;
+
+  __device__ __forceinline__ void init(int wave, int ln, int lp) {
+    wv = wave;
+    lane = ln;
+    Lp = lp;
+  }
+
+  __device__ __forceinline__ int count() const { return NBLK / NW + (wv < NBLK % NW); }
+
+  // Row tile 0 copies rows kbase .. kbase+63 of r0, row tile 1 (NROW == 2) the same rows of r1
+  // (each the (b, h) slice base); the transposed tile copies keys tkey .. tkey+63 of tbase
+  // ([D][Lp] layout).
+  __device__ __forceinline__ void issue(uint32_t lds, const bf16_t* r0, const bf16_t* r1,
+                                        int kbase, int kmax, const bf16_t* tbase,
+                                        int tkey) const {
+    const uint32_t lim = static_cast<uint32_t>(kmax - kbase);  // >= 0: kbase <= kmax
+    const bf16_t* tb = tbase + tkey;
+    const bf16_t* rb0 = r0 + static_cast<size_t>(kbase) * D;
+    const bf16_t* rb1 = r1 + static_cast<size_t>(kbase) * D;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // recompute the offsets here rather than hold them in registers
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      const int blk = wv + i * NW;
+      if (blk >= NBLK) break;
+      if (blk < NROW * LT::KBLK) {
+        const bf16_t* rb = (NROW > 1 && blk >= LT::KBLK) ? rb1 : rb0;
+        const int pos = (blk % LT::KBLK) * 64 + ln;
+        uint32_t r = pos / LT::KROW;
+        int c = pos % LT::KROW;
+        if (c >= LT::KCH) c = 0;
+        r = r < lim ? r : lim;  // also keeps padding rows past the tile inside the slice
+        copy16_to_lds(rb, r * (D * 2) + c * 16, lds + blk * 1024);
+      } else {
+        const int pos = (blk - NROW * LT::KBLK) * 64 + ln;
+        int d = pos / LT::VROW, c = pos % LT::VROW;
+        if (c >= kBN / 8) c = 0;
+        if (d >= D) d = D - 1;
+        copy16_to_lds(tb, static_cast<uint32_t>(d) * Lp * 2 + c * 16, lds + blk * 1024);
+      }
     }
   }
 };
