@@ -36,6 +36,7 @@ constexpr int kTextSplitRows = 16384;      // queries per text-key split
 
 struct BwdParams {
   int B, H, L, C, S, max_tiles;
+  int Lp;  // L rounded up to 64: row stride of the per-(b, h) statistics and transposed copies
   int text_begin, text_len, n_split;
   float scale_log2;  // softmax_scale * log2(e)
   float scale;
@@ -52,7 +53,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16_t* __restrict_
                                                        const bf16_t* __restrict__ dO,
                                                        const float* __restrict__ lse,
                                                        float* __restrict__ Dq,
-                                                       float* __restrict__ lse2, int64_t rows) {
+                                                       float* __restrict__ lse2, int64_t rows,
+                                                       int L, int Lp) {
   constexpr int TPR = D / 8;
   constexpr int RPB = 256 / TPR;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / TPR;
@@ -67,8 +69,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16_t* __restrict_
 #pragma unroll
   for (int o = TPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
   if (row < rows && c == 0) {
-    Dq[row] = s;
-    lse2[row] = lse[row] * kLog2e;
+    const int64_t out = (row / L) * Lp + row % L;  // statistics rows are Lp apart
+    Dq[out] = s;
+    lse2[out] = lse[row] * kLog2e;
   }
 }
 
@@ -146,8 +149,9 @@ __global__ __launch_bounds__(kBwdQNT) void bwd_dq_kernel(
   qf.load(Q + bh_off + static_cast<size_t>(t) * D, g);
   dof.load(dO + bh_off + static_cast<size_t>(t) * D, g);
   const size_t trow = static_cast<size_t>(bh) * p.L + t;
-  const float l2 = lse2[trow];
-  const float dd = Dq[trow];
+  const size_t srow = static_cast<size_t>(bh) * p.Lp + t;
+  const float l2 = lse2[srow];
+  const float dd = Dq[srow];
   const float c2 = p.scale_log2;
 
   f32x16 acc[D / 32];
@@ -329,13 +333,203 @@ __global__ __launch_bounds__(kBwdQNT) void bwd_dq_kernel(
   }
 }
 
+// Key-centric dK/dV over a key tile's anchor queries (bf16). A workgroup owns the tile's 128
+// keys (4 waves x 32; K and V rows in registers as B operands) and streams its anchor query
+// range (the keys' shot, or a split of all queries for text keys) in aligned 32-query tiles,
+// each staged by register-free copies as Q rows, dO rows, Q^T, dO^T and the rows' lse2 / D
+// (two stages). Per tile a wave computes S = Q K^T and dP = dO V^T (lane = key; the Q and dO
+// rows are read in a permuted order so that each lane's values come in runs of 8 queries),
+// P = exp2(S scale log2(e) - lse2) and dS = P (dP - D) on the VALU, then dV += P^T dO and
+// dK += dS^T Q with P^T and dS^T straight from registers. Two workgroups share a CU (at most
+// 256 registers), so one's MFMAs overlap the other's VALU. The sums go out in fp32: to dKa / dVa
+// for video keys (the routed pass adds to them) and to the split partials for text keys.
+template <int D>
+__global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_anchor_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const bf16_t* __restrict__ dO, const bf16_t* __restrict__ QT, const bf16_t* __restrict__ dOT,
+    const float* __restrict__ Dq, uint32_t l2_delta, BwdParams p,
+    const int32_t* __restrict__ ktiles, const int32_t* __restrict__ n_ktiles,
+    float* __restrict__ textK, float* __restrict__ textV, float* __restrict__ dKa,
+    float* __restrict__ dVa) {
+  using QTl = QTiles<D>;
+  using CP = QTileCopier<D, kBwdKNW>;
+  __shared__ __attribute__((aligned(1024))) char st0[QTl::BYTES];
+  __shared__ __attribute__((aligned(1024))) char st1[QTl::BYTES];
+
+  const int nt = n_ktiles[0];
+  const int nwork = nt * p.B * p.H;
+  if (static_cast<int>(blockIdx.x) >= nwork) return;
+  const int lid = xcd_remap(blockIdx.x, nwork);
+  const int bh = lid / nt;
+  const int32_t* kt6 = ktiles + 6 * (lid % nt);
+  const int k0 = kt6[0], k1 = kt6[1], c = kt6[2], qa = kt6[3], qb = kt6[4], sp = kt6[5];
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int ql = lane & 31, g = lane >> 5;
+  const int key = k0 + wv * 32 + ql;
+  const int kl = key < k1 ? key : k1 - 1;
+  const size_t bh_off = static_cast<size_t>(bh) * p.L * D;
+  QFrag<bf16_t, D> kf, vf;
+  kf.load(K + bh_off + static_cast<size_t>(kl) * D, g);
+  vf.load(V + bh_off + static_cast<size_t>(kl) * D, g);
+  const float c2 = p.scale_log2;
+
+  CP cp;
+  cp.init(wv, lane, p.Lp);
+  const int ncopy = cp.count();
+  auto wait_but_newest = [&]() __attribute__((always_inline)) {
+    constexpr int NB = QTl::NBLK / kBwdKNW;
+    if (ncopy == NB) __builtin_amdgcn_s_waitcnt(0x0070 | NB);
+    else __builtin_amdgcn_s_waitcnt(0x0070 | (NB + 1));
+  };
+  const bf16_t* Qbh = Q + bh_off;
+  const bf16_t* dObh = dO + bh_off;
+  const size_t tslice = static_cast<size_t>(bh) * D * p.Lp;
+  const bf16_t* QTbh = QT + tslice;
+  const bf16_t* dOTbh = dOT + tslice;
+  const float* Dbh = Dq + static_cast<size_t>(bh) * p.Lp;
+
+  f32x16 accK[D / 32], accV[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    accK[db] = f32x16{};
+    accV[db] = f32x16{};
+  }
+  const int nqt = qb > qa ? ((qb - 1) >> 5) - (qa >> 5) + 1 : 0;
+  const int qbase0 = qa & ~31;
+  const uint32_t lds0 = lds_addr(st0), lds1 = lds_addr(st1);
+  auto issue = [&](int j, uint32_t lds) __attribute__((always_inline)) {
+    if (j >= nqt) return;
+    cp.issue(lds, Qbh, dObh, QTbh, dOTbh, Dbh, l2_delta, qbase0 + 32 * j, p.L);
+  };
+  auto bar = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const int rq = QTl::RROW * kperm(ql) + g;  // permuted row of this lane's A operand (chunks)
+  auto tile = [&](int j, const char* cur) __attribute__((always_inline)) {
+    // S = Q K^T and dP = dO V^T for 32 queries x the wave's 32 keys
+    f32x16 s = {}, dp = {};
+    const char* qr = cur + QTl::Q_OFF + rq * 16;
+    const char* orr = cur + QTl::DO_OFF + rq * 16;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const bf16x8 aq = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qr + kk * 32));
+      const bf16x8 ao = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(orr + kk * 32));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf.q[kk], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf.q[kk], dp, 0, 0, 0);
+    }
+    // operand reads run two ahead of their MFMAs (bounded registers)
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * (D / 16) - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    // value i of lane group g holds query 16 (i >> 3) + 8 g + (i & 7) of the tile
+    const float* stl = reinterpret_cast<const float*>(cur + QTl::ST_OFF);
+    const int qbase = qbase0 + 32 * j;
+    const bool partial = qbase < qa || qbase + 32 > qb;
+    bf16x8 pa[2], da[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x4 l2a = *reinterpret_cast<const f32x4*>(stl + 16 * h + 8 * g);
+      const f32x4 l2b = *reinterpret_cast<const f32x4*>(stl + 16 * h + 8 * g + 4);
+      const f32x4 dda = *reinterpret_cast<const f32x4*>(stl + 32 + 16 * h + 8 * g);
+      const f32x4 ddb = *reinterpret_cast<const f32x4*>(stl + 32 + 16 * h + 8 * g + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 8 * h + e;
+        const float l2 = e < 4 ? l2a[e] : l2b[e - 4];
+        const float dd = e < 4 ? dda[e] : ddb[e - 4];
+        float pr = fast_exp2(__builtin_fmaf(s[i], c2, -l2));
+        if (partial) {
+          const int qpos = qbase + 16 * h + 8 * g + e;
+          if (qpos < qa || qpos >= qb) pr = 0.f;
+        }
+        pa[h][e] = static_cast<__bf16>(pr);
+        da[h][e] = static_cast<__bf16>(pr * (dp[i] - dd));
+      }
+    }
+    // dV += P^T dO and dK += dS^T Q (B operands: dims of the transposed tiles, 8 queries each)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int toff = (QTl::TROW * (db * 32 + ql) + 2 * ks + g) * 16;
+        const bf16x8 bo =
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(cur + QTl::DOT_OFF + toff));
+        const bf16x8 bq =
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(cur + QTl::QT_OFF + toff));
+        accV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], bo, accV[db], 0, 0, 0);
+        accK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ks], bq, accK[db], 0, 0, 0);
+      }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * (D / 32) - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  };
+
+  if (nqt > 0) {
+    issue(0, lds0);
+    issue(1, lds1);
+    if (nqt > 1) wait_but_newest();
+    else __builtin_amdgcn_s_waitcnt(0x0070);
+    bar();
+    // tile j reads stage j & 1; only tile j+1's copies are in flight while it runs, and they
+    // must land before the barrier; after it, the freed buffer takes tile j+2
+    auto step = [&](int j, const char* cur, uint32_t cur_lds) __attribute__((always_inline)) {
+      tile(j, cur);
+      __builtin_amdgcn_s_waitcnt(0x0070);
+      bar();
+      issue(j + 2, cur_lds);
+    };
+    for (int j = 0; j < nqt; j += 2) {
+      step(j, st0, lds0);
+      if (j + 1 < nqt) step(j + 1, st1, lds1);
+    }
+  }
+
+  // output: accumulator rows are the wave's keys (value i: key 8 (i >> 2) + 4 g + (i & 3)),
+  // columns the dims (lane & 31 of each 32-dim block)
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int kk = k0 + wv * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+    if (kk >= k1) continue;
+    float *dk, *dv;
+    if (c >= 0) {
+      const size_t r = (static_cast<size_t>(bh) * p.L + kk) * D;
+      dk = dKa + r;
+      dv = dVa + r;
+    } else {
+      const size_t r = ((static_cast<size_t>(bh) * p.n_split + sp) * p.text_len +
+                        (kk - p.text_begin)) * D;
+      dk = textK + r;
+      dv = textV + r;
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      dk[db * 32 + ql] = accK[db][i];
+      dv[db * 32 + ql] = accV[db][i];
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kBwdKNT) void bwd_dkdv_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ Dq, const float* __restrict__ lse2,
     BwdParams p, const int32_t* __restrict__ ktiles, const int32_t* __restrict__ n_ktiles,
     const int32_t* __restrict__ bucket_off, const int32_t* __restrict__ bucket_q,
-    float* __restrict__ textK, float* __restrict__ textV, bf16_t* __restrict__ dK,
+    const float* __restrict__ dKa, const float* __restrict__ dVa, bf16_t* __restrict__ dK,
     bf16_t* __restrict__ dV) {
   constexpr int KSTR = D + 8, TSTR = kBwdQT + 4;
   constexpr int MAT = 2 * kBwdQT * KSTR + 2 * D * TSTR;  // Q rows, dO rows, Q^T, dO^T
@@ -349,7 +543,8 @@ __global__ __launch_bounds__(kBwdKNT) void bwd_dkdv_kernel(
   const int bh = lid / nt;
   const int tile = lid % nt;
   const int32_t* kt6 = ktiles + 6 * tile;
-  const int k0 = kt6[0], k1 = kt6[1], c = kt6[2], q0 = kt6[3], q1 = kt6[4], sp = kt6[5];
+  const int k0 = kt6[0], k1 = kt6[1], c = kt6[2];
+  if (c < 0) return;  // text keys: complete after the anchor pass and the split reduction
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int ql = lane & 31, g = lane >> 5;
@@ -361,7 +556,7 @@ __global__ __launch_bounds__(kBwdKNT) void bwd_dkdv_kernel(
   vf.load(V + bh_off + static_cast<size_t>(kl) * D, g);
   const float c2 = p.scale_log2;
 
-  const int na = q1 - q0;
+  const int na = 0, q0 = 0, q1 = 0;  // the anchor queries were done by bwd_dkdv_anchor_kernel
   int nb = 0, bstart = 0;
   if (c >= 0) {
     const int bucket = bh * p.C + c;
@@ -371,12 +566,27 @@ __global__ __launch_bounds__(kBwdKNT) void bwd_dkdv_kernel(
   const int nta = (na + kBwdQT - 1) / kBwdQT;
   const int ntb = (nb + kBwdQT - 1) / kBwdQT;
   const int ntot = nta + ntb;
-  const float* l2bh = lse2 + static_cast<size_t>(bh) * p.L;
-  const float* Dbh = Dq + static_cast<size_t>(bh) * p.L;
+  const float* l2bh = lse2 + static_cast<size_t>(bh) * p.Lp;
+  const float* Dbh = Dq + static_cast<size_t>(bh) * p.Lp;
 
+  // start from the anchor pass's sums for these keys (lane = key, 16 dims per 32-dim block)
   f32x16 accK[D / 32], accV[D / 32];
+  {
+    const size_t kr = (static_cast<size_t>(bh) * p.L + kl) * D;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) { accK[db] = f32x16{}; accV[db] = f32x16{}; }
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d0 = db * 32 + 8 * jj + 4 * g;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(dKa + kr + d0);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(dVa + kr + d0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          accK[db][4 * jj + e] = a[e];
+          accV[db][4 * jj + e] = v[e];
+        }
+      }
+  }
 
   auto row_token = [&](int j, int i) __attribute__((always_inline)) -> int {
     if (j < nta) {
@@ -448,7 +658,7 @@ __global__ __launch_bounds__(kBwdKNT) void bwd_dkdv_kernel(
   }
 
   if (key >= k1) return;
-  if (c >= 0) {
+  {
     bf16_t* kr = dK + bh_off + static_cast<size_t>(key) * D;
     bf16_t* vr = dV + bh_off + static_cast<size_t>(key) * D;
 #pragma unroll
@@ -466,19 +676,6 @@ __global__ __launch_bounds__(kBwdKNT) void bwd_dkdv_kernel(
         const uint32_t v1w = static_cast<uint32_t>(f32_to_bf16(accV[db][4 * jj + 2])) |
                              (static_cast<uint32_t>(f32_to_bf16(accV[db][4 * jj + 3])) << 16);
         *reinterpret_cast<u32x2*>(vr + d0) = u32x2{v0w, v1w};
-      }
-  } else {
-    const size_t prow = ((static_cast<size_t>(bh) * p.n_split + sp) * p.text_len +
-                         (key - p.text_begin)) * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int d0 = db * 32 + 8 * jj + 4 * g;
-        *reinterpret_cast<f32x4*>(textK + prow + d0) =
-            f32x4{accK[db][4 * jj], accK[db][4 * jj + 1], accK[db][4 * jj + 2], accK[db][4 * jj + 3]};
-        *reinterpret_cast<f32x4*>(textV + prow + d0) =
-            f32x4{accV[db][4 * jj], accV[db][4 * jj + 1], accV[db][4 * jj + 2], accV[db][4 * jj + 3]};
       }
   }
 }
@@ -526,8 +723,8 @@ int attn_bwd_text_split(int L) {
 
 namespace {
 struct BwdSizes {
-  size_t dq, l2, dqp, textk, textv, kt;
-  size_t total() const { return dq + l2 + dqp + textk + textv + kt; }
+  size_t dq, l2, dqp, textk, textv, kt, qt, dot, dka, dva;
+  size_t total() const { return dq + l2 + dqp + textk + textv + kt + qt + dot + dka + dva; }
 };
 int kt_rows(int L) { return (L + moc::kBN - 1) / moc::kBN * moc::kBN; }
 size_t al(size_t x) { return (x + 255) / 256 * 256; }
@@ -537,14 +734,21 @@ BwdSizes bwd_sizes(const moc_layout* lay, int S) {
   const size_t sel = rows * static_cast<size_t>(S);
   const size_t text = static_cast<size_t>(lay->text_end - lay->text_begin);
   const size_t ns = static_cast<size_t>(attn_bwd_text_split(lay->L));
-  z.dq = al(sizeof(float) * rows);
-  z.l2 = al(sizeof(float) * rows);
+  // D and lse2 rows are padded to Lp per (b, h) (16-byte aligned 32-query slices)
+  const size_t prow = static_cast<size_t>(lay->B) * lay->H * kt_rows(lay->L);
+  z.dq = al(sizeof(float) * prow);
+  z.l2 = al(sizeof(float) * prow);
   z.dqp = al(sizeof(float) * (sel > 0 ? sel : 1) * lay->d);
   const size_t tp = static_cast<size_t>(lay->B) * lay->H * ns * (text > 0 ? text : 1) * lay->d;
   z.textk = al(sizeof(float) * tp);
   z.textv = al(sizeof(float) * tp);
-  // transposed copy of K, [B*H][d][Lp] bf16, for the dQ kernel's K^T tiles
+  // transposed copies of K (dQ kernel) and of Q and dO (anchor dK/dV kernel), [B*H][d][Lp]
   z.kt = al(static_cast<size_t>(lay->B) * lay->H * lay->d * kt_rows(lay->L) * 2);
+  z.qt = z.kt;
+  z.dot = z.kt;
+  // fp32 dK and dV of video keys after the anchor pass, [B*H*L][d]
+  z.dka = al(sizeof(float) * rows * lay->d);
+  z.dva = z.dka;
   return z;
 }
 }  // namespace
@@ -565,6 +769,10 @@ static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   float* textK = reinterpret_cast<float*>(w); w += z.textk;
   float* textV = reinterpret_cast<float*>(w); w += z.textv;
   bf16_t* Kt = reinterpret_cast<bf16_t*>(w); w += z.kt;
+  bf16_t* Qt = reinterpret_cast<bf16_t*>(w); w += z.qt;
+  bf16_t* dOt = reinterpret_cast<bf16_t*>(w); w += z.dot;
+  float* dKa = reinterpret_cast<float*>(w); w += z.dka;
+  float* dVa = reinterpret_cast<float*>(w); w += z.dva;
   const int Lp = kt_rows(lay->L);
 
   const bf16_t* q = static_cast<const bf16_t*>(Q);
@@ -575,7 +783,7 @@ static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   const int64_t rows = static_cast<int64_t>(lay->B) * lay->H * lay->L;
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL((moc::bwd_prep_kernel<D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, st,
-                     o, g, lse, Dq, l2, rows);
+                     o, g, lse, Dq, l2, rows, lay->L, Lp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -586,8 +794,11 @@ static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   p.n_split = vl->n_text_split;
   p.scale_log2 = scale * moc::kLog2e;
   p.scale = scale;
-  if ((e = launch_transpose_rows(k, Kt, lay->B * lay->H, lay->L, Lp, D, st)) != hipSuccess)
-    return e;
+  p.Lp = Lp;
+  const int BH = lay->B * lay->H;
+  if ((e = launch_transpose_rows(k, Kt, BH, lay->L, Lp, D, st)) != hipSuccess) return e;
+  if ((e = launch_transpose_rows(q, Qt, BH, lay->L, Lp, D, st)) != hipSuccess) return e;
+  if ((e = launch_transpose_rows(g, dOt, BH, lay->L, Lp, D, st)) != hipSuccess) return e;
   if (vl->S > 0 && vl->max_rtiles > 0) {
     p.max_tiles = vl->max_rtiles;
     hipLaunchKernelGGL((moc::bwd_dq_kernel<D, moc::BMODE_ROUTED>), dim3(vl->max_rtiles),
@@ -603,9 +814,15 @@ static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, cons
                      vl->bucket_off, vl->bucket_q, vl->slot, dqp, static_cast<bf16_t*>(dQ));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   p.max_tiles = vl->max_ktiles;
+  // lse2 sits (l2 - Dq) floats after D, in the same [B*H][Lp] layout
+  const uint32_t l2_delta = static_cast<uint32_t>((l2 - Dq) * sizeof(float));
+  hipLaunchKernelGGL((moc::bwd_dkdv_anchor_kernel<D>), dim3(vl->max_ktiles * lay->B * lay->H),
+                     dim3(moc::kBwdKNT), 0, st, q, k, v, g, Qt, dOt, Dq, l2_delta, p, vl->ktiles,
+                     vl->n_ktiles, textK, textV, dKa, dVa);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((moc::bwd_dkdv_kernel<D>), dim3(vl->max_ktiles * lay->B * lay->H),
                      dim3(moc::kBwdKNT), 0, st, q, k, v, g, Dq, l2, p, vl->ktiles, vl->n_ktiles,
-                     vl->bucket_off, vl->bucket_q, textK, textV, static_cast<bf16_t*>(dK),
+                     vl->bucket_off, vl->bucket_q, dKa, dVa, static_cast<bf16_t*>(dK),
                      static_cast<bf16_t*>(dV));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.text_len > 0) {

@@ -218,6 +218,91 @@ struct RowsTCopier {
   }
 };
 
+// ---------------------------------------------------------------------------------------------
+// Query tiles of the key-centric backward: 32 consecutive (aligned) query positions of one
+// (b, h), staged as Q rows and dO rows (pitch D/8 + 1 chunks, A operands of S = Q K^T and
+// dP = dO V^T), Q^T and dO^T rows (D rows of 32 queries, pitch 5 chunks, B operands of
+// dK += dS^T Q and dV += P^T dO), and one block holding lse2[32] and D[32]. The odd pitches keep
+// the 16 lanes of an LDS read pass on 16 different bank slots.
+template <int D>
+struct QTiles {
+  static constexpr int T = 32;                          // queries per tile
+  static constexpr int RROW = D / 8 + 1;                // row pitch (chunks)
+  static constexpr int TROW = T / 8 + 1;                // transposed row pitch (chunks)
+  static constexpr int RBLK = (T * RROW + 63) / 64;     // 1 KB blocks of one row tile
+  static constexpr int TBLK = (D * TROW + 63) / 64;     // 1 KB blocks of one transposed tile
+  static constexpr int NBLK = 2 * RBLK + 2 * TBLK + 1;
+  static constexpr int BYTES = NBLK * 1024;
+  static constexpr int Q_OFF = 0;
+  static constexpr int DO_OFF = RBLK * 1024;
+  static constexpr int QT_OFF = 2 * RBLK * 1024;
+  static constexpr int DOT_OFF = (2 * RBLK + TBLK) * 1024;
+  static constexpr int ST_OFF = (2 * RBLK + 2 * TBLK) * 1024;  // lse2[32] then D[32] (fp32)
+};
+
+// Direct-to-LDS copies of one wave (of NW) for one query tile at aligned position qbase.
+// Rows past L-1 are clamped (their queries are masked); the transposed copies ([D][Lp]) and the
+// statistics ([Lp] per (b, h), 16-byte aligned since Lp and qbase are multiples of 32) stay in
+// their padded rows. Per-lane offsets are recomputed at each issue.
+template <int D, int NW>
+struct QTileCopier {
+  using QT = QTiles<D>;
+  static constexpr int SLOTS = (QT::NBLK + NW - 1) / NW;
+  int wv, lane, Lp;
+
+  __device__ __forceinline__ void init(int wave, int ln, int lp) {
+    wv = wave;
+    lane = ln;
+    Lp = lp;
+  }
+
+  __device__ __forceinline__ int count() const {
+    return QT::NBLK / NW + (wv < QT::NBLK % NW);
+  }
+
+  // Qbh, dObh: [L][D] slices; QTbh, dOTbh: [D][Lp] slices; Dbh: the [Lp] row of D, with the
+  // matching lse2 row l2_delta bytes further on (both arrays share one layout)
+  __device__ __forceinline__ void issue(uint32_t lds, const bf16_t* Qbh, const bf16_t* dObh,
+                                        const bf16_t* QTbh, const bf16_t* dOTbh,
+                                        const float* Dbh, uint32_t l2_delta, int qbase,
+                                        int L) const {
+    const uint32_t lim = static_cast<uint32_t>(L - 1 - qbase);  // >= 0
+    const bf16_t* qb = Qbh + static_cast<size_t>(qbase) * D;
+    const bf16_t* ob = dObh + static_cast<size_t>(qbase) * D;
+    const bf16_t* qt = QTbh + qbase;
+    const bf16_t* ot = dOTbh + qbase;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // recompute the offsets here rather than hold them in registers
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      const int blk = wv + i * NW;
+      if (blk >= QT::NBLK) break;
+      const uint32_t dst = lds + blk * 1024;
+      if (blk < 2 * QT::RBLK) {
+        const bf16_t* rb = blk < QT::RBLK ? qb : ob;
+        const int pos = (blk % QT::RBLK) * 64 + ln;
+        uint32_t r = pos / QT::RROW;
+        int c = pos % QT::RROW;
+        if (c >= D / 8) c = 0;
+        r = r < lim ? r : lim;
+        copy16_to_lds(rb, r * (D * 2) + c * 16, dst);
+      } else if (blk < 2 * QT::RBLK + 2 * QT::TBLK) {
+        const int tb = blk - 2 * QT::RBLK;
+        const bf16_t* src = tb < QT::TBLK ? qt : ot;
+        const int pos = (tb % QT::TBLK) * 64 + ln;
+        int d = pos / QT::TROW, c = pos % QT::TROW;
+        if (c >= QT::T / 8) c = 0;
+        if (d >= D) d = D - 1;
+        copy16_to_lds(src, static_cast<uint32_t>(d) * Lp * 2 + c * 16, dst);
+      } else {
+        // lanes 0-7: lse2[qbase .. +31], lanes 8-15: D[...]; other lanes repeat them
+        const int l16 = ln & 15;
+        copy16_to_lds(Dbh + qbase, (l16 < 8 ? l2_delta : 0u) + (l16 & 7) * 16, dst);
+      }
+    }
+  }
+};
+
 // S^T of one 64-key tile: blocks kb = 0, 1 (32 keys x 32 queries each) with the permuted key
 // order. The two accumulation chains are interleaved so that consecutive MFMAs never depend on
 // each other.
