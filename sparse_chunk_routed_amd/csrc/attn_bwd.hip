@@ -373,6 +373,11 @@ __global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_anchor_kernel(
   QFrag<bf16_t, D> kf, vf;
   kf.load(K + bh_off + static_cast<size_t>(kl) * D, g);
   vf.load(V + bh_off + static_cast<size_t>(kl) * D, g);
+  // Retire these loads before any copy is issued: their first use would otherwise be inside the
+  // tile loop, where the compiler's wait for them would also wait for copies in flight. The asm
+  // "uses" every fragment here, so the compiler waits for the loads at this point.
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) asm volatile("" ::"v"(kf.q[kk]), "v"(vf.q[kk]));
   const float c2 = p.scale_log2;
 
   CP cp;
@@ -411,52 +416,49 @@ __global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_anchor_kernel(
     __builtin_amdgcn_sched_barrier(0);
   };
   const int rq = QTl::RROW * kperm(ql) + g;  // permuted row of this lane's A operand (chunks)
-  auto tile = [&](int j, const char* cur) __attribute__((always_inline)) {
-    // S = Q K^T and dP = dO V^T for 32 queries x the wave's 32 keys
-    f32x16 s = {}, dp = {};
-    const char* qr = cur + QTl::Q_OFF + rq * 16;
-    const char* orr = cur + QTl::DO_OFF + rq * 16;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const bf16x8 aq = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qr + kk * 32));
-      const bf16x8 ao = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(orr + kk * 32));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf.q[kk], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf.q[kk], dp, 0, 0, 0);
-    }
-    // operand reads run two ahead of their MFMAs (bounded registers)
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-    for (int i = 0; i < 2 * (D / 16) - 2; ++i) {
+  // operand reads of an MFMA sequence run one ahead of their MFMAs (bounded registers)
+  auto pace = [&](int nm) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int i = 0; i < nm - 1; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    // value i of lane group g holds query 16 (i >> 3) + 8 g + (i & 7) of the tile
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  };
+  // One 32-query tile, in the order S -> P -> dV, dP -> dS -> dK, so that at most one 32x32
+  // score block and one packed block are live next to the accumulators (dS uses the packed P).
+  auto tile = [&](int j, const char* cur) __attribute__((always_inline)) {
+    const char* qr = cur + QTl::Q_OFF + rq * 16;
+    const char* orr = cur + QTl::DO_OFF + rq * 16;
     const float* stl = reinterpret_cast<const float*>(cur + QTl::ST_OFF);
     const int qbase = qbase0 + 32 * j;
     const bool partial = qbase < qa || qbase + 32 > qb;
-    bf16x8 pa[2], da[2];
+    // S = Q K^T (lane = key; value i of lane group g is query 16 (i >> 3) + 8 g + (i & 7))
+    f32x16 sp = {};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const bf16x8 aq = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qr + kk * 32));
+      sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf.q[kk], sp, 0, 0, 0);
+    }
+    pace(D / 16);
+    // P = exp2(S scale log2(e) - lse2), zero for queries outside [qa, qb)
+    bf16x8 pa[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const f32x4 l2a = *reinterpret_cast<const f32x4*>(stl + 16 * h + 8 * g);
-      const f32x4 l2b = *reinterpret_cast<const f32x4*>(stl + 16 * h + 8 * g + 4);
-      const f32x4 dda = *reinterpret_cast<const f32x4*>(stl + 32 + 16 * h + 8 * g);
-      const f32x4 ddb = *reinterpret_cast<const f32x4*>(stl + 32 + 16 * h + 8 * g + 4);
+      const f32x4 la = *reinterpret_cast<const f32x4*>(stl + 16 * h + 8 * g);
+      const f32x4 lb = *reinterpret_cast<const f32x4*>(stl + 16 * h + 8 * g + 4);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int i = 8 * h + e;
-        const float l2 = e < 4 ? l2a[e] : l2b[e - 4];
-        const float dd = e < 4 ? dda[e] : ddb[e - 4];
-        float pr = fast_exp2(__builtin_fmaf(s[i], c2, -l2));
+        float pr = fast_exp2(__builtin_fmaf(sp[i], c2, -(e < 4 ? la[e] : lb[e - 4])));
         if (partial) {
           const int qpos = qbase + 16 * h + 8 * g + e;
           if (qpos < qa || qpos >= qb) pr = 0.f;
         }
         pa[h][e] = static_cast<__bf16>(pr);
-        da[h][e] = static_cast<__bf16>(pr * (dp[i] - dd));
       }
     }
-    // dV += P^T dO and dK += dS^T Q (B operands: dims of the transposed tiles, 8 queries each)
+    // dV += P^T dO (B operand: dO^T rows, 8 queries each)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -464,18 +466,41 @@ __global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_anchor_kernel(
         const int toff = (QTl::TROW * (db * 32 + ql) + 2 * ks + g) * 16;
         const bf16x8 bo =
             __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(cur + QTl::DOT_OFF + toff));
+        accV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], bo, accV[db], 0, 0, 0);
+      }
+    pace(2 * (D / 32));
+    // dP = dO V^T
+    f32x16 dp = {};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const bf16x8 ao = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(orr + kk * 32));
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf.q[kk], dp, 0, 0, 0);
+    }
+    pace(D / 16);
+    // dS = P (dP - D), with the same bf16-rounded P that entered dV
+    bf16x8 da[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x4 da4 = *reinterpret_cast<const f32x4*>(stl + 32 + 16 * h + 8 * g);
+      const f32x4 db4 = *reinterpret_cast<const f32x4*>(stl + 32 + 16 * h + 8 * g + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 8 * h + e;
+        const float pr = static_cast<float>(pa[h][e]);
+        da[h][e] = static_cast<__bf16>(pr * (dp[i] - (e < 4 ? da4[e] : db4[e - 4])));
+      }
+    }
+    // dK += dS^T Q (B operand: Q^T rows)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int toff = (QTl::TROW * (db * 32 + ql) + 2 * ks + g) * 16;
         const bf16x8 bq =
             __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(cur + QTl::QT_OFF + toff));
-        accV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], bo, accV[db], 0, 0, 0);
         accK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ks], bq, accK[db], 0, 0, 0);
       }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-    for (int i = 0; i < 4 * (D / 32) - 2; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    pace(2 * (D / 32));
   };
 
   if (nqt > 0) {
