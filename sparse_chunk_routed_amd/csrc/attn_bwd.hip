@@ -10,12 +10,14 @@
 // Pairs come in the same blocks as the forward: anchor (a query tile x text U own-shot keys)
 // and routed (a bucket of gathered queries x one chunk). The kernels:
 //   prep      D_t and the base-2 LSE per query row.
+//   qblock    32-query blocks (Q and dO rows, their transposes, lse2 and D, contiguous) of the
+//             whole sequence and of every routed bucket (padded to 32 rows, pads have P = 0).
 //   dq        query-centric, like the forward (S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T):
 //             routed tiles write fp32 partial rows per (query, routed chunk); anchor tiles
 //             merge those partials in ascending chunk order and write dQ.
-//   dkdv      key-centric: a workgroup owns 128 keys of one chunk (4 waves x 32), streams 32-query
-//             tiles of the chunk's shot (anchor) and then of the chunk's routed bucket, and
-//             accumulates dV^T += dO^T P and dK^T += Q^T dS in registers (S = Q K^T).
+//   dkdv      key-centric: a workgroup owns 128 keys of one chunk (4 waves x 32) and streams
+//             the query blocks of the chunk's shot (anchor) and then of the chunk's routed
+//             bucket, accumulating dV += P^T dO and dK += dS^T Q in registers (S = Q K^T).
 //   text      text keys are attended by every query: their key tiles are split over query
 //             ranges into fp32 partials, summed here in a fixed order.
 // No float atomics anywhere, so the result is deterministic. The separate dQ and dK/dV passes
@@ -333,24 +335,23 @@ __global__ __launch_bounds__(kBwdQNT) void bwd_dq_kernel(
   }
 }
 
-// Key-centric dK/dV over a key tile's anchor queries (bf16). A workgroup owns the tile's 128
-// keys (4 waves x 32; K and V rows in registers as B operands) and streams its anchor query
-// range (the keys' shot, or a split of all queries for text keys) in aligned 32-query tiles,
-// each staged by register-free copies as Q rows, dO rows, Q^T, dO^T and the rows' lse2 / D
-// (two stages). Per tile a wave computes S = Q K^T and dP = dO V^T (lane = key; the Q and dO
-// rows are read in a permuted order so that each lane's values come in runs of 8 queries),
+// Key-centric dK/dV (bf16). A workgroup owns a key tile's 128 keys (4 waves x 32; K and V rows
+// in registers as B operands) and streams 32-query blocks: first its anchor range (the keys'
+// shot, or a split of all queries for text keys) from the sequence's blocks, then the chunk's
+// routed bucket from the gathered blocks. Blocks are staged by register-free copies (two
+// stages). Per block a wave computes S = Q K^T and dP = dO V^T (lane = key; the Q and dO rows
+// are read in a permuted order so that each lane's values come in runs of 8 queries),
 // P = exp2(S scale log2(e) - lse2) and dS = P (dP - D) on the VALU, then dV += P^T dO and
 // dK += dS^T Q with P^T and dS^T straight from registers. Two workgroups share a CU (at most
-// 256 registers), so one's MFMAs overlap the other's VALU. The sums go out in fp32: to dKa / dVa
-// for video keys (the routed pass adds to them) and to the split partials for text keys.
+// 256 registers), so one's MFMAs overlap the other's VALU. Video keys are complete at the end
+// (bf16 out); text keys write fp32 partials of their query split.
 template <int D>
-__global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_anchor_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const bf16_t* __restrict__ dO, const bf16_t* __restrict__ QT, const bf16_t* __restrict__ dOT,
-    const float* __restrict__ Dq, uint32_t l2_delta, BwdParams p,
+__global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_kernel(
+    const bf16_t* __restrict__ K, const bf16_t* __restrict__ V, BwdParams p,
     const int32_t* __restrict__ ktiles, const int32_t* __restrict__ n_ktiles,
-    float* __restrict__ textK, float* __restrict__ textV, float* __restrict__ dKa,
-    float* __restrict__ dVa) {
+    const char* __restrict__ qblocks, const char* __restrict__ gblocks,
+    const int32_t* __restrict__ gstart, float* __restrict__ textK, float* __restrict__ textV,
+    bf16_t* __restrict__ dK, bf16_t* __restrict__ dV) {
   using QTl = QTiles<D>;
   using CP = QTileCopier<D, kBwdKNW>;
   __shared__ __attribute__((aligned(1024))) char st0[QTl::BYTES];
@@ -381,19 +382,13 @@ __global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_anchor_kernel(
   const float c2 = p.scale_log2;
 
   CP cp;
-  cp.init(wv, lane, p.Lp);
+  cp.init(wv, lane);
   const int ncopy = cp.count();
   auto wait_but_newest = [&]() __attribute__((always_inline)) {
     constexpr int NB = QTl::NBLK / kBwdKNW;
     if (ncopy == NB) __builtin_amdgcn_s_waitcnt(0x0070 | NB);
     else __builtin_amdgcn_s_waitcnt(0x0070 | (NB + 1));
   };
-  const bf16_t* Qbh = Q + bh_off;
-  const bf16_t* dObh = dO + bh_off;
-  const size_t tslice = static_cast<size_t>(bh) * D * p.Lp;
-  const bf16_t* QTbh = QT + tslice;
-  const bf16_t* dOTbh = dOT + tslice;
-  const float* Dbh = Dq + static_cast<size_t>(bh) * p.Lp;
 
   f32x16 accK[D / 32], accV[D / 32];
 #pragma unroll
@@ -403,10 +398,24 @@ __global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_anchor_kernel(
   }
   const int nqt = qb > qa ? ((qb - 1) >> 5) - (qa >> 5) + 1 : 0;
   const int qbase0 = qa & ~31;
+  // anchor queries: the sequence's query blocks from qa's; routed queries of this chunk: the
+  // bucket's gathered blocks (pads have P = 0)
+  const char* ab = qblocks + (static_cast<size_t>(bh) * (p.Lp >> 5) + (qa >> 5)) * QTl::G_BYTES;
+  const char* gb = gblocks;
+  int ngt = 0;
+  if (c >= 0) {
+    const int bucket = bh * p.C + c;
+    const int g0 = gstart[bucket];
+    ngt = (gstart[bucket + 1] - g0) >> 5;
+    gb += static_cast<size_t>(g0 >> 5) * QTl::G_BYTES;
+  }
+  const int ntot = nqt + ngt;
   const uint32_t lds0 = lds_addr(st0), lds1 = lds_addr(st1);
   auto issue = [&](int j, uint32_t lds) __attribute__((always_inline)) {
-    if (j >= nqt) return;
-    cp.issue(lds, Qbh, dObh, QTbh, dOTbh, Dbh, l2_delta, qbase0 + 32 * j, p.L);
+    if (j >= ntot) return;
+    const char* blk = j < nqt ? ab + static_cast<size_t>(j) * QTl::G_BYTES
+                              : gb + static_cast<size_t>(j - nqt) * QTl::G_BYTES;
+    cp.issue(lds, blk);
   };
   auto bar = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
@@ -432,7 +441,7 @@ __global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_anchor_kernel(
     const char* orr = cur + QTl::DO_OFF + rq * 16;
     const float* stl = reinterpret_cast<const float*>(cur + QTl::ST_OFF);
     const int qbase = qbase0 + 32 * j;
-    const bool partial = qbase < qa || qbase + 32 > qb;
+    const bool partial = j < nqt && (qbase < qa || qbase + 32 > qb);
     // S = Q K^T (lane = key; value i of lane group g is query 16 (i >> 3) + 8 g + (i & 7))
     f32x16 sp = {};
 #pragma unroll
@@ -503,10 +512,10 @@ __global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_anchor_kernel(
     pace(2 * (D / 32));
   };
 
-  if (nqt > 0) {
+  if (ntot > 0) {
     issue(0, lds0);
     issue(1, lds1);
-    if (nqt > 1) wait_but_newest();
+    if (ntot > 1) wait_but_newest();
     else __builtin_amdgcn_s_waitcnt(0x0070);
     bar();
     // tile j reads stage j & 1; only tile j+1's copies are in flight while it runs, and they
@@ -517,191 +526,172 @@ __global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_anchor_kernel(
       bar();
       issue(j + 2, cur_lds);
     };
-    for (int j = 0; j < nqt; j += 2) {
+    for (int j = 0; j < ntot; j += 2) {
       step(j, st0, lds0);
-      if (j + 1 < nqt) step(j + 1, st1, lds1);
+      if (j + 1 < ntot) step(j + 1, st1, lds1);
     }
   }
 
   // output: accumulator rows are the wave's keys (value i: key 8 (i >> 2) + 4 g + (i & 3)),
-  // columns the dims (lane & 31 of each 32-dim block)
+  // columns the dims (lane & 31 of each 32-dim block). Video keys are complete: dK = scale
+  // dS^T Q and dV in bf16. Text keys hold one query split: fp32 partials.
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int kk = k0 + wv * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
     if (kk >= k1) continue;
-    float *dk, *dv;
     if (c >= 0) {
       const size_t r = (static_cast<size_t>(bh) * p.L + kk) * D;
-      dk = dKa + r;
-      dv = dVa + r;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        dK[r + db * 32 + ql] = f32_to_bf16(accK[db][i] * p.scale);
+        dV[r + db * 32 + ql] = f32_to_bf16(accV[db][i]);
+      }
     } else {
       const size_t r = ((static_cast<size_t>(bh) * p.n_split + sp) * p.text_len +
                         (kk - p.text_begin)) * D;
-      dk = textK + r;
-      dv = textV + r;
-    }
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      dk[db * 32 + ql] = accK[db][i];
-      dv[db * 32 + ql] = accV[db][i];
+      for (int db = 0; db < D / 32; ++db) {
+        textK[r + db * 32 + ql] = accK[db][i];
+        textV[r + db * 32 + ql] = accV[db][i];
+      }
     }
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kBwdKNT) void bwd_dkdv_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const bf16_t* __restrict__ dO, const float* __restrict__ Dq, const float* __restrict__ lse2,
-    BwdParams p, const int32_t* __restrict__ ktiles, const int32_t* __restrict__ n_ktiles,
-    const int32_t* __restrict__ bucket_off, const int32_t* __restrict__ bucket_q,
-    const float* __restrict__ dKa, const float* __restrict__ dVa, bf16_t* __restrict__ dK,
-    bf16_t* __restrict__ dV) {
-  constexpr int KSTR = D + 8, TSTR = kBwdQT + 4;
-  constexpr int MAT = 2 * kBwdQT * KSTR + 2 * D * TSTR;  // Q rows, dO rows, Q^T, dO^T
-  constexpr int STAGE = MAT + 4 * kBwdQT;                // + lse2[32], D[32] as floats
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * STAGE];
-
-  const int nt = n_ktiles[0];
-  const int nwork = nt * p.B * p.H;
-  if (static_cast<int>(blockIdx.x) >= nwork) return;
-  const int lid = xcd_remap(blockIdx.x, nwork);
-  const int bh = lid / nt;
-  const int tile = lid % nt;
-  const int32_t* kt6 = ktiles + 6 * tile;
-  const int k0 = kt6[0], k1 = kt6[1], c = kt6[2];
-  if (c < 0) return;  // text keys: complete after the anchor pass and the split reduction
-
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int ql = lane & 31, g = lane >> 5;
-  const int key = k0 + wv * 32 + ql;
-  const int kl = key < k1 ? key : k1 - 1;
-  const size_t bh_off = static_cast<size_t>(bh) * p.L * D;
-  QFrag<bf16_t, D> kf, vf;
-  kf.load(K + bh_off + static_cast<size_t>(kl) * D, g);
-  vf.load(V + bh_off + static_cast<size_t>(kl) * D, g);
-  const float c2 = p.scale_log2;
-
-  const int na = 0, q0 = 0, q1 = 0;  // the anchor queries were done by bwd_dkdv_anchor_kernel
-  int nb = 0, bstart = 0;
-  if (c >= 0) {
-    const int bucket = bh * p.C + c;
-    bstart = bucket_off[bucket];
-    nb = bucket_off[bucket + 1] - bstart;
-  }
-  const int nta = (na + kBwdQT - 1) / kBwdQT;
-  const int ntb = (nb + kBwdQT - 1) / kBwdQT;
-  const int ntot = nta + ntb;
-  const float* l2bh = lse2 + static_cast<size_t>(bh) * p.Lp;
-  const float* Dbh = Dq + static_cast<size_t>(bh) * p.Lp;
-
-  // start from the anchor pass's sums for these keys (lane = key, 16 dims per 32-dim block)
-  f32x16 accK[D / 32], accV[D / 32];
-  {
-    const size_t kr = (static_cast<size_t>(bh) * p.L + kl) * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int d0 = db * 32 + 8 * jj + 4 * g;
-        const f32x4 a = *reinterpret_cast<const f32x4*>(dKa + kr + d0);
-        const f32x4 v = *reinterpret_cast<const f32x4*>(dVa + kr + d0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          accK[db][4 * jj + e] = a[e];
-          accV[db][4 * jj + e] = v[e];
-        }
-      }
-  }
-
-  auto row_token = [&](int j, int i) __attribute__((always_inline)) -> int {
-    if (j < nta) {
-      const int tq = q0 + j * kBwdQT + i;
-      return tq < q1 ? tq : -1;
-    }
-    const int idx = (j - nta) * kBwdQT + i;
-    return idx < nb ? bucket_q[bstart + idx] : -1;
-  };
-  PairTile<D, kBwdQT, kBwdKNT> qt, dt;
-  float st_l2 = 0.f, st_d = 0.f;  // row statistics staged by threads 0..31
-  auto load = [&](int j) __attribute__((always_inline)) {
-    auto row_of = [&](int i) __attribute__((always_inline)) { return row_token(j, i); };
-    qt.load(Q + bh_off, row_of);
-    dt.load(dO + bh_off, row_of);
-    if (threadIdx.x < kBwdQT) {
-      const int tq = row_token(j, threadIdx.x);
-      st_l2 = tq >= 0 ? l2bh[tq] : __builtin_inff();  // an absent row gets P = 0
-      st_d = tq >= 0 ? Dbh[tq] : 0.f;
-    }
-  };
-  auto store = [&](bf16_t* st) __attribute__((always_inline)) {
-    qt.template store_rows<KSTR>(st);
-    dt.template store_rows<KSTR>(st + kBwdQT * KSTR);
-    qt.template store_transposed<TSTR>(st + 2 * kBwdQT * KSTR);
-    dt.template store_transposed<TSTR>(st + 2 * kBwdQT * KSTR + D * TSTR);
-    float* stats = reinterpret_cast<float*>(st + MAT);
-    if (threadIdx.x < kBwdQT) {
-      stats[threadIdx.x] = st_l2;
-      stats[kBwdQT + threadIdx.x] = st_d;
-    }
-  };
-  if (ntot > 0) {
-    load(0);
-    store(lds);
-    if (ntot > 1) load(1);
-  }
+// Start of every (b, h, chunk) bucket's gathered rows: sizes rounded up to 32, scanned in
+// bucket order; gstart[NB] is the total. One workgroup.
+__global__ __launch_bounds__(1024) void bwd_gather_scan_kernel(const int32_t* __restrict__ bucket_off,
+                                                               int NB,
+                                                               int32_t* __restrict__ gstart) {
+  __shared__ int32_t part[1024];
+  const int per = (NB + 1023) / 1024;
+  const int a = threadIdx.x * per;
+  const int e = a + per < NB ? a + per : NB;
+  auto padded = [&](int i) { return (bucket_off[i + 1] - bucket_off[i] + 31) & ~31; };
+  int sum = 0;
+  for (int i = a; i < e; ++i) sum += padded(i);
+  part[threadIdx.x] = sum;
   __syncthreads();
-
-  for (int j = 0; j < ntot; ++j) {
-    const bf16_t* cur = lds + (j & 1) * STAGE;
-    if (j + 1 < ntot) store(lds + ((j + 1) & 1) * STAGE);
-    if (j + 2 < ntot) load(j + 2);
-    const bf16_t* Qs = cur;
-    const bf16_t* dOs = cur + kBwdQT * KSTR;
-    const bf16_t* Qt = cur + 2 * kBwdQT * KSTR;
-    const bf16_t* dOt = Qt + D * TSTR;
-    const float* sl2 = reinterpret_cast<const float*>(cur + MAT);
-    const float* sD = sl2 + kBwdQT;
-    f32x16 s[1], dp;
-    s[0] = mma_nt<D, KSTR>(Qs, 0, kf, ql, g);   // S[q][key]: lane = key, 16 queries
-    dp = mma_nt<D, KSTR>(dOs, 0, vf, ql, g);    // dP[q][key]
-    f32x16 ds[1];
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl2 + 8 * i4 + 4 * g);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(sD + 8 * i4 + 4 * g);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * i4 + e;
-        const float pr = fast_exp2(__builtin_fmaf(s[0][i], c2, -l4[e]));
-        s[0][i] = pr;
-        ds[0][i] = pr * (dp[i] - d4[e]);
-      }
-    }
-    mma_tn<D, 1, TSTR>(dOt, s, accV, ql, g);   // dV^T += dO^T P
-    mma_tn<D, 1, TSTR>(Qt, ds, accK, ql, g);   // dK^T += Q^T dS
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = static_cast<int>(threadIdx.x) >= off ? part[threadIdx.x - off] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
     __syncthreads();
   }
+  int run = threadIdx.x > 0 ? part[threadIdx.x - 1] : 0;
+  for (int i = a; i < e; ++i) {
+    gstart[i] = run;
+    run += padded(i);
+  }
+  if (threadIdx.x == 1023) gstart[NB] = part[1023];
+}
 
-  if (key >= k1) return;
-  {
-    bf16_t* kr = dK + bh_off + static_cast<size_t>(key) * D;
-    bf16_t* vr = dV + bh_off + static_cast<size_t>(key) * D;
+// Query tile blocks (layout QTiles::G_*) for the key-centric kernel: 32 queries' Q and dO rows,
+// their transposes and lse2, D in one contiguous block. tok[r] is the query of row r, or -1 for
+// a pad (zero rows, lse2 = +inf so that P = 0, D = 0). Called by a whole workgroup of 256.
+template <int D>
+__device__ __forceinline__ void build_qblock(const bf16_t* __restrict__ Qbh,
+                                             const bf16_t* __restrict__ dObh,
+                                             const float* __restrict__ l2bh,
+                                             const float* __restrict__ Dbh, const int32_t* tok,
+                                             bf16_t* sq, bf16_t* so, char* __restrict__ blk) {
+  using QTl = QTiles<D>;
+  constexpr int PITCH = D + 4;  // bf16; rows 8 apart land 16 banks apart
+  constexpr int CPR = D / 8;    // 16-byte pieces per row
+  bf16_t* Qg = reinterpret_cast<bf16_t*>(blk);
+  bf16_t* dOg = Qg + 32 * D;
+  bf16_t* QgT = Qg + 2 * 32 * D;
+  bf16_t* dOgT = Qg + 3 * 32 * D;
+  float* Sg = reinterpret_cast<float*>(blk + QTl::G_ST);
+  if (threadIdx.x < 32) {
+    const int t = tok[threadIdx.x];
+    Sg[threadIdx.x] = t >= 0 ? l2bh[t] : __builtin_inff();
+    Sg[32 + threadIdx.x] = t >= 0 ? Dbh[t] : 0.f;
+  }
+  for (int id = threadIdx.x; id < 32 * CPR; id += 256) {
+    const int r = id / CPR, c = id % CPR;
+    const int t = tok[r];
+    u32x4 vq = {0u, 0u, 0u, 0u}, vo = {0u, 0u, 0u, 0u};
+    if (t >= 0) {
+      vq = *reinterpret_cast<const u32x4*>(Qbh + static_cast<size_t>(t) * D + c * 8);
+      vo = *reinterpret_cast<const u32x4*>(dObh + static_cast<size_t>(t) * D + c * 8);
+    }
+    *reinterpret_cast<u32x4*>(Qg + r * D + c * 8) = vq;
+    *reinterpret_cast<u32x4*>(dOg + r * D + c * 8) = vo;
+    u32x2* lq = reinterpret_cast<u32x2*>(sq + r * PITCH + c * 8);
+    u32x2* lo = reinterpret_cast<u32x2*>(so + r * PITCH + c * 8);
+    lq[0] = u32x2{vq[0], vq[1]};
+    lq[1] = u32x2{vq[2], vq[3]};
+    lo[0] = u32x2{vo[0], vo[1]};
+    lo[1] = u32x2{vo[2], vo[3]};
+  }
+  __syncthreads();
+  // transposed rows: row d holds the 32 queries of dim d; 16-byte piece c4 is queries 8 c4 ..
+  for (int id = threadIdx.x; id < D * 4; id += 256) {
+    const int d = id >> 2, c4 = id & 3;
+    uint32_t wq[4], wo[4];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int d0 = db * 32 + 8 * jj + 4 * g;
-        const uint32_t k0w = static_cast<uint32_t>(f32_to_bf16(accK[db][4 * jj] * p.scale)) |
-                             (static_cast<uint32_t>(f32_to_bf16(accK[db][4 * jj + 1] * p.scale)) << 16);
-        const uint32_t k1w = static_cast<uint32_t>(f32_to_bf16(accK[db][4 * jj + 2] * p.scale)) |
-                             (static_cast<uint32_t>(f32_to_bf16(accK[db][4 * jj + 3] * p.scale)) << 16);
-        *reinterpret_cast<u32x2*>(kr + d0) = u32x2{k0w, k1w};
-        const uint32_t v0w = static_cast<uint32_t>(f32_to_bf16(accV[db][4 * jj])) |
-                             (static_cast<uint32_t>(f32_to_bf16(accV[db][4 * jj + 1])) << 16);
-        const uint32_t v1w = static_cast<uint32_t>(f32_to_bf16(accV[db][4 * jj + 2])) |
-                             (static_cast<uint32_t>(f32_to_bf16(accV[db][4 * jj + 3])) << 16);
-        *reinterpret_cast<u32x2*>(vr + d0) = u32x2{v0w, v1w};
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int r = 8 * c4 + 2 * e;
+      wq[e] = static_cast<uint32_t>(sq[r * PITCH + d]) |
+              (static_cast<uint32_t>(sq[(r + 1) * PITCH + d]) << 16);
+      wo[e] = static_cast<uint32_t>(so[r * PITCH + d]) |
+              (static_cast<uint32_t>(so[(r + 1) * PITCH + d]) << 16);
+    }
+    *reinterpret_cast<u32x4*>(QgT + d * 32 + c4 * 8) = u32x4{wq[0], wq[1], wq[2], wq[3]};
+    *reinterpret_cast<u32x4*>(dOgT + d * 32 + c4 * 8) = u32x4{wo[0], wo[1], wo[2], wo[3]};
+  }
+  __syncthreads();
+}
+
+// QB_SEQ: the blocks of every (b, h)'s sequence, Lp / 32 per (b, h) (rows past L are pads);
+// a workgroup builds 8 blocks. QB_ROUTED: the blocks of the routed buckets, one routed tile (256
+// bucket positions) per workgroup; each bucket is padded to a multiple of 32 rows and starts
+// at gstart[bucket].
+enum { QB_SEQ = 0, QB_ROUTED = 1 };
+
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void bwd_qblock_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ dO, const float* __restrict__ Dq,
+    const float* __restrict__ lse2, BwdParams p, const int32_t* __restrict__ rtiles,
+    const int32_t* __restrict__ n_rtiles, const int32_t* __restrict__ bucket_off,
+    const int32_t* __restrict__ bucket_q, const int32_t* __restrict__ gstart,
+    char* __restrict__ blocks) {
+  using QTl = QTiles<D>;
+  __shared__ __attribute__((aligned(16))) bf16_t sq[32 * (D + 4)];
+  __shared__ __attribute__((aligned(16))) bf16_t so[32 * (D + 4)];
+  __shared__ int32_t tok[32];
+  int bh, first, end, b0 = 0, n = 0;
+  size_t blk0;  // block index of position `first`
+  if (MODE == QB_SEQ) {
+    bh = blockIdx.y;
+    first = blockIdx.x * kBwdQBM;
+    end = first + kBwdQBM < p.Lp ? first + kBwdQBM : p.Lp;
+    n = p.L;
+    blk0 = static_cast<size_t>(bh) * (p.Lp >> 5) + (first >> 5);
+  } else {
+    if (static_cast<int>(blockIdx.x) >= n_rtiles[0]) return;
+    const int bucket = rtiles[2 * blockIdx.x];
+    first = rtiles[2 * blockIdx.x + 1];
+    bh = bucket / p.C;
+    b0 = bucket_off[bucket];
+    n = bucket_off[bucket + 1] - b0;
+    const int np = (n + 31) & ~31;
+    end = first + kBwdQBM < np ? first + kBwdQBM : np;
+    blk0 = static_cast<size_t>(gstart[bucket] + first) >> 5;
+  }
+  const bf16_t* Qbh = Q + static_cast<size_t>(bh) * p.L * D;
+  const bf16_t* dObh = dO + static_cast<size_t>(bh) * p.L * D;
+  const float* l2bh = lse2 + static_cast<size_t>(bh) * p.Lp;
+  const float* Dbh = Dq + static_cast<size_t>(bh) * p.Lp;
+  for (int i0 = first; i0 < end; i0 += 32) {
+    if (threadIdx.x < 32) {
+      const int idx = i0 + threadIdx.x;
+      tok[threadIdx.x] = idx < n ? (MODE == QB_SEQ ? idx : bucket_q[b0 + idx]) : -1;
+    }
+    __syncthreads();
+    build_qblock<D>(Qbh, dObh, l2bh, Dbh, tok, sq, so,
+                    blocks + (blk0 + ((i0 - first) >> 5)) * QTl::G_BYTES);
   }
 }
 
@@ -748,11 +738,16 @@ int attn_bwd_text_split(int L) {
 
 namespace {
 struct BwdSizes {
-  size_t dq, l2, dqp, textk, textv, kt, qt, dot, dka, dva;
-  size_t total() const { return dq + l2 + dqp + textk + textv + kt + qt + dot + dka + dva; }
+  size_t dq, l2, dqp, textk, textv, kt, qb, gb, gstart;
+  size_t total() const { return dq + l2 + dqp + textk + textv + kt + qb + gb + gstart; }
 };
 int kt_rows(int L) { return (L + moc::kBN - 1) / moc::kBN * moc::kBN; }
 size_t al(size_t x) { return (x + 255) / 256 * 256; }
+size_t gather_rows(const moc_layout* lay, int S) {
+  const size_t sel = static_cast<size_t>(lay->B) * lay->H * lay->L * static_cast<size_t>(S);
+  const size_t nb = static_cast<size_t>(lay->B) * lay->H * lay->C;
+  return (sel + 31 * nb + 31) / 32 * 32;
+}
 BwdSizes bwd_sizes(const moc_layout* lay, int S) {
   BwdSizes z;
   const size_t rows = static_cast<size_t>(lay->B) * lay->H * lay->L;
@@ -767,13 +762,15 @@ BwdSizes bwd_sizes(const moc_layout* lay, int S) {
   const size_t tp = static_cast<size_t>(lay->B) * lay->H * ns * (text > 0 ? text : 1) * lay->d;
   z.textk = al(sizeof(float) * tp);
   z.textv = al(sizeof(float) * tp);
-  // transposed copies of K (dQ kernel) and of Q and dO (anchor dK/dV kernel), [B*H][d][Lp]
+  // transposed copy of K (dQ kernel), [B*H][d][Lp]
   z.kt = al(static_cast<size_t>(lay->B) * lay->H * lay->d * kt_rows(lay->L) * 2);
-  z.qt = z.kt;
-  z.dot = z.kt;
-  // fp32 dK and dV of video keys after the anchor pass, [B*H*L][d]
-  z.dka = al(sizeof(float) * rows * lay->d);
-  z.dva = z.dka;
+  // 32-query blocks of the dK/dV kernel: the sequence's (Lp / 32 per (b, h)) and the routed
+  // buckets' (each bucket padded to a multiple of 32 rows: at most B*H*L*S + 31 per bucket)
+  const size_t nb = static_cast<size_t>(lay->B) * lay->H * lay->C;
+  const size_t gtile = lay->d == 128 ? moc::QTiles<128>::G_BYTES : moc::QTiles<64>::G_BYTES;
+  z.qb = al(static_cast<size_t>(lay->B) * lay->H * (kt_rows(lay->L) / 32) * gtile);
+  z.gb = al(gather_rows(lay, S) / 32 * gtile);
+  z.gstart = al((nb + 1) * sizeof(int32_t));
   return z;
 }
 }  // namespace
@@ -794,10 +791,9 @@ static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   float* textK = reinterpret_cast<float*>(w); w += z.textk;
   float* textV = reinterpret_cast<float*>(w); w += z.textv;
   bf16_t* Kt = reinterpret_cast<bf16_t*>(w); w += z.kt;
-  bf16_t* Qt = reinterpret_cast<bf16_t*>(w); w += z.qt;
-  bf16_t* dOt = reinterpret_cast<bf16_t*>(w); w += z.dot;
-  float* dKa = reinterpret_cast<float*>(w); w += z.dka;
-  float* dVa = reinterpret_cast<float*>(w); w += z.dva;
+  char* qblocks = w; w += z.qb;
+  char* gblocks = w; w += z.gb;
+  int32_t* gstart = reinterpret_cast<int32_t*>(w); w += z.gstart;
   const int Lp = kt_rows(lay->L);
 
   const bf16_t* q = static_cast<const bf16_t*>(Q);
@@ -812,7 +808,7 @@ static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  BwdParams p;
+  BwdParams p{};
   p.B = lay->B; p.H = lay->H; p.L = lay->L; p.C = lay->C; p.S = vl->S;
   p.text_begin = lay->text_begin;
   p.text_len = lay->text_end - lay->text_begin;
@@ -822,8 +818,21 @@ static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   p.Lp = Lp;
   const int BH = lay->B * lay->H;
   if ((e = launch_transpose_rows(k, Kt, BH, lay->L, Lp, D, st)) != hipSuccess) return e;
-  if ((e = launch_transpose_rows(q, Qt, BH, lay->L, Lp, D, st)) != hipSuccess) return e;
-  if ((e = launch_transpose_rows(g, dOt, BH, lay->L, Lp, D, st)) != hipSuccess) return e;
+  const int NB = BH * lay->C;
+  hipLaunchKernelGGL(moc::bwd_gather_scan_kernel, dim3(1), dim3(1024), 0, st, vl->bucket_off, NB,
+                     gstart);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((moc::bwd_qblock_kernel<D, moc::QB_SEQ>),
+                     dim3((Lp + moc::kBwdQBM - 1) / moc::kBwdQBM, BH), dim3(256), 0, st, q, g, Dq,
+                     l2, p, vl->rtiles, vl->n_rtiles, vl->bucket_off, vl->bucket_q, gstart,
+                     qblocks);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (vl->S > 0 && vl->max_rtiles > 0) {
+    hipLaunchKernelGGL((moc::bwd_qblock_kernel<D, moc::QB_ROUTED>), dim3(vl->max_rtiles),
+                       dim3(256), 0, st, q, g, Dq, l2, p, vl->rtiles, vl->n_rtiles,
+                       vl->bucket_off, vl->bucket_q, gstart, gblocks);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (vl->S > 0 && vl->max_rtiles > 0) {
     p.max_tiles = vl->max_rtiles;
     hipLaunchKernelGGL((moc::bwd_dq_kernel<D, moc::BMODE_ROUTED>), dim3(vl->max_rtiles),
@@ -839,15 +848,9 @@ static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, cons
                      vl->bucket_off, vl->bucket_q, vl->slot, dqp, static_cast<bf16_t*>(dQ));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   p.max_tiles = vl->max_ktiles;
-  // lse2 sits (l2 - Dq) floats after D, in the same [B*H][Lp] layout
-  const uint32_t l2_delta = static_cast<uint32_t>((l2 - Dq) * sizeof(float));
-  hipLaunchKernelGGL((moc::bwd_dkdv_anchor_kernel<D>), dim3(vl->max_ktiles * lay->B * lay->H),
-                     dim3(moc::kBwdKNT), 0, st, q, k, v, g, Qt, dOt, Dq, l2_delta, p, vl->ktiles,
-                     vl->n_ktiles, textK, textV, dKa, dVa);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((moc::bwd_dkdv_kernel<D>), dim3(vl->max_ktiles * lay->B * lay->H),
-                     dim3(moc::kBwdKNT), 0, st, q, k, v, g, Dq, l2, p, vl->ktiles, vl->n_ktiles,
-                     vl->bucket_off, vl->bucket_q, dKa, dVa, static_cast<bf16_t*>(dK),
+                     dim3(moc::kBwdKNT), 0, st, k, v, p, vl->ktiles, vl->n_ktiles, qblocks,
+                     gblocks, gstart, textK, textV, static_cast<bf16_t*>(dK),
                      static_cast<bf16_t*>(dV));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.text_len > 0) {

@@ -259,109 +259,6 @@ __device__ __forceinline__ void pv_accumulate(const float* Vt, const f32x16 (&p)
   }
 }
 
-// acc[db] += A^T-tile[db-block] * B for a contraction over NKB 32-blocks, where the A operand
-// comes from a transposed LDS tile At[D][STR] (row = output dim, column = contraction index)
-// and B is held in the 32x32 output layout (fp32, converted to bf16 per 16-step). This is the
-// P^T / dS^T product of the attention kernels, generic in the contraction length.
-template <int D, int NKB, int STR>
-__device__ __forceinline__ void mma_tn(const bf16_t* At, const f32x16 (&b)[NKB],
-                                       f32x16 (&acc)[D / 32], int ql, int g) {
-#pragma unroll
-  for (int ks = 0; ks < 2 * NKB; ++ks) {
-    const int kb = ks >> 1, hh = ks & 1;
-    bf16x8 pb;
-#pragma unroll
-    for (int ii = 0; ii < 8; ++ii) pb[ii] = static_cast<__bf16>(b[kb][8 * hh + ii]);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const bf16_t* ar = At + (db * 32 + ql) * STR + kb * 32 + 16 * hh + 4 * g;
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(ar);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(ar + 8);
-      const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[db], 0, 0, 0);
-    }
-  }
-}
-
-// 32x32 output block over the full head dim: out = A-rows (32 rows of a row-major LDS tile
-// with stride STR, starting at row0) times B^T where B is a fragment held in registers
-// (QFrag layout). Used for S^T = K Q^T, dP^T = V dO^T, S = Q K^T and dP = dO V^T.
-template <int D, int STR>
-__device__ __forceinline__ f32x16 mma_nt(const bf16_t* A, int row0, const QFrag<bf16_t, D>& b,
-                                         int ql, int g) {
-  f32x16 acc = {};
-  const bf16_t* ar = A + (row0 + ql) * STR + 8 * g;
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ar + 16 * kk));
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b.q[kk], acc, 0, 0, 0);
-  }
-  return acc;
-}
-
-// Stage a ROWS x D bf16 tile of a [rows][D] tensor through registers: every thread of NT owns
-// row pairs (2kp, 2kp+1) x 8 consecutive dims, so the same registers can be written to LDS
-// row-major and/or transposed (pairs of rows packed into 32-bit words).
-template <int D, int ROWS, int NT>
-struct PairTile {
-  static constexpr int DG = D / 8;                  // 8-dim groups
-  static constexpr int PAIRS = ROWS / 2;
-  static constexpr int UNITS = DG * PAIRS;          // (pair, dim group) units
-  static constexpr int UPT = UNITS >= NT ? UNITS / NT : 1;   // units per thread
-  static constexpr bool PARTIAL = UNITS < NT;       // some threads stage nothing
-  static_assert(PARTIAL || UPT * NT == UNITS, "tile split");
-  u32x4 r0[UPT], r1[UPT];
-
-  __device__ __forceinline__ static void unit(int u, int& kp, int& dg) {
-    // consecutive threads take consecutive row pairs of one dim group, which keeps the
-    // transposed 32-bit LDS stores of a wave on distinct banks
-    kp = u % PAIRS;
-    dg = u / PAIRS;
-  }
-  // rows come from `row_of(i)` (token index within the (b,h) slab, or -1 for a zero row)
-  template <typename RowOf>
-  __device__ __forceinline__ void load(const bf16_t* __restrict__ base, RowOf row_of) {
-    if (PARTIAL && static_cast<int>(threadIdx.x) >= UNITS) return;
-#pragma unroll
-    for (int j = 0; j < UPT; ++j) {
-      int kp, dg;
-      unit(threadIdx.x + j * NT, kp, dg);
-      const int ra = row_of(2 * kp), rb = row_of(2 * kp + 1);
-      r0[j] = ra >= 0 ? *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(ra) * D + dg * 8)
-                      : u32x4{0u, 0u, 0u, 0u};
-      r1[j] = rb >= 0 ? *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(rb) * D + dg * 8)
-                      : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  template <int STR>
-  __device__ __forceinline__ void store_rows(bf16_t* dst) const {
-    if (PARTIAL && static_cast<int>(threadIdx.x) >= UNITS) return;
-#pragma unroll
-    for (int j = 0; j < UPT; ++j) {
-      int kp, dg;
-      unit(threadIdx.x + j * NT, kp, dg);
-      *reinterpret_cast<u32x4*>(dst + (2 * kp) * STR + dg * 8) = r0[j];
-      *reinterpret_cast<u32x4*>(dst + (2 * kp + 1) * STR + dg * 8) = r1[j];
-    }
-  }
-  template <int STR>
-  __device__ __forceinline__ void store_transposed(bf16_t* dst) const {
-    if (PARTIAL && static_cast<int>(threadIdx.x) >= UNITS) return;
-    uint32_t* t = reinterpret_cast<uint32_t*>(dst);
-#pragma unroll
-    for (int j = 0; j < UPT; ++j) {
-      int kp, dg;
-      unit(threadIdx.x + j * NT, kp, dg);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t aw = r0[j][w], bw = r1[j][w];
-        t[((dg * 8 + 2 * w) * STR) / 2 + kp] = (aw & 0xffffu) | (bw << 16);
-        t[((dg * 8 + 2 * w + 1) * STR) / 2 + kp] = (aw >> 16) | (bw & 0xffff0000u);
-      }
-    }
-  }
-};
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

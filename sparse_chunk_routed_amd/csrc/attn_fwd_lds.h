@@ -238,39 +238,31 @@ struct QTiles {
   static constexpr int QT_OFF = 2 * RBLK * 1024;
   static constexpr int DOT_OFF = (2 * RBLK + TBLK) * 1024;
   static constexpr int ST_OFF = (2 * RBLK + 2 * TBLK) * 1024;  // lse2[32] then D[32] (fp32)
+  // A query tile block in global memory (one contiguous block): Q rows [32][D], dO rows, Q^T
+  // [D][32], dO^T, then lse2[32] and D[32].
+  static constexpr int G_ROWS = T * D * 2;
+  static constexpr int G_ST = 4 * G_ROWS;
+  static constexpr int G_BYTES = G_ST + 2 * T * 4;
 };
 
-// Direct-to-LDS copies of one wave (of NW) for one query tile at aligned position qbase.
-// Rows past L-1 are clamped (their queries are masked); the transposed copies ([D][Lp]) and the
-// statistics ([Lp] per (b, h), 16-byte aligned since Lp and qbase are multiples of 32) stay in
-// their padded rows. Per-lane offsets are recomputed at each issue.
+// Direct-to-LDS copies of one wave (of NW) for one 32-query tile block (layout QTiles::G_*):
+// every source address is the block base plus a per-lane offset, recomputed at each issue.
 template <int D, int NW>
 struct QTileCopier {
   using QT = QTiles<D>;
   static constexpr int SLOTS = (QT::NBLK + NW - 1) / NW;
-  int wv, lane, Lp;
+  int wv, lane;
 
-  __device__ __forceinline__ void init(int wave, int ln, int lp) {
+  __device__ __forceinline__ void init(int wave, int ln) {
     wv = wave;
     lane = ln;
-    Lp = lp;
   }
 
   __device__ __forceinline__ int count() const {
     return QT::NBLK / NW + (wv < QT::NBLK % NW);
   }
 
-  // Qbh, dObh: [L][D] slices; QTbh, dOTbh: [D][Lp] slices; Dbh: the [Lp] row of D, with the
-  // matching lse2 row l2_delta bytes further on (both arrays share one layout)
-  __device__ __forceinline__ void issue(uint32_t lds, const bf16_t* Qbh, const bf16_t* dObh,
-                                        const bf16_t* QTbh, const bf16_t* dOTbh,
-                                        const float* Dbh, uint32_t l2_delta, int qbase,
-                                        int L) const {
-    const uint32_t lim = static_cast<uint32_t>(L - 1 - qbase);  // >= 0
-    const bf16_t* qb = Qbh + static_cast<size_t>(qbase) * D;
-    const bf16_t* ob = dObh + static_cast<size_t>(qbase) * D;
-    const bf16_t* qt = QTbh + qbase;
-    const bf16_t* ot = dOTbh + qbase;
+  __device__ __forceinline__ void issue(uint32_t lds, const char* blk_base) const {
     int ln = lane;
     asm volatile("" : "+v"(ln));  // recompute the offsets here rather than hold them in registers
 #pragma unroll
@@ -278,27 +270,27 @@ struct QTileCopier {
       const int blk = wv + i * NW;
       if (blk >= QT::NBLK) break;
       const uint32_t dst = lds + blk * 1024;
+      uint32_t off;
       if (blk < 2 * QT::RBLK) {
-        const bf16_t* rb = blk < QT::RBLK ? qb : ob;
+        // Q rows then dO rows: 16-byte piece c of row r into padded LDS rows of RROW pieces
         const int pos = (blk % QT::RBLK) * 64 + ln;
-        uint32_t r = pos / QT::RROW;
-        int c = pos % QT::RROW;
+        int r = pos / QT::RROW, c = pos % QT::RROW;
         if (c >= D / 8) c = 0;
-        r = r < lim ? r : lim;
-        copy16_to_lds(rb, r * (D * 2) + c * 16, dst);
+        if (r >= QT::T) r = QT::T - 1;
+        off = (blk < QT::RBLK ? 0u : QT::G_ROWS) + r * (D * 2) + c * 16;
       } else if (blk < 2 * QT::RBLK + 2 * QT::TBLK) {
+        // Q^T then dO^T: row d holds the 32 queries (4 pieces) of dim d
         const int tb = blk - 2 * QT::RBLK;
-        const bf16_t* src = tb < QT::TBLK ? qt : ot;
         const int pos = (tb % QT::TBLK) * 64 + ln;
         int d = pos / QT::TROW, c = pos % QT::TROW;
         if (c >= QT::T / 8) c = 0;
         if (d >= D) d = D - 1;
-        copy16_to_lds(src, static_cast<uint32_t>(d) * Lp * 2 + c * 16, dst);
+        off = (tb < QT::TBLK ? 2u : 3u) * QT::G_ROWS + d * (QT::T * 2) + c * 16;
       } else {
-        // lanes 0-7: lse2[qbase .. +31], lanes 8-15: D[...]; other lanes repeat them
-        const int l16 = ln & 15;
-        copy16_to_lds(Dbh + qbase, (l16 < 8 ? l2_delta : 0u) + (l16 & 7) * 16, dst);
+        // lse2[32] then D[32]: lanes 0-15; the other lanes repeat them
+        off = QT::G_ST + (ln & 15) * 16;
       }
+      copy16_to_lds(blk_base, off, dst);
     }
   }
 };
