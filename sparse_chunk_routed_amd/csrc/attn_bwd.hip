@@ -400,21 +400,21 @@ __global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_kernel(
   const int qbase0 = qa & ~31;
   // anchor queries: the sequence's query blocks from qa's; routed queries of this chunk: the
   // bucket's gathered blocks (pads have P = 0)
-  const char* ab = qblocks + (static_cast<size_t>(bh) * (p.Lp >> 5) + (qa >> 5)) * QTl::G_BYTES;
+  const char* ab = qblocks + (static_cast<size_t>(bh) * (p.Lp >> 5) + (qa >> 5)) * QTl::BYTES;
   const char* gb = gblocks;
   int ngt = 0;
   if (c >= 0) {
     const int bucket = bh * p.C + c;
     const int g0 = gstart[bucket];
     ngt = (gstart[bucket + 1] - g0) >> 5;
-    gb += static_cast<size_t>(g0 >> 5) * QTl::G_BYTES;
+    gb += static_cast<size_t>(g0 >> 5) * QTl::BYTES;
   }
   const int ntot = nqt + ngt;
   const uint32_t lds0 = lds_addr(st0), lds1 = lds_addr(st1);
   auto issue = [&](int j, uint32_t lds) __attribute__((always_inline)) {
     if (j >= ntot) return;
-    const char* blk = j < nqt ? ab + static_cast<size_t>(j) * QTl::G_BYTES
-                              : gb + static_cast<size_t>(j - nqt) * QTl::G_BYTES;
+    const char* blk = j < nqt ? ab + static_cast<size_t>(j) * QTl::BYTES
+                              : gb + static_cast<size_t>(j - nqt) * QTl::BYTES;
     cp.issue(lds, blk);
   };
   auto bar = [&]() __attribute__((always_inline)) {
@@ -450,8 +450,8 @@ __global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_kernel(
       sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf.q[kk], sp, 0, 0, 0);
     }
     pace(D / 16);
-    // P = exp2(S scale log2(e) - lse2), zero for queries outside [qa, qb)
-    bf16x8 pa[2];
+    // P = exp2(S scale log2(e) - lse2), zero for queries outside [qa, qb) (only the first and
+    // last anchor tiles are partial: one branch per tile)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const f32x4 la = *reinterpret_cast<const f32x4*>(stl + 16 * h + 8 * g);
@@ -459,14 +459,22 @@ __global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int i = 8 * h + e;
-        float pr = fast_exp2(__builtin_fmaf(sp[i], c2, -(e < 4 ? la[e] : lb[e - 4])));
-        if (partial) {
-          const int qpos = qbase + 16 * h + 8 * g + e;
-          if (qpos < qa || qpos >= qb) pr = 0.f;
-        }
-        pa[h][e] = static_cast<__bf16>(pr);
+        sp[i] = fast_exp2(__builtin_fmaf(sp[i], c2, -(e < 4 ? la[e] : lb[e - 4])));
       }
     }
+    if (partial) {
+      const int lo = qa - qbase - 8 * g, hi = qb - qbase - 8 * g;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int off = 16 * (i >> 3) + (i & 7);
+        if (off < lo || off >= hi) sp[i] = 0.f;
+      }
+    }
+    bf16x8 pa[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pa[h][e] = static_cast<__bf16>(sp[8 * h + e]);
     // dV += P^T dO (B operand: dO^T rows, 8 queries each)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -586,27 +594,25 @@ __global__ __launch_bounds__(1024) void bwd_gather_scan_kernel(const int32_t* __
   if (threadIdx.x == 1023) gstart[NB] = part[1023];
 }
 
-// Query tile blocks (layout QTiles::G_*) for the key-centric kernel: 32 queries' Q and dO rows,
-// their transposes and lse2, D in one contiguous block. tok[r] is the query of row r, or -1 for
-// a pad (zero rows, lse2 = +inf so that P = 0, D = 0). Called by a whole workgroup of 256.
+// Query tile images (QTiles layout) for the key-centric kernel: 32 queries' Q and dO rows, their
+// transposes and lse2, D, padded exactly as the kernel stages them. tok[r] is the query of row
+// r, or -1 for a pad (zero rows, lse2 = +inf so that P = 0, D = 0); padding bytes are zero.
+// Called by a whole workgroup of 256.
 template <int D>
 __device__ __forceinline__ void build_qblock(const bf16_t* __restrict__ Qbh,
                                              const bf16_t* __restrict__ dObh,
                                              const float* __restrict__ l2bh,
                                              const float* __restrict__ Dbh, const int32_t* tok,
-                                             bf16_t* sq, bf16_t* so, char* __restrict__ blk) {
+                                             bf16_t* sq, bf16_t* so, float* sst,
+                                             char* __restrict__ img) {
   using QTl = QTiles<D>;
   constexpr int PITCH = D + 4;  // bf16; rows 8 apart land 16 banks apart
   constexpr int CPR = D / 8;    // 16-byte pieces per row
-  bf16_t* Qg = reinterpret_cast<bf16_t*>(blk);
-  bf16_t* dOg = Qg + 32 * D;
-  bf16_t* QgT = Qg + 2 * 32 * D;
-  bf16_t* dOgT = Qg + 3 * 32 * D;
-  float* Sg = reinterpret_cast<float*>(blk + QTl::G_ST);
+  constexpr int RU = QTl::RBLK * 64, TU = QTl::TBLK * 64;  // 16-byte units per region
   if (threadIdx.x < 32) {
     const int t = tok[threadIdx.x];
-    Sg[threadIdx.x] = t >= 0 ? l2bh[t] : __builtin_inff();
-    Sg[32 + threadIdx.x] = t >= 0 ? Dbh[t] : 0.f;
+    sst[threadIdx.x] = t >= 0 ? l2bh[t] : __builtin_inff();
+    sst[32 + threadIdx.x] = t >= 0 ? Dbh[t] : 0.f;
   }
   for (int id = threadIdx.x; id < 32 * CPR; id += 256) {
     const int r = id / CPR, c = id % CPR;
@@ -616,8 +622,6 @@ __device__ __forceinline__ void build_qblock(const bf16_t* __restrict__ Qbh,
       vq = *reinterpret_cast<const u32x4*>(Qbh + static_cast<size_t>(t) * D + c * 8);
       vo = *reinterpret_cast<const u32x4*>(dObh + static_cast<size_t>(t) * D + c * 8);
     }
-    *reinterpret_cast<u32x4*>(Qg + r * D + c * 8) = vq;
-    *reinterpret_cast<u32x4*>(dOg + r * D + c * 8) = vo;
     u32x2* lq = reinterpret_cast<u32x2*>(sq + r * PITCH + c * 8);
     u32x2* lo = reinterpret_cast<u32x2*>(so + r * PITCH + c * 8);
     lq[0] = u32x2{vq[0], vq[1]};
@@ -626,20 +630,36 @@ __device__ __forceinline__ void build_qblock(const bf16_t* __restrict__ Qbh,
     lo[1] = u32x2{vo[2], vo[3]};
   }
   __syncthreads();
-  // transposed rows: row d holds the 32 queries of dim d; 16-byte piece c4 is queries 8 c4 ..
-  for (int id = threadIdx.x; id < D * 4; id += 256) {
-    const int d = id >> 2, c4 = id & 3;
-    uint32_t wq[4], wo[4];
+  // every 16-byte unit of the image, in order (coalesced stores)
+  for (int u = threadIdx.x; u < QTl::NBLK * 64; u += 256) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (u < 2 * RU) {
+      const bf16_t* src = u < RU ? sq : so;
+      const int pu = u % RU;
+      const int r = pu / QTl::RROW, c = pu % QTl::RROW;
+      if (r < QTl::T && c < CPR) {
+        const u32x2* l = reinterpret_cast<const u32x2*>(src + r * PITCH + c * 8);
+        const u32x2 a = l[0], b = l[1];
+        v = u32x4{a[0], a[1], b[0], b[1]};
+      }
+    } else if (u < 2 * RU + 2 * TU) {
+      // transposed row d: 16-byte piece c4 holds queries 8 c4 .. 8 c4 + 7 of dim d
+      const bf16_t* src = u < 2 * RU + TU ? sq : so;
+      const int pu = (u - 2 * RU) % TU;
+      const int d = pu / QTl::TROW, c4 = pu % QTl::TROW;
+      if (d < D && c4 < QTl::T / 8) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 8 * c4 + 2 * e;
-      wq[e] = static_cast<uint32_t>(sq[r * PITCH + d]) |
-              (static_cast<uint32_t>(sq[(r + 1) * PITCH + d]) << 16);
-      wo[e] = static_cast<uint32_t>(so[r * PITCH + d]) |
-              (static_cast<uint32_t>(so[(r + 1) * PITCH + d]) << 16);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 8 * c4 + 2 * e;
+          v[e] = static_cast<uint32_t>(src[r * PITCH + d]) |
+                 (static_cast<uint32_t>(src[(r + 1) * PITCH + d]) << 16);
+        }
+      }
+    } else {
+      const int pu = u - 2 * RU - 2 * TU;  // lse2 in units 0-7, D in 8-15
+      if (pu < 16) v = *reinterpret_cast<const u32x4*>(sst + 4 * pu);
     }
-    *reinterpret_cast<u32x4*>(QgT + d * 32 + c4 * 8) = u32x4{wq[0], wq[1], wq[2], wq[3]};
-    *reinterpret_cast<u32x4*>(dOgT + d * 32 + c4 * 8) = u32x4{wo[0], wo[1], wo[2], wo[3]};
+    *reinterpret_cast<u32x4*>(img + static_cast<size_t>(u) * 16) = v;
   }
   __syncthreads();
 }
@@ -661,6 +681,7 @@ __global__ __launch_bounds__(256) void bwd_qblock_kernel(
   __shared__ __attribute__((aligned(16))) bf16_t sq[32 * (D + 4)];
   __shared__ __attribute__((aligned(16))) bf16_t so[32 * (D + 4)];
   __shared__ int32_t tok[32];
+  __shared__ __attribute__((aligned(16))) float sst[64];
   int bh, first, end, b0 = 0, n = 0;
   size_t blk0;  // block index of position `first`
   if (MODE == QB_SEQ) {
@@ -690,8 +711,8 @@ __global__ __launch_bounds__(256) void bwd_qblock_kernel(
       tok[threadIdx.x] = idx < n ? (MODE == QB_SEQ ? idx : bucket_q[b0 + idx]) : -1;
     }
     __syncthreads();
-    build_qblock<D>(Qbh, dObh, l2bh, Dbh, tok, sq, so,
-                    blocks + (blk0 + ((i0 - first) >> 5)) * QTl::G_BYTES);
+    build_qblock<D>(Qbh, dObh, l2bh, Dbh, tok, sq, so, sst,
+                    blocks + (blk0 + ((i0 - first) >> 5)) * QTl::BYTES);
   }
 }
 
@@ -767,7 +788,7 @@ BwdSizes bwd_sizes(const moc_layout* lay, int S) {
   // 32-query blocks of the dK/dV kernel: the sequence's (Lp / 32 per (b, h)) and the routed
   // buckets' (each bucket padded to a multiple of 32 rows: at most B*H*L*S + 31 per bucket)
   const size_t nb = static_cast<size_t>(lay->B) * lay->H * lay->C;
-  const size_t gtile = lay->d == 128 ? moc::QTiles<128>::G_BYTES : moc::QTiles<64>::G_BYTES;
+  const size_t gtile = lay->d == 128 ? moc::QTiles<128>::BYTES : moc::QTiles<64>::BYTES;
   z.qb = al(static_cast<size_t>(lay->B) * lay->H * (kt_rows(lay->L) / 32) * gtile);
   z.gb = al(gather_rows(lay, S) / 32 * gtile);
   z.gstart = al((nb + 1) * sizeof(int32_t));

@@ -223,7 +223,8 @@ struct RowsTCopier {
 // (b, h), staged as Q rows and dO rows (pitch D/8 + 1 chunks, A operands of S = Q K^T and
 // dP = dO V^T), Q^T and dO^T rows (D rows of 32 queries, pitch 5 chunks, B operands of
 // dK += dS^T Q and dV += P^T dO), and one block holding lse2[32] and D[32]. The odd pitches keep
-// the 16 lanes of an LDS read pass on 16 different bank slots.
+// the 16 lanes of an LDS read pass on 16 different bank slots. The tiles are built in global
+// memory as this exact byte image (padding included), so staging one is a linear copy.
 template <int D>
 struct QTiles {
   static constexpr int T = 32;                          // queries per tile
@@ -238,59 +239,33 @@ struct QTiles {
   static constexpr int QT_OFF = 2 * RBLK * 1024;
   static constexpr int DOT_OFF = (2 * RBLK + TBLK) * 1024;
   static constexpr int ST_OFF = (2 * RBLK + 2 * TBLK) * 1024;  // lse2[32] then D[32] (fp32)
-  // A query tile block in global memory (one contiguous block): Q rows [32][D], dO rows, Q^T
-  // [D][32], dO^T, then lse2[32] and D[32].
-  static constexpr int G_ROWS = T * D * 2;
-  static constexpr int G_ST = 4 * G_ROWS;
-  static constexpr int G_BYTES = G_ST + 2 * T * 4;
 };
 
-// Direct-to-LDS copies of one wave (of NW) for one 32-query tile block (layout QTiles::G_*):
-// every source address is the block base plus a per-lane offset, recomputed at each issue.
+// Direct-to-LDS copies of one wave (of NW) for one query tile image (QTiles layout): the
+// wave copies the 1 KB pieces wv, wv + NW, ...; a lane moves bytes 16 lane .. 16 lane + 15 of
+// each, so the only per-lane value is that one offset.
 template <int D, int NW>
 struct QTileCopier {
   using QT = QTiles<D>;
   static constexpr int SLOTS = (QT::NBLK + NW - 1) / NW;
-  int wv, lane;
+  int wv;
+  uint32_t voff;
 
   __device__ __forceinline__ void init(int wave, int ln) {
     wv = wave;
-    lane = ln;
+    voff = static_cast<uint32_t>(ln) * 16u;
   }
 
   __device__ __forceinline__ int count() const {
     return QT::NBLK / NW + (wv < QT::NBLK % NW);
   }
 
-  __device__ __forceinline__ void issue(uint32_t lds, const char* blk_base) const {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));  // recompute the offsets here rather than hold them in registers
+  __device__ __forceinline__ void issue(uint32_t lds, const char* img) const {
 #pragma unroll
     for (int i = 0; i < SLOTS; ++i) {
       const int blk = wv + i * NW;
       if (blk >= QT::NBLK) break;
-      const uint32_t dst = lds + blk * 1024;
-      uint32_t off;
-      if (blk < 2 * QT::RBLK) {
-        // Q rows then dO rows: 16-byte piece c of row r into padded LDS rows of RROW pieces
-        const int pos = (blk % QT::RBLK) * 64 + ln;
-        int r = pos / QT::RROW, c = pos % QT::RROW;
-        if (c >= D / 8) c = 0;
-        if (r >= QT::T) r = QT::T - 1;
-        off = (blk < QT::RBLK ? 0u : QT::G_ROWS) + r * (D * 2) + c * 16;
-      } else if (blk < 2 * QT::RBLK + 2 * QT::TBLK) {
-        // Q^T then dO^T: row d holds the 32 queries (4 pieces) of dim d
-        const int tb = blk - 2 * QT::RBLK;
-        const int pos = (tb % QT::TBLK) * 64 + ln;
-        int d = pos / QT::TROW, c = pos % QT::TROW;
-        if (c >= QT::T / 8) c = 0;
-        if (d >= D) d = D - 1;
-        off = (tb < QT::TBLK ? 2u : 3u) * QT::G_ROWS + d * (QT::T * 2) + c * 16;
-      } else {
-        // lse2[32] then D[32]: lanes 0-15; the other lanes repeat them
-        off = QT::G_ST + (ln & 15) * 16;
-      }
-      copy16_to_lds(blk_base, off, dst);
+      copy16_to_lds(img + blk * 1024, voff, lds + blk * 1024);
     }
   }
 };
