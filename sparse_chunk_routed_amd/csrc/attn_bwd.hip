@@ -10,8 +10,10 @@
 // Pairs come in the same blocks as the forward: anchor (a query tile x text U own-shot keys)
 // and routed (a bucket of gathered queries x one chunk). The kernels:
 //   prep      D_t and the base-2 LSE per query row.
-//   qblock    32-query blocks (Q and dO rows, their transposes, lse2 and D, contiguous) of the
-//             whole sequence and of every routed bucket (padded to 32 rows, pads have P = 0).
+//   images    the dQ kernel's 64-key tile images (K rows, V rows, K^T) and the dK/dV kernel's
+//             32-query tile images (Q and dO rows, their transposes, lse2 and D) of the whole
+//             sequence and of every routed bucket (padded to 32 rows, pads have P = 0), each
+//             laid out as the kernel's LDS stage so that staging is a linear copy.
 //   dq        query-centric, like the forward (S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T):
 //             routed tiles write fp32 partial rows per (query, routed chunk); anchor tiles
 //             merge those partials in ascending chunk order and write dQ.
@@ -23,7 +25,7 @@
 // No float atomics anywhere, so the result is deterministic. The separate dQ and dK/dV passes
 // recompute S and dP (7 GEMM-units per pair instead of 5).
 #include "attn_common.h"
-#include "attn_fwd_lds.h"
+#include "attn_bwd_lds.h"
 
 namespace moc {
 
@@ -86,8 +88,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16_t* __restrict_
 // and S, dP of tile j, while the other group computes dS of its current tile.
 template <int D, int MODE>
 __global__ __launch_bounds__(kBwdQNT) void bwd_dq_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const bf16_t* __restrict__ Kt, int Lp, const bf16_t* __restrict__ dO,
+    const bf16_t* __restrict__ Q, const char* __restrict__ kvimg, const bf16_t* __restrict__ dO,
     const float* __restrict__ Dq, const float* __restrict__ lse2,
     const int32_t* __restrict__ off, BwdParams p, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ bucket_off,
@@ -95,10 +96,11 @@ __global__ __launch_bounds__(kBwdQNT) void bwd_dq_kernel(
     float* __restrict__ dQp, bf16_t* __restrict__ dQ) {
   static_assert(kBwdQNW == 8, "two groups of four waves");
   using LT = LdsTiles<D>;
-  using CP = RowsTCopier<D, kBwdQNW, 2>;
-  __shared__ __attribute__((aligned(1024))) char st0[CP::BYTES];
-  __shared__ __attribute__((aligned(1024))) char st1[CP::BYTES];
-  __shared__ __attribute__((aligned(1024))) char st2[CP::BYTES];
+  using KI = KvImage<D>;
+  using CP = KvStageCopier<D, kBwdQNW>;
+  __shared__ __attribute__((aligned(1024))) char st0[KI::BYTES];
+  __shared__ __attribute__((aligned(1024))) char st1[KI::BYTES];
+  __shared__ __attribute__((aligned(1024))) char st2[KI::BYTES];
 
   // upper-bound grid: blocks past the device-side work count exit; the rest are remapped so
   // each XCD takes a contiguous range of the real work items
@@ -136,17 +138,15 @@ __global__ __launch_bounds__(kBwdQNT) void bwd_dq_kernel(
   else t = bucket_q[bstart + rr];
 
   CP cp;
-  cp.init(wv, lane, Lp);
+  cp.init(wv, lane);
   const int ncopy = cp.count();
   auto wait_but_newest = [&]() __attribute__((always_inline)) {
-    constexpr int NB = CP::NBLK / kBwdQNW;
+    constexpr int NB = KI::NBLK / kBwdQNW;
     if (ncopy == NB) __builtin_amdgcn_s_waitcnt(0x0070 | NB);
     else __builtin_amdgcn_s_waitcnt(0x0070 | (NB + 1));
   };
   const size_t bh_off = static_cast<size_t>(bh) * p.L * D;
-  const bf16_t* Kbh = K + bh_off;
-  const bf16_t* Vbh = V + bh_off;
-  const bf16_t* Ktbh = Kt + static_cast<size_t>(bh) * D * Lp;
+  const char* imgbh = kvimg + static_cast<size_t>(bh) * (p.Lp / kBN) * KI::BYTES;
   QFrag<bf16_t, D> qf, dof;
   qf.load(Q + bh_off + static_cast<size_t>(t) * D, g);
   dof.load(dO + bh_off + static_cast<size_t>(t) * D, g);
@@ -171,12 +171,14 @@ __global__ __launch_bounds__(kBwdQNT) void bwd_dq_kernel(
     lo = ra > base ? ra - base : 0;
     hi = rb - base < kBN ? rb - base : kBN;
   };
-  const int kmax = p.L - 1;
   const uint32_t lds0 = lds_addr(st0), lds1 = lds_addr(st1), lds2 = lds_addr(st2);
+  // stage j: K and V rows of tile j, K^T of tile j-1 (clamped past the ends: loaded, unread)
   auto issue = [&](int j, uint32_t lds) __attribute__((always_inline)) {
     if (j > ntot || ntot == 0) return;
-    cp.issue(lds, Kbh, Vbh, tile_base(j < ntot ? j : ntot - 1), kmax, Ktbh,
-             tile_base(j > 0 ? j - 1 : 0));
+    const int tr = tile_base(j < ntot ? j : ntot - 1) / kBN;
+    const int tt = tile_base(j > 0 ? j - 1 : 0) / kBN;
+    cp.issue(lds, imgbh + static_cast<size_t>(tr) * KI::BYTES,
+             imgbh + static_cast<size_t>(tt) * KI::BYTES);
   };
 
   f32x16 s[2], dp[2];
@@ -566,6 +568,55 @@ __global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_kernel(
   }
 }
 
+// Key tile images of the dQ kernel (KvImage layout), one workgroup per 64-key tile of a (b, h):
+// K and V rows into the padded row layout, K^T through LDS into the padded transposed layout;
+// padding bytes and rows past L are zero.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_kvimage_kernel(const bf16_t* __restrict__ K,
+                                                          const bf16_t* __restrict__ V, int L,
+                                                          int Lp, char* __restrict__ img) {
+  using LT = LdsTiles<D>;
+  using KI = KvImage<D>;
+  constexpr int PITCH = D + 8;  // bf16
+  __shared__ __attribute__((aligned(16))) bf16_t sk[kBN * PITCH];
+  const int bh = blockIdx.y, k0 = blockIdx.x * kBN;
+  const bf16_t* Kbh = K + static_cast<size_t>(bh) * L * D;
+  const bf16_t* Vbh = V + static_cast<size_t>(bh) * L * D;
+  char* out = img + (static_cast<size_t>(bh) * (Lp / kBN) + blockIdx.x) * KI::BYTES;
+  for (int e = threadIdx.x; e < kBN * LT::KCH; e += 256) {
+    const int r = e / LT::KCH, c = e % LT::KCH;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (k0 + r < L) v = *reinterpret_cast<const u32x4*>(Kbh + static_cast<size_t>(k0 + r) * D + c * 8);
+    *reinterpret_cast<u32x4*>(sk + r * PITCH + c * 8) = v;
+  }
+  __syncthreads();
+  for (int u = threadIdx.x; u < KI::NBLK * 64; u += 256) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (u < KI::ROWBLK * 64) {
+      const bool isv = u >= LT::KBLK * 64;
+      const int pu = u % (LT::KBLK * 64);
+      const int r = pu / LT::KROW, c = pu % LT::KROW;
+      if (r < kBN && c < LT::KCH && k0 + r < L) {
+        if (isv) v = *reinterpret_cast<const u32x4*>(Vbh + static_cast<size_t>(k0 + r) * D + c * 8);
+        else v = *reinterpret_cast<const u32x4*>(sk + r * PITCH + c * 8);
+      }
+    } else {
+      // K^T row d: 16-byte piece c holds keys 8 c .. 8 c + 7 of dim d
+      const int pu = u - KI::ROWBLK * 64;
+      const int d = pu / LT::VROW, c = pu % LT::VROW;
+      if (d < D && c < kBN / 8) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 8 * c + 2 * e;
+          v[e] = static_cast<uint32_t>(sk[r * PITCH + d]) |
+                 (static_cast<uint32_t>(sk[(r + 1) * PITCH + d]) << 16);
+        }
+      }
+    }
+    *reinterpret_cast<u32x4*>(out + static_cast<size_t>(u) * 16) = v;
+  }
+}
+
 // Start of every (b, h, chunk) bucket's gathered rows: sizes rounded up to 32, scanned in
 // bucket order; gstart[NB] is the total. One workgroup.
 __global__ __launch_bounds__(1024) void bwd_gather_scan_kernel(const int32_t* __restrict__ bucket_off,
@@ -747,9 +798,6 @@ namespace moc_host {
 
 using moc::BwdParams;
 
-hipError_t launch_transpose_rows(const void* X, void* Xt, int BH, int L, int Lp, int d,
-                                 hipStream_t st);  // attn_fwd.hip
-
 int attn_bwd_key_rows() { return moc::kBwdKR; }
 
 int attn_bwd_text_split(int L) {
@@ -759,8 +807,8 @@ int attn_bwd_text_split(int L) {
 
 namespace {
 struct BwdSizes {
-  size_t dq, l2, dqp, textk, textv, kt, qb, gb, gstart;
-  size_t total() const { return dq + l2 + dqp + textk + textv + kt + qb + gb + gstart; }
+  size_t dq, l2, dqp, textk, textv, kv, qb, gb, gstart;
+  size_t total() const { return dq + l2 + dqp + textk + textv + kv + qb + gb + gstart; }
 };
 int kt_rows(int L) { return (L + moc::kBN - 1) / moc::kBN * moc::kBN; }
 size_t al(size_t x) { return (x + 255) / 256 * 256; }
@@ -783,8 +831,9 @@ BwdSizes bwd_sizes(const moc_layout* lay, int S) {
   const size_t tp = static_cast<size_t>(lay->B) * lay->H * ns * (text > 0 ? text : 1) * lay->d;
   z.textk = al(sizeof(float) * tp);
   z.textv = al(sizeof(float) * tp);
-  // transposed copy of K (dQ kernel), [B*H][d][Lp]
-  z.kt = al(static_cast<size_t>(lay->B) * lay->H * lay->d * kt_rows(lay->L) * 2);
+  // key tile images of the dQ kernel, Lp / 64 per (b, h)
+  const size_t kvtile = lay->d == 128 ? moc::KvImage<128>::BYTES : moc::KvImage<64>::BYTES;
+  z.kv = al(static_cast<size_t>(lay->B) * lay->H * (kt_rows(lay->L) / moc::kBN) * kvtile);
   // 32-query blocks of the dK/dV kernel: the sequence's (Lp / 32 per (b, h)) and the routed
   // buckets' (each bucket padded to a multiple of 32 rows: at most B*H*L*S + 31 per bucket)
   const size_t nb = static_cast<size_t>(lay->B) * lay->H * lay->C;
@@ -811,7 +860,7 @@ static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   float* dqp = reinterpret_cast<float*>(w); w += z.dqp;
   float* textK = reinterpret_cast<float*>(w); w += z.textk;
   float* textV = reinterpret_cast<float*>(w); w += z.textv;
-  bf16_t* Kt = reinterpret_cast<bf16_t*>(w); w += z.kt;
+  char* kvimg = w; w += z.kv;
   char* qblocks = w; w += z.qb;
   char* gblocks = w; w += z.gb;
   int32_t* gstart = reinterpret_cast<int32_t*>(w); w += z.gstart;
@@ -838,7 +887,9 @@ static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   p.scale = scale;
   p.Lp = Lp;
   const int BH = lay->B * lay->H;
-  if ((e = launch_transpose_rows(k, Kt, BH, lay->L, Lp, D, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL((moc::bwd_kvimage_kernel<D>), dim3(Lp / moc::kBN, BH), dim3(256), 0, st, k,
+                     v, lay->L, Lp, kvimg);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   const int NB = BH * lay->C;
   hipLaunchKernelGGL(moc::bwd_gather_scan_kernel, dim3(1), dim3(1024), 0, st, vl->bucket_off, NB,
                      gstart);
@@ -857,15 +908,15 @@ static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   if (vl->S > 0 && vl->max_rtiles > 0) {
     p.max_tiles = vl->max_rtiles;
     hipLaunchKernelGGL((moc::bwd_dq_kernel<D, moc::BMODE_ROUTED>), dim3(vl->max_rtiles),
-                       dim3(moc::kBwdQNT), 0, st, q, k, v, Kt, Lp, g, Dq, l2, lay->chunk_offsets,
+                       dim3(moc::kBwdQNT), 0, st, q, kvimg, g, Dq, l2, lay->chunk_offsets,
                        p, vl->rtiles, vl->n_rtiles, vl->bucket_off, vl->bucket_q, vl->slot, dqp,
                        static_cast<bf16_t*>(dQ));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   p.max_tiles = vl->max_atiles;
   hipLaunchKernelGGL((moc::bwd_dq_kernel<D, moc::BMODE_ANCHOR>),
-                     dim3(vl->max_atiles * lay->B * lay->H), dim3(moc::kBwdQNT), 0, st, q, k, v,
-                     Kt, Lp, g, Dq, l2, lay->chunk_offsets, p, vl->atiles, vl->n_atiles,
+                     dim3(vl->max_atiles * lay->B * lay->H), dim3(moc::kBwdQNT), 0, st, q, kvimg,
+                     g, Dq, l2, lay->chunk_offsets, p, vl->atiles, vl->n_atiles,
                      vl->bucket_off, vl->bucket_q, vl->slot, dqp, static_cast<bf16_t*>(dQ));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   p.max_tiles = vl->max_ktiles;

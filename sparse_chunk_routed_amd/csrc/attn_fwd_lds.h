@@ -162,114 +162,6 @@ __global__ __launch_bounds__(256) void transpose_rows_kernel(const bf16_t* __res
   }
 }
 
-// Direct-to-LDS copies of one wave for a stage made of NROW row tiles (64 rows of D bf16 each,
-// pitch KROW chunks, rows past kmax clamped) followed by one transposed tile (D rows of 64 keys,
-// pitch VROW chunks). The stage's 1 KB blocks are numbered in that order; wave w copies blocks
-// w, w + NW, ... The per-lane source offsets are recomputed at every issue (a few VALU per
-// copy) so that they hold no registers across the kernel's main loop.
-template <int D, int NW, int NROW>
-struct RowsTCopier {
-  using LT = LdsTiles<D>;
-  static constexpr int NBLK = NROW * LT::KBLK + LT::VBLK;
-  static constexpr int SLOTS = (NBLK + NW - 1) / NW;
-  static constexpr int BYTES = NBLK * 1024;  // LDS bytes of one stage
-  int wv, lane, Lp;
-
-  __device__ __forceinline__ void init(int wave, int ln, int lp) {
-    wv = wave;
-    lane = ln;
-    Lp = lp;
-  }
-
-  __device__ __forceinline__ int count() const { return NBLK / NW + (wv < NBLK % NW); }
-
-  // Row tile 0 copies rows kbase .. kbase+63 of r0, row tile 1 (NROW == 2) the same rows of r1
-  // (each the (b, h) slice base); the transposed tile copies keys tkey .. tkey+63 of tbase
-  // ([D][Lp] layout).
-  __device__ __forceinline__ void issue(uint32_t lds, const bf16_t* r0, const bf16_t* r1,
-                                        int kbase, int kmax, const bf16_t* tbase,
-                                        int tkey) const {
-    const uint32_t lim = static_cast<uint32_t>(kmax - kbase);  // >= 0: kbase <= kmax
-    const bf16_t* tb = tbase + tkey;
-    const bf16_t* rb0 = r0 + static_cast<size_t>(kbase) * D;
-    const bf16_t* rb1 = r1 + static_cast<size_t>(kbase) * D;
-    int ln = lane;
-    asm volatile("" : "+v"(ln));  // recompute the offsets here rather than hold them in registers
-#pragma unroll
-    for (int i = 0; i < SLOTS; ++i) {
-      const int blk = wv + i * NW;
-      if (blk >= NBLK) break;
-      if (blk < NROW * LT::KBLK) {
-        const bf16_t* rb = (NROW > 1 && blk >= LT::KBLK) ? rb1 : rb0;
-        const int pos = (blk % LT::KBLK) * 64 + ln;
-        uint32_t r = pos / LT::KROW;
-        int c = pos % LT::KROW;
-        if (c >= LT::KCH) c = 0;
-        r = r < lim ? r : lim;  // also keeps padding rows past the tile inside the slice
-        copy16_to_lds(rb, r * (D * 2) + c * 16, lds + blk * 1024);
-      } else {
-        const int pos = (blk - NROW * LT::KBLK) * 64 + ln;
-        int d = pos / LT::VROW, c = pos % LT::VROW;
-        if (c >= kBN / 8) c = 0;
-        if (d >= D) d = D - 1;
-        copy16_to_lds(tb, static_cast<uint32_t>(d) * Lp * 2 + c * 16, lds + blk * 1024);
-      }
-    }
-  }
-};
-
-// ---------------------------------------------------------------------------------------------
-// Query tiles of the key-centric backward: 32 consecutive (aligned) query positions of one
-// (b, h), staged as Q rows and dO rows (pitch D/8 + 1 chunks, A operands of S = Q K^T and
-// dP = dO V^T), Q^T and dO^T rows (D rows of 32 queries, pitch 5 chunks, B operands of
-// dK += dS^T Q and dV += P^T dO), and one block holding lse2[32] and D[32]. The odd pitches keep
-// the 16 lanes of an LDS read pass on 16 different bank slots. The tiles are built in global
-// memory as this exact byte image (padding included), so staging one is a linear copy.
-template <int D>
-struct QTiles {
-  static constexpr int T = 32;                          // queries per tile
-  static constexpr int RROW = D / 8 + 1;                // row pitch (chunks)
-  static constexpr int TROW = T / 8 + 1;                // transposed row pitch (chunks)
-  static constexpr int RBLK = (T * RROW + 63) / 64;     // 1 KB blocks of one row tile
-  static constexpr int TBLK = (D * TROW + 63) / 64;     // 1 KB blocks of one transposed tile
-  static constexpr int NBLK = 2 * RBLK + 2 * TBLK + 1;
-  static constexpr int BYTES = NBLK * 1024;
-  static constexpr int Q_OFF = 0;
-  static constexpr int DO_OFF = RBLK * 1024;
-  static constexpr int QT_OFF = 2 * RBLK * 1024;
-  static constexpr int DOT_OFF = (2 * RBLK + TBLK) * 1024;
-  static constexpr int ST_OFF = (2 * RBLK + 2 * TBLK) * 1024;  // lse2[32] then D[32] (fp32)
-};
-
-// Direct-to-LDS copies of one wave (of NW) for one query tile image (QTiles layout): the
-// wave copies the 1 KB pieces wv, wv + NW, ...; a lane moves bytes 16 lane .. 16 lane + 15 of
-// each, so the only per-lane value is that one offset.
-template <int D, int NW>
-struct QTileCopier {
-  using QT = QTiles<D>;
-  static constexpr int SLOTS = (QT::NBLK + NW - 1) / NW;
-  int wv;
-  uint32_t voff;
-
-  __device__ __forceinline__ void init(int wave, int ln) {
-    wv = wave;
-    voff = static_cast<uint32_t>(ln) * 16u;
-  }
-
-  __device__ __forceinline__ int count() const {
-    return QT::NBLK / NW + (wv < QT::NBLK % NW);
-  }
-
-  __device__ __forceinline__ void issue(uint32_t lds, const char* img) const {
-#pragma unroll
-    for (int i = 0; i < SLOTS; ++i) {
-      const int blk = wv + i * NW;
-      if (blk >= QT::NBLK) break;
-      copy16_to_lds(img + blk * 1024, voff, lds + blk * 1024);
-    }
-  }
-};
-
 // S^T of one 64-key tile: blocks kb = 0, 1 (32 keys x 32 queries each) with the permuted key
 // order. The two accumulation chains are interleaved so that consecutive MFMAs never depend on
 // each other.
