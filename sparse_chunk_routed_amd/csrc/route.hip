@@ -98,26 +98,52 @@ __device__ __forceinline__ void finish_query(const float (&bs)[KMAX], const int 
       }
       int npool = n_allowed - nTv;
       int nadd = m < npool ? m : npool;
-      for (int j = 0; j < nadd; ++j) {
-        uint32_t w = h32(p.seed, bh, L, t, 3, j);
-        int idx = static_cast<int>((static_cast<uint64_t>(w) * static_cast<uint64_t>(npool - j)) >> 32);
-        int cnt = 0;
-        int pick = -1;
-        for (int c = 0; c < C && pick < 0; ++c) {
-          const int sc = s_shot[c];
-          if (!(sc >= 0 && sc != sq && (!p.causal || c < cq))) continue;
-          bool used = false;
+      if (nadd > 0) {
+        // The pool in ascending order is the allowed chunks - [0, lim) without the text chunks
+        // [x0, x1) and the own shot [s0, s1) (both contiguous) - minus the original top-k and
+        // the chunks picked so far. A pick is the idx-th set bit of that set, found 32 chunks
+        // at a time.
+        int s0 = cq, s1 = cq + 1;
+        while (s0 > 0 && s_shot[s0 - 1] == sq) --s0;
+        while (s1 < C && s_shot[s1] == sq) ++s1;
+        int x0 = C, x1 = C;
+        for (int c = 0; c < C; ++c)
+          if (s_shot[c] < 0) { x0 = c; break; }
+        for (int c = x0; c < C && s_shot[c] < 0; ++c) x1 = c + 1;
+        const int lim = p.causal ? cq : C;
+        auto range_bits = [](int a, int b, int w) -> uint32_t {
+          const int lo = a - 32 * w > 0 ? a - 32 * w : 0;
+          const int hi = b - 32 * w < 32 ? b - 32 * w : 32;
+          if (hi <= lo) return 0u;
+          const uint32_t ones = hi - lo == 32 ? 0xffffffffu : ((1u << (hi - lo)) - 1u);
+          return ones << lo;
+        };
+        auto pool_word = [&](int w, int npicked) -> uint32_t {
+          uint32_t bits = range_bits(0, lim, w) & ~range_bits(x0, x1, w) & ~range_bits(s0, s1, w);
 #pragma unroll
-          for (int i = 0; i < KMAX; ++i) used |= orig[i] == c;
+          for (int i = 0; i < KMAX; ++i)
+            if (orig[i] != 0x7fffffff && (orig[i] >> 5) == w) bits &= ~(1u << (orig[i] & 31));
 #pragma unroll
-          for (int i = KMAX; i < KMAX + MC; ++i) used |= f[i] == c;
-          if (used) continue;
-          if (cnt == idx) pick = c;
-          ++cnt;
+          for (int i = KMAX; i < KMAX + MC; ++i)
+            if (i - KMAX < npicked && (f[i] >> 5) == w) bits &= ~(1u << (f[i] & 31));
+          return bits;
+        };
+        const int nw = (C + 31) >> 5;
+        for (int j = 0; j < nadd; ++j) {
+          uint32_t w = h32(p.seed, bh, L, t, 3, j);
+          int idx = static_cast<int>((static_cast<uint64_t>(w) * static_cast<uint64_t>(npool - j)) >> 32);
+          int pick = -1;
+          for (int wd = 0; wd < nw && pick < 0; ++wd) {
+            uint32_t bits = pool_word(wd, j);
+            const int cnt = popc(bits);
+            if (idx >= cnt) { idx -= cnt; continue; }
+            for (int i = 0; i < idx; ++i) bits &= bits - 1u;  // drop the idx lowest set bits
+            pick = 32 * wd + __builtin_ctz(bits);
+          }
+#pragma unroll
+          for (int i = KMAX; i < KMAX + MC; ++i) if (i - KMAX == j) f[i] = pick;
+          ++nout;
         }
-#pragma unroll
-        for (int i = KMAX; i < KMAX + MC; ++i) if (i - KMAX == j) f[i] = pick;
-        ++nout;
       }
       // ascending over all slots
 #pragma unroll
@@ -394,6 +420,153 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const bf16_t* __restric
   finish_query<KMAX, NOISE>(bs, bc, n_all, p, bh, t, cq, sq, s_shot, sel, nsel);
 }
 
+
+// Persistent form of route_mfma_kernel for C <= kRouteCB: a workgroup stages the three kbar
+// terms of its (b, h) once and then scores the 256-query tiles gx, gx + G, gx + 2G, ... of that
+// (b, h) with no further barriers; the next tile's queries are loaded while the current tile is
+// scored. The interleaved tile order balances the causal work, which grows along the sequence.
+constexpr int kRouteCB = 128;
+
+template <int D, int KMAX, bool NOISE, int NW>
+__global__ __launch_bounds__(64 * NW) void route_mfma_persist_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ split,
+    const int32_t* __restrict__ off_g, const int32_t* __restrict__ shot_g, RouteParams p,
+    int32_t* __restrict__ sel, int32_t* __restrict__ nsel) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  constexpr int QPB = 32 * NW;
+  constexpr int KSTR = D + 8;
+  __shared__ __attribute__((aligned(16))) bf16_t ks[3 * kRouteCB * KSTR];
+  __shared__ int32_t s_off[MOC_MAX_C + 1];
+  __shared__ int32_t s_shot[MOC_MAX_C];
+  __shared__ int32_t s_sh0[kRouteCB], s_sh1[kRouteCB];  // chunk range [s_sh0, s_sh1) of c's shot
+
+  const int L = p.L, C = p.C;
+  const int bh = blockIdx.y;
+  const int G = gridDim.x;
+  const int ntile = (L + QPB - 1) / QPB;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int ql = lane & 31, g = lane >> 5;
+
+  for (int i = threadIdx.x; i <= C; i += blockDim.x) s_off[i] = off_g[i];
+  for (int i = threadIdx.x; i < C; i += blockDim.x) s_shot[i] = shot_g[i];
+  {
+    const size_t per = static_cast<size_t>(C) * D;
+    const bf16_t* sp = split + static_cast<size_t>(bh) * 3 * per;
+    constexpr int VPR = D / 8;  // 16-byte vectors per row
+    for (int v = threadIdx.x; v < 3 * C * VPR; v += blockDim.x) {
+      const int term = v / (C * VPR);
+      const int rem = v % (C * VPR);
+      const int c = rem / VPR, col = rem % VPR;
+      *reinterpret_cast<u32x4*>(ks + (term * kRouteCB + c) * KSTR + col * 8) =
+          *reinterpret_cast<const u32x4*>(sp + term * per + static_cast<size_t>(c) * D + col * 8);
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < C; c += blockDim.x) {
+    const int sc = s_shot[c];
+    int a = c, b = c + 1;
+    while (a > 0 && s_shot[a - 1] == sc) --a;
+    while (b < C && s_shot[b] == sc) ++b;
+    s_sh0[c] = a;
+    s_sh1[c] = b;
+  }
+  __syncthreads();
+  // text chunks [x0, x1) (contiguous), the same for every query
+  int x0 = C, x1 = C;
+  for (int c = 0; c < C; ++c)
+    if (s_shot[c] < 0) { x0 = c; break; }
+  for (int c = x0; c < C && s_shot[c] < 0; ++c) x1 = c + 1;
+
+  int tile = blockIdx.x;
+  if (tile >= ntile) return;
+  auto tok_of = [&](int tl) __attribute__((always_inline)) {
+    const int t = tl * QPB + wv * 32 + ql;
+    return t < L ? t : L - 1;
+  };
+  QFrag<bf16_t, D> qf, qn;
+  qf.load(Q + (static_cast<size_t>(bh) * L + tok_of(tile)) * D, g);
+  for (; tile < ntile; tile += G) {
+    const int t0 = tile * QPB;
+    const int t = t0 + wv * 32 + ql;
+    const bool live = t < L;
+    const int tq = live ? t : L - 1;
+    // the next tile's queries load while this one is scored
+    if (tile + G < ntile) qn.load(Q + (static_cast<size_t>(bh) * L + tok_of(tile + G)) * D, g);
+    const int cq = chunk_of(s_off, C, tq);
+    const int sq = s_shot[cq];
+    int c_wave = C;
+    if (p.causal) {
+      const int tw = t0 + wv * 32 + 31 < L ? t0 + wv * 32 + 31 : L - 1;
+      c_wave = chunk_of(s_off, C, tw);
+    }
+    const int s0 = s_sh0[cq], s1 = s_sh1[cq];
+    const int lim = live ? (p.causal ? s0 : C) : 0;
+
+    float bs[KMAX];
+    int bc[KMAX];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) { bs[i] = -__builtin_inff(); bc[i] = -1; }
+    int n_allowed = 0;
+    for (int b32 = 0; b32 < C; b32 += 32) {
+      if (b32 >= c_wave) break;  // wave-uniform: no candidate of this wave beyond here
+      f32x16 acc = {};
+#pragma unroll
+      for (int term = 0; term < 3; ++term) {
+        const bf16_t* kr = ks + (term * kRouteCB + b32 + ql) * KSTR + 8 * g;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kr + 16 * kk));
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf.q[kk], acc, 0, 0, 0);
+        }
+      }
+      const int cend = lim < C ? lim : C;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int c = b32 + 8 * (i >> 2) + 4 * g + (i & 3);
+        const bool ok = c < cend && (c < x0 || c >= x1) && (c < s0 || c >= s1);
+        n_allowed += ok ? 1 : 0;
+        if (!(ok && acc[i] > bs[KMAX - 1])) continue;  // cannot enter the top list
+        float cs = acc[i];
+        int ci = c;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {  // strict '>' keeps earlier (lower-id) chunks ahead
+          const bool take = cs > bs[k];
+          const float ts = take ? bs[k] : cs;
+          const int tc = take ? bc[k] : ci;
+          bs[k] = take ? cs : bs[k];
+          bc[k] = take ? ci : bc[k];
+          cs = ts;
+          ci = tc;
+        }
+      }
+    }
+    // merge the partner lane's list (disjoint chunk sets: ties go to the lower chunk id)
+    const int n_all = n_allowed + __shfl_xor(n_allowed, 32);
+    float ps[KMAX];
+    int pc[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) { ps[k] = __shfl_xor(bs[k], 32); pc[k] = __shfl_xor(bc[k], 32); }
+#pragma unroll
+    for (int m = 0; m < KMAX; ++m) {
+      float cs = ps[m];
+      int ci = pc[m];
+      if (ci < 0) continue;
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k) {
+        const bool take = cs > bs[k] || (cs == bs[k] && (bc[k] < 0 || ci < bc[k]));
+        const float ts = take ? bs[k] : cs;
+        const int tc = take ? bc[k] : ci;
+        bs[k] = take ? cs : bs[k];
+        bc[k] = take ? ci : bc[k];
+        cs = ts;
+        ci = tc;
+      }
+    }
+    if (live && g == 0) finish_query<KMAX, NOISE>(bs, bc, n_all, p, bh, t, cq, sq, s_shot, sel, nsel);
+    qf = qn;
+  }
+}
+
 }  // namespace moc
 
 namespace moc_host {
@@ -410,10 +583,25 @@ static hipError_t launch_route_t(const moc_layout* lay, const RouteParams& p, co
     const int64_t n = static_cast<int64_t>(lay->B) * lay->H * lay->C * D;
     hipLaunchKernelGGL((moc::route_split_kernel<D>), dim3((n + 255) / 256), dim3(256), 0, st,
                        kbar, split, lay->C, n);
-    dim3 grid((lay->L + 255) / 256, lay->B * lay->H);
-    hipLaunchKernelGGL((moc::route_mfma_kernel<D, KMAX, NOISE>), grid, dim3(512), 0, st,
-                       static_cast<const moc::bf16_t*>(Q), split, lay->chunk_offsets,
-                       lay->chunk_shot, p, sel, nsel);
+    const int ntile = (lay->L + 255) / 256;
+    const int BH = lay->B * lay->H;
+    if (lay->C <= moc::kRouteCB) {
+      // at most one workgroup per CU (one round), each taking every G-th query tile of its
+      // (b, h); 16 waves per workgroup where the registers of a query allow it (no noise,
+      // top-k <= 4), else 8
+      constexpr int NW = (NOISE || KMAX > 4) ? 8 : 16;
+      const int ntp = (lay->L + 32 * NW - 1) / (32 * NW);
+      int G = 256 / BH;
+      if (G < 1) G = 1;
+      if (G > ntp) G = ntp;
+      hipLaunchKernelGGL((moc::route_mfma_persist_kernel<D, KMAX, NOISE, NW>), dim3(G, BH),
+                         dim3(64 * NW), 0, st, static_cast<const moc::bf16_t*>(Q), split,
+                         lay->chunk_offsets, lay->chunk_shot, p, sel, nsel);
+    } else {
+      hipLaunchKernelGGL((moc::route_mfma_kernel<D, KMAX, NOISE>), dim3(ntile, BH), dim3(512),
+                         0, st, static_cast<const moc::bf16_t*>(Q), split, lay->chunk_offsets,
+                         lay->chunk_shot, p, sel, nsel);
+    }
   } else {
     (void)ws;
     dim3 grid((lay->L + 255) / 256, lay->B * lay->H);
