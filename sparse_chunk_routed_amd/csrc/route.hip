@@ -16,12 +16,18 @@
 // stream, j); p = (word >> 8) * 2^-24 * p_max; nd = min(floor(p * k), |T|) picks, each
 // idx = (word * remaining) >> 32 over the ascending list of what remains. Drop-in: m is the
 // first i with word < Thr_i (Poisson CDF thresholds, truncated at m_cap); picks from the
-// ascending candidates not in the original top-k, the same way.
+// ascending candidates not in the original top-k, the same way (the idx-th set bit of the
+// allowed-and-unused chunk mask).
 //
-// Work decomposition: bf16 queries are scored on MFMA (route_mfma_kernel: 32 queries per wave
-// against 32-chunk blocks of kbar split into three bf16 terms). fp32 queries use route_kernel:
-// one thread per query, 256 queries per workgroup, one (b,h) per grid row; kbar for the (b,h)
-// is staged through LDS in blocks of chunks and read by broadcast.
+// Work decomposition: bf16 queries are scored on MFMA (32 queries per wave against 32-chunk
+// blocks of kbar split into three bf16 terms). For C <= 128, route_mfma_persist_kernel stages
+// the terms once per workgroup and loops over query tiles; its top list holds order-preserving
+// integer keys (score bits, low 7 bits = 127 - chunk id), so an insertion is one integer
+// max/min pair and scores within 2^-16 relative of each other order by lower chunk id. Larger
+// C uses route_mfma_kernel (one tile per workgroup, kbar staged in blocks of 128 chunks, exact
+// float ordering). fp32 queries use route_kernel: one thread per query, 256 queries per
+// workgroup, one (b,h) per grid row; kbar for the (b,h) is staged through LDS in blocks of
+// chunks and read by broadcast.
 #include "attn_common.h"
 #include "moc_params.h"
 
@@ -501,12 +507,28 @@ __global__ __launch_bounds__(64 * NW) void route_mfma_persist_kernel(
     }
     const int s0 = s_sh0[cq], s1 = s_sh1[cq];
     const int lim = live ? (p.causal ? s0 : C) : 0;
-
-    float bs[KMAX];
-    int bc[KMAX];
+    // allowed chunks of this query as a bit set: [0, lim) without the text and own-shot ranges
+    auto range_bits = [](int a, int b, int w) -> uint32_t {
+      const int lo = a - 32 * w > 0 ? a - 32 * w : 0;
+      const int hi = b - 32 * w < 32 ? b - 32 * w : 32;
+      if (hi <= lo) return 0u;
+      const uint32_t ones = hi - lo == 32 ? 0xffffffffu : ((1u << (hi - lo)) - 1u);
+      return ones << lo;
+    };
+    uint32_t okw[kRouteCB / 32];
+    int n_all = 0;
 #pragma unroll
-    for (int i = 0; i < KMAX; ++i) { bs[i] = -__builtin_inff(); bc[i] = -1; }
-    int n_allowed = 0;
+    for (int w = 0; w < kRouteCB / 32; ++w) {
+      okw[w] = range_bits(0, lim, w) & ~range_bits(x0, x1, w) & ~range_bits(s0, s1, w);
+      n_all += popc(okw[w]);
+    }
+
+    // top list as order-preserving keys: the score's bits mapped to a signed int that orders
+    // like the float, low 7 bits replaced by 127 - chunk id (C <= 128), so one integer max
+    // orders by score and, within 2^-16 relative, by lower chunk id. An empty slot is INT_MIN.
+    int tk[KMAX];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) tk[i] = static_cast<int>(0x80000000u);
     for (int b32 = 0; b32 < C; b32 += 32) {
       if (b32 >= c_wave) break;  // wave-uniform: no candidate of this wave beyond here
       f32x16 acc = {};
@@ -519,48 +541,44 @@ __global__ __launch_bounds__(64 * NW) void route_mfma_persist_kernel(
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf.q[kk], acc, 0, 0, 0);
         }
       }
-      const int cend = lim < C ? lim : C;
+      const uint32_t okb = okw[b32 >> 5] >> (4 * g);  // bit 8 j + r: chunk b32 + 8 j + 4 g + r
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int c = b32 + 8 * (i >> 2) + 4 * g + (i & 3);
-        const bool ok = c < cend && (c < x0 || c >= x1) && (c < s0 || c >= s1);
-        n_allowed += ok ? 1 : 0;
-        if (!(ok && acc[i] > bs[KMAX - 1])) continue;  // cannot enter the top list
-        float cs = acc[i];
-        int ci = c;
+        const float sc = acc[i];  // (a bit cast of the vector element itself reads element 0)
+        const int bits = __float_as_int(sc);
+        int key = bits ^ ((bits >> 31) & 0x7fffffff);
+        key = (key & ~127) | (127 - c);
+        key = ((okb >> (8 * (i >> 2) + (i & 3))) & 1u) ? key : static_cast<int>(0x80000000u);
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k) {  // strict '>' keeps earlier (lower-id) chunks ahead
-          const bool take = cs > bs[k];
-          const float ts = take ? bs[k] : cs;
-          const int tc = take ? bc[k] : ci;
-          bs[k] = take ? cs : bs[k];
-          bc[k] = take ? ci : bc[k];
-          cs = ts;
-          ci = tc;
+        for (int k = 0; k < KMAX; ++k) {
+          const int hi = key > tk[k] ? key : tk[k];
+          key = key > tk[k] ? tk[k] : key;
+          tk[k] = hi;
         }
       }
     }
-    // merge the partner lane's list (disjoint chunk sets: ties go to the lower chunk id)
-    const int n_all = n_allowed + __shfl_xor(n_allowed, 32);
-    float ps[KMAX];
-    int pc[KMAX];
+    // merge the partner lane's list (the two lanes hold disjoint chunks); read all of it
+    // before either lane updates its own
+    int pk[KMAX];
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) { ps[k] = __shfl_xor(bs[k], 32); pc[k] = __shfl_xor(bc[k], 32); }
+    for (int m = 0; m < KMAX; ++m) pk[m] = __shfl_xor(tk[m], 32);
 #pragma unroll
     for (int m = 0; m < KMAX; ++m) {
-      float cs = ps[m];
-      int ci = pc[m];
-      if (ci < 0) continue;
+      int key = pk[m];
 #pragma unroll
       for (int k = 0; k < KMAX; ++k) {
-        const bool take = cs > bs[k] || (cs == bs[k] && (bc[k] < 0 || ci < bc[k]));
-        const float ts = take ? bs[k] : cs;
-        const int tc = take ? bc[k] : ci;
-        bs[k] = take ? cs : bs[k];
-        bc[k] = take ? ci : bc[k];
-        cs = ts;
-        ci = tc;
+        const int hi = key > tk[k] ? key : tk[k];
+        key = key > tk[k] ? tk[k] : key;
+        tk[k] = hi;
       }
+    }
+    float bs[KMAX];
+    int bc[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      bs[k] = 0.f;  // not used by finish_query
+      bc[k] = tk[k] == static_cast<int>(0x80000000u) ? -1 : 127 - (tk[k] & 127);
     }
     if (live && g == 0) finish_query<KMAX, NOISE>(bs, bc, n_all, p, bh, t, cq, sq, s_shot, sel, nsel);
     qf = qn;
