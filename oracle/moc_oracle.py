@@ -31,6 +31,10 @@ What is computed (per batch element b and head h; routing is independent per hea
      ([MoC-S] §3.1); lse_t = natural log of the softmax denominator (with the max added back).
   9. Backward with Omega fixed (top-k is non-differentiable, [MoC-S] §3.1 and Appendix A).
  10. Counts: pairs = sum_t |Omega(t)|; FLOPs at 4*d per attended pair ([MoC-S] Eq. 5).
+ 11. Outer-loop context routing ([MoC-S] Appendix I): a coarse router picks, per query segment,
+     the top-M segments by the dot product of mean-pooled features; inner routing (3-6) then
+     only considers chunks of the query's own segment and of the picked segments. See
+     route_outer().
 """
 from __future__ import annotations
 
@@ -181,8 +185,10 @@ def scores(Q, kbar) -> np.ndarray:
 TIE_REL = 1e-4
 
 
-def route(Q, kbar, layout, top_k: int, causal: bool) -> Routing:
-    """Top-min(k, #candidates) chunks per (b, h, t), stored ascending by chunk id."""
+def route(Q, kbar, layout, top_k: int, causal: bool,
+          cand_mask: Optional[np.ndarray] = None) -> Routing:
+    """Top-min(k, #candidates) chunks per (b, h, t), stored ascending by chunk id. With
+    cand_mask (bool [B,H,C,C], row = the query's chunk), a candidate must also be set in it."""
     D = derive(layout)
     s_all = scores(Q, kbar)
     B, H, L, C = s_all.shape
@@ -192,12 +198,13 @@ def route(Q, kbar, layout, top_k: int, causal: bool) -> Routing:
     exempt = np.zeros((B, H, L), dtype=bool)
     for cq in range(C):
         toks = np.arange(D.offsets[cq], D.offsets[cq + 1])
-        cand = candidates(D, cq, causal)
-        n = min(k_eff, len(cand))
-        if n == 0:
-            continue
+        cand0 = candidates(D, cq, causal)
         for b in range(B):
             for h in range(H):
+                cand = cand0 if cand_mask is None else cand0[cand_mask[b, h, cq, cand0]]
+                n = min(k_eff, len(cand))
+                if n == 0:
+                    continue
                 sc = s_all[b, h][np.ix_(toks, cand)]           # [nt, ncand]
                 # order by (-score, chunk id): cand is ascending and the sort is stable
                 order = np.argsort(-sc, axis=1, kind="stable")
@@ -217,7 +224,8 @@ def route(Q, kbar, layout, top_k: int, causal: bool) -> Routing:
 
 def drop_noise_row(D: Derived, top: Sequence[int], b: int, h: int, t: int, H: int,
                    k_eff: int, causal: bool, p_max: float, lam: float, m_cap: int,
-                   seed: int, thr: Optional[List[int]]) -> List[int]:
+                   seed: int, thr: Optional[List[int]],
+                   cand_row: Optional[np.ndarray] = None) -> List[int]:
     """Training-time routing noise for one query ([MoC-S] §3.1; [MoC-D] slide 14).
 
     Readings: drop-off removes min(floor(p*k), |T|) chunks from the routed top-k set T only
@@ -242,7 +250,8 @@ def drop_noise_row(D: Derived, top: Sequence[int], b: int, h: int, t: int, H: in
         r = _rng.h32(seed, _rng.counter(b, h, t, _rng.STREAM_IN_COUNT, 0, H, L))
         m = _rng.poisson_from_word(r, thr, m_cap)
         cq = int(D.chunk_of[t])
-        pool = [int(c) for c in candidates(D, cq, causal) if int(c) not in T]
+        pool = [int(c) for c in candidates(D, cq, causal) if int(c) not in T
+                and (cand_row is None or cand_row[int(c)])]
         for j in range(min(m, len(pool))):
             w = _rng.h32(seed, _rng.counter(b, h, t, _rng.STREAM_IN_PICK, j, H, L))
             idx = (w * len(pool)) >> 32
@@ -251,8 +260,8 @@ def drop_noise_row(D: Derived, top: Sequence[int], b: int, h: int, t: int, H: in
 
 
 def drop_noise(routing: Routing, layout, causal: bool, p_max: float, lam: float,
-               m_cap: int, seed: int, rows: Optional[Iterable[Tuple[int, int, int]]] = None
-               ) -> Tuple[np.ndarray, np.ndarray]:
+               m_cap: int, seed: int, rows: Optional[Iterable[Tuple[int, int, int]]] = None,
+               cand_mask: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Apply drop-off then drop-in. Returns (sel [B,H,L,S], nsel [B,H,L]) with
     S = k_eff + (m_cap if lam > 0 else 0). With `rows`, only those (b,h,t) are computed and
     the other rows are left at -1 / 0."""
@@ -268,7 +277,9 @@ def drop_noise(routing: Routing, layout, causal: bool, p_max: float, lam: float,
     for (b, h, t) in it:
         n = int(routing.nsel[b, h, t])
         top = routing.sel[b, h, t, :n]
-        out = drop_noise_row(D, top, b, h, t, H, k_eff, causal, p_max, lam, m_cap, seed, thr)
+        row = None if cand_mask is None else cand_mask[b, h, int(D.chunk_of[t])]
+        out = drop_noise_row(D, top, b, h, t, H, k_eff, causal, p_max, lam, m_cap, seed, thr,
+                             row)
         sel[b, h, t, :len(out)] = out
         nsel[b, h, t] = len(out)
     return sel, nsel
@@ -435,18 +446,22 @@ def is_dag(C: int, edges: Iterable[Tuple[int, int]]) -> bool:
     return seen == C
 
 
-def check_routing(layout, sel, nsel, top_k: int, causal: bool, exact_count: bool = True) -> None:
-    """Raise AssertionError unless every selection is a legal candidate, ascending and unique,
-    and (exact_count) there are exactly min(k, #candidates) of them."""
+def check_routing(layout, sel, nsel, top_k: int, causal: bool, exact_count: bool = True,
+                  cand_mask: Optional[np.ndarray] = None) -> None:
+    """Raise AssertionError unless every selection is a legal candidate (and set in cand_mask,
+    if given), ascending and unique, and (exact_count) there are exactly min(k, #candidates) of
+    them."""
     D = derive(layout)
     sel = np.asarray(sel)
     B, H, L, S = sel.shape
     for cq in range(D.C):
-        cand = set(int(c) for c in candidates(D, cq, causal))
-        need = min(int(top_k), D.C, len(cand))
+        cand0 = set(int(c) for c in candidates(D, cq, causal))
         for t in range(int(D.offsets[cq]), int(D.offsets[cq + 1])):
             for b in range(B):
                 for h in range(H):
+                    cand = cand0 if cand_mask is None else {
+                        c for c in cand0 if cand_mask[b, h, cq, c]}
+                    need = min(int(top_k), D.C, len(cand))
                     n = int(nsel[b, h, t])
                     row = [int(c) for c in sel[b, h, t, :n]]
                     assert all(c in cand for c in row), (b, h, t, row)
@@ -454,6 +469,115 @@ def check_routing(layout, sel, nsel, top_k: int, causal: bool, exact_count: bool
                     assert all(int(c) == -1 for c in sel[b, h, t, n:]), (b, h, t)
                     if exact_count:
                         assert n == need, (b, h, t, n, need)
+
+
+# ---------------------------------------------------------------------------------------------
+# 11. Outer-loop context routing ([MoC-S] Appendix I)
+# ---------------------------------------------------------------------------------------------
+# Readings. The pages describe a coarse router that picks the top-M large context segments by
+# the similarity of mean-pooled features of the current query block and of the candidate
+# segments, and then hands those segments plus the mandatory context to the inner MoC router.
+#  * Segments are given: contiguous groups of whole chunks (seg_chunk[nseg+1], chunk offsets),
+#    each all text chunks or all video chunks. Text is mandatory context, never a candidate.
+#  * The current query block of a query is its own segment. Its feature is the mean of the
+#    segment's queries; a candidate segment's feature is the mean of its keys. Both are pooled
+#    like chunk keys (exact sum, one binary64 division, RN to binary32).
+#  * Candidates of query segment sq: video segments s != sq, and s < sq when causal (the
+#    autoregressive reading: a segment is generated after the ones it retrieves from).
+#    Score = dot product in binary64; top-min(M, #candidates); an exact tie goes to the lower
+#    segment index; stored ascending.
+#  * Inner routing of a query t considers only chunks of seg(t) and of the picked segments, on
+#    top of the usual candidate rule (3); drop-in draws from that restricted pool. The
+#    mandatory anchors (text, own shot) are unchanged.
+
+@dataclass(frozen=True)
+class Segments:
+    nseg: int
+    chunk_off: np.ndarray     # int64 [nseg+1]
+    tok_off: np.ndarray       # int64 [nseg+1]
+    is_text: np.ndarray       # bool [nseg]
+    seg_of_chunk: np.ndarray  # int64 [C]
+
+
+def derive_segments(layout, seg_chunk) -> Segments:
+    D = derive(layout)
+    so = np.asarray(seg_chunk, dtype=np.int64)
+    nseg = len(so) - 1
+    if nseg < 1 or so[0] != 0 or so[-1] != D.C or np.any(np.diff(so) <= 0):
+        raise ValueError("segment chunk offsets must start at 0, increase strictly, end at C")
+    is_text = np.zeros(nseg, dtype=bool)
+    for sg in range(nseg):
+        t = D.is_text[so[sg]:so[sg + 1]]
+        if t.any() and not t.all():
+            raise ValueError("a segment mixes text and video chunks")
+        is_text[sg] = bool(t.all())
+    seg_of_chunk = np.repeat(np.arange(nseg, dtype=np.int64), np.diff(so))
+    return Segments(nseg, so, D.offsets[so], is_text, seg_of_chunk)
+
+
+@dataclass(frozen=True)
+class _Layout:
+    chunk_offsets: np.ndarray
+    chunk_shot: np.ndarray
+    text_begin: int
+    text_end: int
+
+
+def segment_layout(layout, seg_chunk):
+    """The layout whose chunks are the segments (text segments keep shot id -1)."""
+    G = derive_segments(layout, seg_chunk)
+    shot = np.where(G.is_text, TEXT_SHOT, np.arange(G.nseg))
+    return _Layout(G.tok_off, shot, int(layout.text_begin), int(layout.text_end))
+
+
+@dataclass
+class OuterRouting:
+    seg_sel: np.ndarray     # int32 [B,H,nseg,Msel]: picked segments ascending, -1 padded
+    seg_nsel: np.ndarray    # int32 [B,H,nseg]
+    gap_exempt: np.ndarray  # bool [B,H,nseg]: M-th vs (M+1)-th score gap < TIE_REL relative
+    cand_mask: np.ndarray   # bool [B,H,C,C]: chunks the inner router may consider, per chunk
+    qseg: np.ndarray        # float32 [B,H,nseg,d]
+    kseg: np.ndarray        # float32 [B,H,nseg,d]
+
+
+def segment_candidates(G: Segments, sq: int, causal: bool) -> List[int]:
+    return [s for s in range(G.nseg)
+            if not G.is_text[s] and s != sq and (not causal or s < sq)]
+
+
+def route_outer(Q, K, layout, seg_chunk, M: int, causal: bool) -> OuterRouting:
+    """Coarse top-M segment selection per (b, h, query segment) and the inner candidate mask."""
+    G = derive_segments(layout, seg_chunk)
+    D = derive(layout)
+    slay = segment_layout(layout, seg_chunk)
+    qseg = pool_keys(Q, slay)
+    kseg = pool_keys(K, slay)
+    B, H, nseg, d = qseg.shape
+    msel = min(int(M), nseg)
+    seg_sel = np.full((B, H, nseg, msel), -1, dtype=np.int32)
+    seg_nsel = np.zeros((B, H, nseg), dtype=np.int32)
+    exempt = np.zeros((B, H, nseg), dtype=bool)
+    allowed_segs = np.zeros((B, H, nseg, nseg), dtype=bool)
+    for b in range(B):
+        for h in range(H):
+            for sq in range(nseg):
+                allowed_segs[b, h, sq, sq] = True
+                cand = segment_candidates(G, sq, causal)
+                n = min(msel, len(cand))
+                if n == 0:
+                    continue
+                q = qseg[b, h, sq].astype(np.float64)
+                sc = [float(np.dot(q, kseg[b, h, s].astype(np.float64))) for s in cand]
+                order = sorted(range(len(cand)), key=lambda i: (-sc[i], cand[i]))
+                top = sorted(cand[i] for i in order[:n])
+                seg_sel[b, h, sq, :n] = top
+                seg_nsel[b, h, sq] = n
+                allowed_segs[b, h, sq, top] = True
+                if len(cand) > n:
+                    a, c = sc[order[n - 1]], sc[order[n]]
+                    exempt[b, h, sq] = (a - c) < TIE_REL * max(abs(a), abs(c))
+    cmask = allowed_segs[:, :, G.seg_of_chunk][:, :, :, G.seg_of_chunk]  # [B,H,C,C]
+    return OuterRouting(seg_sel, seg_nsel, exempt, cmask, qseg, kseg)
 
 
 def _as_f64(x) -> np.ndarray:
