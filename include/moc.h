@@ -50,12 +50,14 @@ typedef enum {
 typedef enum { MOC_F32 = 0, MOC_BF16 = 1 } moc_dtype;
 
 /* Workspace kinds for moc_workspace_bytes(). */
-enum { MOC_OP_ROUTE = 0, MOC_OP_VARLEN = 1, MOC_OP_FWD = 2, MOC_OP_BWD = 3 };
+enum { MOC_OP_ROUTE = 0, MOC_OP_VARLEN = 1, MOC_OP_FWD = 2, MOC_OP_BWD = 3, MOC_OP_OUTER = 4 };
 
 /* Hard limits of this build. */
 #define MOC_MAX_C 1024        /* chunks per sequence */
 #define MOC_MAX_TOPK 32       /* min(top_k, C) */
 #define MOC_MAX_DROP_IN 16    /* max_drop_in */
+#define MOC_MAX_SEG 256       /* segments of outer-loop routing */
+#define MOC_MAX_TOPM 16       /* min(M, nseg) of outer-loop routing */
 
 /*
  * Token layout (shared by all batch elements and heads). Chunks are content-aligned token
@@ -142,7 +144,8 @@ typedef struct {
 int32_t moc_sel_width(const moc_route_cfg *cfg, int32_t C);
 
 /* Bytes of device workspace needed by the entry point `op` (MOC_OP_*); 0 on invalid
- * arguments (see moc_last_error()). */
+ * arguments (see moc_last_error()). MOC_OP_OUTER is sized for MOC_MAX_SEG segments (the
+ * segment count is not part of the layout). */
 size_t moc_workspace_bytes(const moc_layout *lay, const moc_route_cfg *cfg, int32_t op);
 
 /*
@@ -160,13 +163,52 @@ moc_status moc_pool_keys(const moc_layout *lay, const void *K, float *kbar, void
  * For each (b,h,t): candidates are chunks c that are not text, not in the query's own shot,
  * and (causal) c < chunk(t); score s_c = q_t . kbar_c (binary32 accumulation of exact
  * products); the min(top_k, #candidates) highest scores are kept (an exact tie keeps the
- * lower chunk id); then drop-off and drop-in are applied when enabled.
+ * lower chunk id; for bf16 queries with C <= 128, scores within 2^-16 relative of each other
+ * count as tied); then drop-off and drop-in are applied when enabled.
  *   sel:  device int32 [B,H,L,S], chunk ids ascending, -1 padded; nsel: int32 [B,H,L].
  *   ws:   MOC_OP_ROUTE workspace (may be NULL when its size is 0).
  */
 moc_status moc_route(const moc_layout *lay, const moc_route_cfg *cfg, const void *Q,
                      const float *kbar, int32_t *sel, int32_t *nsel, void *ws, size_t ws_bytes,
                      void *stream);
+
+/*
+ * Outer-loop context routing (summary, Appendix I: a coarse router first picks the top-M
+ * large context segments by the similarity of mean-pooled features of the current query block
+ * and of the candidate segments; inner MoC routing then works within those segments plus the
+ * mandatory context). Segments are given groups of whole chunks; a query's block is its own
+ * segment.
+ *   seg_chunk: device int32 [nseg+1], 0 = seg_chunk[0] < ... < seg_chunk[nseg] = C; segment s
+ *              is chunks [seg_chunk[s], seg_chunk[s+1]) and holds only text chunks or only
+ *              video chunks (a precondition, like the layout's content).
+ *   nseg in [1, MOC_MAX_SEG]; M >= 0 with min(M, nseg) <= MOC_MAX_TOPM; causal in {0, 1}.
+ *   For each (b, h) and query segment sq: qseg = the mean of the segment's queries and kseg[s]
+ *   = the mean of segment s's keys, both pooled like moc_pool_keys; the candidates are video
+ *   segments s != sq (and s < sq when causal); score = qseg . kseg[s] (binary32
+ *   accumulation); the min(M, #candidates) highest are kept, an exact tie keeping the lower
+ *   segment id.
+ *   seg_sel:   device int32 [B,H,nseg,min(M, nseg)], segment ids ascending, -1 padded.
+ *   seg_nsel:  device int32 [B,H,nseg].
+ *   cand_mask: device uint32 [B,H,C,ceil(C/32)]: bit c' of row (b,h,c) is set iff chunk c'
+ *              lies in chunk c's segment or in a segment picked for it; the input of
+ *              moc_route_masked.
+ *   Q, K: [B,H,L,d] layout dtype. ws: MOC_OP_OUTER workspace (segment offsets and features).
+ */
+moc_status moc_route_outer(const moc_layout *lay, const int32_t *seg_chunk, int32_t nseg,
+                           int32_t M, int32_t causal, const void *Q, const void *K,
+                           int32_t *seg_sel, int32_t *seg_nsel, uint32_t *cand_mask, void *ws,
+                           size_t ws_bytes, void *stream);
+
+/*
+ * Inner routing of outer-loop context routing: moc_route with one more condition - chunk c is
+ * a candidate of query t only if bit c of cand_mask row (b, h, chunk(t)) is set. Drop-in draws
+ * from the same restricted candidates. The mandatory anchors are unaffected.
+ *   cand_mask: device uint32 [B,H,C,ceil(C/32)] (as written by moc_route_outer).
+ *   Every other argument, output and workspace as for moc_route.
+ */
+moc_status moc_route_masked(const moc_layout *lay, const moc_route_cfg *cfg, const void *Q,
+                            const float *kbar, const uint32_t *cand_mask, int32_t *sel,
+                            int32_t *nsel, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Index inversion (write-up 計算效率: packing the (query, key-group) pairs into one

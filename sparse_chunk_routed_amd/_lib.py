@@ -11,14 +11,15 @@ LIB_PATH = os.environ.get("MOC_LIB_PATH") or os.path.join(
 MOC_OK, MOC_EINVAL, MOC_ESHAPE, MOC_EDTYPE, MOC_EWORKSPACE, MOC_EUNSUPPORTED, MOC_EHIP, \
     MOC_EINTERNAL = range(8)
 MOC_F32, MOC_BF16 = 0, 1
-MOC_OP_ROUTE, MOC_OP_VARLEN, MOC_OP_FWD, MOC_OP_BWD = range(4)
+MOC_OP_ROUTE, MOC_OP_VARLEN, MOC_OP_FWD, MOC_OP_BWD, MOC_OP_OUTER = range(5)
 MOC_MAX_C, MOC_MAX_TOPK, MOC_MAX_DROP_IN = 1024, 32, 16
+MOC_MAX_SEG, MOC_MAX_TOPM = 256, 16
 
 # every function include/moc.h declares
 EXPORTS = (
-    "moc_sel_width", "moc_workspace_bytes", "moc_pool_keys", "moc_route", "moc_build_varlen",
-    "moc_attend_fwd", "moc_attend_bwd", "moc_poisson_thresholds", "moc_status_string",
-    "moc_last_error",
+    "moc_sel_width", "moc_workspace_bytes", "moc_pool_keys", "moc_route", "moc_route_outer",
+    "moc_route_masked", "moc_build_varlen", "moc_attend_fwd", "moc_attend_bwd",
+    "moc_poisson_thresholds", "moc_status_string", "moc_last_error",
 )
 
 
@@ -71,6 +72,13 @@ def load() -> ctypes.CDLL:
     lib.moc_route.argtypes = [P(MocLayout), P(MocRouteCfg), c_void_p, c_void_p, c_void_p,
                               c_void_p, c_void_p, c_size_t, c_void_p]
     lib.moc_route.restype = c_int32
+    lib.moc_route_outer.argtypes = [P(MocLayout), c_void_p, c_int32, c_int32, c_int32, c_void_p,
+                                    c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                    c_void_p]
+    lib.moc_route_outer.restype = c_int32
+    lib.moc_route_masked.argtypes = [P(MocLayout), P(MocRouteCfg), c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.moc_route_masked.restype = c_int32
     lib.moc_build_varlen.argtypes = [P(MocLayout), P(MocRouteCfg), c_void_p, c_void_p,
                                      P(MocVarlen), c_void_p, c_void_p, c_size_t, c_void_p]
     lib.moc_build_varlen.restype = c_int32

@@ -148,8 +148,10 @@ def pool_keys(K: torch.Tensor, lay: DeviceLayout) -> torch.Tensor:
 
 
 def route(Q: torch.Tensor, kbar: torch.Tensor, lay: DeviceLayout, cfg: RouteCfg,
-          ws: Optional[torch.Tensor] = None):
-    """(sel [B,H,L,S] int32 ascending, -1 padded; nsel [B,H,L] int32)."""
+          ws: Optional[torch.Tensor] = None, cand_mask: Optional[torch.Tensor] = None):
+    """(sel [B,H,L,S] int32 ascending, -1 padded; nsel [B,H,L] int32). With cand_mask (the
+    int32 view of the uint32 [B,H,C,ceil(C/32)] mask of route_outer), the inner router of
+    outer-loop routing (moc_route_masked)."""
     _check_qkv(Q)
     B, H, Lq, d = Q.shape
     S = sel_width(cfg, lay.C)
@@ -160,11 +162,56 @@ def route(Q: torch.Tensor, kbar: torch.Tensor, lay: DeviceLayout, cfg: RouteCfg,
     need = workspace_bytes(lay, B, H, d, Q.dtype, cfg, L.MOC_OP_ROUTE)
     if need > 0 and (ws is None or ws.numel() < need):
         ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
-    L.check(lib.moc_route(ctypes.byref(s), ctypes.byref(cfg.struct()), _ptr(Q), _ptr(kbar),
-                          _ptr(sel) if S > 0 else None, _ptr(nsel),
-                          _ptr(ws) if need > 0 else None, ws.numel() if need > 0 else 0,
-                          _stream(Q.device)))
+    args = (_ptr(sel) if S > 0 else None, _ptr(nsel), _ptr(ws) if need > 0 else None,
+            ws.numel() if need > 0 else 0, _stream(Q.device))
+    if cand_mask is None:
+        L.check(lib.moc_route(ctypes.byref(s), ctypes.byref(cfg.struct()), _ptr(Q), _ptr(kbar),
+                              *args))
+    else:
+        W = (lay.C + 31) // 32
+        if (cand_mask.dtype != torch.int32 or tuple(cand_mask.shape) != (B, H, lay.C, W)
+                or not cand_mask.is_contiguous() or cand_mask.device != Q.device):
+            raise ValueError(f"cand_mask must be int32 [{B},{H},{lay.C},{W}] on {Q.device}")
+        L.check(lib.moc_route_masked(ctypes.byref(s), ctypes.byref(cfg.struct()), _ptr(Q),
+                                     _ptr(kbar), _ptr(cand_mask), *args))
     return sel, nsel
+
+
+@dataclass
+class OuterRouting:
+    seg_sel: torch.Tensor    # int32 [B,H,nseg,min(M,nseg)] ascending, -1 padded
+    seg_nsel: torch.Tensor   # int32 [B,H,nseg]
+    cand_mask: torch.Tensor  # int32 view of uint32 [B,H,C,ceil(C/32)]
+
+
+def route_outer(Q: torch.Tensor, K: torch.Tensor, lay: DeviceLayout, seg_chunk, M: int,
+                causal: bool, ws: Optional[torch.Tensor] = None) -> OuterRouting:
+    """Outer-loop context routing (moc_route_outer): seg_chunk [nseg+1] are the segments'
+    chunk offsets (host sequence or device int32 tensor)."""
+    _check_qkv(Q)
+    _check_qkv(K)
+    B, H, Lq, d = Q.shape
+    seg = torch.as_tensor(seg_chunk, dtype=torch.int32).to(Q.device).contiguous()
+    h_seg = seg.cpu().tolist()
+    nseg = len(h_seg) - 1
+    if nseg < 1 or h_seg[0] != 0 or h_seg[-1] != lay.C or any(
+            b <= a for a, b in zip(h_seg, h_seg[1:])):
+        raise ValueError("seg_chunk must start at 0, increase strictly and end at C")
+    Ms = min(int(M), nseg)
+    W = (lay.C + 31) // 32
+    seg_sel = torch.empty((B, H, nseg, Ms), dtype=torch.int32, device=Q.device)
+    seg_nsel = torch.empty((B, H, nseg), dtype=torch.int32, device=Q.device)
+    cmask = torch.empty((B, H, lay.C, W), dtype=torch.int32, device=Q.device)
+    s = lay.struct(B, H, d, Q.dtype)
+    need = workspace_bytes(lay, B, H, d, Q.dtype, RouteCfg(0, causal), L.MOC_OP_OUTER)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    lib = L.load()
+    L.check(lib.moc_route_outer(ctypes.byref(s), _ptr(seg), nseg, int(M), int(bool(causal)),
+                                _ptr(Q), _ptr(K), _ptr(seg_sel) if Ms > 0 else None,
+                                _ptr(seg_nsel), _ptr(cmask), _ptr(ws), ws.numel(),
+                                _stream(Q.device)))
+    return OuterRouting(seg_sel, seg_nsel, cmask)
 
 
 class Varlen:

@@ -17,6 +17,10 @@ hipError_t launch_pool(const moc_layout* lay, const void* K, float* kbar, hipStr
 hipError_t launch_route(const moc_layout* lay, const moc::RouteParams& p, const void* Q,
                         const float* kbar, int32_t* sel, int32_t* nsel, void* ws, hipStream_t st);
 size_t route_workspace(const moc_layout* lay);
+size_t outer_workspace(const moc_layout* lay);
+hipError_t launch_route_outer(const moc_layout* lay, const int32_t* seg_chunk, int nseg, int M,
+                              int causal, const void* Q, const void* K, int32_t* seg_sel,
+                              int32_t* seg_nsel, uint32_t* cmask, void* ws, hipStream_t st);
 hipError_t launch_varlen(const moc_layout* lay, const moc::VarlenParams& p, const int32_t* sel,
                          const int32_t* nsel, int32_t* counts, int32_t* totals,
                          int32_t* tile_base, const moc_varlen* out, int64_t* pair_count,
@@ -197,6 +201,7 @@ size_t moc_workspace_bytes(const moc_layout* lay, const moc_route_cfg* cfg, int3
     case MOC_OP_VARLEN: return varlen_sizes(lay, S).total();
     case MOC_OP_FWD: return fwd_bytes(lay, S);
     case MOC_OP_BWD: return moc_host::attn_bwd_workspace(lay, S);
+    case MOC_OP_OUTER: return moc_host::outer_workspace(lay);
     default: fail(MOC_EINVAL, "unknown op %d", op); return 0;
   }
 }
@@ -214,41 +219,91 @@ moc_status moc_pool_keys(const moc_layout* lay, const void* K, float* kbar, void
   }
 }
 
+namespace {
+moc_status route_impl(const moc_layout* lay, const moc_route_cfg* cfg, const void* Q,
+                      const float* kbar, const uint32_t* cmask, int32_t* sel, int32_t* nsel,
+                      void* ws, size_t ws_bytes, void* stream) {
+  moc_status s = check_layout(lay);
+  if (s != MOC_OK) return s;
+  s = check_cfg(lay, cfg);
+  if (s != MOC_OK) return s;
+  const int S = moc_sel_width(cfg, lay->C);
+  if (!Q || !kbar || !nsel || (S > 0 && !sel)) return fail(MOC_EINVAL, "NULL tensor argument");
+  if (static_cast<void*>(sel) == static_cast<void*>(nsel) && S > 0)
+    return fail(MOC_EINVAL, "sel aliases nsel");
+  const size_t need = moc_host::route_workspace(lay);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(MOC_EWORKSPACE, "ROUTE workspace needs %zu bytes (got %zu)", need,
+                ws ? ws_bytes : size_t(0));
+  moc::RouteParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.B = lay->B; p.H = lay->H; p.L = lay->L; p.C = lay->C; p.S = S;
+  p.k_eff = k_eff_of(cfg, lay->C);
+  p.causal = cfg->causal;
+  p.drop_off = cfg->p_max > 0.f ? 1 : 0;
+  p.drop_in = cfg->lambda > 0.f ? 1 : 0;
+  p.m_cap = p.drop_in ? cfg->max_drop_in : 0;
+  p.p_max = cfg->p_max;
+  p.seed = cfg->seed;
+  p.cmask = cmask;
+  p.cmask_w = (lay->C + 31) / 32;
+  if (p.drop_in) {
+    s = moc_poisson_thresholds(cfg->lambda, cfg->max_drop_in, p.thr);
+    if (s != MOC_OK) return s;
+  }
+  return hip_status(moc_host::launch_route(lay, p, Q, kbar, sel, nsel, ws,
+                                           static_cast<hipStream_t>(stream)),
+                    "route launch");
+}
+}  // namespace
+
 moc_status moc_route(const moc_layout* lay, const moc_route_cfg* cfg, const void* Q,
                      const float* kbar, int32_t* sel, int32_t* nsel, void* ws, size_t ws_bytes,
                      void* stream) {
   try {
-    moc_status s = check_layout(lay);
-    if (s != MOC_OK) return s;
-    s = check_cfg(lay, cfg);
-    if (s != MOC_OK) return s;
-    const int S = moc_sel_width(cfg, lay->C);
-    if (!Q || !kbar || !nsel || (S > 0 && !sel)) return fail(MOC_EINVAL, "NULL tensor argument");
-    if (static_cast<void*>(sel) == static_cast<void*>(nsel) && S > 0)
-      return fail(MOC_EINVAL, "sel aliases nsel");
-    const size_t need = moc_host::route_workspace(lay);
-    if (need > 0 && (!ws || ws_bytes < need))
-      return fail(MOC_EWORKSPACE, "ROUTE workspace needs %zu bytes (got %zu)", need,
-                  ws ? ws_bytes : size_t(0));
-    moc::RouteParams p;
-    std::memset(&p, 0, sizeof(p));
-    p.B = lay->B; p.H = lay->H; p.L = lay->L; p.C = lay->C; p.S = S;
-    p.k_eff = k_eff_of(cfg, lay->C);
-    p.causal = cfg->causal;
-    p.drop_off = cfg->p_max > 0.f ? 1 : 0;
-    p.drop_in = cfg->lambda > 0.f ? 1 : 0;
-    p.m_cap = p.drop_in ? cfg->max_drop_in : 0;
-    p.p_max = cfg->p_max;
-    p.seed = cfg->seed;
-    if (p.drop_in) {
-      s = moc_poisson_thresholds(cfg->lambda, cfg->max_drop_in, p.thr);
-      if (s != MOC_OK) return s;
-    }
-    return hip_status(moc_host::launch_route(lay, p, Q, kbar, sel, nsel, ws,
-                                             static_cast<hipStream_t>(stream)),
-                      "route launch");
+    return route_impl(lay, cfg, Q, kbar, nullptr, sel, nsel, ws, ws_bytes, stream);
   } catch (...) {
     return fail(MOC_EINTERNAL, "exception in moc_route");
+  }
+}
+
+moc_status moc_route_masked(const moc_layout* lay, const moc_route_cfg* cfg, const void* Q,
+                            const float* kbar, const uint32_t* cand_mask, int32_t* sel,
+                            int32_t* nsel, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    if (!cand_mask) return fail(MOC_EINVAL, "cand_mask is NULL");
+    return route_impl(lay, cfg, Q, kbar, cand_mask, sel, nsel, ws, ws_bytes, stream);
+  } catch (...) {
+    return fail(MOC_EINTERNAL, "exception in moc_route_masked");
+  }
+}
+
+moc_status moc_route_outer(const moc_layout* lay, const int32_t* seg_chunk, int32_t nseg,
+                           int32_t M, int32_t causal, const void* Q, const void* K,
+                           int32_t* seg_sel, int32_t* seg_nsel, uint32_t* cand_mask, void* ws,
+                           size_t ws_bytes, void* stream) {
+  try {
+    moc_status s = check_layout(lay);
+    if (s != MOC_OK) return s;
+    if (nseg < 1 || nseg > MOC_MAX_SEG || nseg > lay->C)
+      return fail(MOC_ESHAPE, "nseg must be in [1, min(C, %d)] (got %d)", MOC_MAX_SEG, nseg);
+    if (M < 0) return fail(MOC_EINVAL, "M must be >= 0 (got %d)", M);
+    const int Ms = M < nseg ? M : nseg;
+    if (Ms > MOC_MAX_TOPM)
+      return fail(MOC_ESHAPE, "min(M, nseg) = %d exceeds %d", Ms, MOC_MAX_TOPM);
+    if (causal != 0 && causal != 1) return fail(MOC_EINVAL, "causal must be 0 or 1");
+    if (!seg_chunk || !Q || !K || !seg_nsel || !cand_mask || (Ms > 0 && !seg_sel))
+      return fail(MOC_EINVAL, "NULL argument");
+    const size_t need = moc_host::outer_workspace(lay);
+    if (!ws || ws_bytes < need)
+      return fail(MOC_EWORKSPACE, "OUTER workspace needs %zu bytes (got %zu)", need,
+                  ws ? ws_bytes : size_t(0));
+    return hip_status(moc_host::launch_route_outer(lay, seg_chunk, nseg, M, causal, Q, K,
+                                                   seg_sel, seg_nsel, cand_mask, ws,
+                                                   static_cast<hipStream_t>(stream)),
+                      "outer route launch");
+  } catch (...) {
+    return fail(MOC_EINTERNAL, "exception in moc_route_outer");
   }
 }
 

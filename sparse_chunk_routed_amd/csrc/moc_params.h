@@ -13,6 +13,8 @@ struct RouteParams {
   float p_max;
   uint64_t seed;
   uint64_t thr[MOC_MAX_DROP_IN];  // drop-in Poisson CDF thresholds (x 2^32)
+  const uint32_t* cmask;          // optional candidate mask [B*H][C][cmask_w] (outer routing)
+  int cmask_w;
 };
 
 struct VarlenParams {

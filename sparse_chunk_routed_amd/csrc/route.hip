@@ -44,6 +44,14 @@ __device__ __forceinline__ uint32_t h32(uint64_t seed, int bh, int L, int t, int
   return static_cast<uint32_t>(mix64(seed + (ctr + 1) * 0x9E3779B97F4A7C15ull) >> 32);
 }
 
+// Optional candidate mask of outer-loop routing: bit c of row (bh, chunk of the query).
+__device__ __forceinline__ const uint32_t* cmask_row(const RouteParams& p, int bh, int cq) {
+  return p.cmask ? p.cmask + (static_cast<size_t>(bh) * p.C + cq) * p.cmask_w : nullptr;
+}
+__device__ __forceinline__ bool cmask_ok(const uint32_t* row, int c) {
+  return !row || ((row[c >> 5] >> (c & 31)) & 1u);
+}
+
 // Final selection of one query: T = the first min(k_eff, n_allowed) entries of the sorted
 // top list (bs descending, ties by lower chunk id), drop-off / drop-in, ascending write-out.
 template <int KMAX, bool NOISE>
@@ -124,8 +132,10 @@ __device__ __forceinline__ void finish_query(const float (&bs)[KMAX], const int 
           const uint32_t ones = hi - lo == 32 ? 0xffffffffu : ((1u << (hi - lo)) - 1u);
           return ones << lo;
         };
+        const uint32_t* crow = cmask_row(p, bh, cq);
         auto pool_word = [&](int w, int npicked) -> uint32_t {
           uint32_t bits = range_bits(0, lim, w) & ~range_bits(x0, x1, w) & ~range_bits(s0, s1, w);
+          if (crow) bits &= crow[w];
 #pragma unroll
           for (int i = 0; i < KMAX; ++i)
             if (orig[i] != 0x7fffffff && (orig[i] >> 5) == w) bits &= ~(1u << (orig[i] & 31));
@@ -193,6 +203,7 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ Q,
   const int tq = live ? t : L - 1;
   const int cq = chunk_of(s_off, C, tq);
   const int sq = s_shot[cq];
+  const uint32_t* crow = cmask_row(p, bh, cq);
   // highest chunk any thread of this block may need
   int c_end = C;
   if (p.causal) {
@@ -230,7 +241,7 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ Q,
     for (int cc = 0; cc < ncb; ++cc) {
       const int c = cb0 + cc;
       const int sc = s_shot[c];
-      const bool ok = live && sc >= 0 && sc != sq && (!p.causal || c < cq);
+      const bool ok = live && sc >= 0 && sc != sq && (!p.causal || c < cq) && cmask_ok(crow, c);
       if (!__builtin_amdgcn_ballot_w64(ok)) continue;
       const f32x4* kr = reinterpret_cast<const f32x4*>(kb + cc * D);
       float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
@@ -345,6 +356,7 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const bf16_t* __restric
     if (s_shot[c] < 0) { x0 = c; break; }
   for (int c = x0; c < C && s_shot[c] < 0; ++c) x1 = c + 1;
   const int lim = live ? (p.causal ? s0 : C) : 0;
+  const uint32_t* crow = cmask_row(p, bh, cq);
 
   float bs[KMAX];
   int bc[KMAX];
@@ -382,7 +394,8 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const bf16_t* __restric
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int c = cb0 + b32 + 8 * (i >> 2) + 4 * g + (i & 3);
-        const bool ok = c < cend && (c < x0 || c >= x1) && (c < s0 || c >= s1);
+        const bool ok = c < cend && (c < x0 || c >= x1) && (c < s0 || c >= s1) &&
+                        cmask_ok(crow, c);
         n_allowed += ok ? 1 : 0;
         if (!(ok && acc[i] > bs[KMAX - 1])) continue;  // cannot enter the top list
         float cs = acc[i];
@@ -517,9 +530,11 @@ __global__ __launch_bounds__(64 * NW) void route_mfma_persist_kernel(
     };
     uint32_t okw[kRouteCB / 32];
     int n_all = 0;
+    const uint32_t* crow = cmask_row(p, bh, cq);
 #pragma unroll
     for (int w = 0; w < kRouteCB / 32; ++w) {
       okw[w] = range_bits(0, lim, w) & ~range_bits(x0, x1, w) & ~range_bits(s0, s1, w);
+      if (crow) okw[w] &= w < p.cmask_w ? crow[w] : 0u;
       n_all += popc(okw[w]);
     }
 

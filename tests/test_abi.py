@@ -168,3 +168,36 @@ def test_python_layout_validation():
         validate_layout(np.array([0, 3, 6, 9]), np.array([0, 1, 0]), 0, 0)
     with pytest.raises(ValueError):
         validate_layout(np.array([0, 3, 6]), np.array([-1, 0]), 0, 2)
+
+
+@pytest.mark.parametrize("nseg,M,causal,status", [
+    (0, 1, 1, 2),          # no segment
+    (300, 1, 1, 2),        # beyond MOC_MAX_SEG (and C)
+    (5, -1, 1, 1),         # negative M
+    (5, 1, 2, 1),          # bad causal flag
+    (17, 17, 1, 2),        # min(M, nseg) beyond MOC_MAX_TOPM
+])
+def test_route_outer_validation(L, nseg, M, causal, status):
+    lib = L.load()
+    lay = _layout(L)
+    p = ctypes.c_void_p
+    r = lib.moc_route_outer(ctypes.byref(lay), p(1), nseg, M, causal, p(2), p(3), p(4), p(5),
+                            p(6), p(7), 1 << 30, None)
+    assert r == status, lib.moc_last_error()
+
+
+def test_route_outer_and_masked_reject_null_and_small_workspace(L):
+    lib = L.load()
+    lay = _layout(L)
+    p = ctypes.c_void_p
+    need = lib.moc_workspace_bytes(ctypes.byref(lay), ctypes.byref(_cfg(L)), L.MOC_OP_OUTER)
+    assert need > 0
+    assert lib.moc_route_outer(ctypes.byref(lay), None, 5, 1, 1, p(2), p(3), p(4), p(5), p(6),
+                               p(7), need, None) == 1
+    assert lib.moc_route_outer(ctypes.byref(lay), p(1), 5, 1, 1, p(2), p(3), p(4), p(5), p(6),
+                               p(7), need - 1, None) == 4
+    cfg = _cfg(L)
+    assert lib.moc_route_masked(ctypes.byref(lay), ctypes.byref(cfg), p(1), p(2), None, p(3),
+                                p(4), None, 0, None) == 1
+    assert lib.moc_route_masked(ctypes.byref(lay), ctypes.byref(_cfg(L, top_k=-1)), p(1), p(2),
+                                p(9), p(3), p(4), None, 0, None) == 1
