@@ -34,7 +34,7 @@ def parse(argv=None):
     ap.add_argument("--workload", default="headline",
                     choices=["headline", "mid", "short", "tiny", "train", "headline_uniform",
                              "single_shot_c64", "single_shot_c128", "single_shot_c256",
-                             "single_shot_c512", "single_shot_c1024"])
+                             "single_shot_c512", "single_shot_c1024", "headline_outer"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=192,
@@ -103,7 +103,11 @@ def cpu_baseline(w, Q, K, V, rows_n: int):
     kb = mo.pool_keys(K[:, :hs], w.layout)
     t_pool = time.perf_counter() - t0
     t0 = time.perf_counter()
-    r = mo.route(Q[:, :hs], kb, w.layout, w.top_k, w.causal)
+    cmask = None
+    if w.segments is not None:
+        cmask = mo.route_outer(Q[:, :hs], K[:, :hs], w.layout, w.segments, w.outer_M,
+                               w.causal).cand_mask
+    r = mo.route(Q[:, :hs], kb, w.layout, w.top_k, w.causal, cand_mask=cmask)
     t_route = time.perf_counter() - t0
     rng = np.random.default_rng(w.seed)
     ts = sorted(rng.choice(w.L, size=min(rows_n, w.L), replace=False).tolist())
@@ -220,24 +224,34 @@ def main(argv=None) -> int:
     fwd_ws = torch.empty(moc.workspace_bytes(lay, w.B, w.H, w.d, Qd.dtype, cfg, 2),
                          dtype=torch.uint8, device=dev)
 
-    names = ["pool", "route", "varlen", "attend_fwd"] + (["attend_bwd"] if with_bwd else [])
+    outer = w.segments is not None
+    names = (["pool"] + (["route_outer"] if outer else []) + ["route", "varlen", "attend_fwd"]
+             + (["attend_bwd"] if with_bwd else []))
 
     def step(ev=None):
-        def mark(i):
+        i = 0
+
+        def mark():
+            nonlocal i
             if ev is not None:
                 ev[i].record()
-        mark(0)
+            i += 1
+        mark()
         kbar = moc.pool_keys(Kd, lay)
-        mark(1)
-        sel, nsel = moc.route(Qd, kbar, lay, cfg)
-        mark(2)
+        mark()
+        cand_mask = None
+        if outer:
+            cand_mask = moc.route_outer(Qd, Kd, lay, w.segments, w.outer_M, w.causal).cand_mask
+            mark()
+        sel, nsel = moc.route(Qd, kbar, lay, cfg, cand_mask=cand_mask)
+        mark()
         vl = moc.build_varlen(sel, nsel, lay, cfg, w.d, Qd.dtype)
-        mark(3)
+        mark()
         O, lse = moc.attend_fwd(Qd, Kd, Vd, lay, vl, ws=fwd_ws)
-        mark(4)
+        mark()
         if with_bwd:
             moc.attend_bwd(Qd, Kd, Vd, O, lse, dOd, lay, vl)
-            mark(5)
+            mark()
         return vl
 
     for _ in range(a.warmup):
@@ -284,7 +298,9 @@ def main(argv=None) -> int:
         "data": "synthetic (seeded normal Q/V, chunk-clustered K; no trained activations)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "C": w.C,
                    "top_k": w.top_k, "causal": w.causal, "p_max": w.p_max, "lambda": w.lam,
-                   "seed": w.seed, "layout": w.description},
+                   "seed": w.seed, "layout": w.description,
+                   **({"outer_segments": len(w.segments) - 1, "outer_M": w.outer_M}
+                      if w.segments is not None else {})},
         "layer_ms": ms,
         "stages_ms": stage,
         "pairs": pairs,

@@ -20,7 +20,7 @@ round-to-nearest-even (torch CPU ``.to(torch.bfloat16)``) when the workload is b
 from __future__ import annotations
 
 from dataclasses import dataclass, field, replace
-from typing import List, Optional, Sequence
+from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -67,6 +67,8 @@ class Workload:
     max_drop_in: int = 8
     seed: int = 0
     description: str = ""
+    segments: Optional[Tuple[int, ...]] = None  # outer-loop routing: segment chunk offsets
+    outer_M: int = 0
 
     @property
     def L(self) -> int:
@@ -274,9 +276,26 @@ def dense(seed: int = 0, n_shots: int = 8, frames_per_shot: int = 14, **kw) -> W
     return replace(w, **kw)
 
 
+def shot_segments(layout: Layout) -> Tuple[int, ...]:
+    """Segment chunk offsets with one segment per shot (the text chunks form one segment)."""
+    shot = list(layout.chunk_shot)
+    cuts = [0] + [c for c in range(1, len(shot)) if shot[c] != shot[c - 1]] + [len(shot)]
+    return tuple(cuts)
+
+
+def headline_outer(seed: int = 0, **kw) -> Workload:
+    """Headline layout with outer-loop context routing: one segment per shot (and the text),
+    each query segment picks its top-2 earlier shots, and inner top-2 routing runs only within
+    the query's own shot segment and those two."""
+    w = headline(seed)
+    w = replace(w, name="headline_outer", segments=shot_segments(w.layout), outer_M=2,
+                description=w.description + "; outer routing over shots, M=2")
+    return replace(w, **kw)
+
+
 WORKLOADS = {"tiny": tiny, "mid": mid, "headline": headline, "short": short, "train": train,
              "slice": grad_slice, "headline_uniform": headline_uniform,
-             "single_shot": single_shot}
+             "single_shot": single_shot, "headline_outer": headline_outer}
 for _c in (64, 128, 256, 512, 1024):
     WORKLOADS[f"single_shot_c{_c}"] = (lambda c: lambda seed=0, **kw: single_shot(seed, c, **kw))(_c)
 

@@ -8,8 +8,9 @@
 // Segments are given groups of whole chunks (seg_chunk[nseg+1]); a query's block is its own
 // segment. The pass, without host synchronisation:
 //   (a) segment token offsets and kinds (text / video) from the layout;
-//   (b) qseg / kseg: the segment means of Q and of K, by the chunk pooling kernel run on the
-//       segment layout (exact sum, one binary64 division, RN to binary32);
+//   (b) qseg / kseg: the segment means of Q and of K: the chunk pooling kernel's double-double
+//       chunk sums, merged per segment in chunk order, one binary64 division, RN to binary32
+//       (the pooling rule of the chunk means, applied to the segment's tokens);
 //   (c) per (b, h, query segment) one wave scores the candidate segments (video, not itself,
 //       earlier when causal; binary32 dot products summed in a fixed tree order) and keeps the
 //       top min(M, #candidates), an exact tie keeping the lower segment id;
@@ -29,6 +30,30 @@ __global__ __launch_bounds__(256) void outer_seg_kernel(const int32_t* __restric
     seg_tok[s] = chunk_offsets[seg_chunk[s]];
     if (s < nseg) seg_text[s] = chunk_shot[seg_chunk[s]] < 0 ? 1 : 0;
   }
+}
+
+// Segment means from the double-double chunk sums part [B*H][C][D][2]: one workgroup per
+// (segment, b*h), one thread per dim, the segment's chunks merged in ascending order.
+template <int D>
+__global__ __launch_bounds__(D) void outer_seg_mean_kernel(const double* __restrict__ part,
+                                                           const int32_t* __restrict__ seg_chunk,
+                                                           const int32_t* __restrict__ seg_tok,
+                                                           int C, int nseg,
+                                                           float* __restrict__ feat) {
+  const int sg = blockIdx.x, bh = blockIdx.y, j = threadIdx.x;
+  double h = 0.0, l = 0.0;
+  for (int c = seg_chunk[sg]; c < seg_chunk[sg + 1]; ++c) {
+    const double* pc = part + ((static_cast<size_t>(bh) * C + c) * D + j) * 2;
+    const double bhi = pc[0], blo = pc[1];
+    // double-double merge (TwoSum of the high parts, low parts added)
+    const double s = h + bhi;
+    const double bp = s - h;
+    const double e = (h - (s - bp)) + (bhi - bp);
+    l = l + blo + e;
+    h = s;
+  }
+  const double n = static_cast<double>(seg_tok[sg + 1] - seg_tok[sg]);
+  feat[(static_cast<size_t>(bh) * nseg + sg) * D + j] = static_cast<float>((h + l) / n);
 }
 
 // One wave per (query segment, b*h). Lane l holds dims l, l + 64, ... of the query feature.
@@ -130,19 +155,21 @@ __global__ __launch_bounds__(64) void outer_mask_kernel(const int32_t* __restric
 
 namespace moc_host {
 
-hipError_t launch_pool(const moc_layout* lay, const void* K, float* kbar, hipStream_t st);
+hipError_t launch_pool_partial(const moc_layout* lay, const void* X, double* part,
+                               hipStream_t st);
 
 namespace {
 size_t al(size_t x) { return (x + 255) / 256 * 256; }
 struct OuterSizes {
-  size_t tok, text, feat;
-  size_t total() const { return tok + text + 2 * feat; }
+  size_t tok, text, feat, part;
+  size_t total() const { return tok + text + 2 * feat + part; }
 };
 OuterSizes outer_sizes(const moc_layout* lay) {
   OuterSizes z;
   z.tok = al(sizeof(int32_t) * (MOC_MAX_SEG + 1));
   z.text = al(sizeof(int32_t) * MOC_MAX_SEG);
   z.feat = al(sizeof(float) * static_cast<size_t>(lay->B) * lay->H * MOC_MAX_SEG * lay->d);
+  z.part = al(sizeof(double) * 2 * static_cast<size_t>(lay->B) * lay->H * lay->C * lay->d);
   return z;
 }
 }  // namespace
@@ -158,18 +185,24 @@ hipError_t launch_route_outer(const moc_layout* lay, const int32_t* seg_chunk, i
   int32_t* seg_text = reinterpret_cast<int32_t*>(w); w += z.text;
   float* qseg = reinterpret_cast<float*>(w); w += z.feat;
   float* kseg = reinterpret_cast<float*>(w); w += z.feat;
+  double* part = reinterpret_cast<double*>(w); w += z.part;
   hipLaunchKernelGGL(moc::outer_seg_kernel, dim3(1), dim3(256), 0, st, lay->chunk_offsets,
                      lay->chunk_shot, seg_chunk, nseg, seg_tok, seg_text);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // the segment layout: its chunks are the segments (the pooling reads only the offsets)
-  moc_layout sl = *lay;
-  sl.C = nseg;
-  sl.chunk_offsets = seg_tok;
-  sl.chunk_shot = seg_text;
-  if ((e = launch_pool(&sl, Q, qseg, st)) != hipSuccess) return e;
-  if ((e = launch_pool(&sl, K, kseg, st)) != hipSuccess) return e;
   const int BH = lay->B * lay->H;
+  // chunk sums in parallel over all chunks, then one merge per segment (Q, then K)
+  for (int pass = 0; pass < 2; ++pass) {
+    if ((e = launch_pool_partial(lay, pass == 0 ? Q : K, part, st)) != hipSuccess) return e;
+    float* feat = pass == 0 ? qseg : kseg;
+    if (lay->d == 128)
+      hipLaunchKernelGGL((moc::outer_seg_mean_kernel<128>), dim3(nseg, BH), dim3(128), 0, st,
+                         part, seg_chunk, seg_tok, lay->C, nseg, feat);
+    else
+      hipLaunchKernelGGL((moc::outer_seg_mean_kernel<64>), dim3(nseg, BH), dim3(64), 0, st,
+                         part, seg_chunk, seg_tok, lay->C, nseg, feat);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const int Ms = M < nseg ? M : nseg;
   if (lay->d == 128)
     hipLaunchKernelGGL((moc::outer_route_kernel<128>), dim3(nseg, BH), dim3(64), 0, st, qseg,

@@ -32,10 +32,13 @@ __device__ __forceinline__ void dd_merge(double& hi, double& lo, double bhi, dou
   hi = s;
 }
 
-template <typename T, int D>
+// PARTIAL: instead of the mean, write the chunk's double-double sum (hi, lo) to part
+// [B*H][C][D][2], for sums over groups of chunks (outer-loop routing's segment features).
+template <typename T, int D, bool PARTIAL = false>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ K,
                                                    const int32_t* __restrict__ off,
-                                                   float* __restrict__ kbar, int L, int C) {
+                                                   float* __restrict__ kbar, int L, int C,
+                                                   double* __restrict__ part = nullptr) {
   constexpr int VEC = 16 / sizeof(T);
   constexpr int TPR = D / VEC;     // threads per row
   constexpr int RPI = 256 / TPR;   // rows per pass
@@ -83,6 +86,12 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ K,
   for (int j = threadIdx.x; j < D; j += blockDim.x) {
     double h = 0.0, l = 0.0;
     for (int k = 0; k < RPI; ++k) dd_merge(h, l, sh[0][k][j], sh[1][k][j]);
+    if constexpr (PARTIAL) {
+      double* o = part + ((static_cast<size_t>(bh) * C + c) * D + j) * 2;
+      o[0] = h;
+      o[1] = l;
+      continue;
+    }
     // renormalise, then the binary64 sum is the rounded value of h + l
     double s = h + l;
     double mean = s / static_cast<double>(n);
@@ -101,6 +110,27 @@ static hipError_t launch_pool_t(const moc_layout* lay, const void* K, float* kba
   hipLaunchKernelGGL((moc::pool_kernel<T, D>), grid, dim3(256), 0, st,
                      static_cast<const T*>(K), lay->chunk_offsets, kbar, lay->L, lay->C);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_pool_partial_t(const moc_layout* lay, const void* X, double* part,
+                                        hipStream_t st) {
+  dim3 grid(lay->C, lay->B * lay->H);
+  hipLaunchKernelGGL((moc::pool_kernel<T, D, true>), grid, dim3(256), 0, st,
+                     static_cast<const T*>(X), lay->chunk_offsets, nullptr, lay->L, lay->C,
+                     part);
+  return hipGetLastError();
+}
+
+// Double-double chunk sums [B*H][C][d][2] of X (outer-loop routing's segment features).
+hipError_t launch_pool_partial(const moc_layout* lay, const void* X, double* part,
+                               hipStream_t st) {
+  if (lay->dtype == MOC_BF16) {
+    return lay->d == 128 ? launch_pool_partial_t<moc::bf16_t, 128>(lay, X, part, st)
+                         : launch_pool_partial_t<moc::bf16_t, 64>(lay, X, part, st);
+  }
+  return lay->d == 128 ? launch_pool_partial_t<float, 128>(lay, X, part, st)
+                       : launch_pool_partial_t<float, 64>(lay, X, part, st);
 }
 
 hipError_t launch_pool(const moc_layout* lay, const void* K, float* kbar, hipStream_t st) {
