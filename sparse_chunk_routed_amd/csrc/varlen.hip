@@ -123,6 +123,11 @@ __global__ __launch_bounds__(1024) void inv_global_kernel(
   __shared__ int64_t s_anchor;
   __shared__ int32_t off[MOC_MAX_C + 1];
   __shared__ int32_t shot[MOC_MAX_C];
+  // tile emission tables: anchor groups (text, shots) and per-chunk key tile starts
+  __shared__ int32_t g_q0[MOC_MAX_C + 1], g_q1[MOC_MAX_C + 1], g_base[MOC_MAX_C + 1];
+  __shared__ int32_t g_text[MOC_MAX_C + 1];
+  __shared__ int32_t k_base[MOC_MAX_C], k_q0[MOC_MAX_C], k_q1[MOC_MAX_C];
+  __shared__ int32_t s_ng, s_nsp, s_ntxt_k;
   // the serial tile emission below walks the layout: keep it in LDS, not in global memory
   for (int i = threadIdx.x; i <= p.C; i += blockDim.x) off[i] = off_g[i];
   for (int i = threadIdx.x; i < p.C; i += blockDim.x) shot[i] = shot_g[i];
@@ -148,67 +153,83 @@ __global__ __launch_bounds__(1024) void inv_global_kernel(
     }
   }
   if (threadIdx.x == 0) n_rtiles[0] = static_cast<int32_t>(ntile);
-  // anchor tiles (shared by all (b,h)) and the anchor pair total
+  // Anchor tiles (shared by all (b,h)) and backward key tiles. Thread 0 lays out where each
+  // group's tiles start (the text, then every shot; the text keys, then every video chunk);
+  // all threads then write the tiles, in the same order a serial walk would.
+  const int tb = p.text_begin, te = p.text_end;
+  const int nt_txt = te - tb;
+  const int KR = p.key_rows;
   if (threadIdx.x == 0) {
-    const int tb = p.text_begin, te = p.text_end;
-    const int nt_txt = te - tb;
-    int n = 0;
+    int ng = 0, n = 0;
     int64_t anchor = 0;
     if (nt_txt > 0) {
-      for (int q = tb; q < te; q += BM) {
-        int32_t* a = atiles + 6 * n++;
-        a[0] = q; a[1] = q + BM < te ? q + BM : te;
-        a[2] = tb; a[3] = te; a[4] = 0; a[5] = 0;
-      }
+      g_q0[ng] = tb; g_q1[ng] = te; g_base[ng] = n; g_text[ng] = 1; ++ng;
+      n += (nt_txt + BM - 1) / BM;
       anchor += static_cast<int64_t>(nt_txt) * nt_txt;
     }
     int c = 0;
     while (c < p.C) {
-      const int s = shot[c];
-      if (s < 0) { ++c; continue; }
+      const int sh = shot[c];
+      if (sh < 0) { k_q0[c] = 0; k_q1[c] = 0; ++c; continue; }
       const int c0 = c;
-      while (c < p.C && shot[c] == s) ++c;
+      while (c < p.C && shot[c] == sh) ++c;
       const int q0 = off[c0], q1 = off[c];
-      for (int q = q0; q < q1; q += BM) {
-        int32_t* a = atiles + 6 * n++;
-        a[0] = q; a[1] = q + BM < q1 ? q + BM : q1;
-        a[2] = tb; a[3] = te; a[4] = q0; a[5] = q1;
-      }
+      for (int cc = c0; cc < c; ++cc) { k_q0[cc] = q0; k_q1[cc] = q1; }
+      g_q0[ng] = q0; g_q1[ng] = q1; g_base[ng] = n; g_text[ng] = 0; ++ng;
+      n += (q1 - q0 + BM - 1) / BM;
       anchor += static_cast<int64_t>(q1 - q0) * (nt_txt + (q1 - q0));
     }
+    s_ng = ng;
     n_atiles[0] = n;
     s_anchor = anchor;
-    // backward key tiles: text keys x query splits, then every video chunk's keys with its
-    // shot as the anchor query range (a tile never straddles a chunk)
-    const int KR = p.key_rows;
-    int nk = 0;
+    // text key tiles: key blocks x the query splits that are not empty (a prefix of them)
+    int nk = 0, nsp = 0;
     if (nt_txt > 0) {
       const int qs = (p.L + p.n_text_split - 1) / p.n_text_split;
-      for (int k0 = tb; k0 < te; k0 += KR)
-        for (int sp = 0; sp < p.n_text_split; ++sp) {
-          const int qa = sp * qs;
-          const int qb = qa + qs < p.L ? qa + qs : p.L;
-          if (qa >= qb) continue;
-          int32_t* a = ktiles + 6 * nk++;
-          a[0] = k0; a[1] = k0 + KR < te ? k0 + KR : te;
-          a[2] = -1; a[3] = qa; a[4] = qb; a[5] = sp;
-        }
+      while (nsp < p.n_text_split && nsp * qs < p.L) ++nsp;
+      nk = ((nt_txt + KR - 1) / KR) * nsp;
     }
-    c = 0;
-    while (c < p.C) {
-      const int s = shot[c];
-      if (s < 0) { ++c; continue; }
-      const int c0 = c;
-      while (c < p.C && shot[c] == s) ++c;
-      const int q0 = off[c0], q1 = off[c];
-      for (int cc = c0; cc < c; ++cc)
-        for (int k0 = off[cc]; k0 < off[cc + 1]; k0 += KR) {
-          int32_t* a = ktiles + 6 * nk++;
-          a[0] = k0; a[1] = k0 + KR < off[cc + 1] ? k0 + KR : off[cc + 1];
-          a[2] = cc; a[3] = q0; a[4] = q1; a[5] = -1;
-        }
+    s_nsp = nsp;
+    s_ntxt_k = nk;
+    for (int cc = 0; cc < p.C; ++cc) {
+      k_base[cc] = nk;
+      if (shot[cc] >= 0) nk += (off[cc + 1] - off[cc] + KR - 1) / KR;
     }
     n_ktiles[0] = nk;
+  }
+  __syncthreads();
+  for (int gi = 0; gi < s_ng; ++gi) {
+    const int q0 = g_q0[gi], q1 = g_q1[gi];
+    const int nt = (q1 - q0 + BM - 1) / BM;
+    for (int k = threadIdx.x; k < nt; k += blockDim.x) {
+      const int q = q0 + k * BM;
+      int32_t* a = atiles + 6 * (g_base[gi] + k);
+      a[0] = q; a[1] = q + BM < q1 ? q + BM : q1;
+      a[2] = tb; a[3] = te;
+      a[4] = g_text[gi] ? 0 : q0; a[5] = g_text[gi] ? 0 : q1;
+    }
+  }
+  if (nt_txt > 0) {
+    const int qs = (p.L + p.n_text_split - 1) / p.n_text_split;
+    for (int i = threadIdx.x; i < s_ntxt_k; i += blockDim.x) {
+      const int k0 = tb + (i / s_nsp) * KR, sp = i % s_nsp;
+      const int qa = sp * qs;
+      const int qb = qa + qs < p.L ? qa + qs : p.L;
+      int32_t* a = ktiles + 6 * i;
+      a[0] = k0; a[1] = k0 + KR < te ? k0 + KR : te;
+      a[2] = -1; a[3] = qa; a[4] = qb; a[5] = sp;
+    }
+  }
+  for (int cc = 0; cc < p.C; ++cc) {
+    if (shot[cc] < 0) continue;
+    const int a0 = off[cc], a1 = off[cc + 1];
+    const int nt = (a1 - a0 + KR - 1) / KR;
+    for (int k = threadIdx.x; k < nt; k += blockDim.x) {
+      const int k0 = a0 + k * KR;
+      int32_t* a = ktiles + 6 * (k_base[cc] + k);
+      a[0] = k0; a[1] = k0 + KR < a1 ? k0 + KR : a1;
+      a[2] = cc; a[3] = k_q0[cc]; a[4] = k_q1[cc]; a[5] = -1;
+    }
   }
   __syncthreads();
   // pair counts: anchor pairs + routed chunk sizes
