@@ -225,6 +225,7 @@ def main(argv=None) -> int:
                          dtype=torch.uint8, device=dev)
 
     outer = w.segments is not None
+    segs = moc.DeviceSegments(w.segments, lay) if outer else None
     names = (["pool"] + (["route_outer"] if outer else []) + ["route", "varlen", "attend_fwd"]
              + (["attend_bwd"] if with_bwd else []))
 
@@ -241,7 +242,7 @@ def main(argv=None) -> int:
         mark()
         cand_mask = None
         if outer:
-            cand_mask = moc.route_outer(Qd, Kd, lay, w.segments, w.outer_M, w.causal).cand_mask
+            cand_mask = moc.route_outer(Qd, Kd, lay, segs, w.outer_M, w.causal).cand_mask
             mark()
         sel, nsel = moc.route(Qd, kbar, lay, cfg, cand_mask=cand_mask)
         mark()

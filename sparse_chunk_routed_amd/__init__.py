@@ -6,12 +6,12 @@ tensors. Importing it fails if libmoc.so has not been built.
 """
 from . import _lib
 from ._lib import MocError, load
-from .api import (DeviceLayout, ForwardResult, MoCAttention, OuterRouting, RouteCfg, Varlen,
-                  attend_bwd, attend_fwd, build_varlen, forward, pool_keys, route, route_outer,
+from .api import (DeviceLayout, DeviceSegments, ForwardResult, MoCAttention, OuterRouting,
+                  RouteCfg, Varlen, attend_bwd, attend_fwd, build_varlen, forward, pool_keys, route, route_outer,
                   sel_width, validate_layout, workspace_bytes)
 
 load()
 
-__all__ = ["DeviceLayout", "ForwardResult", "MoCAttention", "MocError", "OuterRouting",
-           "RouteCfg", "Varlen", "attend_bwd", "attend_fwd", "build_varlen", "forward",
+__all__ = ["DeviceLayout", "DeviceSegments", "ForwardResult", "MoCAttention", "MocError",
+           "OuterRouting", "RouteCfg", "Varlen", "attend_bwd", "attend_fwd", "build_varlen", "forward",
            "pool_keys", "route", "route_outer", "sel_width", "validate_layout", "workspace_bytes"]

@@ -184,19 +184,41 @@ class OuterRouting:
     cand_mask: torch.Tensor  # int32 view of uint32 [B,H,C,ceil(C/32)]
 
 
+class DeviceSegments:
+    """Outer-routing segments resident on the device: chunk offsets [nseg+1] of groups of whole
+    chunks. The content is validated here on the host copy against the layout (start at 0,
+    increase strictly, end at C, no segment mixing text and video chunks), since the library
+    treats it as a precondition; building one per layout keeps the routing call free of host
+    copies and synchronisation."""
+
+    def __init__(self, seg_chunk: Sequence[int], lay: DeviceLayout):
+        h = [int(x) for x in np.asarray(seg_chunk, dtype=np.int64).ravel()]
+        nseg = len(h) - 1
+        if nseg < 1 or h[0] != 0 or h[-1] != lay.C or any(b <= a for a, b in zip(h, h[1:])):
+            raise ValueError("seg_chunk must start at 0, increase strictly and end at C")
+        if nseg > L.MOC_MAX_SEG:
+            raise ValueError(f"at most {L.MOC_MAX_SEG} segments")
+        for a, b in zip(h, h[1:]):
+            kinds = {int(x) < 0 for x in lay.shot_host[a:b]}
+            if len(kinds) != 1:
+                raise ValueError(f"segment of chunks [{a}, {b}) mixes text and video chunks")
+        self.host = h
+        self.nseg = nseg
+        self.C = lay.C
+        self.dev = torch.tensor(h, dtype=torch.int32, device=lay.offsets.device)
+
+
 def route_outer(Q: torch.Tensor, K: torch.Tensor, lay: DeviceLayout, seg_chunk, M: int,
                 causal: bool, ws: Optional[torch.Tensor] = None) -> OuterRouting:
-    """Outer-loop context routing (moc_route_outer): seg_chunk [nseg+1] are the segments'
-    chunk offsets (host sequence or device int32 tensor)."""
+    """Outer-loop context routing (moc_route_outer): seg_chunk is a DeviceSegments or a host
+    sequence of the segments' chunk offsets [nseg+1] (validated and uploaded per call)."""
     _check_qkv(Q)
     _check_qkv(K)
     B, H, Lq, d = Q.shape
-    seg = torch.as_tensor(seg_chunk, dtype=torch.int32).to(Q.device).contiguous()
-    h_seg = seg.cpu().tolist()
-    nseg = len(h_seg) - 1
-    if nseg < 1 or h_seg[0] != 0 or h_seg[-1] != lay.C or any(
-            b <= a for a, b in zip(h_seg, h_seg[1:])):
-        raise ValueError("seg_chunk must start at 0, increase strictly and end at C")
+    segs = seg_chunk if isinstance(seg_chunk, DeviceSegments) else DeviceSegments(seg_chunk, lay)
+    if segs.C != lay.C or segs.dev.device != Q.device:
+        raise ValueError("segments built for another layout or device")
+    seg, nseg = segs.dev, segs.nseg
     Ms = min(int(M), nseg)
     W = (lay.C + 31) // 32
     seg_sel = torch.empty((B, H, nseg, Ms), dtype=torch.int32, device=Q.device)

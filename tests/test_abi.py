@@ -201,3 +201,15 @@ def test_route_outer_and_masked_reject_null_and_small_workspace(L):
                                 p(4), None, 0, None) == 1
     assert lib.moc_route_masked(ctypes.byref(lay), ctypes.byref(_cfg(L, top_k=-1)), p(1), p(2),
                                 p(9), p(3), p(4), None, 0, None) == 1
+
+
+def test_device_segments_validation():
+    """Segments are checked on the host copy against the layout before any device call."""
+    import moc_inputs as mi
+    import sparse_chunk_routed_amd as moc
+    lay = moc.DeviceLayout.from_layout(mi.build_layout(16, [3, 3, 3, 3], 12), "cpu")
+    s = moc.DeviceSegments([0, 1, 4, 6, 10, 13], lay)
+    assert s.nseg == 5 and s.host == [0, 1, 4, 6, 10, 13]
+    for bad in ([0, 2, 13], [0, 1, 1, 13], [0, 1, 12], [1, 13], [0]):
+        with pytest.raises(ValueError):
+            moc.DeviceSegments(bad, lay)
