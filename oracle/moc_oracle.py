@@ -35,6 +35,10 @@ What is computed (per batch element b and head h; routing is independent per hea
      the top-M segments by the dot product of mean-pooled features; inner routing (3-6) then
      only considers chunks of the query's own segment and of the picked segments. See
      route_outer().
+ 12. Quantised scores ([MoC-S] §5 Conclusion, [MoC-W] 結論, [MoC-D] slide 21 list quantisation
+     among the directions for faster kernels, without fixing a format): Q and K in the OCP
+     microscaling MXFP8 format (e4m3 elements, one power-of-two scale per 32 elements along d),
+     attention (8) over the dequantised values. See mx_quantize().
 """
 from __future__ import annotations
 
@@ -578,6 +582,113 @@ def route_outer(Q, K, layout, seg_chunk, M: int, causal: bool) -> OuterRouting:
                     exempt[b, h, sq] = (a - c) < TIE_REL * max(abs(a), abs(c))
     cmask = allowed_segs[:, :, G.seg_of_chunk][:, :, :, G.seg_of_chunk]  # [B,H,C,C]
     return OuterRouting(seg_sel, seg_nsel, exempt, cmask, qseg, kseg)
+
+
+# ---------------------------------------------------------------------------------------------
+# 12. Quantised scores: MXFP8 Q and K
+# ---------------------------------------------------------------------------------------------
+# Readings. The pages name quantisation only as a direction for faster kernels ([MoC-S] §5;
+# [MoC-W] 結論; [MoC-D] slide 21). This oracle fixes one published format and its plain
+# conversion rule:
+#  * Element format E4M3 of the OCP 8-bit floating point specification (OFP8): sign, 4 exponent
+#    bits with bias 7, 3 mantissa bits; exponent field 0 holds the subnormals m/8 * 2^-6; the
+#    all-ones exponent with mantissa 7 is NaN; no infinities; the largest finite value is 448.
+#  * Shared scale of the OCP Microscaling (MX) specification v1.0: per block of 32 consecutive
+#    elements of a row (along d), X = 2^E with E = floor(log2(max |x|)) - 8 (8 = the largest
+#    exponent of E4M3), stored as the E8M0 code E + 127. Readings where the spec leaves a choice:
+#    E is clamped below at -127 (the smallest E8M0 value), an all-zero block takes E = -127, and
+#    the element x / X is rounded to the nearest E4M3 value with ties to the even code and
+#    saturation at +-448 (|x / X| < 512, so only the top of the range clamps); the sign of a
+#    value that rounds to zero is kept (code 0x80 for negative inputs).
+#  * Attention then runs on the dequantised Q' = codes * X and K' = codes * X in exact
+#    arithmetic (8); V stays in its input precision.
+
+E4M3_MAX = 448.0
+MX_BLOCK = 32
+E4M3_EMAX = 8
+
+
+def e4m3_value(code: int) -> float:
+    """Value of an E4M3 code from its bit fields (NaN for the two NaN codes)."""
+    code = int(code) & 0xFF
+    s, e, m = code >> 7, (code >> 3) & 0xF, code & 7
+    if e == 0xF and m == 7:
+        return math.nan
+    v = math.ldexp(m / 8.0, -6) if e == 0 else math.ldexp(1.0 + m / 8.0, e - 7)
+    return -v if s else v
+
+
+def e4m3_table() -> np.ndarray:
+    """float64 [256]: the value of every code."""
+    return np.array([e4m3_value(c) for c in range(256)])
+
+
+def e4m3_round(v) -> np.ndarray:
+    """Codes (uint8) of finite binary64 values: the nearest E4M3 value to min(|v|, 448), ties to
+    the even code, sign from v (including a negative value that rounds to zero)."""
+    v = np.asarray(v, dtype=np.float64)
+    if not np.all(np.isfinite(v)):
+        raise ValueError("finite inputs only")
+    mag = np.minimum(np.abs(v), E4M3_MAX)
+    pos = e4m3_table()[:127]                       # codes 0..126, strictly increasing
+    hi = np.clip(np.searchsorted(pos, mag, side="left"), 0, 126)   # first value >= mag
+    lo = np.maximum(hi - 1, 0)
+    dlo = mag - pos[lo]
+    dhi = pos[hi] - mag
+    take_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(take_hi, hi, lo).astype(np.uint8)
+    neg = np.signbit(v)
+    return np.where(neg, code | 0x80, code).astype(np.uint8)
+
+
+def mx_scale_exponents(amax) -> np.ndarray:
+    """E of blocks with largest magnitudes amax: floor(log2(amax)) - 8, at least -127; -127 for
+    an all-zero block."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, e = np.frexp(amax)  # amax = f 2^e with f in [0.5, 1): floor(log2 amax) = e - 1
+    E = np.maximum(e.astype(np.int64) - 1 - E4M3_EMAX, -127)
+    return np.where(amax == 0.0, -127, E)
+
+
+def mx_quantize(X) -> Tuple[np.ndarray, np.ndarray]:
+    """MXFP8 of X [..., d] (d a multiple of 32): codes uint8 [..., d] and E8M0 scale codes
+    uint8 [..., d/32]."""
+    X = _as_f64(X)
+    d = X.shape[-1]
+    if d % MX_BLOCK:
+        raise ValueError("d must be a multiple of 32")
+    blocks = X.reshape(-1, MX_BLOCK)
+    E = mx_scale_exponents(np.max(np.abs(blocks), axis=1))
+    codes = e4m3_round(np.ldexp(blocks, -E[:, None]))  # x / 2^E, exact in binary64
+    scales = (E + 127).astype(np.uint8)
+    return codes.reshape(X.shape), scales.reshape(X.shape[:-1] + (d // MX_BLOCK,))
+
+
+def mx_dequantize(codes, scales) -> np.ndarray:
+    """float64 values codes * 2^(scale - 127), blocks of 32 along the last axis."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.int64)
+    vals = e4m3_table()[codes]
+    E = np.repeat(scales - 127, MX_BLOCK, axis=-1)
+    return np.ldexp(vals, E)
+
+
+def attend_mx(Q, K, V, layout, sel, scale: Optional[float] = None,
+              rows: Optional[Sequence[Tuple[int, int, int]]] = None):
+    """Attention (8) with Q and K replaced by their MXFP8 dequantised values (rows are
+    quantised independently, so with `rows` only the heads they touch are quantised)."""
+    if rows is None:
+        return attend(mx_dequantize(*mx_quantize(Q)), mx_dequantize(*mx_quantize(K)), V, layout,
+                      sel, scale=scale)
+    rows = list(rows)
+    Q, K = _as_f64(Q), _as_f64(K)
+    Qd = np.zeros_like(Q)
+    Kd = np.zeros_like(K)
+    for b, h in sorted({(b, h) for b, h, _ in rows}):
+        Kd[b, h] = mx_dequantize(*mx_quantize(K[b, h]))
+    for b, h, t in rows:
+        Qd[b, h, t] = mx_dequantize(*mx_quantize(Q[b, h, t]))
+    return attend(Qd, Kd, V, layout, sel, scale=scale, rows=rows)
 
 
 def _as_f64(x) -> np.ndarray:
