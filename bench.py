@@ -23,6 +23,9 @@ if ROOT not in sys.path:
 
 METRIC = "MoC layer ms + effective TFLOP/s on attended pairs at ~175k tokens, 1 MI355X"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}  # MI355X dense MFMA (bf16), fp32
+# quantised scores: per attended pair 2d FLOPs of S on fp8 (2 x the bf16 rate) and 2d of P.V
+# on bf16, so the time-weighted dense peak of the pair is 4 / (2 / 5033.2 + 2 / 2516.6)
+PEAK_MX_TFLOPS = 4.0 / (2.0 / (2 * 2516.6) + 2.0 / 2516.6)
 PEAK_HBM_GBS = 8000.0
 
 
@@ -34,7 +37,8 @@ def parse(argv=None):
     ap.add_argument("--workload", default="headline",
                     choices=["headline", "mid", "short", "tiny", "train", "headline_uniform",
                              "single_shot_c64", "single_shot_c128", "single_shot_c256",
-                             "single_shot_c512", "single_shot_c1024", "headline_outer"])
+                             "single_shot_c512", "single_shot_c1024", "headline_outer",
+                             "headline_mx"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=192,
@@ -113,7 +117,8 @@ def cpu_baseline(w, Q, K, V, rows_n: int):
     ts = sorted(rng.choice(w.L, size=min(rows_n, w.L), replace=False).tolist())
     rows = [(0, 0, int(t)) for t in ts]
     t0 = time.perf_counter()
-    mo.attend(Q[:, :1], K[:, :1], V[:, :1], w.layout, r.sel[:, :1], rows=rows)
+    att = mo.attend_mx if w.mx_scores else mo.attend
+    att(Q[:, :1], K[:, :1], V[:, :1], w.layout, r.sel[:, :1], rows=rows)
     t_att = time.perf_counter() - t0
     measured = t_pool + t_route + t_att
     full = (t_pool + t_route) * (w.B * w.H / (w.B * hs)) + t_att * (w.B * w.H * w.L / len(rows))
@@ -226,10 +231,14 @@ def main(argv=None) -> int:
 
     outer = w.segments is not None
     segs = moc.DeviceSegments(w.segments, lay) if outer else None
-    names = (["pool"] + (["route_outer"] if outer else []) + ["route", "varlen", "attend_fwd"]
+    mx = w.mx_scores
+    qm = km = None
+    names = (["pool"] + (["route_outer"] if outer else []) + ["route", "varlen"]
+             + (["mx_quantize"] if mx else []) + ["attend_fwd"]
              + (["attend_bwd"] if with_bwd else []))
 
     def step(ev=None):
+        nonlocal qm, km
         i = 0
 
         def mark():
@@ -248,7 +257,13 @@ def main(argv=None) -> int:
         mark()
         vl = moc.build_varlen(sel, nsel, lay, cfg, w.d, Qd.dtype)
         mark()
-        O, lse = moc.attend_fwd(Qd, Kd, Vd, lay, vl, ws=fwd_ws)
+        if mx:
+            qm = moc.mx_quantize(Qd, lay, out=qm)
+            km = moc.mx_quantize(Kd, lay, out=km)
+            mark()
+            O, lse = moc.attend_fwd_mx(qm, km, Vd, lay, vl, ws=fwd_ws)
+        else:
+            O, lse = moc.attend_fwd(Qd, Kd, Vd, lay, vl, ws=fwd_ws)
         mark()
         if with_bwd:
             moc.attend_bwd(Qd, Kd, Vd, O, lse, dOd, lay, vl)
@@ -282,7 +297,7 @@ def main(argv=None) -> int:
     S = moc.sel_width(cfg, w.C)
     pool_bytes = BHLd * s_in + w.B * w.H * w.C * w.d * 4
     route_bytes = BHLd * s_in + w.B * w.H * w.C * w.d * 4 + w.B * w.H * w.L * (S + 1) * 4
-    peak = PEAK_TFLOPS[w.dtype]
+    peak = PEAK_MX_TFLOPS if mx else PEAK_TFLOPS[w.dtype]
     att_tf = fwd_flops / (stage["attend_fwd"] * 1e-3) / 1e12
     out = {
         "metric": METRIC,
@@ -295,13 +310,14 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": "mxfp8 scores + bf16 P.V" if mx else w.dtype,
         "data": "synthetic (seeded normal Q/V, chunk-clustered K; no trained activations)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "C": w.C,
                    "top_k": w.top_k, "causal": w.causal, "p_max": w.p_max, "lambda": w.lam,
                    "seed": w.seed, "layout": w.description,
                    **({"outer_segments": len(w.segments) - 1, "outer_M": w.outer_M}
-                      if w.segments is not None else {})},
+                      if w.segments is not None else {}),
+                   **({"scores": "MXFP8 Q and K (e4m3, 32-element E8M0 blocks)"} if mx else {})},
         "layer_ms": ms,
         "stages_ms": stage,
         "pairs": pairs,
@@ -311,7 +327,9 @@ def main(argv=None) -> int:
         "route_gbs": route_bytes / (stage["route"] * 1e-3) / 1e9,
         "roofline": {
             "bound": "mfma",
-            "kernel": "attention forward (routed + anchor kernels of moc_attend_fwd)",
+            "kernel": ("attention forward with quantised scores (routed + anchor kernels of "
+                       "moc_attend_fwd_mx; peak weighted 2d fp8 + 2d bf16 FLOPs per pair)"
+                       if mx else "attention forward (routed + anchor kernels of moc_attend_fwd)"),
             "achieved": att_tf, "peak": peak, "unit": "TFLOP/s", "frac": att_tf / peak,
             "traffic": recorded_traffic(a.workload if a.seed == 0 else ""),
             "traffic_unit": "HBM bytes per moc_attend_fwd call (rocprofv3 FETCH_SIZE+WRITE_SIZE, "

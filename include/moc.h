@@ -234,6 +234,36 @@ moc_status moc_attend_fwd(const moc_layout *lay, const moc_varlen *vl, const voi
                           void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * MXFP8 quantisation of Q or K for the quantised-scores forward (summary §5 Conclusion,
+ * write-up 結論 and slides, slide 21 name quantisation as a direction for faster kernels and fix
+ * no format). Format: OCP Microscaling MXFP8 - E4M3 elements (OCP OFP8: bias 7, largest finite
+ * 448, no infinities) and, per block of 32 consecutive elements of a row, the E8M0 scale code
+ * E + 127 with E = floor(log2(max |x|)) - 8 clamped below at -127 (-127 for an all-zero
+ * block). Element code: x * 2^-E rounded to the nearest E4M3 value, ties to even, saturated
+ * to +-448; a negative value that rounds to zero is coded 0x80.
+ *   X:      device bf16 [B,H,L,d] (the layout's dtype must be MOC_BF16).
+ *   codes:  device uint8 [B,H,Lp,d], Lp = L rounded up to a multiple of 64; rows >= L zero.
+ *   scales: device uint8 [B,H,Lp,d/32]; rows >= L zero.
+ * Both outputs are fully overwritten. Inputs must be finite.
+ */
+moc_status moc_mx_quantize(const moc_layout *lay, const void *X, uint8_t *codes, uint8_t *scales,
+                           void *stream);
+
+/*
+ * Attention forward with quantised scores: moc_attend_fwd with the scores computed from the
+ * MXFP8 codes and scales of Q and K (as written by moc_mx_quantize) on the block-scaled fp8
+ * matrix cores. The result is the attention of the dequantised Q' = code * 2^E and K' over the
+ * same key sets, with fp32 accumulation; softmax and P.V as in moc_attend_fwd.
+ *   Qc, Kc: device uint8 [B,H,Lp,d]; Qs, Ks: device uint8 [B,H,Lp,d/32].
+ *   V: bf16 [B,H,L,d]; O: bf16 [B,H,L,d]; lse: float [B,H,L]; the layout's dtype must be
+ *   MOC_BF16. ws: MOC_OP_FWD workspace. O and lse must not alias an input.
+ */
+moc_status moc_attend_fwd_mx(const moc_layout *lay, const moc_varlen *vl, const uint8_t *Qc,
+                             const uint8_t *Qs, const uint8_t *Kc, const uint8_t *Ks,
+                             const void *V, float softmax_scale, void *O, float *lse, void *ws,
+                             size_t ws_bytes, void *stream);
+
+/*
  * Attention backward with the routed sets held fixed (summary §3.1 and Appendix A: top-k is
  * not differentiable; gradients reach the selected keys and values only).
  *   Inputs: Q, K, V, O, lse from moc_attend_fwd, dO. Outputs dQ, dK, dV [B,H,L,d] in the

@@ -69,6 +69,7 @@ class Workload:
     description: str = ""
     segments: Optional[Tuple[int, ...]] = None  # outer-loop routing: segment chunk offsets
     outer_M: int = 0
+    mx_scores: bool = False  # quantised scores: Q and K as MXFP8 in the attention
 
     @property
     def L(self) -> int:
@@ -293,9 +294,19 @@ def headline_outer(seed: int = 0, **kw) -> Workload:
     return replace(w, **kw)
 
 
+def headline_mx(seed: int = 0, **kw) -> Workload:
+    """Headline workload with quantised scores: Q and K quantised to MXFP8 for the attention
+    (routing and pooling on the bf16 inputs as before), V and P.V in bf16."""
+    w = headline(seed)
+    w = replace(w, name="headline_mx", mx_scores=True,
+                description=w.description + "; attention scores from MXFP8 Q and K")
+    return replace(w, **kw)
+
+
 WORKLOADS = {"tiny": tiny, "mid": mid, "headline": headline, "short": short, "train": train,
              "slice": grad_slice, "headline_uniform": headline_uniform,
-             "single_shot": single_shot, "headline_outer": headline_outer}
+             "single_shot": single_shot, "headline_outer": headline_outer,
+             "headline_mx": headline_mx}
 for _c in (64, 128, 256, 512, 1024):
     WORKLOADS[f"single_shot_c{_c}"] = (lambda c: lambda seed=0, **kw: single_shot(seed, c, **kw))(_c)
 

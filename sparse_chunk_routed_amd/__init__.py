@@ -6,12 +6,14 @@ tensors. Importing it fails if libmoc.so has not been built.
 """
 from . import _lib
 from ._lib import MocError, load
-from .api import (DeviceLayout, DeviceSegments, ForwardResult, MoCAttention, OuterRouting,
-                  RouteCfg, Varlen, attend_bwd, attend_fwd, build_varlen, forward, pool_keys, route, route_outer,
-                  sel_width, validate_layout, workspace_bytes)
+from .api import (DeviceLayout, DeviceSegments, ForwardResult, MoCAttention, MxTensor,
+                  OuterRouting, RouteCfg, Varlen, attend_bwd, attend_fwd, attend_fwd_mx,
+                  build_varlen, forward, mx_quantize, pool_keys, route, route_outer, sel_width,
+                  validate_layout, workspace_bytes)
 
 load()
 
 __all__ = ["DeviceLayout", "DeviceSegments", "ForwardResult", "MoCAttention", "MocError",
-           "OuterRouting", "RouteCfg", "Varlen", "attend_bwd", "attend_fwd", "build_varlen", "forward",
-           "pool_keys", "route", "route_outer", "sel_width", "validate_layout", "workspace_bytes"]
+           "MxTensor", "OuterRouting", "RouteCfg", "Varlen", "attend_bwd", "attend_fwd",
+           "attend_fwd_mx", "build_varlen", "forward", "mx_quantize", "pool_keys", "route",
+           "route_outer", "sel_width", "validate_layout", "workspace_bytes"]

@@ -19,7 +19,7 @@ MOC_MAX_SEG, MOC_MAX_TOPM = 256, 16
 EXPORTS = (
     "moc_sel_width", "moc_workspace_bytes", "moc_pool_keys", "moc_route", "moc_route_outer",
     "moc_route_masked", "moc_build_varlen", "moc_attend_fwd", "moc_attend_bwd",
-    "moc_poisson_thresholds", "moc_status_string", "moc_last_error",
+    "moc_mx_quantize", "moc_attend_fwd_mx", "moc_poisson_thresholds", "moc_status_string", "moc_last_error",
 )
 
 
@@ -89,6 +89,12 @@ def load() -> ctypes.CDLL:
                                    c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p,
                                    c_void_p, c_void_p, c_size_t, c_void_p]
     lib.moc_attend_bwd.restype = c_int32
+    lib.moc_mx_quantize.argtypes = [P(MocLayout), c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.moc_mx_quantize.restype = c_int32
+    lib.moc_attend_fwd_mx.argtypes = [P(MocLayout), P(MocVarlen), c_void_p, c_void_p, c_void_p,
+                                      c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_void_p,
+                                      c_size_t, c_void_p]
+    lib.moc_attend_fwd_mx.restype = c_int32
     lib.moc_poisson_thresholds.argtypes = [c_float, c_int32, P(c_uint64)]
     lib.moc_poisson_thresholds.restype = c_int32
     lib.moc_status_string.argtypes = [c_int32]

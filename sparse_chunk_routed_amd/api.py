@@ -311,6 +311,55 @@ def attend_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, lay: DeviceLay
     return O, lse
 
 
+@dataclass
+class MxTensor:
+    """MXFP8 rows of a [B,H,L,d] tensor (moc_mx_quantize): codes uint8 [B,H,Lp,d] and E8M0
+    scales uint8 [B,H,Lp,d/32], rows padded to Lp = L rounded up to 64."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    L: int
+
+
+def mx_quantize(X: torch.Tensor, lay: DeviceLayout, out: Optional[MxTensor] = None) -> MxTensor:
+    """MXFP8 quantisation of a bf16 [B,H,L,d] tensor (moc_mx_quantize)."""
+    _check_qkv(X)
+    if X.dtype != torch.bfloat16:
+        raise ValueError("MXFP8 quantisation takes bf16 input")
+    B, H, Lq, d = X.shape
+    Lp = (Lq + 63) // 64 * 64
+    if out is None or out.codes.shape != (B, H, Lp, d):
+        out = MxTensor(torch.empty((B, H, Lp, d), dtype=torch.uint8, device=X.device),
+                       torch.empty((B, H, Lp, d // 32), dtype=torch.uint8, device=X.device), Lq)
+    s = lay.struct(B, H, d, X.dtype)
+    L.check(L.load().moc_mx_quantize(ctypes.byref(s), _ptr(X), _ptr(out.codes), _ptr(out.scales),
+                                     _stream(X.device)))
+    return out
+
+
+def attend_fwd_mx(Qm: MxTensor, Km: MxTensor, V: torch.Tensor, lay: DeviceLayout, vl: Varlen,
+                  scale: Optional[float] = None, ws: Optional[torch.Tensor] = None):
+    """Forward with quantised scores (moc_attend_fwd_mx): (O [B,H,L,d] bf16, lse [B,H,L])."""
+    _check_qkv(V)
+    B, H, Lq, d = V.shape
+    Lp = (Lq + 63) // 64 * 64
+    for m in (Qm, Km):
+        if m.codes.shape != (B, H, Lp, d) or m.scales.shape != (B, H, Lp, d // 32):
+            raise ValueError("MXFP8 operands do not match V's shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    O = torch.empty_like(V)
+    lse = torch.empty((B, H, Lq), dtype=torch.float32, device=V.device)
+    need = workspace_bytes(lay, B, H, d, V.dtype, vl.cfg, L.MOC_OP_FWD)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=V.device)
+    s = lay.struct(B, H, d, V.dtype)
+    L.check(L.load().moc_attend_fwd_mx(ctypes.byref(s), ctypes.byref(vl.struct), _ptr(Qm.codes),
+                                       _ptr(Qm.scales), _ptr(Km.codes), _ptr(Km.scales), _ptr(V),
+                                       float(scale), _ptr(O), _ptr(lse), _ptr(ws), ws.numel(),
+                                       _stream(V.device)))
+    return O, lse
+
+
 def attend_bwd(Q, K, V, O, lse, dO, lay: DeviceLayout, vl: Varlen, scale: Optional[float] = None,
                ws: Optional[torch.Tensor] = None):
     """(dQ, dK, dV) in the input dtype."""

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libmoc.so")
 ARCH = "gfx950"
 
 SOURCES = ["moc_api.hip", "pool.hip", "route.hip", "outer.hip", "varlen.hip", "attn_fwd.hip",
-           "attn_bwd.hip"]
+           "mx.hip", "attn_bwd.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",

@@ -21,6 +21,8 @@
 // half a tile apart so that one group's MFMAs overlap the other group's softmax, with K and
 // V^T tiles copied global -> LDS without registers (attn_fwd_lds.h); the fp32 kernel stages
 // tiles through registers into a double-buffered LDS ring.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "attn_fwd_lds.h"
 
@@ -284,21 +286,25 @@ __global__ __launch_bounds__(kNT) void attn_fwd_kernel(
 // bf16 attention forward: same work decomposition and epilogue as attn_fwd_kernel; two wave
 // groups half a tile apart, K and V^T tiles staged by direct-to-LDS copies into padded
 // 64-key-aligned tiles (three skewed stages) and the permuted key order of attn_fwd_lds.h.
-template <int D, int MODE>
+template <int D, int MODE, bool MX>
 __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ Vt,
-    int Lp, const int32_t* __restrict__ off, AttnParams p, const int32_t* __restrict__ tiles,
+    const void* __restrict__ Qv, const void* __restrict__ Kv, const uint8_t* __restrict__ Qs,
+    const uint8_t* __restrict__ Ks, const bf16_t* __restrict__ Vt, int Lp,
+    const int32_t* __restrict__ off, AttnParams p, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ bucket_off,
     const int32_t* __restrict__ bucket_q, const int32_t* __restrict__ slot,
     float* __restrict__ pO, float* __restrict__ plse, bf16_t* __restrict__ O,
     float* __restrict__ lse) {
   using LT = LdsTiles<D>;
+  using MT = MxTiles<D>;
   static_assert(kNW == 8, "two groups of four waves");
+  constexpr int STAGE = MX ? MT::STAGE : LT::STAGE;
+  constexpr int VOFF = MX ? MT::KBYTES : LT::KBYTES;  // V^T tile within a stage
   // three stage buffers as distinct objects, so that the compiler can tell the LDS written by
   // the in-flight direct-to-LDS copies from the stage being read (no forced wait between them)
-  __shared__ __attribute__((aligned(1024))) char st0[LT::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st1[LT::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st2[LT::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[STAGE];
 
   int bh, q_lo, nq, r1a, r1b, r2a, r2b, bstart = 0;
   if constexpr (MODE == MODE_ANCHOR) {
@@ -338,20 +344,26 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
   }
   // s_waitcnt vmcnt(n) lgkmcnt(0), n = this wave's copies of one stage: all but the newest
   // stage's copies have landed
-  StageCopier<D, kNW> cp;
+  std::conditional_t<MX, MxStageCopier<D, kNW>, StageCopier<D, kNW>> cp;
   cp.init(wv, lane, Lp);
   const int ncopy = cp.count();
   auto wait_but_newest = [&]() __attribute__((always_inline)) {
-    constexpr int NB = LT::KBLK / kNW + LT::VBLK / kNW;
+    constexpr int NB = MX ? MxStageCopier<D, kNW>::NBASE : LT::KBLK / kNW + LT::VBLK / kNW;
     if (ncopy == NB) __builtin_amdgcn_s_waitcnt(0x0070 | NB);
     else if (ncopy == NB + 1) __builtin_amdgcn_s_waitcnt(0x0070 | (NB + 1));
     else __builtin_amdgcn_s_waitcnt(0x0070 | (NB + 2));
   };
   const size_t bh_off = static_cast<size_t>(bh) * p.L * D;
-  const bf16_t* Kbh = K + bh_off;
+  const size_t bhp = static_cast<size_t>(bh) * Lp;  // MX rows are padded to Lp per (b, h)
+  const bf16_t* Kbh = static_cast<const bf16_t*>(Kv) + bh_off;
+  const uint8_t* Kcbh = static_cast<const uint8_t*>(Kv) + bhp * D;
+  const uint8_t* Ksbh = Ks + bhp * MT::NB;
   const bf16_t* Vtbh = Vt + static_cast<size_t>(bh) * D * Lp;
-  QFrag<bf16_t, D> qf;
-  qf.load(Q + bh_off + static_cast<size_t>(tok) * D, g);
+  std::conditional_t<MX, MxQFrag<D>, QFrag<bf16_t, D>> qf;
+  if constexpr (MX)
+    qf.load(static_cast<const uint8_t*>(Qv) + (bhp + tok) * D, Qs + (bhp + tok) * MT::NB, g);
+  else
+    qf.load(static_cast<const bf16_t*>(Qv) + bh_off + static_cast<size_t>(tok) * D, g);
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -379,8 +391,9 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
   const uint32_t lds0 = lds_addr(st0), lds1 = lds_addr(st1), lds2 = lds_addr(st2);
   auto issue = [&](int j, uint32_t lds) __attribute__((always_inline)) {
     if (j > ntot || ntot == 0) return;
-    cp.issue(lds, Kbh, tile_base(j < ntot ? j : ntot - 1), kmax, Vtbh,
-             tile_base(j > 0 ? j - 1 : 0));
+    const int kb = tile_base(j < ntot ? j : ntot - 1), vb = tile_base(j > 0 ? j - 1 : 0);
+    if constexpr (MX) cp.issue(lds, Kcbh, Ksbh, kb, Vtbh, vb);
+    else cp.issue(lds, Kbh, kb, kmax, Vtbh, vb);
   };
 
   // Two wave groups (waves 0-3 and 4-7; wave w and w+4 run on the same SIMD) work on the same
@@ -393,27 +406,38 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
   // j-3, so three LDS buffers give every copy at least three half-steps to land.
   f32x16 s[2];
   bf16x8 pb[4];  // P^T of the previous tile, packed for the four 16-key MFMA steps
-  auto scores = [&](const char* st) __attribute__((always_inline)) { score_tile_swz<D>(st, qf, s, ql, g); };
+  auto scores = [&](const char* st) __attribute__((always_inline)) {
+    if constexpr (MX) score_tile_mx<D>(st, qf, s, ql, g);
+    else score_tile_swz<D>(st, qf, s, ql, g);
+  };
   // steady MFMA half-step: O += V P of tile j-1, then S of tile j, both from stage j
   auto mfma_full = [&](const char* st) __attribute__((always_inline)) {
-    pv_swz_packed<D>(st, pb, acc, ql, g);
+    pv_swz_packed<D, VOFF>(st, pb, acc, ql, g);
     scores(st);
     // operand reads run kReadAhead ahead of the MFMAs that use them (bounded registers)
-    constexpr int NM = 4 * (D / 32) + 2 * (D / 16);
-    __builtin_amdgcn_sched_group_barrier(0x100, kReadAhead, 0);
+    if constexpr (MX) {
+      // P.V: one read per MFMA; S: two code reads per MFMA and two scale reads per tile
+      constexpr int NM = 4 * (D / 32) + 2 * (D / 64);
+      constexpr int NR = 4 * (D / 32) + 4 * (D / 64) + 2;
+      __builtin_amdgcn_sched_group_barrier(0x100, kReadAhead, 0);
+      sched_spread_reads<NR - kReadAhead, NM>();
+    } else {
+      constexpr int NM = 4 * (D / 32) + 2 * (D / 16);
+      __builtin_amdgcn_sched_group_barrier(0x100, kReadAhead, 0);
 #pragma unroll
-    for (int i = 0; i < NM - kReadAhead; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int i = 0; i < NM - kReadAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kReadAhead, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, kReadAhead, 0);
   };
   // last MFMA half-step: O += V P of the last tile, from stage ntot
   auto mfma_last = [&]() __attribute__((always_inline)) {
     const int r = ntot % 3;
-    if (r == 0) pv_swz_packed<D>(st0, pb, acc, ql, g);
-    else if (r == 1) pv_swz_packed<D>(st1, pb, acc, ql, g);
-    else pv_swz_packed<D>(st2, pb, acc, ql, g);
+    if (r == 0) pv_swz_packed<D, VOFF>(st0, pb, acc, ql, g);
+    else if (r == 1) pv_swz_packed<D, VOFF>(st1, pb, acc, ql, g);
+    else pv_swz_packed<D, VOFF>(st2, pb, acc, ql, g);
   };
   auto valu_half = [&](int j) __attribute__((always_inline)) {
     int base, lo, hi;
@@ -642,10 +666,12 @@ static hipError_t launch_fwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   return hipGetLastError();
 }
 
+// bf16 forward; with Qs/Ks non-null, Q and K are MXFP8 codes (rows padded to Lp) and scales
 template <int D>
 static hipError_t launch_fwd_bf16(const moc_layout* lay, const moc_varlen* vl, const void* Q,
-                                  const void* K, const void* V, float scale, void* O, float* lse,
-                                  float* pO, float* plse, void* vt_ws, hipStream_t st) {
+                                  const void* K, const uint8_t* Qs, const uint8_t* Ks,
+                                  const void* V, float scale, void* O, float* lse, float* pO,
+                                  float* plse, void* vt_ws, hipStream_t st) {
   using moc::bf16_t;
   AttnParams p;
   p.B = lay->B; p.H = lay->H; p.L = lay->L; p.C = lay->C; p.S = vl->S;
@@ -654,21 +680,33 @@ static hipError_t launch_fwd_bf16(const moc_layout* lay, const moc_varlen* vl, c
   bf16_t* Vt = static_cast<bf16_t*>(vt_ws);
   hipError_t e = launch_transpose_rows(V, Vt, lay->B * lay->H, lay->L, Lp, D, st);
   if (e != hipSuccess) return e;
-  const bf16_t* q = static_cast<const bf16_t*>(Q);
-  const bf16_t* k = static_cast<const bf16_t*>(K);
+  const bool mx = Qs != nullptr;
   if (vl->S > 0 && vl->max_rtiles > 0) {
     p.max_tiles = vl->max_rtiles;
-    hipLaunchKernelGGL((moc::attn_fwd_bf16_kernel<D, moc::MODE_ROUTED>), dim3(vl->max_rtiles),
-                       dim3(moc::kNT), 0, st, q, k, Vt, Lp, lay->chunk_offsets, p, vl->rtiles,
-                       vl->n_rtiles, vl->bucket_off, vl->bucket_q, vl->slot, pO, plse,
-                       static_cast<bf16_t*>(O), lse);
+    if (mx)
+      hipLaunchKernelGGL((moc::attn_fwd_bf16_kernel<D, moc::MODE_ROUTED, true>),
+                         dim3(vl->max_rtiles), dim3(moc::kNT), 0, st, Q, K, Qs, Ks, Vt, Lp,
+                         lay->chunk_offsets, p, vl->rtiles, vl->n_rtiles, vl->bucket_off,
+                         vl->bucket_q, vl->slot, pO, plse, static_cast<bf16_t*>(O), lse);
+    else
+      hipLaunchKernelGGL((moc::attn_fwd_bf16_kernel<D, moc::MODE_ROUTED, false>),
+                         dim3(vl->max_rtiles), dim3(moc::kNT), 0, st, Q, K, Qs, Ks, Vt, Lp,
+                         lay->chunk_offsets, p, vl->rtiles, vl->n_rtiles, vl->bucket_off,
+                         vl->bucket_q, vl->slot, pO, plse, static_cast<bf16_t*>(O), lse);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   p.max_tiles = vl->max_atiles;
-  hipLaunchKernelGGL((moc::attn_fwd_bf16_kernel<D, moc::MODE_ANCHOR>),
-                     dim3(vl->max_atiles * lay->B * lay->H), dim3(moc::kNT), 0, st, q, k, Vt, Lp,
-                     lay->chunk_offsets, p, vl->atiles, vl->n_atiles, vl->bucket_off,
-                     vl->bucket_q, vl->slot, pO, plse, static_cast<bf16_t*>(O), lse);
+  const int grid = vl->max_atiles * lay->B * lay->H;
+  if (mx)
+    hipLaunchKernelGGL((moc::attn_fwd_bf16_kernel<D, moc::MODE_ANCHOR, true>), dim3(grid),
+                       dim3(moc::kNT), 0, st, Q, K, Qs, Ks, Vt, Lp, lay->chunk_offsets, p,
+                       vl->atiles, vl->n_atiles, vl->bucket_off, vl->bucket_q, vl->slot, pO,
+                       plse, static_cast<bf16_t*>(O), lse);
+  else
+    hipLaunchKernelGGL((moc::attn_fwd_bf16_kernel<D, moc::MODE_ANCHOR, false>), dim3(grid),
+                       dim3(moc::kNT), 0, st, Q, K, Qs, Ks, Vt, Lp, lay->chunk_offsets, p,
+                       vl->atiles, vl->n_atiles, vl->bucket_off, vl->bucket_q, vl->slot, pO,
+                       plse, static_cast<bf16_t*>(O), lse);
   return hipGetLastError();
 }
 
@@ -676,10 +714,21 @@ hipError_t launch_attn_fwd(const moc_layout* lay, const moc_varlen* vl, const vo
                            const void* K, const void* V, float scale, void* O, float* lse,
                            float* pO, float* plse, void* vt_ws, hipStream_t st) {
   if (lay->dtype == MOC_BF16)
-    return lay->d == 128 ? launch_fwd_bf16<128>(lay, vl, Q, K, V, scale, O, lse, pO, plse, vt_ws, st)
-                         : launch_fwd_bf16<64>(lay, vl, Q, K, V, scale, O, lse, pO, plse, vt_ws, st);
+    return lay->d == 128
+               ? launch_fwd_bf16<128>(lay, vl, Q, K, nullptr, nullptr, V, scale, O, lse, pO, plse, vt_ws, st)
+               : launch_fwd_bf16<64>(lay, vl, Q, K, nullptr, nullptr, V, scale, O, lse, pO, plse, vt_ws, st);
   return lay->d == 128 ? launch_fwd_t<float, 128>(lay, vl, Q, K, V, scale, O, lse, pO, plse, st)
                        : launch_fwd_t<float, 64>(lay, vl, Q, K, V, scale, O, lse, pO, plse, st);
+}
+
+// quantised scores: Q and K as MXFP8 codes and scales (rows padded to Lp), V bf16
+hipError_t launch_attn_fwd_mx(const moc_layout* lay, const moc_varlen* vl, const uint8_t* Qc,
+                              const uint8_t* Qs, const uint8_t* Kc, const uint8_t* Ks,
+                              const void* V, float scale, void* O, float* lse, float* pO,
+                              float* plse, void* vt_ws, hipStream_t st) {
+  return lay->d == 128
+             ? launch_fwd_bf16<128>(lay, vl, Qc, Kc, Qs, Ks, V, scale, O, lse, pO, plse, vt_ws, st)
+             : launch_fwd_bf16<64>(lay, vl, Qc, Kc, Qs, Ks, V, scale, O, lse, pO, plse, vt_ws, st);
 }
 
 }  // namespace moc_host

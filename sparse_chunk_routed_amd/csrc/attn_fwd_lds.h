@@ -184,11 +184,11 @@ __device__ __forceinline__ void score_tile_swz(const char* stage, const QFrag<bf
 
 // O^T[db] += V^T P^T for one 64-key tile, P^T packed to bf16 in the permuted output layout:
 // pb[ks] holds values 8 (ks & 1) .. 8 (ks & 1) + 7 of S^T block ks >> 1.
-template <int D>
+template <int D, int VOFF = LdsTiles<D>::KBYTES>
 __device__ __forceinline__ void pv_swz_packed(const char* stage, const bf16x8 (&pb)[4],
                                               f32x16 (&acc)[D / 32], int ql, int g) {
   using LT = LdsTiles<D>;
-  const char* vt = stage + LT::KBYTES + (LT::VROW * ql + g) * 16;
+  const char* vt = stage + VOFF + (LT::VROW * ql + g) * 16;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -197,6 +197,171 @@ __device__ __forceinline__ void pv_swz_packed(const char* stage, const bf16x8 (&
           bf16x8, *reinterpret_cast<const u32x4*>(vt + (db * 32 * LT::VROW + 2 * ks) * 16));
       acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], acc[db], 0, 0, 0);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Quantised scores: K and Q as MXFP8 (e4m3 codes, one E8M0 scale per 32 dims), S^T = K Q^T on
+// the block-scaled fp8 MFMA (32x32x64: each lane holds 32 codes of its row, bytes 0-15 from the
+// first 32-dim block of the step and bytes 16-31 from the second; lane group h supplies the
+// scale of block h of the step for its row).
+//
+// Stage layout: 64 code rows of D bytes with one spare 16-byte chunk per row (odd pitch, as for
+// the bf16 rows), one 1 KB block holding the 64 keys' scale bytes (D/32 per key, key-major),
+// then the V^T tile of the bf16 layout.
+template <int D>
+struct MxTiles {
+  static constexpr int NB = D / 32;                       // scale bytes per row
+  static constexpr int KCH = D / 16;                      // 16-byte chunks of one code row
+  static constexpr int KROW = KCH + 1;                    // padded code row pitch (chunks)
+  static constexpr int KBLK = (kBN * KROW + 63) / 64;     // 1 KB copy blocks of the code rows
+  static constexpr int SOFF = KBLK * 1024;                // the scale block
+  static constexpr int KBYTES = SOFF + 1024;
+  static constexpr int VBLK = LdsTiles<D>::VBLK;
+  static constexpr int VBYTES = VBLK * 1024;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int SCH = kBN * NB / 16;               // 16-byte chunks of the tile's scales
+};
+
+// Direct-to-LDS copies of one wave for one MX stage: blocks w, w + NW, ... of the code rows and
+// scale block (KBLK + 1 blocks) and of the V^T tile. Code and scale rows are padded to a
+// multiple of 64 rows in global memory, so no row is clamped.
+template <int D, int NW>
+struct MxStageCopier {
+  using MT = MxTiles<D>;
+  static constexpr int KB = MT::KBLK + 1;
+  static constexpr int KI = (KB + NW - 1) / NW;
+  static constexpr int VI = (MT::VBLK + NW - 1) / NW;
+  static constexpr int NBASE = KB / NW + MT::VBLK / NW;  // fewest copies of a wave per stage
+  int wv;
+  uint32_t koff[KI];   // byte offset within the tile's code rows, or within its scale bytes
+  uint32_t voff[VI];
+
+  __device__ __forceinline__ void init(int wave, int lane, int Lp) {
+    wv = wave;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int blk = wv + i * NW;
+      if (blk < MT::KBLK) {
+        const int pos = blk * 64 + lane;
+        int r = pos / MT::KROW, c = pos % MT::KROW;
+        if (c >= MT::KCH) c = 0;
+        if (r >= kBN) r = kBN - 1;
+        koff[i] = static_cast<uint32_t>(r * D + c * 16);
+      } else {
+        koff[i] = static_cast<uint32_t>((lane % MT::SCH) * 16);  // lanes past the scales repeat
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int pos = (wv + i * NW) * 64 + lane;
+      int d = pos / LdsTiles<D>::VROW, c = pos % LdsTiles<D>::VROW;
+      if (c >= kBN / 8) c = 0;
+      if (d >= D) d = D - 1;
+      voff[i] = static_cast<uint32_t>(d) * Lp * 2 + c * 16;
+    }
+  }
+
+  __device__ __forceinline__ int count() const {
+    return KB / NW + (wv < KB % NW) + MT::VBLK / NW + (wv < MT::VBLK % NW);
+  }
+
+  // codes/scales of keys kbase .. kbase+63 and V^T keys vbase .. vbase+63 into the stage at `lds`
+  __device__ __forceinline__ void issue(uint32_t lds, const uint8_t* Kc, const uint8_t* Ks,
+                                        int kbase, const bf16_t* Vtbh, int vbase) const {
+    const uint8_t* kc = Kc + static_cast<size_t>(kbase) * D;
+    const uint8_t* ks = Ks + static_cast<size_t>(kbase) * MT::NB;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int blk = wv + i * NW;
+      if (i * NW + NW > KB && blk >= KB) break;
+      if (blk < MT::KBLK) copy16_to_lds(kc, koff[i], lds + blk * 1024);
+      else copy16_to_lds(ks, koff[i], lds + blk * 1024);
+    }
+    const bf16_t* vb = Vtbh + vbase;
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      if (i * NW + NW > MT::VBLK && wv + i * NW >= MT::VBLK) break;
+      copy16_to_lds(vb, voff[i], lds + MT::KBYTES + (wv + i * NW) * 1024);
+    }
+  }
+};
+
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+// The B operand (Q^T) of the scaled fp8 score MFMA for one query row: per 64-dim step m, the
+// lane's 32 codes (dims 64m + 16g .. +15 and 64m + 32 + 16g .. +15), and the row's scale codes
+// shifted so that byte 2m holds the scale of block 2m + g.
+template <int D>
+struct MxQFrag {
+  static constexpr int NM = D / 64;
+  i32x8 q[NM];
+  uint32_t sc;
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ row,
+                                       const uint8_t* __restrict__ srow, int g) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(row + 64 * m + 16 * g);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(row + 64 * m + 32 + 16 * g);
+      q[m] = i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
+                   static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
+                   static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+    }
+    if constexpr (D == 128) sc = *reinterpret_cast<const uint32_t*>(srow) >> (8 * g);
+    else sc = static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(srow)) >> (8 * g);
+  }
+};
+
+// one block-scaled fp8 MFMA (e4m3 x e4m3); OP selects the scale byte of both operands
+template <int OP>
+__device__ __forceinline__ f32x16 mfma_mx(const i32x8& a, const i32x8& b, const f32x16& c,
+                                          uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OP, static_cast<int>(sa),
+                                                         OP, static_cast<int>(sb));
+}
+
+// S^T of one 64-key tile from an MX stage (blocks kb = 0, 1; the permuted key order of the bf16
+// tiles)
+template <int D>
+__device__ __forceinline__ void score_tile_mx(const char* stage, const MxQFrag<D>& qf,
+                                             f32x16 (&s)[2], int ql, int g) {
+  using MT = MxTiles<D>;
+  const int k0 = kperm(ql), k1 = 32 + kperm(ql);
+  const char* row0 = stage + MT::KROW * k0 * 16;
+  const char* row1 = stage + MT::KROW * k1 * 16;
+  uint32_t sa0, sa1;
+  if constexpr (D == 128) {
+    sa0 = *reinterpret_cast<const uint32_t*>(stage + MT::SOFF + 4 * k0) >> (8 * g);
+    sa1 = *reinterpret_cast<const uint32_t*>(stage + MT::SOFF + 4 * k1) >> (8 * g);
+  } else {
+    sa0 = static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(stage + MT::SOFF + 2 * k0)) >> (8 * g);
+    sa1 = static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(stage + MT::SOFF + 2 * k1)) >> (8 * g);
+  }
+  auto arow = [&](const char* row, int m) __attribute__((always_inline)) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(row + (4 * m + g) * 16);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(row + (4 * m + 2 + g) * 16);
+    return i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
+                 static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
+                 static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+  };
+  s[0] = f32x16{};
+  s[1] = f32x16{};
+  s[0] = mfma_mx<0>(arow(row0, 0), qf.q[0], s[0], sa0, qf.sc);
+  s[1] = mfma_mx<0>(arow(row1, 0), qf.q[0], s[1], sa1, qf.sc);
+  if constexpr (D == 128) {
+    s[0] = mfma_mx<2>(arow(row0, 1), qf.q[1], s[0], sa0, qf.sc);
+    s[1] = mfma_mx<2>(arow(row1, 1), qf.q[1], s[1], sa1, qf.sc);
+  }
+}
+
+// sched_group_barrier pattern: after each of NM MFMAs, an even share of NR operand reads
+template <int NR, int NM, int I = 0>
+__device__ __forceinline__ void sched_spread_reads() {
+  if constexpr (I < NM) {
+    constexpr int n = (NR * (I + 1)) / NM - (NR * I) / NM;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, 0);
+    sched_spread_reads<NR, NM, I + 1>();
   }
 }
 

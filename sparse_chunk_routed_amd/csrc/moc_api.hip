@@ -29,6 +29,12 @@ hipError_t launch_attn_fwd(const moc_layout* lay, const moc_varlen* vl, const vo
                            const void* K, const void* V, float scale, void* O, float* lse,
                            float* pO, float* plse, void* vt_ws, hipStream_t st);
 size_t attn_fwd_vt_bytes(const moc_layout* lay);
+hipError_t launch_attn_fwd_mx(const moc_layout* lay, const moc_varlen* vl, const uint8_t* Qc,
+                              const uint8_t* Qs, const uint8_t* Kc, const uint8_t* Ks,
+                              const void* V, float scale, void* O, float* lse, float* pO,
+                              float* plse, void* vt_ws, hipStream_t st);
+hipError_t launch_mx_quantize(const moc_layout* lay, const void* X, uint8_t* codes,
+                              uint8_t* scales, hipStream_t st);
 hipError_t launch_attn_bwd(const moc_layout* lay, const moc_varlen* vl, const void* Q,
                            const void* K, const void* V, const void* O, const float* lse,
                            const void* dO, float scale, void* dQ, void* dK, void* dV,
@@ -399,6 +405,60 @@ moc_status moc_attend_fwd(const moc_layout* lay, const moc_varlen* vl, const voi
                       "attention forward launch");
   } catch (...) {
     return fail(MOC_EINTERNAL, "exception in moc_attend_fwd");
+  }
+}
+
+moc_status moc_mx_quantize(const moc_layout* lay, const void* X, uint8_t* codes, uint8_t* scales,
+                           void* stream) {
+  try {
+    moc_status s = check_layout(lay);
+    if (s != MOC_OK) return s;
+    if (lay->dtype != MOC_BF16) return fail(MOC_EDTYPE, "MXFP8 quantisation takes bf16 input");
+    if (!X || !codes || !scales) return fail(MOC_EINVAL, "NULL tensor argument");
+    if (static_cast<const void*>(codes) == X || static_cast<const void*>(scales) == X ||
+        codes == scales)
+      return fail(MOC_EINVAL, "outputs alias");
+    return hip_status(moc_host::launch_mx_quantize(lay, X, codes, scales,
+                                                   static_cast<hipStream_t>(stream)),
+                      "MXFP8 quantisation launch");
+  } catch (...) {
+    return fail(MOC_EINTERNAL, "exception in moc_mx_quantize");
+  }
+}
+
+moc_status moc_attend_fwd_mx(const moc_layout* lay, const moc_varlen* vl, const uint8_t* Qc,
+                             const uint8_t* Qs, const uint8_t* Kc, const uint8_t* Ks,
+                             const void* V, float softmax_scale, void* O, float* lse, void* ws,
+                             size_t ws_bytes, void* stream) {
+  try {
+    moc_status s = check_layout(lay);
+    if (s != MOC_OK) return s;
+    s = check_varlen(lay, vl);
+    if (s != MOC_OK) return s;
+    if (lay->dtype != MOC_BF16) return fail(MOC_EDTYPE, "quantised scores need a bf16 layout");
+    if (!Qc || !Qs || !Kc || !Ks || !V || !O || !lse)
+      return fail(MOC_EINVAL, "NULL tensor argument");
+    const void* ins[] = {Qc, Qs, Kc, Ks, V};
+    for (const void* a : ins)
+      if (a == O || a == static_cast<const void*>(lse)) return fail(MOC_EINVAL, "outputs alias inputs");
+    if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+      return fail(MOC_EINVAL, "softmax_scale must be finite and > 0");
+    const size_t need = fwd_bytes(lay, vl->S);
+    if (!ws || ws_bytes < need)
+      return fail(MOC_EWORKSPACE, "FWD workspace needs %zu bytes (got %zu)", need,
+                  ws ? ws_bytes : size_t(0));
+    const int64_t rows = static_cast<int64_t>(lay->B) * lay->H * lay->L * vl->S;
+    char* w = static_cast<char*>(ws);
+    float* pO = reinterpret_cast<float*>(w);
+    w += align_up(sizeof(float) * (rows > 0 ? rows : 1) * lay->d);
+    float* plse = reinterpret_cast<float*>(w);
+    w += align_up(sizeof(float) * (rows > 0 ? rows : 1));
+    return hip_status(moc_host::launch_attn_fwd_mx(lay, vl, Qc, Qs, Kc, Ks, V, softmax_scale, O,
+                                                   lse, pO, plse, w,
+                                                   static_cast<hipStream_t>(stream)),
+                      "quantised-scores attention forward launch");
+  } catch (...) {
+    return fail(MOC_EINTERNAL, "exception in moc_attend_fwd_mx");
   }
 }
 

@@ -213,3 +213,22 @@ def test_device_segments_validation():
     for bad in ([0, 2, 13], [0, 1, 1, 13], [0, 1, 12], [1, 13], [0]):
         with pytest.raises(ValueError):
             moc.DeviceSegments(bad, lay)
+
+
+def test_mx_entry_points_reject_bad_arguments(L):
+    """Host-side validation of the quantised-scores entry points (nothing is launched)."""
+    lib = L.load()
+    p = ctypes.c_void_p
+    f32 = _layout(L, dtype=0)
+    bf = _layout(L, dtype=1)
+    assert lib.moc_mx_quantize(ctypes.byref(f32), p(1), p(2), p(3), None) == 3   # dtype
+    assert lib.moc_mx_quantize(ctypes.byref(bf), None, p(2), p(3), None) == 1    # NULL
+    assert lib.moc_mx_quantize(ctypes.byref(bf), p(1), p(2), p(2), None) == 1    # alias
+    assert lib.moc_mx_quantize(ctypes.byref(_layout(L, dtype=1, d=96)), p(1), p(2), p(3),
+                               None) == 2                                        # d
+    vl = L.MocVarlen()
+    assert lib.moc_attend_fwd_mx(ctypes.byref(bf), ctypes.byref(vl), p(1), p(2), p(3), p(4),
+                                 p(5), ctypes.c_float(0.125), p(6), p(7), p(8), 1 << 30,
+                                 None) == 1                                      # unfilled varlen
+    assert lib.moc_attend_fwd_mx(ctypes.byref(bf), None, p(1), p(2), p(3), p(4), p(5),
+                                 ctypes.c_float(0.125), p(6), p(7), p(8), 1 << 30, None) == 1
