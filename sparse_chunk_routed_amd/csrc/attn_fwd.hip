@@ -42,6 +42,11 @@ constexpr int kBM = kNW * 32 * kQB;    // queries per workgroup
 #define MOC_ATTN_RA 4
 #endif
 constexpr int kReadAhead = MOC_ATTN_RA;  // LDS operand reads in flight ahead of the MFMAs
+#ifndef MOC_ATTN_PRE
+#define MOC_ATTN_PRE 4
+#endif
+// V^T operands of a wave's next MFMA half-step read during its softmax half-step
+constexpr int kPre = MOC_ATTN_PRE;
 
 struct AttnParams {
   int B, H, L, C, S;
@@ -300,11 +305,12 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
   static_assert(kNW == 8, "two groups of four waves");
   constexpr int STAGE = MX ? MT::STAGE : LT::STAGE;
   constexpr int VOFF = MX ? MT::KBYTES : LT::KBYTES;  // V^T tile within a stage
-  // three stage buffers as distinct objects, so that the compiler can tell the LDS written by
+  // four stage buffers as distinct objects, so that the compiler can tell the LDS written by
   // the in-flight direct-to-LDS copies from the stage being read (no forced wait between them)
   __shared__ __attribute__((aligned(1024))) char st0[STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[STAGE];
   __shared__ __attribute__((aligned(1024))) char st2[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st3[STAGE];
 
   int bh, q_lo, nq, r1a, r1b, r2a, r2b, bstart = 0;
   if constexpr (MODE == MODE_ANCHOR) {
@@ -385,15 +391,14 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
   };
   const int kmax = p.L - 1;
   auto tile_base = [&](int j) __attribute__((always_inline)) { return j < n1 ? (m1a + j) * kBN : (m2a + j - n1) * kBN; };
-  // Skewed stage j (0 <= j <= ntot) holds K of tile j and V^T of tile j-1: both are read in the
-  // same pair of half-steps (see below). Indices past the ends are clamped; those halves are
-  // loaded but never read, so every wave issues the same number of copies per stage.
-  const uint32_t lds0 = lds_addr(st0), lds1 = lds_addr(st1), lds2 = lds_addr(st2);
+  // Stage j (0 <= j < ntot) holds K and V^T of tile j, in buffer j % 4.
+  const uint32_t lds0 = lds_addr(st0), lds1 = lds_addr(st1), lds2 = lds_addr(st2),
+                 lds3 = lds_addr(st3);
   auto issue = [&](int j, uint32_t lds) __attribute__((always_inline)) {
-    if (j > ntot || ntot == 0) return;
-    const int kb = tile_base(j < ntot ? j : ntot - 1), vb = tile_base(j > 0 ? j - 1 : 0);
-    if constexpr (MX) cp.issue(lds, Kcbh, Ksbh, kb, Vtbh, vb);
-    else cp.issue(lds, Kbh, kb, kmax, Vtbh, vb);
+    if (j >= ntot) return;
+    const int base = tile_base(j);
+    if constexpr (MX) cp.issue(lds, Kcbh, Ksbh, base, Vtbh, base);
+    else cp.issue(lds, Kbh, base, kmax, Vtbh, base);
   };
 
   // Two wave groups (waves 0-3 and 4-7; wave w and w+4 run on the same SIMD) work on the same
@@ -401,43 +406,48 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
   // previous tile, then S of the current one) while the other runs the softmax of its current
   // tile on the VALU, so the matrix cores of each SIMD stay busy during the exp / max / sum
   // work. Half-step t ends with a workgroup barrier; group 0 runs MFMAs on even t, group 1 on
-  // odd t. Skewed stage j is read in half-steps 2j (group 0) and 2j+1 (group 1); its copies
-  // are issued in half-step 2j-4 (group 1) or 2j-3 (group 0) into the buffer freed by stage
-  // j-3, so three LDS buffers give every copy at least three half-steps to land.
+  // odd t. A wave streams its MFMA operands from LDS at a bounded rate of its own, so during
+  // its softmax half-step it also reads the first kPre V^T operands of the P.V that follows
+  // (preload): the two waves of a SIMD then read LDS at the same time. Stage j is read in
+  // half-steps 2j (S, group 0) to 2j+3 (P.V, group 1); its copies are issued in half-step 2j-4
+  // (group 1) or 2j-3 (group 0), both softmax half-steps, into the buffer of stage j-4, and
+  // waited for at the end of half-step 2j-1.
   f32x16 s[2];
   bf16x8 pb[4];  // P^T of the previous tile, packed for the four 16-key MFMA steps
   auto scores = [&](const char* st) __attribute__((always_inline)) {
     if constexpr (MX) score_tile_mx<D>(st, qf, s, ql, g);
     else score_tile_swz<D>(st, qf, s, ql, g);
   };
-  // steady MFMA half-step: O += V P of tile j-1, then S of tile j, both from stage j
-  auto mfma_full = [&](const char* st) __attribute__((always_inline)) {
-    pv_swz_packed<D, VOFF>(st, pb, acc, ql, g);
-    scores(st);
+  bf16x8 pre[kPre > 0 ? kPre : 1];  // V^T operands read ahead for the next P.V
+  auto preload = [&](const char* st) __attribute__((always_inline)) {
+    if constexpr (kPre > 0) pv_preload<D, VOFF, kPre>(st, pre, ql, g);
+  };
+  // steady MFMA half-step: O += V P of tile j-1 (stage stp), then S of tile j (stage stc)
+  auto mfma_full = [&](const char* stp, const char* stc) __attribute__((always_inline)) {
+    pv_swz_packed<D, VOFF, kPre>(stp, pb, acc, ql, g, pre);
+    scores(stc);
     // operand reads run kReadAhead ahead of the MFMAs that use them (bounded registers)
     if constexpr (MX) {
-      // P.V: one read per MFMA; S: two code reads per MFMA and two scale reads per tile
+      // P.V: one read per MFMA (less the preloaded ones); S: two code reads per MFMA and two
+      // scale reads per tile
       constexpr int NM = 4 * (D / 32) + 2 * (D / 64);
-      constexpr int NR = 4 * (D / 32) + 4 * (D / 64) + 2;
+      constexpr int NR = 4 * (D / 32) - kPre + 4 * (D / 64) + 2;
       __builtin_amdgcn_sched_group_barrier(0x100, kReadAhead, 0);
       sched_spread_reads<NR - kReadAhead, NM>();
     } else {
       constexpr int NM = 4 * (D / 32) + 2 * (D / 16);
+      constexpr int NR = NM - kPre;
       __builtin_amdgcn_sched_group_barrier(0x100, kReadAhead, 0);
-#pragma unroll
-      for (int i = 0; i < NM - kReadAhead; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, kReadAhead, 0);
+      sched_spread_reads<NR - kReadAhead, NM>();
     }
   };
-  // last MFMA half-step: O += V P of the last tile, from stage ntot
+  // last MFMA half-step: O += V P of the last tile
   auto mfma_last = [&]() __attribute__((always_inline)) {
-    const int r = ntot % 3;
-    if (r == 0) pv_swz_packed<D, VOFF>(st0, pb, acc, ql, g);
-    else if (r == 1) pv_swz_packed<D, VOFF>(st1, pb, acc, ql, g);
-    else pv_swz_packed<D, VOFF>(st2, pb, acc, ql, g);
+    const int r = (ntot - 1) & 3;
+    if (r == 0) pv_swz_packed<D, VOFF, kPre>(st0, pb, acc, ql, g, pre);
+    else if (r == 1) pv_swz_packed<D, VOFF, kPre>(st1, pb, acc, ql, g, pre);
+    else if (r == 2) pv_swz_packed<D, VOFF, kPre>(st2, pb, acc, ql, g, pre);
+    else pv_swz_packed<D, VOFF, kPre>(st3, pb, acc, ql, g, pre);
   };
   auto valu_half = [&](int j) __attribute__((always_inline)) {
     int base, lo, hi;
@@ -487,70 +497,71 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  // end of half-step 2i+1: stage i+1 must have landed; stage i+2 (issued at 2i) may stay in flight
-  auto wait_next = [&](int i) __attribute__((always_inline)) {
-    if (i + 2 <= ntot) wait_but_newest();
+  // stage i complete (its first read is in the next half-step); stage i+1 may stay in flight
+  auto wait_stage = [&](int i) __attribute__((always_inline)) {
+    if (i + 1 < ntot) wait_but_newest();
     else __builtin_amdgcn_s_waitcnt(0x0070);
   };
 
   if (ntot > 0) {
-    // prologue: stages 0 and 1 in flight (stage 1 exists since ntot >= 1), wait for stage 0
     issue(0, lds0);
     issue(1, lds1);
-    wait_but_newest();
+    wait_stage(0);
     bar();
     if (wv < 4) {
-      // group 0: half-step 2j = MFMAs of stage j, 2j+1 = softmax of tile j. Its copies of stage
-      // j+2 go out at the start of half-step 2j+1 (the buffer was last read in 2j-1), where the
-      // wave has slack, and not together with group 1's copies.
+      // group 0: half-step 2j = MFMAs (P.V of tile j-1, S of tile j), 2j+1 = softmax of tile j
       scores(st0);
       bar();
       issue(2, lds2);
+      preload(st0);
       valu_half(0);
-      wait_next(0);
+      wait_stage(1);
       bar();
-      auto step = [&](int j, const char* cur, uint32_t nxt2) __attribute__((always_inline)) {
-        mfma_full(cur);
+      auto step = [&](int j, const char* stp, const char* stc, uint32_t lds_j2) __attribute__((always_inline)) {
+        mfma_full(stp, stc);
         bar();
-        issue(j + 2, nxt2);
+        issue(j + 2, lds_j2);  // the buffer of stage j-2, last read in half-step 2j-1
+        preload(stc);
         valu_half(j);
-        wait_next(j);
+        wait_stage(j + 1);
         bar();
       };
-      for (int j = 1; j < ntot; j += 3) {
-        step(j, st1, lds0);
-        if (j + 1 < ntot) step(j + 1, st2, lds1);
-        if (j + 2 < ntot) step(j + 2, st0, lds2);
+      for (int j = 1; j < ntot; j += 4) {
+        step(j, st0, st1, lds3);
+        if (j + 1 < ntot) step(j + 1, st1, st2, lds0);
+        if (j + 2 < ntot) step(j + 2, st2, st3, lds1);
+        if (j + 3 < ntot) step(j + 3, st3, st0, lds2);
       }
       mfma_last();  // half-step 2 ntot
       bar();
-      wait_next(ntot);  // idle half-step 2 ntot + 1
-      bar();
+      bar();  // idle half-step 2 ntot + 1
     } else {
-      // group 1: idle half-step 0, then 2j+1 = MFMAs of stage j, 2j+2 = softmax of tile j
+      // group 1: idle half-step 0, then 2j+1 = MFMAs of tiles j-1 / j, 2j+2 = softmax of tile j
       issue(2, lds2);
       bar();
       scores(st0);
-      wait_next(0);
+      wait_stage(1);
       bar();
-      issue(3, lds0);
+      issue(3, lds3);
+      preload(st0);
       valu_half(0);
       bar();
-      auto step = [&](int j, const char* cur, uint32_t cur_lds) __attribute__((always_inline)) {
-        mfma_full(cur);
-        wait_next(j);
+      auto step = [&](int j, const char* stp, const char* stc, uint32_t lds_j3) __attribute__((always_inline)) {
+        mfma_full(stp, stc);
+        wait_stage(j + 1);
         bar();
-        issue(j + 3, cur_lds);  // stage j+3 reuses stage j's buffer, read for the last time above
+        issue(j + 3, lds_j3);  // the buffer of stage j-1, last read in half-step 2j+1
+        preload(stc);
         valu_half(j);
         bar();
       };
-      for (int j = 1; j < ntot; j += 3) {
-        step(j, st1, lds1);
-        if (j + 1 < ntot) step(j + 1, st2, lds2);
-        if (j + 2 < ntot) step(j + 2, st0, lds0);
+      for (int j = 1; j < ntot; j += 4) {
+        step(j, st0, st1, lds0);
+        if (j + 1 < ntot) step(j + 1, st1, st2, lds1);
+        if (j + 2 < ntot) step(j + 2, st2, st3, lds2);
+        if (j + 3 < ntot) step(j + 3, st3, st0, lds3);
       }
       mfma_last();  // half-step 2 ntot + 1
-      wait_next(ntot);
       bar();
     }
   }

@@ -183,20 +183,44 @@ __device__ __forceinline__ void score_tile_swz(const char* stage, const QFrag<bf
 }
 
 // O^T[db] += V^T P^T for one 64-key tile, P^T packed to bf16 in the permuted output layout:
-// pb[ks] holds values 8 (ks & 1) .. 8 (ks & 1) + 7 of S^T block ks >> 1.
-template <int D, int VOFF = LdsTiles<D>::KBYTES>
+// pb[ks] holds values 8 (ks & 1) .. 8 (ks & 1) + 7 of S^T block ks >> 1. The first NPRE V^T
+// operands (in (ks, db) order) were read ahead of time into pre (pv_preload).
+template <int D, int VOFF, int NPRE>
 __device__ __forceinline__ void pv_swz_packed(const char* stage, const bf16x8 (&pb)[4],
-                                              f32x16 (&acc)[D / 32], int ql, int g) {
+                                              f32x16 (&acc)[D / 32], int ql, int g,
+                                              const bf16x8* pre) {
   using LT = LdsTiles<D>;
   const char* vt = stage + VOFF + (LT::VROW * ql + g) * 16;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const bf16x8 a = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(vt + (db * 32 * LT::VROW + 2 * ks) * 16));
+      const int i = ks * (D / 32) + db;
+      const bf16x8 a = i < NPRE ? pre[i]
+                                : __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                                 vt + (db * 32 * LT::VROW + 2 * ks) * 16));
       acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], acc[db], 0, 0, 0);
     }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void pv_swz_packed(const char* stage, const bf16x8 (&pb)[4],
+                                              f32x16 (&acc)[D / 32], int ql, int g) {
+  pv_swz_packed<D, LdsTiles<D>::KBYTES, 0>(stage, pb, acc, ql, g, nullptr);
+}
+
+// The first NPRE V^T operand reads of pv_swz_packed for a stage, issued early (by a wave that
+// is not running MFMAs at the time, so that its LDS reads overlap the other wave's).
+template <int D, int VOFF, int NPRE>
+__device__ __forceinline__ void pv_preload(const char* stage, bf16x8* pre, int ql, int g) {
+  using LT = LdsTiles<D>;
+  const char* vt = stage + VOFF + (LT::VROW * ql + g) * 16;
+#pragma unroll
+  for (int i = 0; i < NPRE; ++i) {
+    const int ks = i / (D / 32), db = i % (D / 32);
+    pre[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                            vt + (db * 32 * LT::VROW + 2 * ks) * 16));
   }
 }
 
