@@ -53,7 +53,6 @@ def parse(argv=None):
     return ap.parse_args(argv)
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_fwd_headline_traffic.txt")
 TRAFFIC_SOURCES = ["sparse_chunk_routed_amd/csrc/attn_fwd.hip",
                    "sparse_chunk_routed_amd/csrc/attn_fwd_lds.h",
                    "sparse_chunk_routed_amd/csrc/attn_common.h",
@@ -61,14 +60,15 @@ TRAFFIC_SOURCES = ["sparse_chunk_routed_amd/csrc/attn_fwd.hip",
 
 
 def recorded_traffic(workload: str):
-    """HBM bytes per attention-forward call from the committed rocprofv3 counter summary, or
-    None when the workload differs or the kernel sources changed since the counters were
-    taken."""
+    """HBM bytes per attention-forward call from the committed rocprofv3 counter summary of
+    this workload (profiles/attention_fwd_<workload>_traffic.txt), or None when there is none
+    or the kernel sources changed since the counters were taken."""
     import hashlib
-    if workload != "headline" or not os.path.exists(TRAFFIC_FILE):
+    path = os.path.join(ROOT, "profiles", f"attention_fwd_{workload}_traffic.txt")
+    if not workload or not os.path.exists(path):
         return None
     rec = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if line.strip() and not line.startswith("#"):
             k, v = line.split()
             rec[k] = v
@@ -332,8 +332,8 @@ def main(argv=None) -> int:
                        if mx else "attention forward (routed + anchor kernels of moc_attend_fwd)"),
             "achieved": att_tf, "peak": peak, "unit": "TFLOP/s", "frac": att_tf / peak,
             "traffic": recorded_traffic(a.workload if a.seed == 0 else ""),
-            "traffic_unit": "HBM bytes per moc_attend_fwd call (rocprofv3 FETCH_SIZE+WRITE_SIZE, "
-                            "copy-calibrated)",
+            "traffic_unit": ("HBM bytes per attention-forward call: V transpose + routed + "
+                             "anchor kernels (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)"),
         },
         "cpu_baseline": None,
     }
