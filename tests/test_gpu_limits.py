@@ -1,0 +1,66 @@
+"""GPU parity at the limits of the C ABI and in the degenerate layouts of the method, through
+the C ABI against the oracle: MOC_MAX_C chunks with min(top_k, C) = MOC_MAX_TOPK and
+max_drop_in = MOC_MAX_DROP_IN (selection width 48) on the per-tile router, forward and
+backward; a single chunk; text only; one-token chunks. Bars as in the other parity tests."""
+import numpy as np
+import pytest
+
+import moc_inputs as mi
+from oracle import moc_oracle as mo
+import test_gpu_backward as tb
+from test_gpu_parity import Run, TOL, _check_selection, _say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_max_chunks_topk_and_drop_in():
+    """C = 1024 (32 text tokens + 1023 chunks of 16 tokens in 33 shots), top-k 32, drop-off
+    p_max 0.5 and drop-in lambda 4 capped at 16: the widest selection rows the ABI allows."""
+    sizes = [32] + [16] * 1023
+    shots = [-1] + [i // 31 for i in range(1023)]
+    lay = mi.layout_from_chunks(sizes, shots)
+    assert lay.C == 1024
+    w = mi.Workload("limits", 1, 2, 64, "bf16", lay, top_k=32, causal=True,
+                    clustered_keys=True, p_max=0.5, lam=4.0, max_drop_in=16, seed=7)
+    g = tb._run(w, backward=True)
+    assert g["sel"].shape[-1] == 48
+    changed = tb._check_noise(w, g)
+    assert changed > 0
+    assert int(g["nsel"].max()) > 32  # drop-in filled rows past top-k
+    O, _ = mo.attend(g["Q"], g["K"], g["V"], w.layout, g["sel"])
+    err = float(np.max(np.abs(g["O"] - O)))
+    _say(f"limits: forward max|dO|={err:.3e}")
+    assert err <= TOL["bf16"]
+    tb._check_grads(w, g)
+
+
+@pytest.mark.parametrize("case", ["one_chunk", "text_only", "token_chunks"])
+def test_degenerate_layouts(case):
+    """One chunk (no candidates; attention is the chunk itself), a text-only sequence (every
+    query attends all text, nothing to route), and chunks of one token each."""
+    if case == "one_chunk":
+        lay = mi.layout_from_chunks([100], [0])
+        w = mi.Workload(case, 1, 2, 64, "f32", lay, top_k=2, causal=True, clustered_keys=False,
+                        seed=1)
+    elif case == "text_only":
+        lay = mi.layout_from_chunks([40, 30], [-1, -1])
+        w = mi.Workload(case, 2, 1, 128, "bf16", lay, top_k=3, causal=False,
+                        clustered_keys=False, seed=2)
+    else:
+        lay = mi.layout_from_chunks([1] * 64, [i // 8 for i in range(64)])
+        w = mi.Workload(case, 1, 2, 64, "bf16", lay, top_k=3, causal=True, clustered_keys=True,
+                        seed=3)
+    run = Run(w)
+    kb = mo.pool_keys(run.K, lay)
+    assert np.array_equal(run.h_kbar.view(np.uint32), kb.view(np.uint32))
+    r = mo.route(run.Q, kb, lay, w.top_k, w.causal)
+    _check_selection(run, r)
+    mo.check_routing(lay, run.h_sel, run.h_nsel, w.top_k, w.causal)
+    assert np.array_equal(run.h_pairs, mo.pair_counts(lay, run.h_sel))
+    O, lse = mo.attend(run.Q, run.K, run.V, lay, run.h_sel)
+    err = float(np.max(np.abs(run.h_O - O)))
+    lerr = float(np.max(np.abs(run.h_lse - lse)))
+    _say(f"{case}: L={lay.L} C={lay.C} max|dO|={err:.3e} max|dlse|={lerr:.3e}")
+    assert err <= TOL[w.dtype] and lerr <= TOL[w.dtype]
+    if case != "token_chunks":
+        assert int(run.h_nsel.max()) == 0  # nothing to route
