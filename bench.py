@@ -38,7 +38,7 @@ def parse(argv=None):
                     choices=["headline", "mid", "short", "tiny", "train", "headline_uniform",
                              "single_shot_c64", "single_shot_c128", "single_shot_c256",
                              "single_shot_c512", "single_shot_c1024", "headline_outer",
-                             "headline_mx"])
+                             "headline_mx", "headline_h3"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=192,
@@ -78,6 +78,41 @@ def recorded_traffic(workload: str):
     if h.hexdigest() != rec.get("kernel_sources_sha256"):
         return None
     return int(rec["fetch_bytes_per_launch"]) + int(rec["write_bytes_per_launch"])
+
+
+def measured_peaks(dev) -> dict:
+    """Ceilings re-measured on this GPU next to the published ones: a plain device copy (HBM
+    GB/s, read + write) and register-only MFMA loops (moc_probe_mfma: bf16, and fp8 with block
+    scales), each the best of three timed launches after a warm-up."""
+    import torch
+    import sparse_chunk_routed_amd as moc
+
+    def best(fn, reps=3):
+        fn()
+        out = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            out.append(a.elapsed_time(b) * 1e-3)
+        return min(out)
+
+    n = 1 << 31
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    t_copy = best(lambda: dst.copy_(src))
+    del src, dst
+    blocks, iters = 1024, 4096
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    waves_mfma = blocks * 4 * iters * 8
+    t_bf16 = best(lambda: moc.probe_mfma(False, blocks, iters, sink))
+    t_fp8 = best(lambda: moc.probe_mfma(True, blocks, iters, sink))
+    return {"hbm_copy_gbs": 2 * n / t_copy / 1e9,
+            "mfma_bf16_tflops": waves_mfma * 2 * 32 * 32 * 16 / t_bf16 / 1e12,
+            "mfma_fp8_tflops": waves_mfma * 2 * 32 * 32 * 64 / t_fp8 / 1e12,
+            "how": "device copy of 2 GiB; register-only MFMA loops, 4,096 waves x 8 chains"}
 
 
 def copy_calibration() -> int:
@@ -286,6 +321,7 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms = total_ms / a.steps
+    step_ms = sorted(e[0].elapsed_time(e[-1]) for e in evs)
     stage = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / a.steps
              for j, n in enumerate(names)}
     pairs = int(vl.pair_count.sum().item())
@@ -319,6 +355,8 @@ def main(argv=None) -> int:
                       if w.segments is not None else {}),
                    **({"scores": "MXFP8 Q and K (e4m3, 32-element E8M0 blocks)"} if mx else {})},
         "layer_ms": ms,
+        "step_ms_median": step_ms[len(step_ms) // 2],
+        "step_ms_min": step_ms[0],
         "stages_ms": stage,
         "pairs": pairs,
         "pruned_fraction": 1.0 - pairs / (w.B * w.H * w.L * w.L),
@@ -339,6 +377,16 @@ def main(argv=None) -> int:
     }
     if with_bwd:
         out["backward_tflops"] = bwd_flops / (stage["attend_bwd"] * 1e-3) / 1e12
+    # the same fractions against ceilings re-measured on this GPU
+    mp = measured_peaks(dev)
+    mpeak = (4.0 / (2.0 / mp["mfma_fp8_tflops"] + 2.0 / mp["mfma_bf16_tflops"]) if mx
+             else mp["mfma_bf16_tflops"])
+    out["measured_peaks"] = mp
+    out["roofline"]["frac_of_measured_peak"] = att_tf / mpeak
+    out["pool_hbm_frac"] = out["pool_gbs"] / PEAK_HBM_GBS
+    out["route_hbm_frac"] = out["route_gbs"] / PEAK_HBM_GBS
+    out["pool_frac_of_measured_copy"] = out["pool_gbs"] / mp["hbm_copy_gbs"]
+    out["route_frac_of_measured_copy"] = out["route_gbs"] / mp["hbm_copy_gbs"]
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, Q, K, V, a.cpu_rows)

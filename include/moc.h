@@ -264,6 +264,16 @@ moc_status moc_attend_fwd_mx(const moc_layout *lay, const moc_varlen *vl, const 
                              size_t ws_bytes, void *stream);
 
 /*
+ * Measurement aid, not a step of the layer: a register-only MFMA loop that shows the matrix-core
+ * rate the chip sustains (its clock and power limits included). Launches `blocks` workgroups of
+ * 4 waves; every wave runs `iters` rounds of 8 independent 32x32x16 bf16 MFMAs (fp8 = 0) or
+ * 32x32x64 e4m3 MFMAs with unit E8M0 scales (fp8 = 1) and writes one float per thread to sink
+ * (device float [blocks * 256]). FLOPs = blocks * 4 * iters * 8 * 2 * 32 * 32 * (16 or 64); the
+ * caller times the launch on `stream`.
+ */
+moc_status moc_probe_mfma(int32_t fp8, int32_t blocks, int32_t iters, float *sink, void *stream);
+
+/*
  * Attention backward with the routed sets held fixed (summary §3.1 and Appendix A: top-k is
  * not differentiable; gradients reach the selected keys and values only).
  *   Inputs: Q, K, V, O, lse from moc_attend_fwd, dO. Outputs dQ, dK, dV [B,H,L,d] in the

@@ -294,6 +294,15 @@ def headline_outer(seed: int = 0, **kw) -> Workload:
     return replace(w, **kw)
 
 
+def headline_h3(seed: int = 0, **kw) -> Workload:
+    """One GPU's share of the headline layer sharded four ways by head: H=3 at the full
+    175,232-token layout (routing and attention are independent per head)."""
+    w = headline(seed)
+    w = replace(w, name="headline_h3", H=3,
+                description=w.description + "; 3 of 12 heads (a 4-way head shard)")
+    return replace(w, **kw)
+
+
 def headline_mx(seed: int = 0, **kw) -> Workload:
     """Headline workload with quantised scores: Q and K quantised to MXFP8 for the attention
     (routing and pooling on the bf16 inputs as before), V and P.V in bf16."""
@@ -306,7 +315,7 @@ def headline_mx(seed: int = 0, **kw) -> Workload:
 WORKLOADS = {"tiny": tiny, "mid": mid, "headline": headline, "short": short, "train": train,
              "slice": grad_slice, "headline_uniform": headline_uniform,
              "single_shot": single_shot, "headline_outer": headline_outer,
-             "headline_mx": headline_mx}
+             "headline_mx": headline_mx, "headline_h3": headline_h3}
 for _c in (64, 128, 256, 512, 1024):
     WORKLOADS[f"single_shot_c{_c}"] = (lambda c: lambda seed=0, **kw: single_shot(seed, c, **kw))(_c)
 

@@ -8,12 +8,14 @@ from . import _lib
 from ._lib import MocError, load
 from .api import (DeviceLayout, DeviceSegments, ForwardResult, MoCAttention, MxTensor,
                   OuterRouting, RouteCfg, Varlen, attend_bwd, attend_fwd, attend_fwd_mx,
-                  build_varlen, forward, mx_quantize, pool_keys, route, route_outer, sel_width,
+                  build_varlen, forward, mx_quantize, pool_keys, probe_mfma, route, route_outer,
+                  sel_width,
                   validate_layout, workspace_bytes)
 
 load()
 
 __all__ = ["DeviceLayout", "DeviceSegments", "ForwardResult", "MoCAttention", "MocError",
            "MxTensor", "OuterRouting", "RouteCfg", "Varlen", "attend_bwd", "attend_fwd",
-           "attend_fwd_mx", "build_varlen", "forward", "mx_quantize", "pool_keys", "route",
+           "attend_fwd_mx", "build_varlen", "forward", "mx_quantize", "pool_keys", "probe_mfma",
+           "route",
            "route_outer", "sel_width", "validate_layout", "workspace_bytes"]

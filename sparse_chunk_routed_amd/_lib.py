@@ -19,7 +19,7 @@ MOC_MAX_SEG, MOC_MAX_TOPM = 256, 16
 EXPORTS = (
     "moc_sel_width", "moc_workspace_bytes", "moc_pool_keys", "moc_route", "moc_route_outer",
     "moc_route_masked", "moc_build_varlen", "moc_attend_fwd", "moc_attend_bwd",
-    "moc_mx_quantize", "moc_attend_fwd_mx", "moc_poisson_thresholds", "moc_status_string", "moc_last_error",
+    "moc_mx_quantize", "moc_attend_fwd_mx", "moc_probe_mfma", "moc_poisson_thresholds", "moc_status_string", "moc_last_error",
 )
 
 
@@ -53,14 +53,14 @@ _lib = None
 
 
 def load() -> ctypes.CDLL:
-    """Load libmoc.so (built in-tree by `python -m sparse_chunk_routed_amd.build`). There is no
+    """Load libmoc.so (built in-tree by `python sparse_chunk_routed_amd/build.py`). There is no
     fallback: a missing library is an error."""
     global _lib
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing; build it with "
-                          "`python -m sparse_chunk_routed_amd.build`")
+                          "`python sparse_chunk_routed_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P = POINTER
     lib.moc_sel_width.argtypes = [P(MocRouteCfg), c_int32]
@@ -95,6 +95,8 @@ def load() -> ctypes.CDLL:
                                       c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_void_p,
                                       c_size_t, c_void_p]
     lib.moc_attend_fwd_mx.restype = c_int32
+    lib.moc_probe_mfma.argtypes = [c_int32, c_int32, c_int32, c_void_p, c_void_p]
+    lib.moc_probe_mfma.restype = c_int32
     lib.moc_poisson_thresholds.argtypes = [c_float, c_int32, P(c_uint64)]
     lib.moc_poisson_thresholds.restype = c_int32
     lib.moc_status_string.argtypes = [c_int32]

@@ -360,6 +360,15 @@ def attend_fwd_mx(Qm: MxTensor, Km: MxTensor, V: torch.Tensor, lay: DeviceLayout
     return O, lse
 
 
+def probe_mfma(fp8: bool, blocks: int, iters: int, sink: torch.Tensor) -> None:
+    """Launch the register-only MFMA loop (moc_probe_mfma) on the current stream; sink is a
+    device float tensor of blocks * 256 elements. A measurement aid, not a layer step."""
+    if sink.dtype != torch.float32 or sink.numel() < blocks * 256 or sink.device.type != "cuda":
+        raise ValueError("sink must be a device float tensor of blocks * 256 elements")
+    L.check(L.load().moc_probe_mfma(int(bool(fp8)), int(blocks), int(iters), _ptr(sink),
+                                    _stream(sink.device)))
+
+
 def attend_bwd(Q, K, V, O, lse, dO, lay: DeviceLayout, vl: Varlen, scale: Optional[float] = None,
                ws: Optional[torch.Tensor] = None):
     """(dQ, dK, dV) in the input dtype."""

@@ -1,6 +1,9 @@
 """Build libmoc.so (the HIP kernels + C ABI) in-tree for gfx950 with hipcc.
 
-Usage: python -m sparse_chunk_routed_amd.build [--jobs N] [--verbose]
+Usage: python sparse_chunk_routed_amd/build.py [--jobs N] [--verbose]
+
+Run as a script (or loaded by file path): importing the package would load the library that
+this rebuilds.
 """
 from __future__ import annotations
 
@@ -20,7 +23,7 @@ LIB = os.path.join(PKG, "libmoc.so")
 ARCH = "gfx950"
 
 SOURCES = ["moc_api.hip", "pool.hip", "route.hip", "outer.hip", "varlen.hip", "attn_fwd.hip",
-           "mx.hip", "attn_bwd.hip"]
+           "mx.hip", "attn_bwd.hip", "probe.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",

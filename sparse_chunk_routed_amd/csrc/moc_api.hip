@@ -35,6 +35,7 @@ hipError_t launch_attn_fwd_mx(const moc_layout* lay, const moc_varlen* vl, const
                               float* plse, void* vt_ws, hipStream_t st);
 hipError_t launch_mx_quantize(const moc_layout* lay, const void* X, uint8_t* codes,
                               uint8_t* scales, hipStream_t st);
+hipError_t launch_mfma_probe(int fp8, int blocks, int iters, float* sink, hipStream_t st);
 hipError_t launch_attn_bwd(const moc_layout* lay, const moc_varlen* vl, const void* Q,
                            const void* K, const void* V, const void* O, const float* lse,
                            const void* dO, float scale, void* dQ, void* dK, void* dV,
@@ -459,6 +460,21 @@ moc_status moc_attend_fwd_mx(const moc_layout* lay, const moc_varlen* vl, const 
                       "quantised-scores attention forward launch");
   } catch (...) {
     return fail(MOC_EINTERNAL, "exception in moc_attend_fwd_mx");
+  }
+}
+
+moc_status moc_probe_mfma(int32_t fp8, int32_t blocks, int32_t iters, float* sink,
+                          void* stream) {
+  try {
+    if (fp8 != 0 && fp8 != 1) return fail(MOC_EINVAL, "fp8 must be 0 or 1");
+    if (blocks < 1 || blocks > 65535) return fail(MOC_EINVAL, "blocks must be in [1, 65535]");
+    if (iters < 1 || iters > 10000000) return fail(MOC_EINVAL, "iters must be in [1, 1e7]");
+    if (!sink) return fail(MOC_EINVAL, "sink is NULL");
+    return hip_status(moc_host::launch_mfma_probe(fp8, blocks, iters, sink,
+                                                  static_cast<hipStream_t>(stream)),
+                      "MFMA probe launch");
+  } catch (...) {
+    return fail(MOC_EINTERNAL, "exception in moc_probe_mfma");
   }
 }
 

@@ -232,3 +232,12 @@ def test_mx_entry_points_reject_bad_arguments(L):
                                  None) == 1                                      # unfilled varlen
     assert lib.moc_attend_fwd_mx(ctypes.byref(bf), None, p(1), p(2), p(3), p(4), p(5),
                                  ctypes.c_float(0.125), p(6), p(7), p(8), 1 << 30, None) == 1
+
+
+def test_probe_rejects_bad_arguments(L):
+    lib = L.load()
+    p = ctypes.c_void_p
+    assert lib.moc_probe_mfma(2, 1, 1, p(8), None) == 1
+    assert lib.moc_probe_mfma(0, 0, 1, p(8), None) == 1
+    assert lib.moc_probe_mfma(0, 1, 0, p(8), None) == 1
+    assert lib.moc_probe_mfma(1, 1, 1, None, None) == 1
