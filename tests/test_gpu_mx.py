@@ -114,11 +114,19 @@ def test_attend_mx_random_layouts(seed):
 
 def test_attend_mx_headline_sampled():
     """The full-size headline workload in the launch configuration the benchmark times;
-    sampled rows of three heads."""
+    sampled rows of three heads. Also reports how far quantising Q and K moves the output from
+    the unquantised attention (a change of the function, bounded loosely here, not parity)."""
     w = mi.WORKLOADS["headline"]()
     g = _mx_run(w)
     rows = [r for r in _sample_rows(w, 24) if r[1] in (0, 5, 11)]
     _compare(w, g, rows)
+    O, lse = mo.attend(g["Q"], g["K"], g["V"], w.layout, g["sel"], rows=rows)
+    got = np.stack([g["O"][b, h, t] for b, h, t in rows])
+    gl = np.array([g["lse"][b, h, t] for b, h, t in rows])
+    d_o, d_l = np.abs(got - O), np.abs(gl - lse)
+    _say(f"quantisation effect vs unquantised attention: O max {d_o.max():.3e} mean "
+         f"{d_o.mean():.3e} (|O| mean {np.abs(O).mean():.3e}); lse max {d_l.max():.3e}")
+    assert d_o.max() < 0.25 and d_l.max() < 0.5
 
 
 def test_attend_mx_deterministic():
