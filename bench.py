@@ -41,8 +41,8 @@ def parse(argv=None):
                              "headline_mx", "headline_h3"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=192,
-                    help="query rows of the oracle attention sample (one head)")
+    ap.add_argument("--cpu-rows", type=int, default=768,
+                    help="query rows of the oracle attention sample (spread over the heads)")
     ap.add_argument("--sweep", default="",
                     help="comma-separated shot counts: instead of the one-line benchmark, time "
                          "the MoC layer on n shots of 21,840 tokens (+512 text) against dense "
@@ -129,7 +129,9 @@ def copy_calibration() -> int:
 
 
 def cpu_baseline(w, Q, K, V, rows_n: int):
-    """The oracle timed on a bounded sample of the same workload, extrapolated linearly."""
+    """The oracle timed on a bounded sample of the same workload: pooling and routing in full
+    (every head), attention on a seeded sample of query rows spread over the heads, extrapolated
+    linearly to every row."""
     import numpy as np
     from oracle import moc_oracle as mo
     try:
@@ -137,33 +139,33 @@ def cpu_baseline(w, Q, K, V, rows_n: int):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         threads = 1
-    hs = min(2, w.H)
     t0 = time.perf_counter()
-    kb = mo.pool_keys(K[:, :hs], w.layout)
+    kb = mo.pool_keys(K, w.layout)
     t_pool = time.perf_counter() - t0
     t0 = time.perf_counter()
     cmask = None
     if w.segments is not None:
-        cmask = mo.route_outer(Q[:, :hs], K[:, :hs], w.layout, w.segments, w.outer_M,
-                               w.causal).cand_mask
-    r = mo.route(Q[:, :hs], kb, w.layout, w.top_k, w.causal, cand_mask=cmask)
+        cmask = mo.route_outer(Q, K, w.layout, w.segments, w.outer_M, w.causal).cand_mask
+    r = mo.route(Q, kb, w.layout, w.top_k, w.causal, cand_mask=cmask)
     t_route = time.perf_counter() - t0
     rng = np.random.default_rng(w.seed)
-    ts = sorted(rng.choice(w.L, size=min(rows_n, w.L), replace=False).tolist())
-    rows = [(0, 0, int(t)) for t in ts]
+    n = min(rows_n, w.B * w.H * w.L)
+    flat = np.sort(rng.choice(w.B * w.H * w.L, size=n, replace=False))
+    rows = [(int(i // (w.H * w.L)), int(i // w.L % w.H), int(i % w.L)) for i in flat]
     t0 = time.perf_counter()
     att = mo.attend_mx if w.mx_scores else mo.attend
-    att(Q[:, :1], K[:, :1], V[:, :1], w.layout, r.sel[:, :1], rows=rows)
+    att(Q, K, V, w.layout, r.sel, rows=rows)
     t_att = time.perf_counter() - t0
     measured = t_pool + t_route + t_att
-    full = (t_pool + t_route) * (w.B * w.H / (w.B * hs)) + t_att * (w.B * w.H * w.L / len(rows))
-    pairs = int(mo.pair_counts(w.layout, r.sel[:, :1])[0, 0]) * w.B * w.H
+    full = t_pool + t_route + t_att * (w.B * w.H * w.L / len(rows))
+    pairs = int(mo.pair_counts(w.layout, r.sel).sum())
     flops = 4 * w.d * pairs
     return {
         "value": flops / full / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-        "sample": (f"fp64 numpy oracle: pool+route on {hs} of {w.H} heads, attention on "
-                   f"{len(rows)} query rows of head 0; measured {measured:.1f} s, extrapolated "
-                   f"linearly to the full layer = {full:.1f} s"),
+        "sample": (f"fp64 numpy oracle: pool and route on all {w.B * w.H} heads, attention on "
+                   f"{len(rows)} seeded query rows across the heads; measured {measured:.1f} s "
+                   f"(pool {t_pool:.1f}, route {t_route:.1f}, attention {t_att:.1f}), "
+                   f"extrapolated linearly to all {w.B * w.H * w.L} rows = {full:.1f} s"),
         "measured_s": measured, "extrapolated_full_layer_s": full,
     }
 
