@@ -19,8 +19,9 @@
 // owns one query), 8 waves x 32 queries per workgroup, 64-key tiles, lazy rescaling of the
 // running max (only when it grows by more than 2^8). The bf16 kernel runs its two wave groups
 // half a tile apart so that one group's MFMAs overlap the other group's softmax, with K and
-// V^T tiles copied global -> LDS without registers (attn_fwd_lds.h); the fp32 kernel stages
-// tiles through registers into a double-buffered LDS ring.
+// V^T tiles copied global -> LDS without registers into four rotating stages (attn_fwd_lds.h);
+// with MXFP8 codes for Q and K (quantised scores) S runs on the block-scaled fp8 MFMA. The fp32
+// kernel stages tiles through registers into a double-buffered LDS ring.
 #include <type_traits>
 
 #include "attn_common.h"
@@ -290,7 +291,8 @@ __global__ __launch_bounds__(kNT) void attn_fwd_kernel(
 
 // bf16 attention forward: same work decomposition and epilogue as attn_fwd_kernel; two wave
 // groups half a tile apart, K and V^T tiles staged by direct-to-LDS copies into padded
-// 64-key-aligned tiles (three skewed stages) and the permuted key order of attn_fwd_lds.h.
+// 64-key-aligned tiles (four rotating stages) and the permuted key order of attn_fwd_lds.h.
+// MX: Q and K are MXFP8 codes and scales (rows padded to Lp), S on the block-scaled fp8 MFMA.
 template <int D, int MODE, bool MX>
 __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
     const void* __restrict__ Qv, const void* __restrict__ Kv, const uint8_t* __restrict__ Qs,
