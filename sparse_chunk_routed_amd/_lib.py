@@ -5,6 +5,8 @@ import ctypes
 import os
 from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_uint64, c_void_p
 
+# The in-tree build; MOC_LIB_PATH may name another build of the same library (to compare kernel
+# variants of one source tree). There is no fallback of any kind when the library is missing.
 LIB_PATH = os.environ.get("MOC_LIB_PATH") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "libmoc.so")
 
