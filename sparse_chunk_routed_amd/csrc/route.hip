@@ -472,12 +472,17 @@ __global__ __launch_bounds__(64 * NW) void route_mfma_persist_kernel(
     const size_t per = static_cast<size_t>(C) * D;
     const bf16_t* sp = split + static_cast<size_t>(bh) * 3 * per;
     constexpr int VPR = D / 8;  // 16-byte vectors per row
-    for (int v = threadIdx.x; v < 3 * C * VPR; v += blockDim.x) {
-      const int term = v / (C * VPR);
-      const int rem = v % (C * VPR);
+    // LDS rows [chunk][term]: a wave's reads of one 32-chunk block are one base address plus
+    // immediate offsets; rows of chunks C..kRouteCB-1 are zero, so that their (masked) scores
+    // stay finite
+    for (int v = threadIdx.x; v < 3 * kRouteCB * VPR; v += blockDim.x) {
+      const int term = v / (kRouteCB * VPR);
+      const int rem = v % (kRouteCB * VPR);
       const int c = rem / VPR, col = rem % VPR;
-      *reinterpret_cast<u32x4*>(ks + (term * kRouteCB + c) * KSTR + col * 8) =
-          *reinterpret_cast<const u32x4*>(sp + term * per + static_cast<size_t>(c) * D + col * 8);
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (c < C)
+        x = *reinterpret_cast<const u32x4*>(sp + term * per + static_cast<size_t>(c) * D + col * 8);
+      *reinterpret_cast<u32x4*>(ks + (c * 3 + term) * KSTR + col * 8) = x;
     }
   }
   __syncthreads();
@@ -546,17 +551,29 @@ __global__ __launch_bounds__(64 * NW) void route_mfma_persist_kernel(
     for (int i = 0; i < KMAX; ++i) tk[i] = static_cast<int>(0x80000000u);
     for (int b32 = 0; b32 < C; b32 += 32) {
       if (b32 >= c_wave) break;  // wave-uniform: no candidate of this wave beyond here
+      // Candidates outside the allowed set start from -inf, so their score stays -inf and its
+      // key ranks below every finite score (above the empty slot); finish_query keeps only
+      // the first min(k, #allowed) keys, which are then all allowed. A block allowed for the
+      // whole wave skips this.
+      const uint32_t okb = okw[b32 >> 5] >> (4 * g);  // bit 8 j + r: chunk b32 + 8 j + 4 g + r
       f32x16 acc = {};
+      if (__builtin_amdgcn_ballot_w64((okb & 0x0f0f0f0fu) != 0x0f0f0f0fu) != 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = __builtin_amdgcn_sbfe(static_cast<int>(okb), 8 * (i >> 2) + (i & 3), 1);
+          acc[i] = __int_as_float(~m & static_cast<int>(0xff800000u));
+        }
+      }
+      const bf16_t* kr = ks + (b32 + ql) * 3 * KSTR + 8 * g;
 #pragma unroll
       for (int term = 0; term < 3; ++term) {
-        const bf16_t* kr = ks + (term * kRouteCB + b32 + ql) * KSTR + 8 * g;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kr + 16 * kk));
+          const bf16x8 a = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(kr + term * KSTR + 16 * kk));
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf.q[kk], acc, 0, 0, 0);
         }
       }
-      const uint32_t okb = okw[b32 >> 5] >> (4 * g);  // bit 8 j + r: chunk b32 + 8 j + 4 g + r
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int c = b32 + 8 * (i >> 2) + 4 * g + (i & 3);
@@ -564,7 +581,6 @@ __global__ __launch_bounds__(64 * NW) void route_mfma_persist_kernel(
         const int bits = __float_as_int(sc);
         int key = bits ^ ((bits >> 31) & 0x7fffffff);
         key = (key & ~127) | (127 - c);
-        key = ((okb >> (8 * (i >> 2) + (i & 3))) & 1u) ? key : static_cast<int>(0x80000000u);
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
           const int hi = key > tk[k] ? key : tk[k];
