@@ -10,8 +10,8 @@ frame-aligned video chunks grouped into shots (Mixture of Contexts summary, §3.
 Chunking and Routing"; §4 "Experiments": 8 shots x 8 s, 480p, 12 fps, about 180k tokens), and a
 latent frame of 30 x 52 = 1,560 patches. The actual LCT activations are not available, so seeded
 normal tensors stand in for them; keys are clustered per chunk so that chunk descriptors differ
-(the pages argue tokens of one chunk are highly redundant, jxzklqfsx.com write-up, section
-"實驗 / 定性結果").
+(the jxzklqfsx.com write-up, section "實驗 / 定性結果", notes that the tokens of one chunk are
+highly redundant).
 
 Random streams (numpy.random.default_rng): layout=seed, Q=seed+1, K centres=seed+2,
 K noise=seed+3, V=seed+4, dO=seed+5. Tensors are drawn in fp32 and rounded to bf16 with

@@ -2,7 +2,7 @@
 //
 // Source: "Mixture of Contexts for Long Video Generation | Summary" §3.1 and Appendix A (top-k is
 // a discrete, non-differentiable choice; gradients reach the keys/values that were selected,
-// and the pages' implementation wraps the attention in a custom autograd function).
+// and the summarised implementation wraps the attention in a custom autograd function).
 //
 // For every attended pair (t, j), with x_tj = scale q_t.k_j and P_tj = exp(x_tj - lse_t):
 //   dV_j += P_tj dO_t;  dP_tj = dO_t.v_j;  dS_tj = P_tj (dP_tj - D_t) with D_t = dO_t.O_t;

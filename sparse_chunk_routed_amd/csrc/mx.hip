@@ -1,8 +1,8 @@
 // MXFP8 quantisation of Q or K rows for the quantised-scores attention.
 //
-// Source: the pages list quantisation among the directions for faster kernels ("Mixture of
-// Contexts for Long Video Generation | Summary" §5 Conclusion; jxzklqfsx.com write-up, 結論;
-// docswell slides, slide 21) without fixing a format. The format here is OCP Microscaling
+// Source: "Mixture of Contexts for Long Video Generation | Summary" §5 Conclusion, the
+// jxzklqfsx.com write-up (section 結論) and the docswell slides (slide 21) name quantisation
+// among the directions for faster kernels, without fixing a format. The format here is OCP Microscaling
 // MXFP8: E4M3 elements (OCP OFP8: bias 7, largest finite 448) and per block of 32 consecutive
 // elements of a row one E8M0 scale 2^E with E = floor(log2(max |x|)) - 8, clamped below at
 // -127. An element is x * 2^-E (exact: a power-of-two scaling of a bf16 value) rounded to the
