@@ -1,4 +1,4 @@
-"""The layer's entry points enqueue kernels only (no memset, copy or synchronisation), so a whole
+"""Graph capture and the autograd wrapper. The layer's entry points enqueue kernels only (no memset, copy or synchronisation), so a whole
 step - pool, route, inversion, attention forward, and the backward - can be captured in one HIP
 graph. Each replay must equal the eager result bit for bit, with eager work and synchronisation
 between the replays and new inputs written into the captured buffers."""
@@ -52,3 +52,32 @@ def test_layer_step_replays_equal_eager():
         for name, a, b in zip(("sel", "O", "lse", "dQ", "dK", "dV"), outs, ref):
             assert torch.equal(a, b), (r, name)
         _say(f"replay {r}: sel, O, lse, dQ, dK, dV equal the eager step")
+
+
+def test_autograd_function_matches_entry_points_and_oracle():
+    """MoCAttention (torch.autograd.Function): the forward is moc_attend_fwd over the routed
+    sets, the gradients are moc_attend_bwd's (bit for bit) and match the oracle's backward."""
+    import numpy as np
+    import sparse_chunk_routed_amd as moc
+    from oracle import moc_oracle as mo
+    dev = torch.device("cuda:0")
+    w = mi.grad_slice()
+    Q, K, V, dO = mi.make_qkv(w, with_dout=True)
+    lay = moc.DeviceLayout.from_layout(w.layout, dev)
+    cfg = moc.RouteCfg(w.top_k, w.causal, w.p_max, w.lam, w.max_drop_in, w.seed)
+    Qd, Kd, Vd = (x.to(dev).requires_grad_(True) for x in (Q, K, V))
+    O = moc.MoCAttention.apply(Qd, Kd, Vd, lay, cfg)
+    O.backward(dO.to(dev))
+    r = moc.forward(Qd.detach(), Kd.detach(), Vd.detach(), lay, cfg)
+    gq, gk, gv = moc.attend_bwd(Qd.detach(), Kd.detach(), Vd.detach(), r.O, r.lse, dO.to(dev),
+                                lay, r.varlen)
+    torch.cuda.synchronize()
+    assert torch.equal(O.detach(), r.O)
+    for a, b in ((Qd.grad, gq), (Kd.grad, gk), (Vd.grad, gv)):
+        assert torch.equal(a, b)
+    sel = r.sel.cpu().numpy()
+    rq, rk, rv = mo.attend_bwd(Q, K, V, dO, w.layout, sel)
+    for name, a, b in (("dQ", Qd.grad, rq), ("dK", Kd.grad, rk), ("dV", Vd.grad, rv)):
+        err = float(np.max(np.abs(a.float().cpu().numpy() - b)))
+        _say(f"autograd {name}: max|err| vs oracle {err:.3e}")
+        assert err <= 1e-2
