@@ -1,7 +1,10 @@
-"""Graph capture and the autograd wrapper. The layer's entry points enqueue kernels only (no memset, copy or synchronisation), so a whole
+"""Graph capture and the autograd wrapper.
+
+The layer's entry points enqueue kernels only (no memset, copy or synchronisation), so a whole
 step - pool, route, inversion, attention forward, and the backward - can be captured in one HIP
 graph. Each replay must equal the eager result bit for bit, with eager work and synchronisation
-between the replays and new inputs written into the captured buffers."""
+between the replays and new inputs written into the captured buffers. The autograd wrapper must
+give moc_attend_bwd's gradients."""
 import pytest
 import torch
 
