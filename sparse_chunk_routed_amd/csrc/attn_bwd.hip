@@ -37,6 +37,7 @@ constexpr int kBwdKNT = 64 * kBwdKNW;
 constexpr int kBwdKR = 32 * kBwdKNW;       // keys per key tile
 constexpr int kBwdQT = 32;                 // queries per dkdv step
 constexpr int kTextSplitRows = 16384;      // queries per text-key split
+constexpr int kDkdvAhead = 3;              // dkdv: LDS operand reads in flight per MFMA sequence
 
 struct BwdParams {
   int B, H, L, C, S, max_tiles;
@@ -427,14 +428,16 @@ __global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_kernel(
     __builtin_amdgcn_sched_barrier(0);
   };
   const int rq = QTl::RROW * kperm(ql) + g;  // permuted row of this lane's A operand (chunks)
-  // operand reads of an MFMA sequence run one ahead of their MFMAs (bounded registers)
+  // the operand reads of an MFMA sequence run kDkdvAhead ahead of their MFMAs: an LDS read
+  // takes longer than one MFMA, so fewer in flight leave every MFMA waiting on its operand
+  // (and more do not fit the 256 registers)
   auto pace = [&](int nm) __attribute__((always_inline)) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    for (int i = 0; i < nm - 1; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, kDkdvAhead, 0);
+    for (int i = 0; i < nm - kDkdvAhead; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kDkdvAhead, 0);
   };
   // One 32-query tile, in the order S -> P -> dV, dP -> dS -> dK, so that at most one 32x32
   // score block and one packed block are live next to the accumulators (dS uses the packed P).
