@@ -444,6 +444,8 @@ __global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_kernel(
   auto tile = [&](int j, const char* cur) __attribute__((always_inline)) {
     const char* qr = cur + QTl::Q_OFF + rq * 16;
     const char* orr = cur + QTl::DO_OFF + rq * 16;
+    // this lane's column of the transposed tiles: the (ks, db) operands are immediate offsets
+    const char* tr = cur + (QTl::TROW * ql + g) * 16;
     const float* stl = reinterpret_cast<const float*>(cur + QTl::ST_OFF);
     const int qbase = qbase0 + 32 * j;
     const bool partial = j < nqt && (qbase < qa || qbase + 32 > qb);
@@ -485,9 +487,8 @@ __global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_kernel(
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const int toff = (QTl::TROW * (db * 32 + ql) + 2 * ks + g) * 16;
-        const bf16x8 bo =
-            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(cur + QTl::DOT_OFF + toff));
+        const bf16x8 bo = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(tr + QTl::DOT_OFF + (QTl::TROW * 32 * db + 2 * ks) * 16));
         accV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], bo, accV[db], 0, 0, 0);
       }
     pace(2 * (D / 32));
@@ -517,9 +518,8 @@ __global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_kernel(
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const int toff = (QTl::TROW * (db * 32 + ql) + 2 * ks + g) * 16;
-        const bf16x8 bq =
-            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(cur + QTl::QT_OFF + toff));
+        const bf16x8 bq = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(tr + QTl::QT_OFF + (QTl::TROW * 32 * db + 2 * ks) * 16));
         accK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ks], bq, accK[db], 0, 0, 0);
       }
     pace(2 * (D / 32));
