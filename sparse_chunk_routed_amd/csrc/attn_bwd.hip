@@ -37,6 +37,7 @@ constexpr int kBwdKNT = 64 * kBwdKNW;
 constexpr int kBwdKR = 32 * kBwdKNW;       // keys per key tile
 constexpr int kBwdQT = 32;                 // queries per dkdv step
 constexpr int kTextSplitRows = 16384;      // queries per text-key split
+constexpr int kDqAhead = 3;                // dq: LDS operand reads in flight per MFMA sequence
 constexpr int kDkdvAhead = 3;              // dkdv: LDS operand reads in flight per MFMA sequence
 
 struct BwdParams {
@@ -193,15 +194,15 @@ __global__ __launch_bounds__(kBwdQNT) void bwd_dq_kernel(
     // forward stage whose K tile starts one row tile later
     pv_swz_packed<D>(st + LT::KBYTES, dsb, acc, ql, g);
     sdp(st);
-    // operand reads run two ahead of their MFMAs (bounded registers)
+    // operand reads run kDqAhead ahead of their MFMAs (bounded registers)
     constexpr int NM = 4 * (D / 32) + 4 * (D / 16);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, kDqAhead, 0);
 #pragma unroll
-    for (int i = 0; i < NM - 2; ++i) {
+    for (int i = 0; i < NM - kDqAhead; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kDqAhead, 0);
   };
   auto mfma_last = [&]() __attribute__((always_inline)) {
     const int rl = ntot % 3;

@@ -428,19 +428,19 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
   auto mfma_full = [&](const char* stp, const char* stc) __attribute__((always_inline)) {
     pv_swz_packed<D, VOFF, kPre>(stp, pb, acc, ql, g, pre);
     scores(stc);
-    // operand reads run kReadAhead ahead of the MFMAs that use them (bounded registers)
+    // operand reads run kReadAhead ahead of the MFMAs that use them, all the way to the last
+    // MFMA (bounded registers; an even spread of the reads over the MFMAs fell behind the
+    // last ones, which then each waited for their operand)
     if constexpr (MX) {
       // P.V: one read per MFMA (less the preloaded ones); S: two code reads per MFMA and two
       // scale reads per tile
       constexpr int NM = 4 * (D / 32) + 2 * (D / 64);
       constexpr int NR = 4 * (D / 32) - kPre + 4 * (D / 64) + 2;
-      __builtin_amdgcn_sched_group_barrier(0x100, kReadAhead, 0);
-      sched_spread_reads<NR - kReadAhead, NM>();
+      sched_lead_reads<NM, NR, kReadAhead, 4 * (D / 32), kPre, 2, 2>();
     } else {
       constexpr int NM = 4 * (D / 32) + 2 * (D / 16);
       constexpr int NR = NM - kPre;
-      __builtin_amdgcn_sched_group_barrier(0x100, kReadAhead, 0);
-      sched_spread_reads<NR - kReadAhead, NM>();
+      sched_lead_reads<NM, NR, kReadAhead, 4 * (D / 32), kPre, 0, 1>();
     }
   };
   // last MFMA half-step: O += V P of the last tile

@@ -378,14 +378,26 @@ __device__ __forceinline__ void score_tile_mx(const char* stage, const MxQFrag<D
   }
 }
 
-// sched_group_barrier pattern: after each of NM MFMAs, an even share of NR operand reads
-template <int NR, int NM, int I = 0>
-__device__ __forceinline__ void sched_spread_reads() {
+// Operand reads consumed up to and including MFMA i of an MFMA half-step: NPV P.V MFMAs, the
+// first NPRE of them on preloaded operands and the others one read each, then the score MFMAs,
+// SFIRST reads before the first of them and SREADS per MFMA.
+constexpr int half_step_reads(int i, int npv, int npre, int sfirst, int sreads) {
+  return i < npv ? (i - npre + 1 > 0 ? i - npre + 1 : 0)
+                 : (npv - npre) + sfirst + sreads * (i - npv + 1);
+}
+
+// sched_group_barrier pattern that keeps the reads A ahead of the MFMAs that consume them: before
+// MFMA i, the reads of MFMAs up to i plus A more are issued (all NR at the end).
+template <int NM, int NR, int A, int NPV, int NPRE, int SFIRST, int SREADS, int I = 0>
+__device__ __forceinline__ void sched_lead_reads() {
   if constexpr (I < NM) {
-    constexpr int n = (NR * (I + 1)) / NM - (NR * I) / NM;
+    constexpr int want = half_step_reads(I, NPV, NPRE, SFIRST, SREADS) + A;
+    constexpr int prev_want = I == 0 ? 0 : half_step_reads(I - 1, NPV, NPRE, SFIRST, SREADS) + A;
+    constexpr int cur = want < NR ? want : NR;
+    constexpr int prev = prev_want < NR ? prev_want : NR;
+    if constexpr (cur > prev) __builtin_amdgcn_sched_group_barrier(0x100, cur - prev, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, 0);
-    sched_spread_reads<NR, NM, I + 1>();
+    sched_lead_reads<NM, NR, A, NPV, NPRE, SFIRST, SREADS, I + 1>();
   }
 }
 
