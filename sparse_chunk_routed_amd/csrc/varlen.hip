@@ -232,19 +232,15 @@ __global__ __launch_bounds__(1024) void inv_global_kernel(
     }
   }
   __syncthreads();
-  // pair counts: anchor pairs + routed chunk sizes
-  for (int bh = 0; bh < p.B * p.H; ++bh) {
-    int64_t s = 0;
-    for (int c = threadIdx.x; c < p.C; c += blockDim.x)
-      s += static_cast<int64_t>(totals[bh * p.C + c]) * (off[c + 1] - off[c]);
-    part[threadIdx.x] = s;
-    __syncthreads();
-    for (int w = blockDim.x / 2; w > 0; w >>= 1) {
-      if (static_cast<int>(threadIdx.x) < w) part[threadIdx.x] += part[threadIdx.x + w];
-      __syncthreads();
-    }
-    if (threadIdx.x == 0) pair_count[bh] = s_anchor + part[0];
-    __syncthreads();
+  // pair counts: anchor pairs + routed chunk sizes, one wave per (b, h) (integer sums: exact in
+  // any order)
+  const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  for (int bh = threadIdx.x >> 6; bh < p.B * p.H; bh += nw) {
+    long long s = 0;
+    for (int c = lane; c < p.C; c += 64)
+      s += static_cast<long long>(totals[bh * p.C + c]) * (off[c + 1] - off[c]);
+    for (int w = 32; w > 0; w >>= 1) s += __shfl_xor(s, w);
+    if (lane == 0) pair_count[bh] = s_anchor + s;
   }
 }
 
