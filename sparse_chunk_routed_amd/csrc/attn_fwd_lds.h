@@ -390,6 +390,8 @@ constexpr int half_step_reads(int i, int npv, int npre, int sfirst, int sreads) 
 // MFMA i, the reads of MFMAs up to i plus A more are issued (all NR at the end).
 template <int NM, int NR, int A, int NPV, int NPRE, int SFIRST, int SREADS, int I = 0>
 __device__ __forceinline__ void sched_lead_reads() {
+  static_assert(half_step_reads(NM - 1, NPV, NPRE, SFIRST, SREADS) == NR,
+                "the read count of the half-step does not match its MFMAs");
   if constexpr (I < NM) {
     constexpr int want = half_step_reads(I, NPV, NPRE, SFIRST, SREADS) + A;
     constexpr int prev_want = I == 0 ? 0 : half_step_reads(I - 1, NPV, NPRE, SFIRST, SREADS) + A;
