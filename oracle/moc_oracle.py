@@ -371,16 +371,42 @@ def attend_bwd(Q, K, V, dO, layout, sel, scale: Optional[float] = None):
             Kbh, Vbh = K[b, h], V[b, h]
             for t in range(L):
                 keys = key_set(D, t, sel[b, h, t])
-                x = (Kbh[keys] @ Q[b, h, t]) * scale
-                p = np.exp(x - np.max(x))
-                p /= np.sum(p)
-                g = dO[b, h, t]
-                dV[b, h, keys] += np.outer(p, g)
-                dp = Vbh[keys] @ g
-                ds = p * (dp - np.dot(p, dp))
+                p, ds = _bwd_row(Q[b, h, t], Kbh, Vbh, dO[b, h, t], keys, scale)
+                dV[b, h, keys] += np.outer(p, dO[b, h, t])
                 dQ[b, h, t] = scale * (ds @ Kbh[keys])
                 dK[b, h, keys] += scale * np.outer(ds, Q[b, h, t])
     return dQ, dK, dV
+
+
+def _bwd_row(q, Kbh, Vbh, g, keys, scale):
+    """P and dS of one query over its key set (the steps of attend_bwd for one row)."""
+    x = (Kbh[keys] @ q) * scale
+    p = np.exp(x - np.max(x))
+    p /= np.sum(p)
+    dp = Vbh[keys] @ g
+    ds = p * (dp - np.dot(p, dp))
+    return p, ds
+
+
+def attend_bwd_dq_rows(Q, K, V, dO, layout, sel, rows: Sequence[Tuple[int, int, int]],
+                       scale: Optional[float] = None) -> np.ndarray:
+    """dQ of attend_bwd for the listed (b, h, t) rows only ([n, d]): a query's gradient
+    depends on its own key set alone, so sampled rows of a large input cost one row each."""
+    D = derive(layout)
+    d = Q.shape[-1]  # NumPy array or torch tensor (bf16 included)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    sel = np.asarray(sel)
+    out = np.zeros((len(rows), d))
+    heads = {}
+    for i, (b, h, t) in enumerate(rows):
+        if (b, h) not in heads:  # one fp64 copy of K and V per head
+            heads = {(b, h): (_as_f64(K[b, h]), _as_f64(V[b, h]))}
+        Kbh, Vbh = heads[(b, h)]
+        keys = key_set(D, t, sel[b, h, t])
+        _, ds = _bwd_row(_as_f64(Q[b, h, t]), Kbh, Vbh, _as_f64(dO[b, h, t]), keys, scale)
+        out[i] = scale * (ds @ Kbh[keys])
+    return out
 
 
 # ---------------------------------------------------------------------------------------------

@@ -112,3 +112,45 @@ def test_noise_headline_sampled():
             n_ex += 1
     _say(f"headline noise: {len(rows)} rows, {n_ex} tie-exempt differences")
     assert np.array_equal(g["pairs"], mo.pair_counts(w.layout, g["sel"]))
+
+
+def test_backward_headline_sampled():
+    """The backward at full size: the train workload (175,232 tokens, 12 heads, routing noise)
+    that the train benchmark times.
+    * dQ on sampled rows of every head against the oracle, over the oracle's own routing plus
+      noise (rows whose selection is a near-tie exemption are skipped).
+    * Over every key of every head, sum_j dV_j = sum_t dO_t: each query's softmax sums to one.
+      The expected value comes from the inputs. The kernel rounds P to bf16 before the dV
+      MFMAs, so a query's P sums to one within 2^-9 at worst (a fully concentrated row). Against
+      standard-normal dO, the error of sum_t eps_t dO_t then has a standard deviation of at most
+      2^-9 sqrt(L). The tolerance is 4 of those, 2^-7 sqrt(L) (about 3.3, with a signal of about
+      sqrt(L) = 418). Losing a tenth of the attention mass would move the sum by about 40."""
+    w = mi.train()
+    g = _run(w, backward=True)
+    kb = mo.pool_keys(g["K"], w.layout)
+    r = mo.route(g["Q"], kb, w.layout, w.top_k, w.causal)
+    rng = np.random.default_rng(7)
+    rows = [(0, h, int(t)) for h in range(w.H) for t in rng.choice(w.L, 6, replace=False)]
+    sel, _ = mo.drop_noise(r, w.layout, w.causal, w.p_max, w.lam, w.max_drop_in, w.seed,
+                           rows=rows)
+    use = []
+    for row in rows:
+        if list(g["sel"][row]) == list(sel[row]):
+            use.append(row)
+        else:
+            assert r.gap_exempt[row], (row, list(g["sel"][row]), list(sel[row]))
+    ref = mo.attend_bwd_dq_rows(g["Q"], g["K"], g["V"], g["dO"], w.layout, sel, use)
+    got = np.stack([g["dQ"][row] for row in use])
+    err = float(np.max(np.abs(got - ref)))
+    _say(f"dQ rows={len(use)} of {len(rows)}: max|err|={err:.3e} "
+         f"(max|ref|={np.max(np.abs(ref)):.3e})")
+    assert len(use) >= len(rows) // 2
+    assert err <= TOL, err
+    dv_sum = g["dV"].astype(np.float64).sum(axis=2)
+    do_sum = g["dO"].double().sum(dim=2).numpy()
+    derr = float(np.max(np.abs(dv_sum - do_sum)))
+    tol = 2.0 ** -7 * np.sqrt(w.L)
+    _say(f"sum_j dV_j vs sum_t dO_t: max|diff|={derr:.3e} (tol {tol:.2f}, "
+         f"max|sum dO|={np.max(np.abs(do_sum)):.1f})")
+    assert derr <= tol, derr
+

@@ -110,6 +110,23 @@ def test_masked_sdpa_equivalence_random_layouts(seed):
     assert np.max(np.abs(dQ - q.grad.numpy())) < 1e-11
     assert np.max(np.abs(dK - k.grad.numpy())) < 1e-11
     assert np.max(np.abs(dV - v.grad.numpy())) < 1e-11
+    # dQ of single rows (what the full-size GPU test samples) against the same SDPA gradient
+    rows = [(b, h, int(t)) for b in range(B) for h in range(H)
+            for t in rng.choice(lay.L, size=min(5, lay.L), replace=False)]
+    dq_rows = mo.attend_bwd_dq_rows(Q, K, V, dO, lay, r.sel, rows, scale=scale)
+    want = np.stack([q.grad.numpy()[row] for row in rows])
+    assert np.max(np.abs(dq_rows - want)) < 1e-11
+    # the same rows from bf16 torch tensors (the GPU tests' inputs) equal the rows computed from
+    # the bf16 values in fp64
+    tb = [torch.tensor(x).to(torch.bfloat16) for x in (Q, K, V, dO)]
+    fb = [x.double().numpy() for x in tb]
+    a = mo.attend_bwd_dq_rows(*tb, lay, r.sel, rows, scale=scale)
+    b = mo.attend_bwd_dq_rows(*fb, lay, r.sel, rows, scale=scale)
+    assert np.array_equal(a, b)
+    # every softmax row sums to one and every dS row to zero, so over all keys
+    # sum_j dV_j = sum_t dO_t and sum_j dK_j = 0 (per b, h and dimension)
+    assert np.max(np.abs(dV.sum(axis=2) - dO.sum(axis=2))) < 1e-11
+    assert np.max(np.abs(dK.sum(axis=2))) < 1e-11
     # anchors are always inside Omega (spec: text + own shot always present)
     D = mo.derive(lay)
     for t in range(lay.L):
