@@ -127,6 +127,10 @@ def test_masked_sdpa_equivalence_random_layouts(seed):
     # sum_j dV_j = sum_t dO_t and sum_j dK_j = 0 (per b, h and dimension)
     assert np.max(np.abs(dV.sum(axis=2) - dO.sum(axis=2))) < 1e-11
     assert np.max(np.abs(dK.sum(axis=2))) < 1e-11
+    # both sides are scale * sum over pairs of dS_tj (q_t . k_j): sum_t q_t.dQ_t = sum_j k_j.dK_j
+    lhs = np.einsum("bhtd,bhtd->bh", Q, dQ)
+    rhs = np.einsum("bhtd,bhtd->bh", K, dK)
+    assert np.max(np.abs(lhs - rhs)) < 1e-11
     # anchors are always inside Omega (spec: text + own shot always present)
     D = mo.derive(lay)
     for t in range(lay.L):
