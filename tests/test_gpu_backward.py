@@ -79,14 +79,15 @@ def test_noise_and_backward_slice(k):
     _check_grads(w, g)
 
 
-@pytest.mark.parametrize("seed", range(3))
+@pytest.mark.parametrize("seed", range(6))
 def test_backward_random_layouts(seed):
     rng = np.random.default_rng(500 + seed)
     lay = mi.make_random_layout(rng, max_shots=4, max_frames=3, max_chunk=200,
-                                frame_is_shot=(seed == 2))
-    w = mi.Workload(f"bwd{seed}", 2, 2, [64, 128, 64][seed], "bf16", lay,
-                    top_k=[1, 3, 2][seed], causal=bool(seed != 1), clustered_keys=True,
-                    p_max=[0.0, 0.5, 0.3][seed], lam=[0.0, 2.0, 1.0][seed], seed=seed)
+                                frame_is_shot=seed in (2, 5))
+    w = mi.Workload(f"bwd{seed}", 2, 2, [64, 128, 64, 128, 64, 128][seed], "bf16", lay,
+                    top_k=min(lay.C, [1, 3, 2, 0, 4, 2][seed]), causal=seed not in (1, 4),
+                    clustered_keys=True, p_max=[0.0, 0.5, 0.3, 0.2, 0.0, 0.4][seed],
+                    lam=[0.0, 2.0, 1.0, 0.5, 1.5, 0.0][seed], seed=seed)
     g = _run(w, backward=True)
     _check_noise(w, g)
     _check_grads(w, g)

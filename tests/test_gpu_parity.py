@@ -209,18 +209,18 @@ def test_dense_equivalence_tiny():
         assert err <= TOL["f32"]
 
 
-@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("seed", range(8))
 def test_random_layouts(seed):
     """Irregular chunk sizes, text first/last/absent, frame-is-shot, B=2, both head sizes,
     both dtypes, causal on/off, k from 0 to all."""
     rng = np.random.default_rng(1000 + seed)
     lay = mi.make_random_layout(rng, max_shots=5, max_frames=4, max_chunk=300,
-                                frame_is_shot=(seed == 3))
+                                frame_is_shot=seed in (3, 7))
     dtype = "bf16" if seed % 2 else "f32"
-    d = 128 if seed in (1, 2) else 64
-    top_k = [0, 1, 3, lay.C][seed]
-    w = mi.Workload(f"rand{seed}", 2, 2, d, dtype, lay, top_k=top_k, causal=bool(seed != 2),
-                    clustered_keys=bool(seed % 2), seed=seed)
+    d = 128 if seed in (1, 2, 5, 6) else 64
+    top_k = min(lay.C, [0, 1, 3, lay.C, 2, 5, lay.C - 1, 4][seed])
+    w = mi.Workload(f"rand{seed}", 2, 2, d, dtype, lay, top_k=top_k,
+                    causal=seed not in (2, 6), clustered_keys=bool(seed % 2), seed=seed)
     run = Run(w)
     kb = mo.pool_keys(run.K, lay)
     assert np.array_equal(run.h_kbar.view(np.uint32), kb.view(np.uint32))
