@@ -488,8 +488,8 @@ __global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_kernel(
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const bf16x8 bo = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(tr + QTl::DOT_OFF + (QTl::TROW * 32 * db + 2 * ks) * 16));
+        const int toff = QTl::DOT_OFF + (QTl::TROW * 32 * db + 2 * ks) * 16;  // compile-time
+        const bf16x8 bo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tr + toff));
         accV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], bo, accV[db], 0, 0, 0);
       }
     pace(2 * (D / 32));
@@ -519,8 +519,8 @@ __global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_kernel(
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const bf16x8 bq = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(tr + QTl::QT_OFF + (QTl::TROW * 32 * db + 2 * ks) * 16));
+        const int toff = QTl::QT_OFF + (QTl::TROW * 32 * db + 2 * ks) * 16;  // compile-time
+        const bf16x8 bq = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tr + toff));
         accK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ks], bq, accK[db], 0, 0, 0);
       }
     pace(2 * (D / 32));
