@@ -100,14 +100,17 @@ def test_attend_mx_slice():
     _compare(w, _mx_run(w))
 
 
-@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("seed", range(5))
 def test_attend_mx_random_layouts(seed):
-    """Irregular chunks, B = 2, both head sizes, causal on and off, ragged L (L % 64 != 0)."""
+    """Irregular chunks, B = 2, both head sizes, causal on and off, k from 0 to all, frame-is-
+    shot, ragged L (L % 64 != 0)."""
     rng = np.random.default_rng(2000 + seed)
-    lay = mi.make_random_layout(rng, max_shots=5, max_frames=4, max_chunk=300)
-    d = 64 if seed == 0 else 128
-    w = mi.Workload(f"mxrand{seed}", 2, 2, d, "bf16", lay, top_k=[1, 3][seed],
-                    causal=bool(seed == 0), clustered_keys=True, seed=seed)
+    lay = mi.make_random_layout(rng, max_shots=5, max_frames=4, max_chunk=300,
+                                frame_is_shot=(seed == 3))
+    d = 64 if seed in (0, 2) else 128
+    w = mi.Workload(f"mxrand{seed}", 2, 2, d, "bf16", lay,
+                    top_k=min(lay.C, [1, 3, 0, lay.C, 2][seed]),
+                    causal=seed in (0, 3, 4), clustered_keys=bool(seed != 2), seed=seed)
     _say(f"{w.name}: L={w.L} (L % 64 = {w.L % 64}) C={w.C} d={d}")
     _compare(w, _mx_run(w))
 
