@@ -199,3 +199,87 @@ def test_drop_noise_reduces_to_identity_when_disabled():
     lay, r = _noise_setup(3)
     sel, nsel = mo.drop_noise(r, lay, True, 0.0, 0.0, 8, seed=1)
     assert np.array_equal(sel, r.sel) and np.array_equal(nsel, r.nsel)
+
+
+def _pick_layout():
+    """Text + 12 single-frame shots of 10,000 tokens: a query of the last frame has the 11
+    earlier frames (chunks 1..11) as causal candidates, and there are 10,000 such queries."""
+    lay = mi.build_layout(16, [1] * 12, 10_000, frame_is_shot=True)
+    D = mo.derive(lay)
+    ts = range(int(lay.chunk_offsets[-2]), int(lay.chunk_offsets[-1]))
+    return lay, D, ts
+
+
+def _chi2_uniform(counts):
+    """Chi-square statistic and degrees of freedom of counts against a uniform law."""
+    from scipy.stats import chi2
+    c = np.asarray(list(counts.values()), dtype=np.float64)
+    e = c.sum() / len(c)
+    stat = float(np.sum((c - e) ** 2 / e))
+    return stat, chi2.ppf(0.999, len(c) - 1)
+
+
+def test_drop_off_picks_uniform_subsets():
+    """Drop-off removes its floor(p k) chunks uniformly at random from the routed set ([MoC-S]
+    §3.1, "at random"): given the number dropped, every subset of that size is equally likely.
+    k = 4, p_max = 1 makes nd uniform on {0, 1, 2, 3}; over 1e5 queries (10 seeds x 10,000
+    queries) each nd >= 1 gets a chi-square test over its C(4, nd) subsets."""
+    from itertools import combinations
+    lay, D, ts = _pick_layout()
+    T = [1, 4, 7, 10]
+    by_nd = {nd: {frozenset(s): 0 for s in combinations(T, nd)} for nd in (1, 2, 3)}
+    n_nd = np.zeros(5)
+    for seed in range(10):
+        for t in ts:
+            out = mo.drop_noise_row(D, T, 0, 0, t, 1, 4, True, 1.0, 0.0, 8, seed, None)
+            dropped = frozenset(T) - frozenset(out)
+            n_nd[len(dropped)] += 1
+            if dropped:
+                by_nd[len(dropped)][dropped] += 1
+    assert n_nd[4] == 0
+    assert np.all(np.abs(n_nd[:4] / n_nd.sum() - 0.25) < 0.01)  # floor(4 u) is uniform
+    for nd, counts in by_nd.items():
+        stat, lim = _chi2_uniform(counts)
+        assert stat < lim, (nd, stat, lim, counts)
+
+
+def test_drop_in_picks_uniform_subsets():
+    """Drop-in adds min(m, |pool|) chunks uniformly at random from the candidates not already
+    routed: given m, every m-subset of the pool is equally likely. T = {3, 8} leaves a pool of 9
+    chunks; lambda = 2 puts about 27% of 1e5 queries at m = 1 and 27% at m = 2 (chi-square over
+    9 and 36 subsets)."""
+    lay, D, ts = _pick_layout()
+    T = [3, 8]
+    pool = [c for c in range(1, 12) if c not in T]
+    thr = orng.poisson_thresholds(float(np.float32(2.0)), 8)
+    counts = {1: {}, 2: {}}
+    from itertools import combinations
+    for m in (1, 2):
+        counts[m] = {frozenset(s): 0 for s in combinations(pool, m)}
+    for seed in range(10):
+        for t in ts:
+            out = mo.drop_noise_row(D, T, 0, 0, t, 1, 2, True, 0.0, 2.0, 8, seed, thr)
+            added = frozenset(out) - frozenset(T)
+            assert frozenset(T) <= frozenset(out) and added <= frozenset(pool)
+            if len(added) in counts:
+                counts[len(added)][added] += 1
+    for m, c in counts.items():
+        assert sum(c.values()) > 20_000
+        stat, lim = _chi2_uniform(c)
+        assert stat < lim, (m, stat, lim)
+
+
+def test_drop_in_never_re_adds_dropped_chunks():
+    """Drop-off then drop-in: the drop-in pool is the candidates minus the ORIGINAL routed set,
+    so a dropped chunk never comes back in the same draw."""
+    lay, D, ts = _pick_layout()
+    T = [2, 5, 6, 9, 11]
+    thr = orng.poisson_thresholds(float(np.float32(3.0)), 8)
+    seen_drop = 0
+    for t in list(ts)[:5000]:
+        out = mo.drop_noise_row(D, T, 0, 0, t, 1, 5, True, 1.0, 3.0, 8, 3, thr)
+        kept = set(out) & set(T)
+        dropped = set(T) - kept
+        seen_drop += bool(dropped)
+        assert not (dropped & set(out))
+    assert seen_drop > 3000

@@ -166,3 +166,80 @@ def test_layout_validation():
     bad = mi.Layout(lay.chunk_offsets, lay.chunk_shot, 0, 3)  # text range cuts a chunk
     with pytest.raises(ValueError):
         mo.derive(bad)
+
+
+# ---------------------------------------------------------------------------------------------
+# The tie report of route(): gap_exempt marks a query whose k-th and (k+1)-th best candidate
+# scores are closer than 1e-4 of the larger magnitude (the near-tie reading of the parity bar;
+# an exact tie is decided by the lower chunk id). These pins build kbar from constant-per-chunk
+# keys and a unit query, so every score is a chosen number.
+# ---------------------------------------------------------------------------------------------
+
+def _scored_route(scores, k, d=4):
+    """Route one query placed after len(scores) single-frame shots whose chunk descriptors give
+    the listed scores (chunk c+1 scores scores[c]); returns (routing, query token)."""
+    n = len(scores)
+    lay = mi.build_layout(2, [1] * (n + 1), 3, frame_is_shot=True)  # text, n frames, own frame
+    kb = np.zeros((1, 1, lay.C, d), dtype=np.float64)
+    for c, s in enumerate(scores):
+        kb[0, 0, c + 1, 0] = s
+    K = np.repeat(kb, np.diff(lay.chunk_offsets), axis=2)
+    kbar = mo.pool_keys(K, lay)
+    Q = np.zeros((1, 1, lay.L, d))
+    t = lay.L - 1  # a query of the last frame: causal candidates are frames 1..n
+    Q[0, 0, t, 0] = 1.0
+    return mo.route(Q, kbar, lay, k, True), t
+
+
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_tie_report_band_edges(sign):
+    """Gap of 0.5e-4 or 0.9e-4 relative: exempt; 1.1e-4 or 2e-4: not. Scores are placed out of
+    chunk order; with sign = -1 the boundary pair is negative (the band is relative to the
+    larger magnitude)."""
+    for gap, want in ((0.5e-4, True), (2e-4, False), (0.9e-4, True), (1.1e-4, False)):
+        if sign > 0:  # k = 2 best: chunk 2 (0.9), chunk 4 (0.5); then chunk 1 just below
+            sc = [0.5 * (1.0 - gap), 0.9, 0.1, 0.5]
+        else:         # k = 2 best: chunk 2 (-0.2), chunk 4 (-0.5); then chunk 1 just below
+            sc = [-0.5 * (1.0 + gap), -0.2, -3.0, -0.5]
+        r, t = _scored_route(sc, 2)
+        s = np.sort(np.asarray(sc, dtype=np.float32).astype(np.float64))[::-1]
+        rel = (s[1] - s[2]) / max(abs(s[1]), abs(s[2]))
+        assert abs(rel - gap) < 1e-6  # the constructed gap survives rounding to binary32
+        assert list(r.sel[0, 0, t, :2]) == [2, 4]
+        assert bool(r.gap_exempt[0, 0, t]) is want, (gap, sign, rel)
+
+
+def test_tie_report_exact_ties_and_few_candidates():
+    # an exact tie at a non-zero score is inside the band; it is decided by the lower chunk id
+    r, t = _scored_route([0.2, 0.7, 0.7, 0.1], 1)
+    assert bool(r.gap_exempt[0, 0, t])
+    assert list(r.sel[0, 0, t, :1]) == [2]
+    # an exact tie at zero is not (the band is empty); the lower chunk id wins
+    r, t = _scored_route([-0.2, 0.0, 0.0, -0.1], 1)
+    assert not bool(r.gap_exempt[0, 0, t])
+    assert list(r.sel[0, 0, t, :1]) == [2]
+    # #candidates <= k: every candidate is taken, nothing is ever exempt, even with equal scores
+    for k in (3, 4, 6):
+        r, t = _scored_route([0.5, 0.5, 0.5], k)
+        assert not bool(r.gap_exempt[0, 0, t])
+        assert list(r.sel[0, 0, t, :r.nsel[0, 0, t]]) == [1, 2, 3]
+
+
+def test_tie_report_compares_sorted_neighbours():
+    """The flag compares the k-th and (k+1)-th of the sorted order, not neighbours in chunk
+    order: two near-equal scores far from the k boundary leave the query not exempt."""
+    r, t = _scored_route([0.40000, 0.99, 0.40001, 0.2, 0.7], 2)
+    assert not bool(r.gap_exempt[0, 0, t])        # 0.7 vs 0.40001 at the boundary
+    r, t = _scored_route([0.40000, 0.99, 0.40001, 0.2, 0.7], 3)
+    assert bool(r.gap_exempt[0, 0, t])            # 0.40001 vs 0.40000 at the boundary
+
+
+def test_tie_report_is_rare_on_seeded_workloads():
+    """On the tiny workload and the gradient slice only a handful of queries carry the flag
+    (measured: 1 of 8,448 and 5 of 50,688); a flag set too broadly would empty every selection
+    check that skips flagged queries."""
+    for w in (mi.tiny(), mi.grad_slice()):
+        Q, K, V = mi.make_qkv(w)
+        r = mo.route(Q, mo.pool_keys(K, w.layout), w.layout, w.top_k, w.causal)
+        frac = float(r.gap_exempt.mean())
+        assert frac < 1e-3, (w.name, frac)
