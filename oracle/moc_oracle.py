@@ -77,6 +77,8 @@ def derive(layout) -> Derived:
     C = len(shot)
     if len(off) != C + 1 or off[0] != 0 or np.any(np.diff(off) <= 0):
         raise ValueError("chunk offsets must start at 0 and increase strictly")
+    if np.any(shot < TEXT_SHOT):
+        raise ValueError("shot ids are -1 (text) or >= 0")
     L = int(off[-1])
     tb, te = int(layout.text_begin), int(layout.text_end)
     is_text = np.zeros(C, dtype=bool)
@@ -145,9 +147,9 @@ def pool_keys(K, layout) -> np.ndarray:
             for c in range(D.C):
                 a, e = int(D.offsets[c]), int(D.offsets[c + 1])
                 n = e - a
-                blk = K[b, h, a:e, :]
+                cols = K[b, h, a:e, :].T.tolist()  # one list of n values per dimension
                 for j in range(d):
-                    s = math.fsum(blk[:, j].tolist())  # exact sum, rounded once to binary64
+                    s = math.fsum(cols[j])  # exact sum, rounded once to binary64
                     out[b, h, c, j] = np.float32(s / float(n))
     return out
 
@@ -192,24 +194,26 @@ TIE_REL = 1e-4
 def route(Q, kbar, layout, top_k: int, causal: bool,
           cand_mask: Optional[np.ndarray] = None) -> Routing:
     """Top-min(k, #candidates) chunks per (b, h, t), stored ascending by chunk id. With
-    cand_mask (bool [B,H,C,C], row = the query's chunk), a candidate must also be set in it."""
+    cand_mask (bool [B,H,C,C], row = the query's chunk), a candidate must also be set in it.
+    Scores are formed one head at a time (the same products as scores(), in less memory)."""
     D = derive(layout)
-    s_all = scores(Q, kbar)
-    B, H, L, C = s_all.shape
+    B, H, L, _ = Q.shape
+    C = D.C
     k_eff = min(int(top_k), C)
     sel = np.full((B, H, L, k_eff), -1, dtype=np.int32)
     nsel = np.zeros((B, H, L), dtype=np.int32)
     exempt = np.zeros((B, H, L), dtype=bool)
-    for cq in range(C):
-        toks = np.arange(D.offsets[cq], D.offsets[cq + 1])
-        cand0 = candidates(D, cq, causal)
-        for b in range(B):
-            for h in range(H):
-                cand = cand0 if cand_mask is None else cand0[cand_mask[b, h, cq, cand0]]
+    cands = [candidates(D, cq, causal) for cq in range(C)]
+    for b in range(B):
+        for h in range(H):
+            s_bh = scores(Q[b:b + 1, h:h + 1], np.asarray(kbar)[b:b + 1, h:h + 1])[0, 0]
+            for cq in range(C):
+                toks = np.arange(D.offsets[cq], D.offsets[cq + 1])
+                cand = cands[cq] if cand_mask is None else cands[cq][cand_mask[b, h, cq, cands[cq]]]
                 n = min(k_eff, len(cand))
                 if n == 0:
                     continue
-                sc = s_all[b, h][np.ix_(toks, cand)]           # [nt, ncand]
+                sc = s_bh[np.ix_(toks, cand)]           # [nt, ncand]
                 # order by (-score, chunk id): cand is ascending and the sort is stable
                 order = np.argsort(-sc, axis=1, kind="stable")
                 top = cand[order[:, :n]]
@@ -409,6 +413,122 @@ def attend_bwd_dq_rows(Q, K, V, dO, layout, sel, rows: Sequence[Tuple[int, int, 
     return out
 
 
+def anchor_groups(D: Derived) -> List[Tuple[np.ndarray, np.ndarray]]:
+    """(queries, anchor keys) for every group of queries that share their anchor set: the text
+    queries (anchor = the text) and, for every shot, the shot's queries (anchor = text U shot)."""
+    out = []
+    for s in sorted(set(int(x) for x in D.shot)):
+        toks = shot_range_tokens(D, s)
+        out.append((toks, anchor_keys(D, int(toks[0]))))
+    return out
+
+
+def attend_heads(Q, K, V, layout, sel, heads: Sequence[Tuple[int, int]],
+                 scale: Optional[float] = None, dO=None, block: int = 1024):
+    """Every query row of the listed (b, h) heads, forward (and backward when dO is given):
+    the quantities of attend() and attend_bwd() for those heads, in fp64, for inputs too large
+    for the one-row-at-a-time form. Plain torch CPU ops in float64 (its matrix products and
+    elementwise functions use every host core).
+
+    Omega(t) is the disjoint union of Anch(t) and the routed chunks of t (step 8): routed chunks
+    are never text or own-shot chunks, and each is listed once. The softmax over Omega(t) is
+    therefore taken over the concatenation of the query's scores on those parts - its maximum and
+    its sum of exponentials are the maximum and the sum over the parts. Queries that share their
+    anchor set are handled together, up to `block` rows at a time, so that the anchor scores of a
+    block are one matrix product; the routed scores of a chunk are one product over the block's
+    queries that routed to it. Within a row nothing is reordered beyond the summation order of
+    the products and sums.
+
+    Returns (O, lse) - or (O, lse, dQ, dK, dV) with dO - as dicts of float64 NumPy arrays keyed
+    by (b, h): O, dQ, dK, dV [L, d] and lse [L]."""
+    import torch
+    D = derive(layout)
+    d = Q.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    sel = np.asarray(sel)
+    f64 = torch.float64
+
+    def t64(x):
+        return torch.from_numpy(np.ascontiguousarray(_as_f64(x)))
+
+    res = {k: {} for k in ("O", "lse", "dQ", "dK", "dV")}
+    for (b, h) in heads:
+        Qh, Kh, Vh = t64(Q[b, h]), t64(K[b, h]), t64(V[b, h])
+        G = None if dO is None else t64(dO[b, h])
+        L = Qh.shape[0]
+        O = torch.zeros((L, d), dtype=f64)
+        lse = torch.zeros(L, dtype=f64)
+        if G is not None:
+            dQ = torch.zeros((L, d), dtype=f64)
+            dK = torch.zeros((L, d), dtype=f64)
+            dV = torch.zeros((L, d), dtype=f64)
+        for toks, akeys in anchor_groups(D):
+            ak = torch.from_numpy(akeys)
+            Ka, Va = Kh[ak], Vh[ak]
+            for i0 in range(0, len(toks), block):
+                qb_np = toks[i0:i0 + block]
+                # routed parts: chunk -> rows of the block that routed to it
+                parts = {}
+                for i, t in enumerate(qb_np):
+                    row = [int(c) for c in sel[b, h, t] if c >= 0]
+                    own = D.shot[D.chunk_of[t]]
+                    if len(set(row)) != len(row) or any(D.is_text[c] or D.shot[c] == own
+                                                        for c in row):
+                        raise ValueError(f"routed set of query {t} is not disjoint from its "
+                                         "anchors or lists a chunk twice")
+                    for c in row:
+                        parts.setdefault(c, []).append(i)
+                parts = [(torch.tensor(ix), slice(int(D.offsets[c]), int(D.offsets[c + 1])))
+                         for c, ix in sorted(parts.items())]
+                qb = torch.from_numpy(qb_np)
+                Qb = Qh[qb]
+                xa = (Qb @ Ka.T) * scale
+                xr = [(Qb[ix] @ Kh[ks].T) * scale for ix, ks in parts]
+                m = xa.amax(dim=1)
+                for (ix, _), x in zip(parts, xr):
+                    m.scatter_reduce_(0, ix, x.amax(dim=1), reduce="amax")
+                ea = torch.exp(xa - m[:, None])
+                er = [torch.exp(x - m[ix, None]) for (ix, _), x in zip(parts, xr)]
+                z = ea.sum(dim=1)
+                for (ix, _), e in zip(parts, er):
+                    z.index_add_(0, ix, e.sum(dim=1))
+                pa = ea / z[:, None]
+                pr = [e / z[ix, None] for (ix, _), e in zip(parts, er)]
+                o = pa @ Va
+                for (ix, ks), p in zip(parts, pr):
+                    o.index_add_(0, ix, p @ Vh[ks])
+                O[qb] = o
+                lse[qb] = m + torch.log(z)
+                if G is None:
+                    continue
+                gb = G[qb]
+                dpa = gb @ Va.T
+                dpr = [gb[ix] @ Vh[ks].T for ix, ks in parts]
+                Dt = (pa * dpa).sum(dim=1)
+                for (ix, _), p, dp in zip(parts, pr, dpr):
+                    Dt.index_add_(0, ix, (p * dp).sum(dim=1))
+                dsa = pa * (dpa - Dt[:, None])
+                dsr = [p * (dp - Dt[ix, None]) for (ix, _), p, dp in zip(parts, pr, dpr)]
+                dq = dsa @ Ka
+                for (ix, ks), ds in zip(parts, dsr):
+                    dq.index_add_(0, ix, ds @ Kh[ks])
+                dQ[qb] = scale * dq
+                dK.index_add_(0, ak, scale * (dsa.T @ Qb))
+                dV.index_add_(0, ak, pa.T @ gb)
+                for (ix, ks), p, ds in zip(parts, pr, dsr):
+                    dK[ks] += scale * (ds.T @ Qb[ix])
+                    dV[ks] += p.T @ gb[ix]
+        res["O"][(b, h)], res["lse"][(b, h)] = O.numpy(), lse.numpy()
+        if G is not None:
+            res["dQ"][(b, h)] = dQ.numpy()
+            res["dK"][(b, h)] = dK.numpy()
+            res["dV"][(b, h)] = dV.numpy()
+    if dO is None:
+        return res["O"], res["lse"]
+    return res["O"], res["lse"], res["dQ"], res["dK"], res["dV"]
+
+
 # ---------------------------------------------------------------------------------------------
 # 10. Counts and invariants
 # ---------------------------------------------------------------------------------------------
@@ -504,9 +624,10 @@ def check_routing(layout, sel, nsel, top_k: int, causal: bool, exact_count: bool
 # ---------------------------------------------------------------------------------------------
 # 11. Outer-loop context routing ([MoC-S] Appendix I)
 # ---------------------------------------------------------------------------------------------
-# Readings. The pages describe a coarse router that picks the top-M large context segments by
-# the similarity of mean-pooled features of the current query block and of the candidate
-# segments, and then hands those segments plus the mandatory context to the inner MoC router.
+# Readings. The pages add a first, coarse level of routing for long generation: whole segments
+# are ranked by how well the averaged features of the current block of queries match the
+# averaged features of each candidate segment, and the ordinary MoC router then only looks at
+# chunks inside the best M of them (plus the mandatory context).
 #  * Segments are given: contiguous groups of whole chunks (seg_chunk[nseg+1], chunk offsets),
 #    each all text chunks or all video chunks. Text is mandatory context, never a candidate.
 #  * The current query block of a query is its own segment. Its feature is the mean of the

@@ -24,7 +24,9 @@ def test_max_chunks_topk_and_drop_in():
                     clustered_keys=True, p_max=0.5, lam=4.0, max_drop_in=16, seed=7)
     g = tb._run(w, backward=True)
     assert g["sel"].shape[-1] == 48
-    changed = tb._check_noise(w, g)
+    # 1,023 candidate chunks and top-32: the 32nd and 33rd best scores sit close together, so
+    # the oracle flags about 0.8% of the queries as near-ties (none differ on the GPU so far)
+    changed = tb._check_noise(w, g, tie_frac_max=2e-2)
     assert changed > 0
     assert int(g["nsel"].max()) > 32  # drop-in filled rows past top-k
     O, _ = mo.attend(g["Q"], g["K"], g["V"], w.layout, g["sel"])
@@ -54,7 +56,7 @@ def test_degenerate_layouts(case):
     kb = mo.pool_keys(run.K, lay)
     assert np.array_equal(run.h_kbar.view(np.uint32), kb.view(np.uint32))
     r = mo.route(run.Q, kb, lay, w.top_k, w.causal)
-    _check_selection(run, r)
+    _check_selection(run, r, kb)
     mo.check_routing(lay, run.h_sel, run.h_nsel, w.top_k, w.causal)
     assert np.array_equal(run.h_pairs, mo.pair_counts(lay, run.h_sel))
     O, lse = mo.attend(run.Q, run.K, run.V, lay, run.h_sel)

@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import moc_inputs as mi
+import parity_checks as pc
 from oracle import moc_oracle as mo
 from test_gpu_parity import _say
 
@@ -132,3 +133,48 @@ def test_outer_all_segments_equals_plain_routing():
     b = moc.route(Qd, kbar, lay, cfg, cand_mask=out.cand_mask)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_outer_headline_full_size():
+    """The headline_outer workload the benchmark times (175,232 tokens, 12 heads, one segment per
+    shot and the text, M = 2, inner top-2): coarse selections of every (head, query segment)
+    against the oracle's, the candidate mask bit-exact, every inner selection against the
+    oracle's masked routing (tie exemption, legality within the mask), pair counts exact, and the
+    attention on sampled rows of every head."""
+    import sparse_chunk_routed_amd as moc
+    w = mi.headline_outer()
+    dev = torch.device("cuda:0")
+    Q, K, V = mi.make_qkv(w)
+    lay = moc.DeviceLayout.from_layout(w.layout, dev)
+    Qd, Kd, Vd = Q.to(dev), K.to(dev), V.to(dev)
+    out = moc.route_outer(Qd, Kd, lay, w.segments, w.outer_M, w.causal)
+    cfg = moc.RouteCfg(w.top_k, w.causal, 0.0, 0.0, w.max_drop_in, w.seed)
+    kbar = moc.pool_keys(Kd, lay)
+    sel, nsel = moc.route(Qd, kbar, lay, cfg, cand_mask=out.cand_mask)
+    vl = moc.build_varlen(sel, nsel, lay, cfg, w.d, Qd.dtype)
+    O, lse = moc.attend_fwd(Qd, Kd, Vd, lay, vl)
+    torch.cuda.synchronize()
+    g_seg, g_nseg = out.seg_sel.cpu().numpy(), out.seg_nsel.cpu().numpy()
+    orr = mo.route_outer(Q, K, w.layout, w.segments, w.outer_M, w.causal)
+    same = np.all(np.sort(g_seg, -1) == np.sort(orr.seg_sel, -1), -1) & (g_nseg == orr.seg_nsel)
+    assert not (~same & ~orr.gap_exempt).any(), np.argwhere(~same)[:5]
+    _say(f"coarse selections: {int(same.sum())}/{same.size} equal, "
+         f"{int((~same).sum())} tie-exempt differ")
+    want = _mask_from_seg_sel(g_seg, g_nseg, w.segments, w.C)
+    assert np.array_equal(_bits_to_bool(out.cand_mask.cpu().numpy(), w.C), want)
+    kb = mo.pool_keys(K, w.layout)
+    assert np.array_equal(kbar.cpu().numpy().view(np.uint32), kb.view(np.uint32))
+    r = mo.route(Q, kb, w.layout, w.top_k, w.causal, cand_mask=want)
+    hsel, hnsel = sel.cpu().numpy(), nsel.cpu().numpy()
+    pc.check_selection(w.layout, hsel, hnsel, r.sel, r.nsel, r, Q, kb, w.causal,
+                       label="headline_outer inner")
+    pc.check_legal(w.layout, hsel, hnsel, w.top_k, w.causal, cand_mask=want)
+    assert np.array_equal(vl.pair_count.cpu().numpy(), mo.pair_counts(w.layout, hsel))
+    rng = np.random.default_rng(11)
+    rows = [(0, h, int(t)) for h in range(w.H) for t in rng.choice(w.L, 16, replace=False)]
+    Oo, lo = mo.attend(Q, K, V, w.layout, hsel, rows=rows)
+    hO, hl = O.float().cpu().numpy(), lse.cpu().numpy()
+    err = float(np.max(np.abs(np.stack([hO[row] for row in rows]) - Oo)))
+    lerr = float(np.max(np.abs(np.array([hl[row] for row in rows]) - lo)))
+    _say(f"headline_outer attention rows={len(rows)} max|dO|={err:.3e} max|dlse|={lerr:.3e}")
+    assert err <= 1e-2 and lerr <= 1e-2

@@ -14,6 +14,7 @@ import pytest
 import torch
 
 import moc_inputs as mi
+import parity_checks as pc
 from oracle import moc_oracle as mo
 
 pytestmark = pytest.mark.gpu
@@ -31,8 +32,7 @@ def _moc():
     return moc
 
 
-def _say(msg):
-    print(f"[gpu] {msg}", flush=True)
+_say = pc.say
 
 
 class Run:
@@ -67,27 +67,12 @@ class Run:
         _say("gpu path done")
 
 
-def _check_selection(run: Run, o_route, rows=None):
-    """Set-equality of selections with the tie exemption; returns the number exempted."""
-    w = run.w
-    k_eff = o_route.k_eff
-    gsel = run.h_sel[..., :k_eff] if run.h_sel.shape[-1] >= k_eff else run.h_sel
-    exempt = o_route.gap_exempt
-    B, H, L = run.h_nsel.shape
-    if rows is None:
-        same = np.all(np.sort(gsel, axis=-1) == np.sort(o_route.sel, axis=-1), axis=-1)
-        same &= run.h_nsel == o_route.nsel
-        bad = ~same & ~exempt
-        assert not bad.any(), f"{int(bad.sum())} selections differ, first at {np.argwhere(bad)[:5]}"
-        return int((~same & exempt).sum())
-    n_ex = 0
-    for (b, h, t) in rows:
-        g = sorted(int(c) for c in gsel[b, h, t] if c >= 0)
-        o = sorted(int(c) for c in o_route.sel[b, h, t] if c >= 0)
-        if g != o:
-            assert exempt[b, h, t], (b, h, t, g, o)
-            n_ex += 1
-    return n_ex
+def _check_selection(run: Run, o_route, kb, rows=None, label=None):
+    """Selections against the oracle's (tie exemption, bounded and checked; see
+    parity_checks.check_selection); returns the number of flagged queries that differ."""
+    return pc.check_selection(run.w.layout, run.h_sel, run.h_nsel, o_route.sel, o_route.nsel,
+                              o_route, run.Q, kb, run.causal, rows=rows,
+                              label=label or run.w.name)
 
 
 def _attend_rows(run: Run, rows, tol):
@@ -131,8 +116,7 @@ def test_pool_bit_exact_tiny(tiny_run):
 def test_route_tiny(tiny_run):
     kb = mo.pool_keys(tiny_run.K, tiny_run.w.layout)
     r = mo.route(tiny_run.Q, kb, tiny_run.w.layout, tiny_run.top_k, tiny_run.causal)
-    n_ex = _check_selection(tiny_run, r)
-    _say(f"tiny: tie-exempt queries differing: {n_ex}")
+    _check_selection(tiny_run, r, kb)
     mo.check_routing(tiny_run.w.layout, tiny_run.h_sel, tiny_run.h_nsel, tiny_run.top_k,
                      tiny_run.causal)
 
@@ -225,7 +209,7 @@ def test_random_layouts(seed):
     kb = mo.pool_keys(run.K, lay)
     assert np.array_equal(run.h_kbar.view(np.uint32), kb.view(np.uint32))
     r = mo.route(run.Q, kb, lay, top_k, w.causal)
-    _check_selection(run, r)
+    _check_selection(run, r, kb)
     mo.check_routing(lay, run.h_sel, run.h_nsel, top_k, w.causal)
     assert np.array_equal(run.h_pairs, mo.pair_counts(lay, run.h_sel))
     O, lse = mo.attend(run.Q, run.K, run.V, lay, run.h_sel)
@@ -253,8 +237,9 @@ def test_full_size_sampled(name):
     assert np.array_equal(run.h_kbar.view(np.uint32), kb.view(np.uint32))
     _say("pool bit-exact")
     r = mo.route(run.Q, kb, w.layout, w.top_k, w.causal)
-    n_ex = _check_selection(run, r)
-    _say(f"selections equal (tie-exempt differing: {n_ex})")
+    _check_selection(run, r, kb)
+    pc.check_legal(w.layout, run.h_sel, run.h_nsel, w.top_k, w.causal)
+    _say("every selection legal")
     assert np.array_equal(run.h_pairs, mo.pair_counts(w.layout, run.h_sel))
     rows = _sample_rows(w, 24)
     _attend_rows(run, rows, TOL[w.dtype])

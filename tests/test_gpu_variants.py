@@ -5,7 +5,10 @@
   6,300 tokens, chunk sizes 64 to 1,024): pooled means bit-exact, every selection (tie
   exemption), pair counts exact, attention on sampled rows, and the backward at chunk 256.
 * Dense attention as a layout: one shot holding every token and no routing, which is the
-  same-GPU dense baseline of the length sweep; checked against plain softmax attention.
+  same-GPU dense baseline of the length sweep; checked against plain softmax attention, at
+  small lengths in full and at the 8-shot length (175,232 tokens) on sampled rows.
+* The longest layout of the length sweep, 24 shots of 14 frames (524,672 tokens): pooled means
+  bit-exact, every selection, pair counts exact, attention on sampled rows.
 """
 import math
 
@@ -14,6 +17,7 @@ import pytest
 import torch
 
 import moc_inputs as mi
+import parity_checks as pc
 from oracle import moc_oracle as mo
 from test_gpu_parity import TOL, Run, _attend_rows, _check_selection, _sample_rows, _say
 
@@ -28,8 +32,7 @@ def test_single_shot_fixed_chunks(chunk):
     kb = mo.pool_keys(run.K, w.layout)
     assert np.array_equal(run.h_kbar.view(np.uint32), kb.view(np.uint32))
     r = mo.route(run.Q, kb, w.layout, w.top_k, w.causal)
-    n_ex = _check_selection(run, r)
-    _say(f"c{chunk}: selections equal (tie-exempt differing: {n_ex})")
+    _check_selection(run, r, kb)
     mo.check_routing(w.layout, run.h_sel, run.h_nsel, w.top_k, w.causal)
     assert np.array_equal(run.h_pairs, mo.pair_counts(w.layout, run.h_sel))
     _attend_rows(run, _sample_rows(w, 40, seed=chunk), TOL[w.dtype])
@@ -78,3 +81,35 @@ def test_dense_layout(L):
         lerr = np.max(np.abs(run.h_lse[0, h] - lse))
         _say(f"dense L={L} head {h}: max|dO|={err:.3e} max|dlse|={lerr:.3e}")
         assert err <= TOL["bf16"] and lerr <= TOL["bf16"]
+
+
+def test_dense_layout_8_shot_length_sampled():
+    """The length sweep's dense baseline at 8 shots: one shot of 175,232 tokens, no routing, so
+    every query attends every key. Sampled rows of every head against plain softmax attention
+    (the oracle's key set is the whole sequence)."""
+    w = mi.dense(n_shots=8)
+    run = Run(w)
+    assert int(run.h_pairs.sum()) == w.B * w.H * w.L * w.L
+    rng = np.random.default_rng(3)
+    rows = [(0, h, int(t)) for h in range(w.H)
+            for t in list(rng.choice(w.L, 3, replace=False)) + [0, w.L - 1]]
+    _attend_rows(run, rows, TOL[w.dtype])
+
+
+def test_shots24_sampled():
+    """The 24-shot layout of the length sweep (512 text + 24 shots x 14 frames x 1,560 tokens =
+    524,672 tokens, C = 337, top-k 2): pooled means bit-exact for every head and chunk, every
+    selection against the oracle (tie exemption, legality), pair counts exact, and attention on
+    sampled rows and chunk edges of every head."""
+    w = mi.shots(n_shots=24)
+    assert w.L == 524_672 and w.C == 337
+    run = Run(w)
+    kb = mo.pool_keys(run.K, w.layout)
+    assert np.array_equal(run.h_kbar.view(np.uint32), kb.view(np.uint32))
+    _say("pool bit-exact")
+    r = mo.route(run.Q, kb, w.layout, w.top_k, w.causal)
+    _check_selection(run, r, kb)
+    pc.check_legal(w.layout, run.h_sel, run.h_nsel, w.top_k, w.causal)
+    assert np.array_equal(run.h_pairs, mo.pair_counts(w.layout, run.h_sel))
+    _say(f"pairs {int(run.h_pairs.sum())} exact")
+    _attend_rows(run, _sample_rows(w, 8, seed=24), TOL[w.dtype])

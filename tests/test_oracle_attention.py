@@ -215,3 +215,49 @@ def test_backward_finite_differences():
             num[idx] = (fp - fm) / (2 * eps)
         err = np.max(np.abs(num - G)) / max(1e-12, np.max(np.abs(G)))
         assert err < 1e-7, (name, err)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_attend_heads_equals_masked_sdpa(seed):
+    """attend_heads (every row of a head, queries grouped by anchor set, row blocks of 3 so that
+    groups split) against torch SDPA with the rule-built mask, forward, LSE and autograd
+    backward, on random layouts with drop-off / drop-in noise (routed sets of varying size)."""
+    rng = np.random.default_rng(700 + seed)
+    lay = mi.make_random_layout(rng, max_shots=4, max_frames=3, max_chunk=11,
+                                frame_is_shot=seed == 3)
+    B, H, d = 2, 2, 8
+    top_k = int(rng.integers(0, lay.C + 1))
+    causal = seed % 2 == 0
+    Q, K, r = _route_random(lay, B, H, d, top_k, causal, seed=800 + seed)
+    sel, _ = mo.drop_noise(r, lay, causal, 0.5, 1.5, 4, seed)
+    V = _rand((B, H, lay.L, d), 900 + seed)
+    dO = _rand((B, H, lay.L, d), 950 + seed)
+    scale = 0.29
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    O, lse, dQ, dK, dV = mo.attend_heads(Q, K, V, lay, sel, heads, scale=scale, dO=dO, block=3)
+    M = _mask_from_rules(lay, sel)
+    q, k, v, o, lse_t = _sdpa(Q, K, V, M, scale)
+    (o * torch.tensor(dO)).sum().backward()
+    for (b, h) in heads:
+        assert np.max(np.abs(O[(b, h)] - o.detach().numpy()[b, h])) < 1e-12
+        assert np.max(np.abs(lse[(b, h)] - lse_t.detach().numpy()[b, h])) < 1e-12
+        assert np.max(np.abs(dQ[(b, h)] - q.grad.numpy()[b, h])) < 1e-11
+        assert np.max(np.abs(dK[(b, h)] - k.grad.numpy()[b, h])) < 1e-11
+        assert np.max(np.abs(dV[(b, h)] - v.grad.numpy()[b, h])) < 1e-11
+    # forward only returns the same O and LSE
+    O2, lse2 = mo.attend_heads(Q, K, V, lay, sel, heads[:1], scale=scale)
+    assert np.max(np.abs(O2[heads[0]] - O[heads[0]])) < 1e-13
+
+
+def test_attend_heads_rejects_routed_sets_overlapping_the_anchors():
+    lay = mi.build_layout(3, [2, 2], 4)
+    Q, K, r = _route_random(lay, 1, 1, 4, top_k=1, causal=True, seed=41)
+    V = _rand((1, 1, lay.L, 4), 42)
+    bad = r.sel.copy()
+    t = lay.L - 1
+    bad[0, 0, t, 0] = int(mo.derive(lay).chunk_of[t])  # its own chunk (own shot)
+    with pytest.raises(ValueError):
+        mo.attend_heads(Q, K, V, lay, bad, [(0, 0)])
+    bad = np.concatenate([r.sel, r.sel], axis=-1)  # every routed chunk listed twice
+    with pytest.raises(ValueError):
+        mo.attend_heads(Q, K, V, lay, bad, [(0, 0)])
