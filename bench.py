@@ -80,12 +80,30 @@ def recorded_traffic(workload: str):
     return int(rec["fetch_bytes_per_launch"]) + int(rec["write_bytes_per_launch"])
 
 
+def _probe_lib():
+    """The benchmark's helper library (register-only MFMA loops, built next to libmoc.so by
+    sparse_chunk_routed_amd/build.py); not part of the layer's library."""
+    import ctypes
+    path = os.path.join(ROOT, "sparse_chunk_routed_amd", "libmoc_bench_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.moc_bench_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+    lib.moc_bench_probe_mfma.restype = ctypes.c_int
+    return lib
+
+
 def measured_peaks(dev) -> dict:
     """Ceilings re-measured on this GPU next to the published ones: a plain device copy (HBM
-    GB/s, read + write) and register-only MFMA loops (moc_probe_mfma: bf16, and fp8 with block
-    scales), each the best of three timed launches after a warm-up."""
+    GB/s, read + write) and register-only MFMA loops (moc_bench_probe_mfma: bf16, and fp8 with
+    block scales), each the best of three timed launches after a warm-up."""
     import torch
-    import sparse_chunk_routed_amd as moc
+    probe = _probe_lib()
+
+    def probe_mfma(fp8, blocks, iters, sink):
+        st = torch.cuda.current_stream(dev).cuda_stream
+        rc = probe.moc_bench_probe_mfma(int(fp8), blocks, iters, sink.data_ptr(), st)
+        if rc != 0:
+            raise RuntimeError(f"moc_bench_probe_mfma returned {rc}")
 
     def best(fn, reps=3):
         fn()
@@ -107,8 +125,8 @@ def measured_peaks(dev) -> dict:
     blocks, iters = 1024, 4096
     sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
     waves_mfma = blocks * 4 * iters * 8
-    t_bf16 = best(lambda: moc.probe_mfma(False, blocks, iters, sink))
-    t_fp8 = best(lambda: moc.probe_mfma(True, blocks, iters, sink))
+    t_bf16 = best(lambda: probe_mfma(False, blocks, iters, sink))
+    t_fp8 = best(lambda: probe_mfma(True, blocks, iters, sink))
     return {"hbm_copy_gbs": 2 * n / t_copy / 1e9,
             "mfma_bf16_tflops": waves_mfma * 2 * 32 * 32 * 16 / t_bf16 / 1e12,
             "mfma_fp8_tflops": waves_mfma * 2 * 32 * 32 * 64 / t_fp8 / 1e12,
@@ -134,11 +152,11 @@ def cpu_baseline(w, Q, K, V, rows_n: int):
     linearly to every row."""
     import numpy as np
     from oracle import moc_oracle as mo
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    from threadpoolctl import threadpool_limits
+    affinity = len(os.sched_getaffinity(0))  # the host cores this process may run on
+    # the oracle's BLAS gets all of them, within the OpenMP thread budget when one is set
+    threads = min(affinity, int(os.environ.get("OMP_NUM_THREADS", affinity) or affinity))
+    limit = threadpool_limits(limits=threads)
     t0 = time.perf_counter()
     kb = mo.pool_keys(K, w.layout)
     t_pool = time.perf_counter() - t0
@@ -160,8 +178,10 @@ def cpu_baseline(w, Q, K, V, rows_n: int):
     full = t_pool + t_route + t_att * (w.B * w.H * w.L / len(rows))
     pairs = int(mo.pair_counts(w.layout, r.sel).sum())
     flops = 4 * w.d * pairs
+    limit.unregister()
     return {
         "value": flops / full / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "affinity_cores": affinity,
         "sample": (f"fp64 numpy oracle: pool and route on all {w.B * w.H} heads, attention on "
                    f"{len(rows)} seeded query rows across the heads; measured {measured:.1f} s "
                    f"(pool {t_pool:.1f}, route {t_route:.1f}, attention {t_att:.1f}), "

@@ -23,8 +23,9 @@
  *   - Workspaces are sized with moc_workspace_bytes(). Distinct workspaces allow concurrent
  *     calls on distinct streams; calls sharing a workspace must be ordered by the caller.
  *   - Layout arrays live on the device, so their content (monotone offsets, contiguous shots,
- *     text on chunk boundaries) is a precondition, not checked here; the Python binding checks
- *     it on a host copy.
+ *     text on chunk boundaries) is a precondition that the host cannot check without a copy.
+ *     The Python binding checks it on a host copy; a C caller can set moc_layout.check to have
+ *     every call check it on the device first (see moc_check_layout).
  */
 #ifndef MOC_H_
 #define MOC_H_
@@ -44,7 +45,8 @@ typedef enum {
   MOC_EWORKSPACE = 4,   /* workspace pointer null or smaller than moc_workspace_bytes() */
   MOC_EUNSUPPORTED = 5, /* a valid request this build does not implement */
   MOC_EHIP = 6,         /* a HIP launch or runtime call failed */
-  MOC_EINTERNAL = 7     /* unexpected internal error (no C++ exception crosses the ABI) */
+  MOC_EINTERNAL = 7,    /* unexpected internal error (no C++ exception crosses the ABI) */
+  MOC_ELAYOUT = 8       /* the layout content failed the check (moc_layout_status) */
 } moc_status;
 
 typedef enum { MOC_F32 = 0, MOC_BF16 = 1 } moc_dtype;
@@ -68,6 +70,14 @@ enum { MOC_OP_ROUTE = 0, MOC_OP_VARLEN = 1, MOC_OP_FWD = 2, MOC_OP_BWD = 3, MOC_
  *                  every text chunk carries -1, and no other chunk does.
  *   [text_begin, text_end): the caption tokens, a union of whole chunks; may be empty.
  *   dtype: MOC_F32 or MOC_BF16; d in {64, 128}; 1 <= C <= min(L, MOC_MAX_C).
+ *   check: NULL, or a device uint32 word that turns on the device check of the content above.
+ *          Every entry point then first runs the check kernel, which ORs the violations it
+ *          finds (MOC_LAYOUT_* bits) into *check, and every kernel of the call does no work
+ *          when *check is non-zero at its start - so a malformed layout is never used to index
+ *          memory. The caller zeroes the word before the first call and reads it after the
+ *          stream has run (moc_layout_status turns it into a status and a message). A word
+ *          left non-zero keeps later calls that share it from running. Outputs of a rejected
+ *          call are not written.
  */
 typedef struct {
   int32_t B, H, L, d;
@@ -76,7 +86,17 @@ typedef struct {
   const int32_t *chunk_offsets;
   const int32_t *chunk_shot;
   int32_t text_begin, text_end;
+  uint32_t *check;
 } moc_layout;
+
+/* Bits of the layout check word (several may be set). */
+#define MOC_LAYOUT_BAD_START 1u       /* chunk_offsets[0] != 0 */
+#define MOC_LAYOUT_NOT_INCREASING 2u  /* chunk_offsets not strictly increasing */
+#define MOC_LAYOUT_BAD_END 4u         /* chunk_offsets[C] != L */
+#define MOC_LAYOUT_BAD_SHOT_ID 8u     /* a shot id below -1 */
+#define MOC_LAYOUT_BAD_TEXT 16u       /* a chunk straddles the text range, or shot -1 is not
+                                         exactly the chunks inside it */
+#define MOC_LAYOUT_SHOT_SPLIT 32u     /* a shot's chunks are not contiguous */
 
 /*
  * Routing configuration (summary §3.1-3.2; slides "Mixture of Contexts for Long Video
@@ -173,10 +193,10 @@ moc_status moc_route(const moc_layout *lay, const moc_route_cfg *cfg, const void
                      void *stream);
 
 /*
- * Outer-loop context routing (summary, Appendix I: a coarse router first picks the top-M
- * large context segments by the similarity of mean-pooled features of the current query block
- * and of the candidate segments; inner MoC routing then works within those segments plus the
- * mandatory context). Segments are given groups of whole chunks; a query's block is its own
+ * Outer-loop context routing (summary, Appendix I: routing on two levels - segments are
+ * ranked by comparing the averaged queries of the current block with the averaged keys of each
+ * other segment, and the chunk router then only considers the best M segments; the mandatory
+ * context is kept). Segments are given groups of whole chunks; a query's block is its own
  * segment.
  *   seg_chunk: device int32 [nseg+1], 0 = seg_chunk[0] < ... < seg_chunk[nseg] = C; segment s
  *              is chunks [seg_chunk[s], seg_chunk[s+1]) and holds only text chunks or only
@@ -264,16 +284,6 @@ moc_status moc_attend_fwd_mx(const moc_layout *lay, const moc_varlen *vl, const 
                              size_t ws_bytes, void *stream);
 
 /*
- * Measurement aid, not a step of the layer: a register-only MFMA loop that shows the matrix-core
- * rate the chip sustains (its clock and power limits included). Launches `blocks` workgroups of
- * 4 waves; every wave runs `iters` rounds of 8 independent 32x32x16 bf16 MFMAs (fp8 = 0) or
- * 32x32x64 e4m3 MFMAs with unit E8M0 scales (fp8 = 1) and writes one float per thread to sink
- * (device float [blocks * 256]). FLOPs = blocks * 4 * iters * 8 * 2 * 32 * 32 * (16 or 64); the
- * caller times the launch on `stream`.
- */
-moc_status moc_probe_mfma(int32_t fp8, int32_t blocks, int32_t iters, float *sink, void *stream);
-
-/*
  * Attention backward with the routed sets held fixed (summary §3.1 and Appendix A: top-k is
  * not differentiable; gradients reach the selected keys and values only).
  *   Inputs: Q, K, V, O, lse from moc_attend_fwd, dO. Outputs dQ, dK, dV [B,H,L,d] in the
@@ -286,6 +296,25 @@ moc_status moc_attend_bwd(const moc_layout *lay, const moc_varlen *vl, const voi
                           const void *K, const void *V, const void *O, const float *lse,
                           const void *dO, float softmax_scale, void *dQ, void *dK, void *dV,
                           void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Layout content check (summary §3.2: chunks follow frame, shot and caption boundaries;
+ * write-up 計算效率: the boundary tables of the packed sequence).
+ * moc_check_layout enqueues only the check kernel on `stream`: one workgroup reads
+ * chunk_offsets[0..C] and chunk_shot[0..C-1] and ORs the MOC_LAYOUT_* bits of every violation
+ * into *lay->check (which must be set). The other entry points run the same kernel first
+ * whenever lay->check is set.
+ */
+moc_status moc_check_layout(const moc_layout *lay, void *stream);
+
+/* The same check on host arrays (offsets [C+1], shot ids [C]): the MOC_LAYOUT_* bits, 0 for a
+ * valid layout. Needs no GPU. */
+uint32_t moc_layout_check_host(const int32_t *chunk_offsets, const int32_t *chunk_shot, int32_t C,
+                               int32_t L, int32_t text_begin, int32_t text_end);
+
+/* MOC_OK for a check word of 0; otherwise MOC_ELAYOUT, with the violations spelled out in
+ * moc_last_error(). */
+moc_status moc_layout_status(uint32_t word);
 
 /* Host-side helper: the drop-in Poisson thresholds the routing kernel uses,
  * thr[i] = min(2^32, floor(2^32 * P(m <= i))) for i < max_drop_in (binary64, C library exp). */

@@ -11,7 +11,10 @@ LIB_PATH = os.environ.get("MOC_LIB_PATH") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "libmoc.so")
 
 MOC_OK, MOC_EINVAL, MOC_ESHAPE, MOC_EDTYPE, MOC_EWORKSPACE, MOC_EUNSUPPORTED, MOC_EHIP, \
-    MOC_EINTERNAL = range(8)
+    MOC_EINTERNAL, MOC_ELAYOUT = range(9)
+# bits of the layout check word
+MOC_LAYOUT_BAD_START, MOC_LAYOUT_NOT_INCREASING, MOC_LAYOUT_BAD_END, MOC_LAYOUT_BAD_SHOT_ID, \
+    MOC_LAYOUT_BAD_TEXT, MOC_LAYOUT_SHOT_SPLIT = 1, 2, 4, 8, 16, 32
 MOC_F32, MOC_BF16 = 0, 1
 MOC_OP_ROUTE, MOC_OP_VARLEN, MOC_OP_FWD, MOC_OP_BWD, MOC_OP_OUTER = range(5)
 MOC_MAX_C, MOC_MAX_TOPK, MOC_MAX_DROP_IN = 1024, 32, 16
@@ -21,14 +24,16 @@ MOC_MAX_SEG, MOC_MAX_TOPM = 256, 16
 EXPORTS = (
     "moc_sel_width", "moc_workspace_bytes", "moc_pool_keys", "moc_route", "moc_route_outer",
     "moc_route_masked", "moc_build_varlen", "moc_attend_fwd", "moc_attend_bwd",
-    "moc_mx_quantize", "moc_attend_fwd_mx", "moc_probe_mfma", "moc_poisson_thresholds", "moc_status_string", "moc_last_error",
+    "moc_mx_quantize", "moc_attend_fwd_mx", "moc_poisson_thresholds", "moc_status_string",
+    "moc_last_error", "moc_check_layout", "moc_layout_check_host", "moc_layout_status",
 )
 
 
 class MocLayout(ctypes.Structure):
     _fields_ = [("B", c_int32), ("H", c_int32), ("L", c_int32), ("d", c_int32),
                 ("dtype", c_int32), ("C", c_int32), ("chunk_offsets", c_void_p),
-                ("chunk_shot", c_void_p), ("text_begin", c_int32), ("text_end", c_int32)]
+                ("chunk_shot", c_void_p), ("text_begin", c_int32), ("text_end", c_int32),
+                ("check", c_void_p)]
 
 
 class MocRouteCfg(ctypes.Structure):
@@ -97,10 +102,14 @@ def load() -> ctypes.CDLL:
                                       c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_void_p,
                                       c_size_t, c_void_p]
     lib.moc_attend_fwd_mx.restype = c_int32
-    lib.moc_probe_mfma.argtypes = [c_int32, c_int32, c_int32, c_void_p, c_void_p]
-    lib.moc_probe_mfma.restype = c_int32
     lib.moc_poisson_thresholds.argtypes = [c_float, c_int32, P(c_uint64)]
     lib.moc_poisson_thresholds.restype = c_int32
+    lib.moc_check_layout.argtypes = [P(MocLayout), c_void_p]
+    lib.moc_check_layout.restype = c_int32
+    lib.moc_layout_check_host.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32]
+    lib.moc_layout_check_host.restype = ctypes.c_uint32
+    lib.moc_layout_status.argtypes = [ctypes.c_uint32]
+    lib.moc_layout_status.restype = c_int32
     lib.moc_status_string.argtypes = [c_int32]
     lib.moc_status_string.restype = c_char_p
     lib.moc_last_error.argtypes = []

@@ -35,13 +35,17 @@ def _dtype_code(dt: torch.dtype) -> int:
 class DeviceLayout:
     """A token layout resident on the device: chunk offsets [C+1], chunk shot ids [C]
     (-1 = text) and the text range. The content is validated here on the host copy, since the
-    library treats it as a precondition."""
+    library treats it as a precondition. With device_check=True the library also checks it on
+    the device at the start of every call (moc_layout.check): the word lives in `check_word`
+    and check_status() reads it."""
 
     def __init__(self, chunk_offsets: Sequence[int], chunk_shot: Sequence[int], text_begin: int,
-                 text_end: int, device="cuda"):
+                 text_end: int, device="cuda", device_check: bool = False,
+                 validate: bool = True):
         off = np.asarray(chunk_offsets, dtype=np.int64)
         shot = np.asarray(chunk_shot, dtype=np.int64)
-        validate_layout(off, shot, int(text_begin), int(text_end))
+        if validate:
+            validate_layout(off, shot, int(text_begin), int(text_end))
         self.C = int(len(shot))
         self.L = int(off[-1])
         self.text_begin, self.text_end = int(text_begin), int(text_end)
@@ -49,6 +53,23 @@ class DeviceLayout:
         self.shot_host = shot.astype(np.int32)
         self.offsets = torch.from_numpy(self.offsets_host.copy()).to(device)
         self.shot = torch.from_numpy(self.shot_host.copy()).to(device)
+        self.check_word = (torch.zeros(1, dtype=torch.int32, device=device) if device_check
+                           else None)
+
+    def check_status(self) -> None:
+        """Wait for the device, then raise MocError(MOC_ELAYOUT) if the check word is set."""
+        if self.check_word is None:
+            return
+        word = int(self.check_word.item()) & 0xFFFFFFFF
+        lib = L.load()
+        L.check(lib.moc_layout_status(word))
+
+    def check_on_device(self) -> None:
+        """Enqueue only the layout check (moc_check_layout) on the current stream."""
+        if self.check_word is None:
+            raise ValueError("built without device_check")
+        s = self.struct(1, 1, 64, torch.bfloat16)
+        L.check(L.load().moc_check_layout(ctypes.byref(s), _stream(self.offsets.device)))
 
     @classmethod
     def from_layout(cls, lay, device="cuda") -> "DeviceLayout":
@@ -56,7 +77,17 @@ class DeviceLayout:
 
     def struct(self, B: int, H: int, d: int, dtype: torch.dtype) -> L.MocLayout:
         return L.MocLayout(B, H, self.L, d, _dtype_code(dtype), self.C, self.offsets.data_ptr(),
-                           self.shot.data_ptr(), self.text_begin, self.text_end)
+                           self.shot.data_ptr(), self.text_begin, self.text_end,
+                           None if self.check_word is None else self.check_word.data_ptr())
+
+
+def layout_check_host(off, shot, tb: int, te: int) -> int:
+    """The library's layout check on host arrays (moc_layout_check_host): MOC_LAYOUT_* bits, 0
+    for a valid layout."""
+    o = np.ascontiguousarray(off, dtype=np.int32)
+    sh = np.ascontiguousarray(shot, dtype=np.int32)
+    return int(L.load().moc_layout_check_host(o.ctypes.data, sh.ctypes.data, len(sh),
+                                               int(o[-1]), int(tb), int(te)))
 
 
 def validate_layout(off: np.ndarray, shot: np.ndarray, tb: int, te: int) -> None:
@@ -358,15 +389,6 @@ def attend_fwd_mx(Qm: MxTensor, Km: MxTensor, V: torch.Tensor, lay: DeviceLayout
                                        float(scale), _ptr(O), _ptr(lse), _ptr(ws), ws.numel(),
                                        _stream(V.device)))
     return O, lse
-
-
-def probe_mfma(fp8: bool, blocks: int, iters: int, sink: torch.Tensor) -> None:
-    """Launch the register-only MFMA loop (moc_probe_mfma) on the current stream; sink is a
-    device float tensor of blocks * 256 elements. A measurement aid, not a layer step."""
-    if sink.dtype != torch.float32 or sink.numel() < blocks * 256 or sink.device.type != "cuda":
-        raise ValueError("sink must be a device float tensor of blocks * 256 elements")
-    L.check(L.load().moc_probe_mfma(int(bool(fp8)), int(blocks), int(iters), _ptr(sink),
-                                    _stream(sink.device)))
 
 
 def attend_bwd(Q, K, V, O, lse, dO, lay: DeviceLayout, vl: Varlen, scale: Optional[float] = None,

@@ -20,10 +20,13 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoc.so")
+# benchmark helper (register-only MFMA loops), a library of its own that only bench.py loads
+PROBE_LIB = os.path.join(PKG, "libmoc_bench_probe.so")
+PROBE_SOURCE = "probe.hip"
 ARCH = "gfx950"
 
 SOURCES = ["moc_api.hip", "pool.hip", "route.hip", "outer.hip", "varlen.hip", "attn_fwd.hip",
-           "mx.hip", "attn_bwd.hip", "probe.hip"]
+           "mx.hip", "attn_bwd.hip", "layout_check.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
@@ -57,18 +60,25 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(jobs: int = 0, verbose: bool = False) -> str:
-    """Compile every source and link libmoc.so. Always recompiles."""
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4)
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link of {os.path.basename(out)} failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, out)
+
+
+def build(jobs: int = 0, verbose: bool = False) -> str:
+    """Compile every source and link libmoc.so (and the benchmark's probe library). Always
+    recompiles."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + [PROBE_SOURCE]
+    jobs = jobs or min(len(srcs), os.cpu_count() or 4)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], PROBE_LIB)
     return LIB
 
 

@@ -46,6 +46,7 @@ struct BwdParams {
   int text_begin, text_len, n_split;
   float scale_log2;  // softmax_scale * log2(e)
   float scale;
+  const uint32_t* chk;  // layout check word (moc_layout.check) or NULL
 };
 
 enum { BMODE_ANCHOR = 0, BMODE_ROUTED = 1 };
@@ -60,7 +61,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16_t* __restrict_
                                                        const float* __restrict__ lse,
                                                        float* __restrict__ Dq,
                                                        float* __restrict__ lse2, int64_t rows,
-                                                       int L, int Lp) {
+                                                       int L, int Lp,
+                                                       const uint32_t* __restrict__ chk) {
+  if (layout_rejected(chk)) return;
   constexpr int TPR = D / 8;
   constexpr int RPB = 256 / TPR;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / TPR;
@@ -103,6 +106,7 @@ __global__ __launch_bounds__(kBwdQNT) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) char st0[KI::BYTES];
   __shared__ __attribute__((aligned(1024))) char st1[KI::BYTES];
   __shared__ __attribute__((aligned(1024))) char st2[KI::BYTES];
+  if (layout_rejected(p.chk)) return;
 
   // upper-bound grid: blocks past the device-side work count exit; the rest are remapped so
   // each XCD takes a contiguous range of the real work items
@@ -360,6 +364,7 @@ __global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_kernel(
   using CP = QTileCopier<D, kBwdKNW>;
   __shared__ __attribute__((aligned(1024))) char st0[QTl::BYTES];
   __shared__ __attribute__((aligned(1024))) char st1[QTl::BYTES];
+  if (layout_rejected(p.chk)) return;
 
   const int nt = n_ktiles[0];
   const int nwork = nt * p.B * p.H;
@@ -578,7 +583,9 @@ __global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_kernel(
 template <int D>
 __global__ __launch_bounds__(256) void bwd_kvimage_kernel(const bf16_t* __restrict__ K,
                                                           const bf16_t* __restrict__ V, int L,
-                                                          int Lp, char* __restrict__ img) {
+                                                          int Lp, char* __restrict__ img,
+                                                          const uint32_t* __restrict__ chk) {
+  if (layout_rejected(chk)) return;
   using LT = LdsTiles<D>;
   using KI = KvImage<D>;
   constexpr int PITCH = D + 8;  // bf16
@@ -625,8 +632,10 @@ __global__ __launch_bounds__(256) void bwd_kvimage_kernel(const bf16_t* __restri
 // bucket order; gstart[NB] is the total. One workgroup.
 __global__ __launch_bounds__(1024) void bwd_gather_scan_kernel(const int32_t* __restrict__ bucket_off,
                                                                int NB,
-                                                               int32_t* __restrict__ gstart) {
+                                                               int32_t* __restrict__ gstart,
+                                                               const uint32_t* __restrict__ chk) {
   __shared__ int32_t part[1024];
+  if (layout_rejected(chk)) return;
   const int per = (NB + 1023) / 1024;
   const int a = threadIdx.x * per;
   const int e = a + per < NB ? a + per : NB;
@@ -737,6 +746,7 @@ __global__ __launch_bounds__(256) void bwd_qblock_kernel(
   __shared__ __attribute__((aligned(16))) bf16_t so[32 * (D + 4)];
   __shared__ int32_t tok[32];
   __shared__ __attribute__((aligned(16))) float sst[64];
+  if (layout_rejected(p.chk)) return;
   int bh, first, end, b0 = 0, n = 0;
   size_t blk0;  // block index of position `first`
   if (MODE == QB_SEQ) {
@@ -778,6 +788,7 @@ __global__ __launch_bounds__(256) void bwd_text_reduce_kernel(const float* __res
                                                               BwdParams p,
                                                               bf16_t* __restrict__ dK,
                                                               bf16_t* __restrict__ dV) {
+  if (layout_rejected(p.chk)) return;
   const int64_t n = static_cast<int64_t>(p.B) * p.H * p.text_len * D;
   const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (e >= n) return;
@@ -878,7 +889,7 @@ static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   const int64_t rows = static_cast<int64_t>(lay->B) * lay->H * lay->L;
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL((moc::bwd_prep_kernel<D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, st,
-                     o, g, lse, Dq, l2, rows, lay->L, Lp);
+                     o, g, lse, Dq, l2, rows, lay->L, Lp, lay->check);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -890,13 +901,14 @@ static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   p.scale_log2 = scale * moc::kLog2e;
   p.scale = scale;
   p.Lp = Lp;
+  p.chk = lay->check;
   const int BH = lay->B * lay->H;
   hipLaunchKernelGGL((moc::bwd_kvimage_kernel<D>), dim3(Lp / moc::kBN, BH), dim3(256), 0, st, k,
-                     v, lay->L, Lp, kvimg);
+                     v, lay->L, Lp, kvimg, lay->check);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int NB = BH * lay->C;
   hipLaunchKernelGGL(moc::bwd_gather_scan_kernel, dim3(1), dim3(1024), 0, st, vl->bucket_off, NB,
-                     gstart);
+                     gstart, lay->check);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((moc::bwd_qblock_kernel<D, moc::QB_SEQ>),
                      dim3((Lp + moc::kBwdQBM - 1) / moc::kBwdQBM, BH), dim3(256), 0, st, q, g, Dq,

@@ -53,6 +53,7 @@ struct AttnParams {
   int B, H, L, C, S;
   int max_tiles;
   float scale_log2;  // softmax_scale * log2(e)
+  const uint32_t* chk;  // layout check word (moc_layout.check) or NULL
 };
 
 enum { MODE_ANCHOR = 0, MODE_ROUTED = 1 };
@@ -68,6 +69,7 @@ __global__ __launch_bounds__(kNT) void attn_fwd_kernel(
   using TL = Tiles<T, D, kNT>;
   constexpr int QB = kQB;
   __shared__ __attribute__((aligned(16))) T lds[2 * TL::STAGE];
+  if (layout_rejected(p.chk)) return;
 
   // The grid is an upper bound of the work list (its length lives on the device): blocks
   // past the real count exit, and the rest are remapped so that each XCD takes a contiguous
@@ -313,6 +315,7 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) char st1[STAGE];
   __shared__ __attribute__((aligned(1024))) char st2[STAGE];
   __shared__ __attribute__((aligned(1024))) char st3[STAGE];
+  if (layout_rejected(p.chk)) return;
 
   int bh, q_lo, nq, r1a, r1b, r2a, r2b, bstart = 0;
   if constexpr (MODE == MODE_ANCHOR) {
@@ -636,14 +639,14 @@ int attn_vt_rows(int L) { return (L + moc::kBN - 1) / moc::kBN * moc::kBN; }
 
 // X [BH][L][d] -> X^T [BH][d][Lp] (bf16), the only instantiation of the transpose kernel
 hipError_t launch_transpose_rows(const void* X, void* Xt, int BH, int L, int Lp, int d,
-                                 hipStream_t st) {
+                                 const uint32_t* chk, hipStream_t st) {
   using moc::bf16_t;
   if (d == 128)
     hipLaunchKernelGGL((moc::transpose_rows_kernel<128>), dim3(Lp / moc::kBN, BH), dim3(256), 0,
-                       st, static_cast<const bf16_t*>(X), static_cast<bf16_t*>(Xt), L, Lp);
+                       st, static_cast<const bf16_t*>(X), static_cast<bf16_t*>(Xt), L, Lp, chk);
   else
     hipLaunchKernelGGL((moc::transpose_rows_kernel<64>), dim3(Lp / moc::kBN, BH), dim3(256), 0,
-                       st, static_cast<const bf16_t*>(X), static_cast<bf16_t*>(Xt), L, Lp);
+                       st, static_cast<const bf16_t*>(X), static_cast<bf16_t*>(Xt), L, Lp, chk);
   return hipGetLastError();
 }
 
@@ -659,6 +662,7 @@ static hipError_t launch_fwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   AttnParams p;
   p.B = lay->B; p.H = lay->H; p.L = lay->L; p.C = lay->C; p.S = vl->S;
   p.scale_log2 = scale * moc::kLog2e;
+  p.chk = lay->check;
   const T* q = static_cast<const T*>(Q);
   const T* k = static_cast<const T*>(K);
   const T* v = static_cast<const T*>(V);
@@ -689,9 +693,10 @@ static hipError_t launch_fwd_bf16(const moc_layout* lay, const moc_varlen* vl, c
   AttnParams p;
   p.B = lay->B; p.H = lay->H; p.L = lay->L; p.C = lay->C; p.S = vl->S;
   p.scale_log2 = scale * moc::kLog2e;
+  p.chk = lay->check;
   const int Lp = attn_vt_rows(lay->L);
   bf16_t* Vt = static_cast<bf16_t*>(vt_ws);
-  hipError_t e = launch_transpose_rows(V, Vt, lay->B * lay->H, lay->L, Lp, D, st);
+  hipError_t e = launch_transpose_rows(V, Vt, lay->B * lay->H, lay->L, Lp, D, lay->check, st);
   if (e != hipSuccess) return e;
   const bool mx = Qs != nullptr;
   if (vl->S > 0 && vl->max_rtiles > 0) {

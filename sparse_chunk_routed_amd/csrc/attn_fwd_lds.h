@@ -139,8 +139,10 @@ struct StageCopier {
 template <int D>
 __global__ __launch_bounds__(256) void transpose_rows_kernel(const bf16_t* __restrict__ V,
                                                              bf16_t* __restrict__ Vt, int L,
-                                                             int Lp) {
+                                                             int Lp,
+                                                             const uint32_t* __restrict__ chk) {
   __shared__ __attribute__((aligned(16))) bf16_t tile[kBN * (D + 8)];
+  if (layout_rejected(chk)) return;
   const int bh = blockIdx.y;
   const int k0 = blockIdx.x * kBN;
   for (int e = threadIdx.x; e < kBN * D / 8; e += blockDim.x) {

@@ -35,7 +35,6 @@ hipError_t launch_attn_fwd_mx(const moc_layout* lay, const moc_varlen* vl, const
                               float* plse, void* vt_ws, hipStream_t st);
 hipError_t launch_mx_quantize(const moc_layout* lay, const void* X, uint8_t* codes,
                               uint8_t* scales, hipStream_t st);
-hipError_t launch_mfma_probe(int fp8, int blocks, int iters, float* sink, hipStream_t st);
 hipError_t launch_attn_bwd(const moc_layout* lay, const moc_varlen* vl, const void* Q,
                            const void* K, const void* V, const void* O, const float* lse,
                            const void* dO, float scale, void* dQ, void* dK, void* dV,
@@ -44,6 +43,8 @@ size_t attn_bwd_workspace(const moc_layout* lay, int S);
 int attn_tile_rows();
 int attn_bwd_key_rows();
 int attn_bwd_text_split(int L);
+hipError_t launch_layout_check(const moc_layout* lay, hipStream_t st);
+uint32_t layout_check_host(const int32_t* off, const int32_t* shot, int C, int L, int tb, int te);
 }  // namespace moc_host
 
 namespace {
@@ -152,6 +153,14 @@ moc_status hip_status(hipError_t e, const char* what) {
   return fail(MOC_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// With moc_layout.check set, every entry point first enqueues the layout check kernel; the
+// call's kernels then skip their work if the word is non-zero.
+moc_status run_layout_check(const moc_layout* lay, void* stream) {
+  if (!lay->check) return MOC_OK;
+  return hip_status(moc_host::launch_layout_check(lay, static_cast<hipStream_t>(stream)),
+                    "layout check launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -166,6 +175,7 @@ const char* moc_status_string(moc_status s) {
     case MOC_EUNSUPPORTED: return "MOC_EUNSUPPORTED";
     case MOC_EHIP: return "MOC_EHIP";
     case MOC_EINTERNAL: return "MOC_EINTERNAL";
+    case MOC_ELAYOUT: return "MOC_ELAYOUT";
   }
   return "MOC_UNKNOWN";
 }
@@ -219,6 +229,7 @@ moc_status moc_pool_keys(const moc_layout* lay, const void* K, float* kbar, void
     if (s != MOC_OK) return s;
     if (!K || !kbar) return fail(MOC_EINVAL, "K or kbar is NULL");
     if (static_cast<const void*>(kbar) == K) return fail(MOC_EINVAL, "kbar aliases K");
+    if ((s = run_layout_check(lay, stream)) != MOC_OK) return s;
     return hip_status(moc_host::launch_pool(lay, K, kbar, static_cast<hipStream_t>(stream)),
                       "pool launch");
   } catch (...) {
@@ -254,10 +265,12 @@ moc_status route_impl(const moc_layout* lay, const moc_route_cfg* cfg, const voi
   p.seed = cfg->seed;
   p.cmask = cmask;
   p.cmask_w = (lay->C + 31) / 32;
+  p.chk = lay->check;
   if (p.drop_in) {
     s = moc_poisson_thresholds(cfg->lambda, cfg->max_drop_in, p.thr);
     if (s != MOC_OK) return s;
   }
+  if ((s = run_layout_check(lay, stream)) != MOC_OK) return s;
   return hip_status(moc_host::launch_route(lay, p, Q, kbar, sel, nsel, ws,
                                            static_cast<hipStream_t>(stream)),
                     "route launch");
@@ -305,6 +318,7 @@ moc_status moc_route_outer(const moc_layout* lay, const int32_t* seg_chunk, int3
     if (!ws || ws_bytes < need)
       return fail(MOC_EWORKSPACE, "OUTER workspace needs %zu bytes (got %zu)", need,
                   ws ? ws_bytes : size_t(0));
+    if ((s = run_layout_check(lay, stream)) != MOC_OK) return s;
     return hip_status(moc_host::launch_route_outer(lay, seg_chunk, nseg, M, causal, Q, K,
                                                    seg_sel, seg_nsel, cand_mask, ws,
                                                    static_cast<hipStream_t>(stream)),
@@ -355,6 +369,8 @@ moc_status moc_build_varlen(const moc_layout* lay, const moc_route_cfg* cfg, con
     p.text_begin = lay->text_begin; p.text_end = lay->text_end;
     p.key_rows = moc_host::attn_bwd_key_rows(); p.max_ktiles = z.max_ktiles;
     p.n_text_split = z.n_text_split;
+    p.chk = lay->check;
+    if ((s = run_layout_check(lay, stream)) != MOC_OK) return s;
     return hip_status(moc_host::launch_varlen(lay, p, sel, nsel, counts, totals, tile_base, out,
                                               pair_count, static_cast<hipStream_t>(stream)),
                       "varlen launch");
@@ -401,6 +417,7 @@ moc_status moc_attend_fwd(const moc_layout* lay, const moc_varlen* vl, const voi
     float* plse = reinterpret_cast<float*>(w);
     w += align_up(sizeof(float) * (rows > 0 ? rows : 1));
     void* vt = w;  // transposed V (bf16 layouts)
+    if ((s = run_layout_check(lay, stream)) != MOC_OK) return s;
     return hip_status(moc_host::launch_attn_fwd(lay, vl, Q, K, V, softmax_scale, O, lse, pO, plse,
                                                 vt, static_cast<hipStream_t>(stream)),
                       "attention forward launch");
@@ -419,6 +436,7 @@ moc_status moc_mx_quantize(const moc_layout* lay, const void* X, uint8_t* codes,
     if (static_cast<const void*>(codes) == X || static_cast<const void*>(scales) == X ||
         codes == scales)
       return fail(MOC_EINVAL, "outputs alias");
+    if ((s = run_layout_check(lay, stream)) != MOC_OK) return s;
     return hip_status(moc_host::launch_mx_quantize(lay, X, codes, scales,
                                                    static_cast<hipStream_t>(stream)),
                       "MXFP8 quantisation launch");
@@ -454,27 +472,13 @@ moc_status moc_attend_fwd_mx(const moc_layout* lay, const moc_varlen* vl, const 
     w += align_up(sizeof(float) * (rows > 0 ? rows : 1) * lay->d);
     float* plse = reinterpret_cast<float*>(w);
     w += align_up(sizeof(float) * (rows > 0 ? rows : 1));
+    if ((s = run_layout_check(lay, stream)) != MOC_OK) return s;
     return hip_status(moc_host::launch_attn_fwd_mx(lay, vl, Qc, Qs, Kc, Ks, V, softmax_scale, O,
                                                    lse, pO, plse, w,
                                                    static_cast<hipStream_t>(stream)),
                       "quantised-scores attention forward launch");
   } catch (...) {
     return fail(MOC_EINTERNAL, "exception in moc_attend_fwd_mx");
-  }
-}
-
-moc_status moc_probe_mfma(int32_t fp8, int32_t blocks, int32_t iters, float* sink,
-                          void* stream) {
-  try {
-    if (fp8 != 0 && fp8 != 1) return fail(MOC_EINVAL, "fp8 must be 0 or 1");
-    if (blocks < 1 || blocks > 65535) return fail(MOC_EINVAL, "blocks must be in [1, 65535]");
-    if (iters < 1 || iters > 10000000) return fail(MOC_EINVAL, "iters must be in [1, 1e7]");
-    if (!sink) return fail(MOC_EINVAL, "sink is NULL");
-    return hip_status(moc_host::launch_mfma_probe(fp8, blocks, iters, sink,
-                                                  static_cast<hipStream_t>(stream)),
-                      "MFMA probe launch");
-  } catch (...) {
-    return fail(MOC_EINTERNAL, "exception in moc_probe_mfma");
   }
 }
 
@@ -501,6 +505,8 @@ moc_status moc_attend_bwd(const moc_layout* lay, const moc_varlen* vl, const voi
     if (!ws || ws_bytes < need)
       return fail(MOC_EWORKSPACE, "BWD workspace needs %zu bytes (got %zu)", need,
                   ws ? ws_bytes : size_t(0));
+    if (lay->dtype != MOC_BF16) return fail(MOC_EUNSUPPORTED, "backward not available");
+    if ((s = run_layout_check(lay, stream)) != MOC_OK) return s;
     hipError_t e = moc_host::launch_attn_bwd(lay, vl, Q, K, V, O, lse, dO, softmax_scale, dQ, dK,
                                              dV, ws, ws_bytes, static_cast<hipStream_t>(stream));
     if (e == hipErrorNotSupported) return fail(MOC_EUNSUPPORTED, "backward not available");
@@ -508,6 +514,43 @@ moc_status moc_attend_bwd(const moc_layout* lay, const moc_varlen* vl, const voi
   } catch (...) {
     return fail(MOC_EINTERNAL, "exception in moc_attend_bwd");
   }
+}
+
+moc_status moc_check_layout(const moc_layout* lay, void* stream) {
+  try {
+    moc_status s = check_layout(lay);
+    if (s != MOC_OK) return s;
+    if (!lay->check) return fail(MOC_EINVAL, "moc_check_layout needs lay->check");
+    return run_layout_check(lay, stream);
+  } catch (...) {
+    return fail(MOC_EINTERNAL, "exception in moc_check_layout");
+  }
+}
+
+uint32_t moc_layout_check_host(const int32_t* chunk_offsets, const int32_t* chunk_shot, int32_t C,
+                               int32_t L, int32_t text_begin, int32_t text_end) {
+  if (!chunk_offsets || !chunk_shot || C < 1) return MOC_LAYOUT_BAD_START | MOC_LAYOUT_BAD_END;
+  return moc_host::layout_check_host(chunk_offsets, chunk_shot, C, L, text_begin, text_end);
+}
+
+moc_status moc_layout_status(uint32_t word) {
+  if (word == 0) return MOC_OK;
+  static const struct { uint32_t bit; const char* what; } kBits[] = {
+      {MOC_LAYOUT_BAD_START, "chunk_offsets[0] != 0"},
+      {MOC_LAYOUT_NOT_INCREASING, "chunk offsets not strictly increasing"},
+      {MOC_LAYOUT_BAD_END, "chunk_offsets[C] != L"},
+      {MOC_LAYOUT_BAD_SHOT_ID, "a shot id below -1"},
+      {MOC_LAYOUT_BAD_TEXT, "a chunk straddles the text range, or shot -1 is not exactly the "
+                            "text chunks"},
+      {MOC_LAYOUT_SHOT_SPLIT, "a shot's chunks are not contiguous"},
+  };
+  std::string msg = "layout check word 0x";
+  char hex[16];
+  snprintf(hex, sizeof(hex), "%x", word);
+  msg += hex;
+  for (const auto& b : kBits)
+    if (word & b.bit) msg += std::string("; ") + b.what;
+  return fail(MOC_ELAYOUT, "%s", msg.c_str());
 }
 
 }  // extern "C"

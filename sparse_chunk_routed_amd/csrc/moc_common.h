@@ -55,6 +55,13 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
 
 __device__ __forceinline__ int popc(uint32_t x) { return __builtin_popcount(x); }
 
+// The layout check word of the call (moc_layout.check, NULL when the check is off): a kernel
+// whose call's layout failed the device check returns at its start, before reading anything the
+// layout would index.
+__device__ __forceinline__ bool layout_rejected(const uint32_t* check) {
+  return check != nullptr && *check != 0u;
+}
+
 // Chunk containing token t: largest c with off[c] <= t (off has C+1 entries).
 __device__ __forceinline__ int chunk_of(const int32_t* off, int C, int t) {
   int lo = 0, hi = C - 1;

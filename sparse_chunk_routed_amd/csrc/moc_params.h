@@ -15,12 +15,14 @@ struct RouteParams {
   uint64_t thr[MOC_MAX_DROP_IN];  // drop-in Poisson CDF thresholds (x 2^32)
   const uint32_t* cmask;          // optional candidate mask [B*H][C][cmask_w] (outer routing)
   int cmask_w;
+  const uint32_t* chk;            // layout check word (moc_layout.check) or NULL
 };
 
 struct VarlenParams {
   int B, H, L, C, S, nqt, tile_rows, max_rtiles, max_atiles;
   int text_begin, text_end;
   int key_rows, max_ktiles, n_text_split;  // backward key tiles
+  const uint32_t* chk;                     // layout check word (moc_layout.check) or NULL
 };
 
 }  // namespace moc

@@ -19,7 +19,9 @@ typedef __attribute__((ext_vector_type(4))) uint32_t mx_u32x4;
 template <int D>
 __global__ __launch_bounds__(256) void mx_quant_kernel(const bf16_t* __restrict__ X, int L, int Lp,
                                                        int64_t nblk, uint8_t* __restrict__ codes,
-                                                       uint8_t* __restrict__ scales) {
+                                                       uint8_t* __restrict__ scales,
+                                                       const uint32_t* __restrict__ chk) {
+  if (layout_rejected(chk)) return;
   constexpr int NB = D / 32;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= nblk) return;
@@ -83,10 +85,10 @@ hipError_t launch_mx_quantize(const moc_layout* lay, const void* X, uint8_t* cod
   const moc::bf16_t* x = static_cast<const moc::bf16_t*>(X);
   if (lay->d == 128)
     hipLaunchKernelGGL((moc::mx_quant_kernel<128>), dim3(static_cast<unsigned>(grid)), dim3(256),
-                       0, st, x, lay->L, Lp, nblk, codes, scales);
+                       0, st, x, lay->L, Lp, nblk, codes, scales, lay->check);
   else
     hipLaunchKernelGGL((moc::mx_quant_kernel<64>), dim3(static_cast<unsigned>(grid)), dim3(256),
-                       0, st, x, lay->L, Lp, nblk, codes, scales);
+                       0, st, x, lay->L, Lp, nblk, codes, scales, lay->check);
   return hipGetLastError();
 }
 

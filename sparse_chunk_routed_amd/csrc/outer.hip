@@ -1,9 +1,10 @@
 // K2b: outer-loop context routing - a coarse router over large context segments.
 //
-// Source: "Mixture of Contexts for Long Video Generation | Summary", Appendix I (a coarse router
-// first selects the top-M large context segments by the similarity of mean-pooled features of
-// the current query block and of the candidate segments, then passes those segments and the
-// mandatory context to the inner MoC router).
+// Source: "Mixture of Contexts for Long Video Generation | Summary", Appendix I. Routing runs on
+// two levels there for long autoregressive generation: whole segments are ranked first, by
+// comparing averaged features of the current block of queries with averaged features of each
+// other segment, and the ordinary chunk router then only looks inside the few best segments
+// (the mandatory context stays attached).
 //
 // Segments are given groups of whole chunks (seg_chunk[nseg+1]); a query's block is its own
 // segment. The pass, without host synchronisation:
@@ -25,7 +26,9 @@ __global__ __launch_bounds__(256) void outer_seg_kernel(const int32_t* __restric
                                                         const int32_t* __restrict__ chunk_shot,
                                                         const int32_t* __restrict__ seg_chunk,
                                                         int nseg, int32_t* __restrict__ seg_tok,
-                                                        int32_t* __restrict__ seg_text) {
+                                                        int32_t* __restrict__ seg_text,
+                                                        const uint32_t* __restrict__ chk) {
+  if (layout_rejected(chk)) return;
   for (int s = threadIdx.x; s <= nseg; s += blockDim.x) {
     seg_tok[s] = chunk_offsets[seg_chunk[s]];
     if (s < nseg) seg_text[s] = chunk_shot[seg_chunk[s]] < 0 ? 1 : 0;
@@ -39,7 +42,9 @@ __global__ __launch_bounds__(D) void outer_seg_mean_kernel(const double* __restr
                                                            const int32_t* __restrict__ seg_chunk,
                                                            const int32_t* __restrict__ seg_tok,
                                                            int C, int nseg,
-                                                           float* __restrict__ feat) {
+                                                           float* __restrict__ feat,
+                                                           const uint32_t* __restrict__ chk) {
+  if (layout_rejected(chk)) return;
   const int sg = blockIdx.x, bh = blockIdx.y, j = threadIdx.x;
   double h = 0.0, l = 0.0;
   for (int c = seg_chunk[sg]; c < seg_chunk[sg + 1]; ++c) {
@@ -63,7 +68,9 @@ __global__ __launch_bounds__(64) void outer_route_kernel(const float* __restrict
                                                          const int32_t* __restrict__ seg_text,
                                                          int nseg, int M, int Ms, int causal,
                                                          int32_t* __restrict__ seg_sel,
-                                                         int32_t* __restrict__ seg_nsel) {
+                                                         int32_t* __restrict__ seg_nsel,
+                                                         const uint32_t* __restrict__ chk) {
+  if (layout_rejected(chk)) return;
   constexpr int DPL = D / 64;
   const int sq = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
   const float* q = qseg + (static_cast<size_t>(bh) * nseg + sq) * D;
@@ -129,7 +136,9 @@ __global__ __launch_bounds__(64) void outer_mask_kernel(const int32_t* __restric
                                                         const int32_t* __restrict__ seg_sel,
                                                         const int32_t* __restrict__ seg_nsel,
                                                         int Ms, int C, int W,
-                                                        uint32_t* __restrict__ cmask) {
+                                                        uint32_t* __restrict__ cmask,
+                                                        const uint32_t* __restrict__ chk) {
+  if (layout_rejected(chk)) return;
   const int cq = blockIdx.x, bh = blockIdx.y;
   // the segment holding chunk cq: the last s with seg_chunk[s] <= cq
   int lo = 0, hi = nseg;  // seg_chunk[lo] <= cq < seg_chunk[hi]
@@ -187,7 +196,7 @@ hipError_t launch_route_outer(const moc_layout* lay, const int32_t* seg_chunk, i
   float* kseg = reinterpret_cast<float*>(w); w += z.feat;
   double* part = reinterpret_cast<double*>(w); w += z.part;
   hipLaunchKernelGGL(moc::outer_seg_kernel, dim3(1), dim3(256), 0, st, lay->chunk_offsets,
-                     lay->chunk_shot, seg_chunk, nseg, seg_tok, seg_text);
+                     lay->chunk_shot, seg_chunk, nseg, seg_tok, seg_text, lay->check);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int BH = lay->B * lay->H;
@@ -197,23 +206,23 @@ hipError_t launch_route_outer(const moc_layout* lay, const int32_t* seg_chunk, i
     float* feat = pass == 0 ? qseg : kseg;
     if (lay->d == 128)
       hipLaunchKernelGGL((moc::outer_seg_mean_kernel<128>), dim3(nseg, BH), dim3(128), 0, st,
-                         part, seg_chunk, seg_tok, lay->C, nseg, feat);
+                         part, seg_chunk, seg_tok, lay->C, nseg, feat, lay->check);
     else
       hipLaunchKernelGGL((moc::outer_seg_mean_kernel<64>), dim3(nseg, BH), dim3(64), 0, st,
-                         part, seg_chunk, seg_tok, lay->C, nseg, feat);
+                         part, seg_chunk, seg_tok, lay->C, nseg, feat, lay->check);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int Ms = M < nseg ? M : nseg;
   if (lay->d == 128)
     hipLaunchKernelGGL((moc::outer_route_kernel<128>), dim3(nseg, BH), dim3(64), 0, st, qseg,
-                       kseg, seg_text, nseg, Ms, Ms, causal, seg_sel, seg_nsel);
+                       kseg, seg_text, nseg, Ms, Ms, causal, seg_sel, seg_nsel, lay->check);
   else
     hipLaunchKernelGGL((moc::outer_route_kernel<64>), dim3(nseg, BH), dim3(64), 0, st, qseg,
-                       kseg, seg_text, nseg, Ms, Ms, causal, seg_sel, seg_nsel);
+                       kseg, seg_text, nseg, Ms, Ms, causal, seg_sel, seg_nsel, lay->check);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int W = (lay->C + 31) / 32;
   hipLaunchKernelGGL(moc::outer_mask_kernel, dim3(lay->C, BH), dim3(64), 0, st, seg_chunk, nseg,
-                     seg_sel, seg_nsel, Ms, lay->C, W, cmask);
+                     seg_sel, seg_nsel, Ms, lay->C, W, cmask, lay->check);
   return hipGetLastError();
 }
 

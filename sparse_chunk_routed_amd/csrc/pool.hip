@@ -38,11 +38,13 @@ template <typename T, int D, bool PARTIAL = false>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ K,
                                                    const int32_t* __restrict__ off,
                                                    float* __restrict__ kbar, int L, int C,
+                                                   const uint32_t* __restrict__ chk,
                                                    double* __restrict__ part = nullptr) {
   constexpr int VEC = 16 / sizeof(T);
   constexpr int TPR = D / VEC;     // threads per row
   constexpr int RPI = 256 / TPR;   // rows per pass
   __shared__ double sh[2][RPI][D];
+  if (layout_rejected(chk)) return;
 
   const int c = blockIdx.x;
   const int bh = blockIdx.y;
@@ -108,7 +110,8 @@ static hipError_t launch_pool_t(const moc_layout* lay, const void* K, float* kba
                                 hipStream_t st) {
   dim3 grid(lay->C, lay->B * lay->H);
   hipLaunchKernelGGL((moc::pool_kernel<T, D>), grid, dim3(256), 0, st,
-                     static_cast<const T*>(K), lay->chunk_offsets, kbar, lay->L, lay->C);
+                     static_cast<const T*>(K), lay->chunk_offsets, kbar, lay->L, lay->C,
+                     lay->check);
   return hipGetLastError();
 }
 
@@ -118,7 +121,7 @@ static hipError_t launch_pool_partial_t(const moc_layout* lay, const void* X, do
   dim3 grid(lay->C, lay->B * lay->H);
   hipLaunchKernelGGL((moc::pool_kernel<T, D, true>), grid, dim3(256), 0, st,
                      static_cast<const T*>(X), lay->chunk_offsets, nullptr, lay->L, lay->C,
-                     part);
+                     lay->check, part);
   return hipGetLastError();
 }
 

@@ -1,6 +1,14 @@
-// Measurement aid, not a step of the layer: register-only MFMA loops that show the matrix-core
-// rate this chip sustains under its clock and power limits (bf16 32x32x16, and fp8 32x32x64 with
-// E8M0 block scales), next to which the attention kernels' MFMA rates are read.
+// Benchmark helper, not part of libmoc and not a step of the layer: register-only MFMA loops
+// that show the matrix-core rate this chip sustains under its clock and power limits (bf16
+// 32x32x16, and fp8 32x32x64 with E8M0 block scales), next to which the attention kernels' MFMA
+// rates are read. Built on its own into libmoc_bench_probe.so, which only the benchmark loads.
+//
+//   int moc_bench_probe_mfma(int fp8, int blocks, int iters, float* sink, void* stream)
+//     Launches `blocks` workgroups of 4 waves on `stream` (a hipStream_t); every wave runs `iters`
+//     rounds of 8 independent 32x32x16 bf16 MFMAs (fp8 = 0) or 32x32x64 e4m3 MFMAs with unit
+//     scales (fp8 = 1) and writes one float per thread to sink (device float [blocks * 256]).
+//     FLOPs = blocks * 4 * iters * 8 * 2 * 32 * 32 * (16 or 64). Returns 0 when launched, 1 on a
+//     bad argument, 2 when the launch fails.
 #include "moc_common.h"
 
 namespace moc {
@@ -51,16 +59,16 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* __res
 
 }  // namespace moc
 
-namespace moc_host {
-
-hipError_t launch_mfma_probe(int fp8, int blocks, int iters, float* sink, hipStream_t st) {
+extern "C" int moc_bench_probe_mfma(int fp8, int blocks, int iters, float* sink, void* stream) {
+  if ((fp8 != 0 && fp8 != 1) || blocks < 1 || blocks > 65535 || iters < 1 || iters > 10000000 ||
+      !sink)
+    return 1;
+  hipStream_t st = static_cast<hipStream_t>(stream);
   if (fp8)
     hipLaunchKernelGGL((moc::mfma_probe_kernel<true>), dim3(blocks), dim3(256), 0, st, iters,
                        sink);
   else
     hipLaunchKernelGGL((moc::mfma_probe_kernel<false>), dim3(blocks), dim3(256), 0, st, iters,
                        sink);
-  return hipGetLastError();
+  return hipGetLastError() == hipSuccess ? 0 : 2;
 }
-
-}  // namespace moc_host

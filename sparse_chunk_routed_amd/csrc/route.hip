@@ -189,6 +189,7 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ Q,
   __shared__ float kb[CB * D];
   __shared__ int32_t s_off[MOC_MAX_C + 1];
   __shared__ int32_t s_shot[MOC_MAX_C];
+  if (layout_rejected(p.chk)) return;
 
   const int L = p.L, C = p.C;
   const int bh = blockIdx.y;
@@ -280,7 +281,9 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ Q,
 template <int D>
 __global__ __launch_bounds__(256) void route_split_kernel(const float* __restrict__ kbar,
                                                           bf16_t* __restrict__ split, int C,
-                                                          int64_t n) {
+                                                          int64_t n,
+                                                          const uint32_t* __restrict__ chk) {
+  if (layout_rejected(chk)) return;
   const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (e >= n) return;
   const int64_t per = static_cast<int64_t>(C) * D;
@@ -318,6 +321,7 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const bf16_t* __restric
   __shared__ __attribute__((aligned(16))) bf16_t ks[3 * CB * KSTR];
   __shared__ int32_t s_off[MOC_MAX_C + 1];
   __shared__ int32_t s_shot[MOC_MAX_C];
+  if (layout_rejected(p.chk)) return;
 
   const int L = p.L, C = p.C;
   const int bh = blockIdx.y;
@@ -458,6 +462,7 @@ __global__ __launch_bounds__(64 * NW) void route_mfma_persist_kernel(
   __shared__ int32_t s_off[MOC_MAX_C + 1];
   __shared__ int32_t s_shot[MOC_MAX_C];
   __shared__ int32_t s_sh0[kRouteCB], s_sh1[kRouteCB];  // chunk range [s_sh0, s_sh1) of c's shot
+  if (layout_rejected(p.chk)) return;
 
   const int L = p.L, C = p.C;
   const int bh = blockIdx.y;
@@ -631,7 +636,7 @@ static hipError_t launch_route_t(const moc_layout* lay, const RouteParams& p, co
     moc::bf16_t* split = static_cast<moc::bf16_t*>(ws);
     const int64_t n = static_cast<int64_t>(lay->B) * lay->H * lay->C * D;
     hipLaunchKernelGGL((moc::route_split_kernel<D>), dim3((n + 255) / 256), dim3(256), 0, st,
-                       kbar, split, lay->C, n);
+                       kbar, split, lay->C, n, p.chk);
     const int ntile = (lay->L + 255) / 256;
     const int BH = lay->B * lay->H;
     if (lay->C <= moc::kRouteCB) {

@@ -48,6 +48,7 @@ __global__ __launch_bounds__(256) void inv_count_kernel(const int32_t* __restric
                                                         VarlenParams p,
                                                         int32_t* __restrict__ counts) {
   __shared__ uint32_t bm[MOC_MAX_C * kInvWords];
+  if (layout_rejected(p.chk)) return;
   const int tile = blockIdx.x, bh = blockIdx.y;
   build_bitmap(bm, sel, nsel, bh, tile, p);
   for (int c = threadIdx.x; c < p.C; c += blockDim.x) {
@@ -61,8 +62,10 @@ __global__ __launch_bounds__(256) void inv_count_kernel(const int32_t* __restric
 // Exclusive scan of one bucket's per-tile counts (in place); bucket total -> totals.
 __global__ __launch_bounds__(256) void inv_scan_bucket_kernel(int32_t* __restrict__ counts,
                                                               int32_t* __restrict__ totals,
-                                                              int nqt) {
+                                                              int nqt,
+                                                              const uint32_t* __restrict__ chk) {
   __shared__ int32_t part[256];
+  if (layout_rejected(chk)) return;
   int32_t* row = counts + static_cast<size_t>(blockIdx.x) * nqt;
   const int per = (nqt + 255) / 256;
   const int a = threadIdx.x * per;
@@ -128,6 +131,7 @@ __global__ __launch_bounds__(1024) void inv_global_kernel(
   __shared__ int32_t g_text[MOC_MAX_C + 1];
   __shared__ int32_t k_base[MOC_MAX_C], k_q0[MOC_MAX_C], k_q1[MOC_MAX_C];
   __shared__ int32_t s_ng, s_nsp, s_ntxt_k;
+  if (layout_rejected(p.chk)) return;
   // the serial tile emission below walks the layout: keep it in LDS, not in global memory
   for (int i = threadIdx.x; i <= p.C; i += blockDim.x) off[i] = off_g[i];
   for (int i = threadIdx.x; i < p.C; i += blockDim.x) shot[i] = shot_g[i];
@@ -252,6 +256,7 @@ __global__ __launch_bounds__(256) void inv_scatter_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ bucket_q,
                                                           int32_t* __restrict__ slot) {
   __shared__ uint32_t bm[MOC_MAX_C * kInvWords];
+  if (layout_rejected(p.chk)) return;
   const int tile = blockIdx.x, bh = blockIdx.y;
   build_bitmap(bm, sel, nsel, bh, tile, p);
   const int t = tile * kInvTile + threadIdx.x;
@@ -289,7 +294,7 @@ hipError_t launch_varlen(const moc_layout* lay, const VarlenParams& p, const int
   hipLaunchKernelGGL(moc::inv_count_kernel, dim3(p.nqt, BH), dim3(256), 0, st, sel, nsel, p,
                      counts);
   hipLaunchKernelGGL(moc::inv_scan_bucket_kernel, dim3(NB), dim3(256), 0, st, counts, totals,
-                     p.nqt);
+                     p.nqt, p.chk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(moc::inv_global_kernel, dim3(1), dim3(1024), 0, st, totals,
