@@ -193,6 +193,23 @@ moc_status moc_route(const moc_layout *lay, const moc_route_cfg *cfg, const void
                      void *stream);
 
 /*
+ * moc_route without a workspace, for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same routing, with
+ * the same results, whose only scratch - the three bf16 terms of kbar that the MFMA router reads,
+ * B*H*C*d*6 bytes for bf16 queries, none for fp32 - lives in a static 16 MiB device buffer that
+ * the library holds on every GPU it runs on until the process ends. Allocates nothing and calls
+ * no allocating routine; the buffer's device address is looked up once per GPU on the first call
+ * there. Every call on one GPU shares that buffer and it keeps the last call's contents (it is
+ * fully rewritten before it is read): calls that overlap on one GPU, on different streams or
+ * from different threads, race and must be ordered by the caller.
+ *   Limit: B*H*C*d*6 <= 16 MiB (e.g. 12 heads x 1,024 chunks x d = 128 fits); a larger
+ *   request returns MOC_ESHAPE before anything is enqueued.
+ *   Arguments, outputs and every other rule as for moc_route.
+ */
+moc_status moc_route_noalloc(const moc_layout *lay, const moc_route_cfg *cfg, const void *Q,
+                             const float *kbar, int32_t *sel, int32_t *nsel, void *stream);
+
+/*
  * Outer-loop context routing (summary, Appendix I: routing on two levels - segments are
  * ranked by comparing the averaged queries of the current block with the averaged keys of each
  * other segment, and the chunk router then only considers the best M segments; the mandatory

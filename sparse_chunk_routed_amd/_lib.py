@@ -26,6 +26,7 @@ EXPORTS = (
     "moc_route_masked", "moc_build_varlen", "moc_attend_fwd", "moc_attend_bwd",
     "moc_mx_quantize", "moc_attend_fwd_mx", "moc_poisson_thresholds", "moc_status_string",
     "moc_last_error", "moc_check_layout", "moc_layout_check_host", "moc_layout_status",
+    "moc_route_noalloc",
 )
 
 
@@ -83,6 +84,9 @@ def load() -> ctypes.CDLL:
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                     c_void_p]
     lib.moc_route_outer.restype = c_int32
+    lib.moc_route_noalloc.argtypes = [P(MocLayout), P(MocRouteCfg), c_void_p, c_void_p,
+                                      c_void_p, c_void_p, c_void_p]
+    lib.moc_route_noalloc.restype = c_int32
     lib.moc_route_masked.argtypes = [P(MocLayout), P(MocRouteCfg), c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.moc_route_masked.restype = c_int32

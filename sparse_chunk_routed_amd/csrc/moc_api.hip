@@ -17,6 +17,8 @@ hipError_t launch_pool(const moc_layout* lay, const void* K, float* kbar, hipStr
 hipError_t launch_route(const moc_layout* lay, const moc::RouteParams& p, const void* Q,
                         const float* kbar, int32_t* sel, int32_t* nsel, void* ws, hipStream_t st);
 size_t route_workspace(const moc_layout* lay);
+size_t route_noalloc_limit();
+void* route_noalloc_scratch(hipError_t* err);
 size_t outer_workspace(const moc_layout* lay);
 hipError_t launch_route_outer(const moc_layout* lay, const int32_t* seg_chunk, int nseg, int M,
                               int causal, const void* Q, const void* K, int32_t* seg_sel,
@@ -284,6 +286,29 @@ moc_status moc_route(const moc_layout* lay, const moc_route_cfg* cfg, const void
     return route_impl(lay, cfg, Q, kbar, nullptr, sel, nsel, ws, ws_bytes, stream);
   } catch (...) {
     return fail(MOC_EINTERNAL, "exception in moc_route");
+  }
+}
+
+moc_status moc_route_noalloc(const moc_layout* lay, const moc_route_cfg* cfg, const void* Q,
+                             const float* kbar, int32_t* sel, int32_t* nsel, void* stream) {
+  try {
+    moc_status s = check_layout(lay);
+    if (s != MOC_OK) return s;
+    const size_t need = moc_host::route_workspace(lay);
+    if (need > moc_host::route_noalloc_limit())
+      return fail(MOC_ESHAPE,
+                  "moc_route_noalloc: B*H*C*d*6 = %zu bytes of scratch exceed its %zu-byte "
+                  "static buffer (use moc_route with a workspace)",
+                  need, moc_host::route_noalloc_limit());
+    void* ws = nullptr;
+    if (need > 0) {
+      hipError_t e = hipSuccess;
+      ws = moc_host::route_noalloc_scratch(&e);
+      if (!ws) return hip_status(e == hipSuccess ? hipErrorUnknown : e, "scratch lookup");
+    }
+    return route_impl(lay, cfg, Q, kbar, nullptr, sel, nsel, ws, need, stream);
+  } catch (...) {
+    return fail(MOC_EINTERNAL, "exception in moc_route_noalloc");
   }
 }
 

@@ -28,6 +28,8 @@
 // float ordering). fp32 queries use route_kernel: one thread per query, 256 queries per
 // workgroup, one (b,h) per grid row; kbar for the (b,h) is staged through LDS in blocks of
 // chunks and read by broadcast.
+#include <mutex>
+
 #include "attn_common.h"
 #include "moc_params.h"
 
@@ -623,9 +625,46 @@ __global__ __launch_bounds__(64 * NW) void route_mfma_persist_kernel(
 
 }  // namespace moc
 
+namespace moc {
+
+// Scratch of moc_route_noalloc: the three bf16 terms of kbar ([B*H][3][C][d], as route_split_kernel
+// writes them), for callers that cannot allocate. One copy per GPU, kept until the process ends
+// and shared by every call on that GPU. In host code `scratch` only names the symbol: kernels get
+// the device address that route_noalloc_scratch() looks up.
+constexpr size_t kRouteScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kRouteScratchBytes];
+
+}  // namespace moc
+
 namespace moc_host {
 
 using moc::RouteParams;
+
+constexpr int kMaxDevices = 64;
+
+size_t route_noalloc_limit() { return moc::kRouteScratchBytes; }
+
+// Device address of `scratch` on the current device, looked up once per device (with that device
+// current) and cached; nullptr with the HIP error in *err when the lookup fails.
+void* route_noalloc_scratch(hipError_t* err) {
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(moc::scratch));
+    if (*err != hipSuccess) return nullptr;
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
 
 template <typename T, int D, int KMAX, bool NOISE>
 static hipError_t launch_route_t(const moc_layout* lay, const RouteParams& p, const void* Q,

@@ -346,3 +346,20 @@ def test_layout_check_host_agrees_with_the_validators(L):
                                                bits, py_ok, or_ok)
         n_bad += bits != 0
     assert n_bad > 500
+
+
+def test_route_noalloc_rejects_requests_beyond_its_static_buffer(L):
+    """moc_route_noalloc keeps the kbar split (B*H*C*d*6 bytes for bf16) in a 16 MiB static
+    buffer: a larger request is refused on the host before anything is enqueued."""
+    lib = L.load()
+    lay = mi.build_layout(0, [1024], 2)  # 1,024 single-frame chunks, L = 2,048
+    ok = L.MocLayout(1, 12, lay.L, 128, 1, lay.C, 1, 1, 0, 0)   # 12*1024*128*6 = 9.4 MiB
+    big = L.MocLayout(1, 24, lay.L, 128, 1, lay.C, 1, 1, 0, 0)  # 18.9 MiB
+    cfg = _cfg(L, top_k=2)
+    p = ctypes.c_void_p
+    assert lib.moc_route_noalloc(ctypes.byref(big), ctypes.byref(cfg), p(1), p(2), p(3), p(4),
+                                 None) == L.MOC_ESHAPE
+    assert "16777216-byte static buffer" in lib.moc_last_error().decode()
+    assert lib.moc_workspace_bytes(ctypes.byref(ok), ctypes.byref(cfg), L.MOC_OP_ROUTE) <= 16 << 20
+    # the usual argument checks still run first
+    assert lib.moc_route_noalloc(None, ctypes.byref(cfg), p(1), p(2), p(3), p(4), None) == 1
