@@ -2,6 +2,10 @@
 
 Usage: python sparse_chunk_routed_amd/build.py [--jobs N] [--verbose]
 
+MOC_BUILD_DEFINES (extra -D flags) and MOC_BUILD_OUT (another output path for libmoc) build a
+variant of the library from the same sources next to the in-tree one, to compare kernels on one
+GPU (MOC_LIB_PATH then selects it at load time).
+
 Run as a script (or loaded by file path): importing the package would load the library that
 this rebuilds.
 """
@@ -44,10 +48,13 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmoc)")
 
 
+EXTRA_DEFINES = [d for d in os.environ.get("MOC_BUILD_DEFINES", "").split() if d]
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c",
-                                     os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + HIPCC_FLAGS + EXTRA_DEFINES + ["-I", INCLUDE, "-I", CSRC, "-c",
+                                                     os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -77,9 +84,11 @@ def build(jobs: int = 0, verbose: bool = False) -> str:
     jobs = jobs or min(len(srcs), os.cpu_count() or 4)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    _link(objs[:-1], LIB)
-    _link(objs[-1:], PROBE_LIB)
-    return LIB
+    out = os.environ.get("MOC_BUILD_OUT") or LIB
+    _link(objs[:-1], out)
+    if out == LIB:
+        _link(objs[-1:], PROBE_LIB)
+    return out
 
 
 def main(argv=None) -> int:

@@ -9,9 +9,11 @@
 // not depend on the summation order: every bf16 input and every fp32 input whose exponents
 // span less than ~80 binades is summed exactly before the single binary64 division.
 //
-// Work decomposition: one workgroup per (b, h, chunk). A chunk is a contiguous run of n_c rows
-// of d elements, so the workgroup streams it with 16-byte coalesced loads; each thread owns
-// 16/sizeof(T) consecutive columns of every RPI-th row. HBM-bound: one read of K.
+// Work decomposition: one workgroup per (b, h, chunk) and column half (bf16, d = 128: 1,356
+// chunks of a 12-head headline layer would otherwise leave a ragged last round of workgroups).
+// A chunk is a contiguous run of n_c rows of d elements, so the workgroup streams its columns
+// with 16-byte coalesced loads; each thread owns 16/sizeof(T) consecutive columns of every
+// RPI-th row. HBM-bound: one read of K.
 #include "moc_common.h"
 
 namespace moc {
@@ -34,23 +36,27 @@ __device__ __forceinline__ void dd_merge(double& hi, double& lo, double bhi, dou
 
 // PARTIAL: instead of the mean, write the chunk's double-double sum (hi, lo) to part
 // [B*H][C][D][2], for sums over groups of chunks (outer-loop routing's segment features).
-template <typename T, int D, bool PARTIAL = false>
+// NS: workgroups per chunk, each owning D / NS consecutive columns (blockIdx.z), so that more,
+// shorter workgroups leave a shorter tail; the columns' sums are independent.
+template <typename T, int D, bool PARTIAL = false, int NS = 1>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ K,
                                                    const int32_t* __restrict__ off,
                                                    float* __restrict__ kbar, int L, int C,
                                                    const uint32_t* __restrict__ chk,
                                                    double* __restrict__ part = nullptr) {
   constexpr int VEC = 16 / sizeof(T);
-  constexpr int TPR = D / VEC;     // threads per row
+  constexpr int DW = D / NS;       // columns of this workgroup
+  constexpr int TPR = DW / VEC;    // threads per row
   constexpr int RPI = 256 / TPR;   // rows per pass
-  __shared__ double sh[2][RPI][D];
+  __shared__ double sh[2][RPI][DW];
   if (layout_rejected(chk)) return;
 
   const int c = blockIdx.x;
   const int bh = blockIdx.y;
+  const int col0 = static_cast<int>(blockIdx.z) * DW;
   const int r0 = off[c];
   const int n = off[c + 1] - r0;
-  const T* base = K + (static_cast<size_t>(bh) * L + r0) * D;
+  const T* base = K + (static_cast<size_t>(bh) * L + r0) * D + col0;
   const int tr = threadIdx.x / TPR;
   const int tc = threadIdx.x % TPR;
 
@@ -85,11 +91,11 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ K,
     sh[1][tr][tc * VEC + i] = lo[i];
   }
   __syncthreads();
-  for (int j = threadIdx.x; j < D; j += blockDim.x) {
+  for (int j = threadIdx.x; j < DW; j += blockDim.x) {
     double h = 0.0, l = 0.0;
     for (int k = 0; k < RPI; ++k) dd_merge(h, l, sh[0][k][j], sh[1][k][j]);
     if constexpr (PARTIAL) {
-      double* o = part + ((static_cast<size_t>(bh) * C + c) * D + j) * 2;
+      double* o = part + ((static_cast<size_t>(bh) * C + c) * D + col0 + j) * 2;
       o[0] = h;
       o[1] = l;
       continue;
@@ -97,7 +103,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ K,
     // renormalise, then the binary64 sum is the rounded value of h + l
     double s = h + l;
     double mean = s / static_cast<double>(n);
-    kbar[(static_cast<size_t>(bh) * C + c) * D + j] = static_cast<float>(mean);
+    kbar[(static_cast<size_t>(bh) * C + c) * D + col0 + j] = static_cast<float>(mean);
   }
 }
 
@@ -108,8 +114,11 @@ namespace moc_host {
 template <typename T, int D>
 static hipError_t launch_pool_t(const moc_layout* lay, const void* K, float* kbar,
                                 hipStream_t st) {
-  dim3 grid(lay->C, lay->B * lay->H);
-  hipLaunchKernelGGL((moc::pool_kernel<T, D>), grid, dim3(256), 0, st,
+  // two workgroups per chunk (each 128 bytes of every bf16 row at d = 128) where the grid
+  // would otherwise be only a few rounds of workgroups deep
+  constexpr int NS = (sizeof(T) == 2 && D == 128) ? 2 : 1;
+  dim3 grid(lay->C, lay->B * lay->H, NS);
+  hipLaunchKernelGGL((moc::pool_kernel<T, D, false, NS>), grid, dim3(256), 0, st,
                      static_cast<const T*>(K), lay->chunk_offsets, kbar, lay->L, lay->C,
                      lay->check);
   return hipGetLastError();
