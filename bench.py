@@ -283,8 +283,10 @@ def main(argv=None) -> int:
     dOd = tensors[3].to(dev) if with_bwd else None
     lay = moc.DeviceLayout.from_layout(w.layout, dev)
     cfg = moc.RouteCfg(w.top_k, w.causal, w.p_max, w.lam, w.max_drop_in, w.seed)
-    fwd_ws = torch.empty(moc.workspace_bytes(lay, w.B, w.H, w.d, Qd.dtype, cfg, 2),
-                         dtype=torch.uint8, device=dev)
+    # the attention workspaces are sized for the routing's real total of routed rows (read once
+    # in the warm-up; the inputs are the same every step), not for the static bound B*H*L*S
+    cap = {"rows": None}
+    fwd_ws = bwd_ws = None
 
     outer = w.segments is not None
     segs = moc.DeviceSegments(w.segments, lay) if outer else None
@@ -313,6 +315,8 @@ def main(argv=None) -> int:
         sel, nsel = moc.route(Qd, kbar, lay, cfg, cand_mask=cand_mask)
         mark()
         vl = moc.build_varlen(sel, nsel, lay, cfg, w.d, Qd.dtype)
+        if cap["rows"] is not None:
+            vl.set_capacity(cap["rows"])
         mark()
         if mx:
             qm = moc.mx_quantize(Qd, lay, out=qm)
@@ -323,13 +327,28 @@ def main(argv=None) -> int:
             O, lse = moc.attend_fwd(Qd, Kd, Vd, lay, vl, ws=fwd_ws)
         mark()
         if with_bwd:
-            moc.attend_bwd(Qd, Kd, Vd, O, lse, dOd, lay, vl)
+            moc.attend_bwd(Qd, Kd, Vd, O, lse, dOd, lay, vl, ws=bwd_ws)
             mark()
         return vl
+
+    # one untimed pass at the default capacity gives the routing's total and the default sizes
+    vl0 = step()
+    ws_default = {"fwd": vl0.workspace_bytes(2), "bwd": vl0.workspace_bytes(3)}
+    cap["rows"] = vl0.total()
+    vl0.set_capacity(cap["rows"])
+    ws_used = {"fwd": vl0.workspace_bytes(2), "bwd": vl0.workspace_bytes(3)}
+    # the forward's workspace is dead once it returns (the backward reads O and lse, not the
+    # partial rows), so a step's forward and backward share one buffer of the larger size
+    fwd_ws = torch.empty(max(ws_used["fwd"], ws_used["bwd"] if with_bwd else 0),
+                         dtype=torch.uint8, device=dev)
+    bwd_ws = fwd_ws if with_bwd else None
+    del vl0
+    torch.cuda.empty_cache()
 
     for _ in range(a.warmup):
         vl = step()
     torch.cuda.synchronize()
+    vl.check_status()  # every routed row fitted the capacity
     print(f"[bench] warmup done ({a.warmup} steps)", file=sys.stderr, flush=True)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
            for _ in range(a.steps)]
@@ -383,6 +402,14 @@ def main(argv=None) -> int:
         "pairs": pairs,
         "pruned_fraction": 1.0 - pairs / (w.B * w.H * w.L * w.L),
         "attention_tflops": att_tf,
+        "workspace_bytes": {
+            "route": moc.workspace_bytes(lay, w.B, w.H, w.d, Qd.dtype, cfg, 0),
+            "varlen": int(vl.ws.numel()),
+            "fwd": ws_used["fwd"], "bwd": ws_used["bwd"] if with_bwd else 0,
+            "attention_buffer": int(fwd_ws.numel()),
+            "fwd_at_static_bound": ws_default["fwd"],
+            "bwd_at_static_bound": ws_default["bwd"] if with_bwd else 0,
+            "routed_rows": cap["rows"], "routed_rows_static_bound": int(vl.struct.routed_max)},
         "pool_gbs": pool_bytes / (stage["pool"] * 1e-3) / 1e9,
         "route_gbs": route_bytes / (stage["route"] * 1e-3) / 1e9,
         "roofline": {

@@ -140,6 +140,13 @@ typedef struct {
  *               anchor query range q0, q1, text split index), n_ktiles[0] valid, shared by every
  *               (b, h). A key tile never straddles a chunk; text keys, which every query
  *               attends, are split into n_text_split query ranges.
+ *   routed_max: B*H*L*S, the most routed (query, chunk) rows any routing of this shape has.
+ *   routed_cap: routed rows the attention workspaces are sized for (moc_attend_workspace_bytes);
+ *               routed_max after moc_build_varlen, lowered with moc_varlen_set_capacity.
+ *   status:     device word in the VARLEN workspace. Every attention call first writes it: bit 1
+ *               when the routing's total (bucket_off[B*H*C]) exceeds routed_cap, bit 2 when the
+ *               layout check word (moc_layout.check) is set; all kernels of the call then do no
+ *               work. moc_varlen_status reads it.
  */
 typedef struct {
   int32_t S;
@@ -158,7 +165,14 @@ typedef struct {
   int32_t n_text_split;
   int32_t *ktiles;
   int32_t *n_ktiles;
+  int64_t routed_max;
+  int64_t routed_cap;
+  uint32_t *status;
 } moc_varlen;
+
+/* moc_varlen.status bits */
+#define MOC_VARLEN_OVER_CAPACITY 1u  /* more routed rows than routed_cap */
+#define MOC_VARLEN_BAD_LAYOUT 2u     /* the layout check word was non-zero */
 
 /* Selection width S for a route configuration and chunk count (see moc_varlen.S). */
 int32_t moc_sel_width(const moc_route_cfg *cfg, int32_t C);
@@ -167,6 +181,30 @@ int32_t moc_sel_width(const moc_route_cfg *cfg, int32_t C);
  * arguments (see moc_last_error()). MOC_OP_OUTER is sized for MOC_MAX_SEG segments (the
  * segment count is not part of the layout). */
 size_t moc_workspace_bytes(const moc_layout *lay, const moc_route_cfg *cfg, int32_t op);
+
+/*
+ * Workspace sizing from the real routing instead of its static bound. The attention workspaces
+ * hold one row per routed (query, chunk) pair - partial outputs in the forward, partial dQ rows
+ * and gathered query images in the backward - and moc_workspace_bytes sizes them for
+ * B*H*L*S rows, which drop-in noise makes several times the rows a routing really has.
+ *   moc_varlen_total: the routing's total routed rows, bucket_off[B*H*C]. The one call of this
+ *     library that synchronises: it waits for `stream`, then copies the count to the host.
+ *   moc_varlen_set_capacity: sets vl->routed_cap (0 <= routed_cap <= vl->routed_max). Host
+ *     only; the varlen contents are unchanged. A capacity at least the total (a total from
+ *     moc_varlen_total, or a bound the caller trusts for its routing noise) gives the same
+ *     results as the default.
+ *   moc_attend_workspace_bytes: bytes of the MOC_OP_FWD or MOC_OP_BWD workspace for
+ *     vl->routed_cap rows; moc_attend_fwd(_mx) and moc_attend_bwd require at least this much.
+ *     0 on invalid arguments.
+ *   moc_varlen_status: waits for `stream` and reads vl->status: MOC_EWORKSPACE when the last
+ *     attention call found more routed rows than routed_cap (it then wrote none of its outputs),
+ *     MOC_ELAYOUT when the layout check word was set, MOC_OK otherwise.
+ */
+moc_status moc_varlen_total(const moc_layout *lay, const moc_varlen *vl, int64_t *total,
+                            void *stream);
+moc_status moc_varlen_set_capacity(moc_varlen *vl, int64_t routed_cap);
+size_t moc_attend_workspace_bytes(const moc_layout *lay, const moc_varlen *vl, int32_t op);
+moc_status moc_varlen_status(const moc_varlen *vl, void *stream);
 
 /*
  * Mean-pooled chunk keys (summary §3.1: each chunk is represented by the mean of its keys;
@@ -263,7 +301,9 @@ moc_status moc_build_varlen(const moc_layout *lay, const moc_route_cfg *cfg, con
  * softmax(q_i K_Omega^T / sqrt(d)) V_Omega; no token-level causal mask inside Omega).
  *   O:   [B,H,L,d] layout dtype; lse: device float [B,H,L], natural-log softmax denominator.
  *   softmax_scale: > 0 (usually 1/sqrt(d)).
- *   ws:  MOC_OP_FWD workspace: per-(query, routed chunk) partial results in fp32.
+ *   ws:  workspace of moc_attend_workspace_bytes(lay, vl, MOC_OP_FWD) bytes (per-(query, routed
+ *        chunk) partial results in fp32 for vl->routed_cap rows; moc_workspace_bytes(...,
+ *        MOC_OP_FWD) is the size at the default capacity).
  *   O and lse must not alias Q, K or V.
  */
 moc_status moc_attend_fwd(const moc_layout *lay, const moc_varlen *vl, const void *Q,
@@ -293,7 +333,7 @@ moc_status moc_mx_quantize(const moc_layout *lay, const void *X, uint8_t *codes,
  * same key sets, with fp32 accumulation; softmax and P.V as in moc_attend_fwd.
  *   Qc, Kc: device uint8 [B,H,Lp,d]; Qs, Ks: device uint8 [B,H,Lp,d/32].
  *   V: bf16 [B,H,L,d]; O: bf16 [B,H,L,d]; lse: float [B,H,L]; the layout's dtype must be
- *   MOC_BF16. ws: MOC_OP_FWD workspace. O and lse must not alias an input.
+ *   MOC_BF16. ws: as for moc_attend_fwd. O and lse must not alias an input.
  */
 moc_status moc_attend_fwd_mx(const moc_layout *lay, const moc_varlen *vl, const uint8_t *Qc,
                              const uint8_t *Qs, const uint8_t *Kc, const uint8_t *Ks,
@@ -304,8 +344,9 @@ moc_status moc_attend_fwd_mx(const moc_layout *lay, const moc_varlen *vl, const 
  * Attention backward with the routed sets held fixed (summary §3.1 and Appendix A: top-k is
  * not differentiable; gradients reach the selected keys and values only).
  *   Inputs: Q, K, V, O, lse from moc_attend_fwd, dO. Outputs dQ, dK, dV [B,H,L,d] in the
- *   layout dtype, fully overwritten. ws: MOC_OP_BWD workspace (fp32 row statistics,
- *   per-(query, routed chunk) dQ partials and text-key partials). Deterministic: no float
+ *   layout dtype, fully overwritten. ws: workspace of moc_attend_workspace_bytes(lay, vl,
+ *   MOC_OP_BWD) bytes (fp32 row statistics, per-(query, routed chunk) dQ partials and gathered
+ *   query images for vl->routed_cap rows, text-key partials). Deterministic: no float
  *   atomics; partial results are merged in a fixed order. bf16 layouts only (an fp32 layout
  *   returns MOC_EUNSUPPORTED).
  */

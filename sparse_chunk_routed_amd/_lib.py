@@ -12,6 +12,7 @@ LIB_PATH = os.environ.get("MOC_LIB_PATH") or os.path.join(
 
 MOC_OK, MOC_EINVAL, MOC_ESHAPE, MOC_EDTYPE, MOC_EWORKSPACE, MOC_EUNSUPPORTED, MOC_EHIP, \
     MOC_EINTERNAL, MOC_ELAYOUT = range(9)
+MOC_VARLEN_OVER_CAPACITY, MOC_VARLEN_BAD_LAYOUT = 1, 2
 # bits of the layout check word
 MOC_LAYOUT_BAD_START, MOC_LAYOUT_NOT_INCREASING, MOC_LAYOUT_BAD_END, MOC_LAYOUT_BAD_SHOT_ID, \
     MOC_LAYOUT_BAD_TEXT, MOC_LAYOUT_SHOT_SPLIT = 1, 2, 4, 8, 16, 32
@@ -26,7 +27,8 @@ EXPORTS = (
     "moc_route_masked", "moc_build_varlen", "moc_attend_fwd", "moc_attend_bwd",
     "moc_mx_quantize", "moc_attend_fwd_mx", "moc_poisson_thresholds", "moc_status_string",
     "moc_last_error", "moc_check_layout", "moc_layout_check_host", "moc_layout_status",
-    "moc_route_noalloc",
+    "moc_route_noalloc", "moc_varlen_total", "moc_varlen_set_capacity",
+    "moc_attend_workspace_bytes", "moc_varlen_status",
 )
 
 
@@ -48,7 +50,8 @@ class MocVarlen(ctypes.Structure):
                 ("slot", c_void_p), ("rtiles", c_void_p), ("n_rtiles", c_void_p),
                 ("atiles", c_void_p), ("n_atiles", c_void_p), ("scratch", c_void_p),
                 ("max_ktiles", c_int32), ("n_text_split", c_int32), ("ktiles", c_void_p),
-                ("n_ktiles", c_void_p)]
+                ("n_ktiles", c_void_p), ("routed_max", c_int64), ("routed_cap", c_int64),
+                ("status", c_void_p)]
 
 
 class MocError(RuntimeError):
@@ -114,6 +117,14 @@ def load() -> ctypes.CDLL:
     lib.moc_layout_check_host.restype = ctypes.c_uint32
     lib.moc_layout_status.argtypes = [ctypes.c_uint32]
     lib.moc_layout_status.restype = c_int32
+    lib.moc_varlen_total.argtypes = [P(MocLayout), P(MocVarlen), P(c_int64), c_void_p]
+    lib.moc_varlen_total.restype = c_int32
+    lib.moc_varlen_set_capacity.argtypes = [P(MocVarlen), c_int64]
+    lib.moc_varlen_set_capacity.restype = c_int32
+    lib.moc_attend_workspace_bytes.argtypes = [P(MocLayout), P(MocVarlen), c_int32]
+    lib.moc_attend_workspace_bytes.restype = c_size_t
+    lib.moc_varlen_status.argtypes = [P(MocVarlen), c_void_p]
+    lib.moc_varlen_status.restype = c_int32
     lib.moc_status_string.argtypes = [c_int32]
     lib.moc_status_string.restype = c_char_p
     lib.moc_last_error.argtypes = []

@@ -271,13 +271,15 @@ class Varlen:
     """The inverted index (per-chunk query buckets, slots, work tiles) and its workspace."""
 
     def __init__(self, struct: L.MocVarlen, ws: torch.Tensor, pair_count: torch.Tensor,
-                 cfg: RouteCfg, lay: DeviceLayout, B: int, H: int):
+                 cfg: RouteCfg, lay: DeviceLayout, B: int, H: int, d: int = 128,
+                 dtype: torch.dtype = torch.bfloat16):
         self.struct = struct
         self.ws = ws
         self.pair_count = pair_count
         self.cfg = cfg
         self.layout = lay
         self.B, self.H = B, H
+        self.d, self.dtype = d, dtype
 
     @property
     def S(self) -> int:
@@ -305,6 +307,37 @@ class Varlen:
     def n_atiles(self) -> int:
         return int(self._view(self.struct.n_atiles, 1).item())
 
+    def _lay(self):
+        return self.layout.struct(self.B, self.H, self.d, self.dtype)
+
+    def total(self) -> int:
+        """Total routed (query, chunk) rows of the routing (moc_varlen_total: waits for the
+        current stream)."""
+        t = ctypes.c_int64(0)
+        s = self._lay()
+        L.check(L.load().moc_varlen_total(ctypes.byref(s), ctypes.byref(self.struct),
+                                          ctypes.byref(t), _stream(self.ws.device)))
+        return int(t.value)
+
+    def set_capacity(self, routed_cap: int) -> None:
+        """Size the attention workspaces for `routed_cap` routed rows (moc_varlen_set_capacity);
+        a capacity below total() makes the attention calls write nothing (check_status)."""
+        L.check(L.load().moc_varlen_set_capacity(ctypes.byref(self.struct), int(routed_cap)))
+
+    def workspace_bytes(self, op: int) -> int:
+        """Bytes of the FWD or BWD workspace at the current capacity."""
+        s = self._lay()
+        n = int(L.load().moc_attend_workspace_bytes(ctypes.byref(s), ctypes.byref(self.struct),
+                                                    op))
+        if n == 0:
+            raise L.MocError(L.MOC_EINVAL, L.load().moc_last_error().decode())
+        return n
+
+    def check_status(self) -> None:
+        """Wait for the current stream; raise MocError if the last attention call found more
+        routed rows than the capacity (MOC_EWORKSPACE) or a set layout check word."""
+        L.check(L.load().moc_varlen_status(ctypes.byref(self.struct), _stream(self.ws.device)))
+
 
 def build_varlen(sel: torch.Tensor, nsel: torch.Tensor, lay: DeviceLayout, cfg: RouteCfg,
                  d: int, dtype: torch.dtype) -> Varlen:
@@ -319,7 +352,7 @@ def build_varlen(sel: torch.Tensor, nsel: torch.Tensor, lay: DeviceLayout, cfg: 
     L.check(lib.moc_build_varlen(ctypes.byref(s), ctypes.byref(cfg.struct()),
                                  _ptr(sel) if S > 0 else None, _ptr(nsel), ctypes.byref(vs),
                                  _ptr(pair), _ptr(ws), ws_n, _stream(nsel.device)))
-    return Varlen(vs, ws, pair, cfg, lay, B, H)
+    return Varlen(vs, ws, pair, cfg, lay, B, H, d, dtype)
 
 
 def attend_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, lay: DeviceLayout,
@@ -331,7 +364,7 @@ def attend_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, lay: DeviceLay
         scale = 1.0 / math.sqrt(d)
     O = torch.empty_like(Q)
     lse = torch.empty((B, H, Lq), dtype=torch.float32, device=Q.device)
-    need = workspace_bytes(lay, B, H, d, Q.dtype, vl.cfg, L.MOC_OP_FWD)
+    need = vl.workspace_bytes(L.MOC_OP_FWD)
     if ws is None or ws.numel() < need:
         ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
     s = lay.struct(B, H, d, Q.dtype)
@@ -380,7 +413,7 @@ def attend_fwd_mx(Qm: MxTensor, Km: MxTensor, V: torch.Tensor, lay: DeviceLayout
         scale = 1.0 / math.sqrt(d)
     O = torch.empty_like(V)
     lse = torch.empty((B, H, Lq), dtype=torch.float32, device=V.device)
-    need = workspace_bytes(lay, B, H, d, V.dtype, vl.cfg, L.MOC_OP_FWD)
+    need = vl.workspace_bytes(L.MOC_OP_FWD)
     if ws is None or ws.numel() < need:
         ws = torch.empty(need, dtype=torch.uint8, device=V.device)
     s = lay.struct(B, H, d, V.dtype)
@@ -401,7 +434,7 @@ def attend_bwd(Q, K, V, O, lse, dO, lay: DeviceLayout, vl: Varlen, scale: Option
     dQ = torch.empty_like(Q)
     dK = torch.empty_like(K)
     dV = torch.empty_like(V)
-    need = workspace_bytes(lay, B, H, d, Q.dtype, vl.cfg, L.MOC_OP_BWD)
+    need = vl.workspace_bytes(L.MOC_OP_BWD)
     if ws is None or ws.numel() < need:
         ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
     s = lay.struct(B, H, d, Q.dtype)

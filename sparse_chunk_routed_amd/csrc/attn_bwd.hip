@@ -827,15 +827,14 @@ struct BwdSizes {
 };
 int kt_rows(int L) { return (L + moc::kBN - 1) / moc::kBN * moc::kBN; }
 size_t al(size_t x) { return (x + 255) / 256 * 256; }
-size_t gather_rows(const moc_layout* lay, int S) {
-  const size_t sel = static_cast<size_t>(lay->B) * lay->H * lay->L * static_cast<size_t>(S);
+// gathered rows of the routed buckets: each bucket padded to a multiple of 32
+size_t gather_rows(const moc_layout* lay, size_t sel) {
   const size_t nb = static_cast<size_t>(lay->B) * lay->H * lay->C;
   return (sel + 31 * nb + 31) / 32 * 32;
 }
-BwdSizes bwd_sizes(const moc_layout* lay, int S) {
+// sel: routed (query, chunk) rows the workspace holds (the varlen capacity)
+BwdSizes bwd_sizes(const moc_layout* lay, size_t sel) {
   BwdSizes z;
-  const size_t rows = static_cast<size_t>(lay->B) * lay->H * lay->L;
-  const size_t sel = rows * static_cast<size_t>(S);
   const size_t text = static_cast<size_t>(lay->text_end - lay->text_begin);
   const size_t ns = static_cast<size_t>(attn_bwd_text_split(lay->L));
   // D and lse2 rows are padded to Lp per (b, h) (16-byte aligned 32-query slices)
@@ -850,17 +849,19 @@ BwdSizes bwd_sizes(const moc_layout* lay, int S) {
   const size_t kvtile = lay->d == 128 ? moc::KvImage<128>::BYTES : moc::KvImage<64>::BYTES;
   z.kv = al(static_cast<size_t>(lay->B) * lay->H * (kt_rows(lay->L) / moc::kBN) * kvtile);
   // 32-query blocks of the dK/dV kernel: the sequence's (Lp / 32 per (b, h)) and the routed
-  // buckets' (each bucket padded to a multiple of 32 rows: at most B*H*L*S + 31 per bucket)
+  // buckets' (each bucket padded to a multiple of 32 rows: at most sel + 31 per bucket)
   const size_t nb = static_cast<size_t>(lay->B) * lay->H * lay->C;
   const size_t gtile = lay->d == 128 ? moc::QTiles<128>::BYTES : moc::QTiles<64>::BYTES;
   z.qb = al(static_cast<size_t>(lay->B) * lay->H * (kt_rows(lay->L) / 32) * gtile);
-  z.gb = al(gather_rows(lay, S) / 32 * gtile);
+  z.gb = al(gather_rows(lay, sel) / 32 * gtile);
   z.gstart = al((nb + 1) * sizeof(int32_t));
   return z;
 }
 }  // namespace
 
-size_t attn_bwd_workspace(const moc_layout* lay, int S) { return bwd_sizes(lay, S).total(); }
+size_t attn_bwd_workspace(const moc_layout* lay, int64_t routed_rows) {
+  return bwd_sizes(lay, static_cast<size_t>(routed_rows)).total();
+}
 
 template <int D>
 static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, const void* Q,
@@ -868,7 +869,7 @@ static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, cons
                                const void* dO, float scale, void* dQ, void* dK, void* dV,
                                void* ws, hipStream_t st) {
   using moc::bf16_t;
-  const BwdSizes z = bwd_sizes(lay, vl->S);
+  const BwdSizes z = bwd_sizes(lay, static_cast<size_t>(vl->routed_cap));
   char* w = static_cast<char*>(ws);
   float* Dq = reinterpret_cast<float*>(w); w += z.dq;
   float* l2 = reinterpret_cast<float*>(w); w += z.l2;
@@ -889,7 +890,7 @@ static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   const int64_t rows = static_cast<int64_t>(lay->B) * lay->H * lay->L;
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL((moc::bwd_prep_kernel<D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, st,
-                     o, g, lse, Dq, l2, rows, lay->L, Lp, lay->check);
+                     o, g, lse, Dq, l2, rows, lay->L, Lp, vl->status);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -901,14 +902,14 @@ static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   p.scale_log2 = scale * moc::kLog2e;
   p.scale = scale;
   p.Lp = Lp;
-  p.chk = lay->check;
+  p.chk = vl->status;
   const int BH = lay->B * lay->H;
   hipLaunchKernelGGL((moc::bwd_kvimage_kernel<D>), dim3(Lp / moc::kBN, BH), dim3(256), 0, st, k,
-                     v, lay->L, Lp, kvimg, lay->check);
+                     v, lay->L, Lp, kvimg, vl->status);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int NB = BH * lay->C;
   hipLaunchKernelGGL(moc::bwd_gather_scan_kernel, dim3(1), dim3(1024), 0, st, vl->bucket_off, NB,
-                     gstart, lay->check);
+                     gstart, vl->status);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((moc::bwd_qblock_kernel<D, moc::QB_SEQ>),
                      dim3((Lp + moc::kBwdQBM - 1) / moc::kBwdQBM, BH), dim3(256), 0, st, q, g, Dq,

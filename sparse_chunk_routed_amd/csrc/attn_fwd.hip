@@ -662,7 +662,7 @@ static hipError_t launch_fwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   AttnParams p;
   p.B = lay->B; p.H = lay->H; p.L = lay->L; p.C = lay->C; p.S = vl->S;
   p.scale_log2 = scale * moc::kLog2e;
-  p.chk = lay->check;
+  p.chk = vl->status;
   const T* q = static_cast<const T*>(Q);
   const T* k = static_cast<const T*>(K);
   const T* v = static_cast<const T*>(V);
@@ -693,10 +693,10 @@ static hipError_t launch_fwd_bf16(const moc_layout* lay, const moc_varlen* vl, c
   AttnParams p;
   p.B = lay->B; p.H = lay->H; p.L = lay->L; p.C = lay->C; p.S = vl->S;
   p.scale_log2 = scale * moc::kLog2e;
-  p.chk = lay->check;
+  p.chk = vl->status;
   const int Lp = attn_vt_rows(lay->L);
   bf16_t* Vt = static_cast<bf16_t*>(vt_ws);
-  hipError_t e = launch_transpose_rows(V, Vt, lay->B * lay->H, lay->L, Lp, D, lay->check, st);
+  hipError_t e = launch_transpose_rows(V, Vt, lay->B * lay->H, lay->L, Lp, D, vl->status, st);
   if (e != hipSuccess) return e;
   const bool mx = Qs != nullptr;
   if (vl->S > 0 && vl->max_rtiles > 0) {

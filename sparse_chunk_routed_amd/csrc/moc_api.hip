@@ -41,7 +41,8 @@ hipError_t launch_attn_bwd(const moc_layout* lay, const moc_varlen* vl, const vo
                            const void* K, const void* V, const void* O, const float* lse,
                            const void* dO, float scale, void* dQ, void* dK, void* dV,
                            void* ws, size_t ws_bytes, hipStream_t st);
-size_t attn_bwd_workspace(const moc_layout* lay, int S);
+size_t attn_bwd_workspace(const moc_layout* lay, int64_t routed_rows);
+hipError_t launch_varlen_guard(const moc_layout* lay, const moc_varlen* vl, hipStream_t st);
 int attn_tile_rows();
 int attn_bwd_key_rows();
 int attn_bwd_text_split(int L);
@@ -108,11 +109,11 @@ moc_status check_cfg(const moc_layout* lay, const moc_route_cfg* cfg) {
 
 struct VarlenSizes {
   size_t counts, totals, tile_base, bucket_off, bucket_q, slot, rtiles, n_rtiles, atiles, n_atiles,
-      ktiles, n_ktiles;
+      ktiles, n_ktiles, status;
   int max_rtiles, max_atiles, max_ktiles, n_text_split, nqt;
   size_t total() const {
     return counts + totals + tile_base + bucket_off + bucket_q + slot + rtiles + n_rtiles + atiles +
-           n_atiles + ktiles + n_ktiles;
+           n_atiles + ktiles + n_ktiles + status;
   }
 };
 
@@ -140,11 +141,17 @@ VarlenSizes varlen_sizes(const moc_layout* lay, int S) {
   z.max_ktiles = (lay->L + KR - 1) / KR + lay->C + (text + KR - 1) / KR * z.n_text_split;
   z.ktiles = align_up(sizeof(int32_t) * 6 * z.max_ktiles);
   z.n_ktiles = kAlign;
+  z.status = kAlign;
   return z;
 }
 
-size_t fwd_bytes(const moc_layout* lay, int S) {
-  const int64_t rows = static_cast<int64_t>(lay->B) * lay->H * lay->L * S;
+// routed (query, chunk) rows of the static bound: every query of every (b, h) routed S times
+int64_t routed_max_of(const moc_layout* lay, int S) {
+  return static_cast<int64_t>(lay->B) * lay->H * lay->L * S;
+}
+
+// FWD workspace: partial output rows and their LSE for `rows` routed rows, then V^T
+size_t fwd_bytes(const moc_layout* lay, int64_t rows) {
   const int64_t r = rows > 0 ? rows : 1;
   return align_up(sizeof(float) * r * lay->d) + align_up(sizeof(float) * r) +
          align_up(moc_host::attn_fwd_vt_bytes(lay));
@@ -218,8 +225,8 @@ size_t moc_workspace_bytes(const moc_layout* lay, const moc_route_cfg* cfg, int3
   switch (op) {
     case MOC_OP_ROUTE: return moc_host::route_workspace(lay);
     case MOC_OP_VARLEN: return varlen_sizes(lay, S).total();
-    case MOC_OP_FWD: return fwd_bytes(lay, S);
-    case MOC_OP_BWD: return moc_host::attn_bwd_workspace(lay, S);
+    case MOC_OP_FWD: return fwd_bytes(lay, routed_max_of(lay, S));
+    case MOC_OP_BWD: return moc_host::attn_bwd_workspace(lay, routed_max_of(lay, S));
     case MOC_OP_OUTER: return moc_host::outer_workspace(lay);
     default: fail(MOC_EINVAL, "unknown op %d", op); return 0;
   }
@@ -381,6 +388,9 @@ moc_status moc_build_varlen(const moc_layout* lay, const moc_route_cfg* cfg, con
     out->n_atiles = reinterpret_cast<int32_t*>(w); w += z.n_atiles;
     out->ktiles = reinterpret_cast<int32_t*>(w); w += z.ktiles;
     out->n_ktiles = reinterpret_cast<int32_t*>(w); w += z.n_ktiles;
+    out->status = reinterpret_cast<uint32_t*>(w); w += z.status;
+    out->routed_max = routed_max_of(lay, S);
+    out->routed_cap = out->routed_max;
     out->max_ktiles = z.max_ktiles;
     out->n_text_split = z.n_text_split;
     out->scratch = counts;
@@ -404,6 +414,15 @@ moc_status moc_build_varlen(const moc_layout* lay, const moc_route_cfg* cfg, con
   }
 }
 
+// The guards of an attention call: the layout check (when moc_layout.check is set), then the
+// capacity guard that writes vl->status, which every kernel of the call reads first.
+static moc_status run_guards(const moc_layout* lay, const moc_varlen* vl, void* stream) {
+  moc_status s = run_layout_check(lay, stream);
+  if (s != MOC_OK) return s;
+  return hip_status(moc_host::launch_varlen_guard(lay, vl, static_cast<hipStream_t>(stream)),
+                    "varlen guard launch");
+}
+
 static moc_status check_varlen(const moc_layout* lay, const moc_varlen* vl) {
   if (!vl) return fail(MOC_EINVAL, "varlen is NULL");
   if (vl->S < 0 || vl->tile_rows != moc_host::attn_tile_rows() || !vl->bucket_off || !vl->bucket_q || !vl->slot ||
@@ -412,8 +431,11 @@ static moc_status check_varlen(const moc_layout* lay, const moc_varlen* vl) {
   const VarlenSizes z = varlen_sizes(lay, vl->S);
   if (vl->max_rtiles != z.max_rtiles || vl->max_atiles != z.max_atiles ||
       vl->max_ktiles != z.max_ktiles || vl->n_text_split != z.n_text_split || !vl->ktiles ||
-      !vl->n_ktiles)
+      !vl->n_ktiles || !vl->status || vl->routed_max != routed_max_of(lay, vl->S))
     return fail(MOC_EINVAL, "varlen struct built for another layout");
+  if (vl->routed_cap < 0 || vl->routed_cap > vl->routed_max)
+    return fail(MOC_EINVAL, "routed_cap %lld outside [0, %lld]",
+                static_cast<long long>(vl->routed_cap), static_cast<long long>(vl->routed_max));
   return MOC_OK;
 }
 
@@ -431,18 +453,18 @@ moc_status moc_attend_fwd(const moc_layout* lay, const moc_varlen* vl, const voi
       return fail(MOC_EINVAL, "outputs alias inputs");
     if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
       return fail(MOC_EINVAL, "softmax_scale must be finite and > 0");
-    const size_t need = fwd_bytes(lay, vl->S);
+    const size_t need = fwd_bytes(lay, vl->routed_cap);
     if (!ws || ws_bytes < need)
       return fail(MOC_EWORKSPACE, "FWD workspace needs %zu bytes (got %zu)", need,
                   ws ? ws_bytes : size_t(0));
-    const int64_t rows = static_cast<int64_t>(lay->B) * lay->H * lay->L * vl->S;
+    const int64_t rows = vl->routed_cap;
     char* w = static_cast<char*>(ws);
     float* pO = reinterpret_cast<float*>(w);
     w += align_up(sizeof(float) * (rows > 0 ? rows : 1) * lay->d);
     float* plse = reinterpret_cast<float*>(w);
     w += align_up(sizeof(float) * (rows > 0 ? rows : 1));
     void* vt = w;  // transposed V (bf16 layouts)
-    if ((s = run_layout_check(lay, stream)) != MOC_OK) return s;
+    if ((s = run_guards(lay, vl, stream)) != MOC_OK) return s;
     return hip_status(moc_host::launch_attn_fwd(lay, vl, Q, K, V, softmax_scale, O, lse, pO, plse,
                                                 vt, static_cast<hipStream_t>(stream)),
                       "attention forward launch");
@@ -487,17 +509,17 @@ moc_status moc_attend_fwd_mx(const moc_layout* lay, const moc_varlen* vl, const 
       if (a == O || a == static_cast<const void*>(lse)) return fail(MOC_EINVAL, "outputs alias inputs");
     if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
       return fail(MOC_EINVAL, "softmax_scale must be finite and > 0");
-    const size_t need = fwd_bytes(lay, vl->S);
+    const size_t need = fwd_bytes(lay, vl->routed_cap);
     if (!ws || ws_bytes < need)
       return fail(MOC_EWORKSPACE, "FWD workspace needs %zu bytes (got %zu)", need,
                   ws ? ws_bytes : size_t(0));
-    const int64_t rows = static_cast<int64_t>(lay->B) * lay->H * lay->L * vl->S;
+    const int64_t rows = vl->routed_cap;
     char* w = static_cast<char*>(ws);
     float* pO = reinterpret_cast<float*>(w);
     w += align_up(sizeof(float) * (rows > 0 ? rows : 1) * lay->d);
     float* plse = reinterpret_cast<float*>(w);
     w += align_up(sizeof(float) * (rows > 0 ? rows : 1));
-    if ((s = run_layout_check(lay, stream)) != MOC_OK) return s;
+    if ((s = run_guards(lay, vl, stream)) != MOC_OK) return s;
     return hip_status(moc_host::launch_attn_fwd_mx(lay, vl, Qc, Qs, Kc, Ks, V, softmax_scale, O,
                                                    lse, pO, plse, w,
                                                    static_cast<hipStream_t>(stream)),
@@ -526,12 +548,12 @@ moc_status moc_attend_bwd(const moc_layout* lay, const moc_varlen* vl, const voi
     if (dQ == dK || dQ == dV || dK == dV) return fail(MOC_EINVAL, "gradient outputs alias");
     if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
       return fail(MOC_EINVAL, "softmax_scale must be finite and > 0");
-    const size_t need = moc_host::attn_bwd_workspace(lay, vl->S);
+    const size_t need = moc_host::attn_bwd_workspace(lay, vl->routed_cap);
     if (!ws || ws_bytes < need)
       return fail(MOC_EWORKSPACE, "BWD workspace needs %zu bytes (got %zu)", need,
                   ws ? ws_bytes : size_t(0));
     if (lay->dtype != MOC_BF16) return fail(MOC_EUNSUPPORTED, "backward not available");
-    if ((s = run_layout_check(lay, stream)) != MOC_OK) return s;
+    if ((s = run_guards(lay, vl, stream)) != MOC_OK) return s;
     hipError_t e = moc_host::launch_attn_bwd(lay, vl, Q, K, V, O, lse, dO, softmax_scale, dQ, dK,
                                              dV, ws, ws_bytes, static_cast<hipStream_t>(stream));
     if (e == hipErrorNotSupported) return fail(MOC_EUNSUPPORTED, "backward not available");
@@ -576,6 +598,67 @@ moc_status moc_layout_status(uint32_t word) {
   for (const auto& b : kBits)
     if (word & b.bit) msg += std::string("; ") + b.what;
   return fail(MOC_ELAYOUT, "%s", msg.c_str());
+}
+
+moc_status moc_varlen_total(const moc_layout* lay, const moc_varlen* vl, int64_t* total,
+                            void* stream) {
+  try {
+    moc_status s = check_layout(lay);
+    if (s != MOC_OK) return s;
+    if ((s = check_varlen(lay, vl)) != MOC_OK) return s;
+    if (!total) return fail(MOC_EINVAL, "total is NULL");
+    s = hip_status(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "stream synchronise");
+    if (s != MOC_OK) return s;
+    const int64_t nb = static_cast<int64_t>(lay->B) * lay->H * lay->C;
+    int32_t v = 0;
+    s = hip_status(hipMemcpy(&v, vl->bucket_off + nb, sizeof(v), hipMemcpyDeviceToHost),
+                   "copy of the routed total");
+    if (s != MOC_OK) return s;
+    *total = v;
+    return MOC_OK;
+  } catch (...) {
+    return fail(MOC_EINTERNAL, "exception in moc_varlen_total");
+  }
+}
+
+moc_status moc_varlen_set_capacity(moc_varlen* vl, int64_t routed_cap) {
+  if (!vl || !vl->status) return fail(MOC_EINVAL, "varlen struct not filled by moc_build_varlen");
+  if (routed_cap < 0 || routed_cap > vl->routed_max)
+    return fail(MOC_EINVAL, "routed_cap %lld outside [0, %lld]",
+                static_cast<long long>(routed_cap), static_cast<long long>(vl->routed_max));
+  vl->routed_cap = routed_cap;
+  return MOC_OK;
+}
+
+size_t moc_attend_workspace_bytes(const moc_layout* lay, const moc_varlen* vl, int32_t op) {
+  if (check_layout(lay) != MOC_OK) return 0;
+  if (check_varlen(lay, vl) != MOC_OK) return 0;
+  if (op == MOC_OP_FWD) return fwd_bytes(lay, vl->routed_cap);
+  if (op == MOC_OP_BWD) return moc_host::attn_bwd_workspace(lay, vl->routed_cap);
+  fail(MOC_EINVAL, "op must be MOC_OP_FWD or MOC_OP_BWD (got %d)", op);
+  return 0;
+}
+
+moc_status moc_varlen_status(const moc_varlen* vl, void* stream) {
+  try {
+    if (!vl || !vl->status) return fail(MOC_EINVAL, "varlen struct not filled by moc_build_varlen");
+    moc_status s = hip_status(hipStreamSynchronize(static_cast<hipStream_t>(stream)),
+                              "stream synchronise");
+    if (s != MOC_OK) return s;
+    uint32_t w = 0;
+    s = hip_status(hipMemcpy(&w, vl->status, sizeof(w), hipMemcpyDeviceToHost),
+                   "copy of the status word");
+    if (s != MOC_OK) return s;
+    if (w & MOC_VARLEN_OVER_CAPACITY)
+      return fail(MOC_EWORKSPACE, "the routing has more routed rows than routed_cap = %lld; the "
+                                  "attention call wrote nothing",
+                  static_cast<long long>(vl->routed_cap));
+    if (w & MOC_VARLEN_BAD_LAYOUT)
+      return fail(MOC_ELAYOUT, "the layout check word was set; the attention call wrote nothing");
+    return MOC_OK;
+  } catch (...) {
+    return fail(MOC_EINTERNAL, "exception in moc_varlen_status");
+  }
 }
 
 }  // extern "C"

@@ -278,11 +278,30 @@ __global__ __launch_bounds__(256) void inv_scatter_kernel(const int32_t* __restr
   for (int j = n; j < p.S; ++j) slot[row * p.S + j] = -1;
 }
 
+// Guard of an attention call: the routing's total routed rows against the capacity its
+// workspace was sized for, and the layout check word, into the varlen status word that every
+// kernel of the call reads first (layout_rejected).
+__global__ void varlen_guard_kernel(const int32_t* __restrict__ total, int64_t cap,
+                                    const uint32_t* __restrict__ layout_word,
+                                    uint32_t* __restrict__ status) {
+  uint32_t st = 0u;
+  if (static_cast<int64_t>(total[0]) > cap) st |= MOC_VARLEN_OVER_CAPACITY;
+  if (layout_word != nullptr && layout_word[0] != 0u) st |= MOC_VARLEN_BAD_LAYOUT;
+  status[0] = st;
+}
+
 }  // namespace moc
 
 namespace moc_host {
 
 using moc::VarlenParams;
+
+hipError_t launch_varlen_guard(const moc_layout* lay, const moc_varlen* vl, hipStream_t st) {
+  const int64_t nb = static_cast<int64_t>(lay->B) * lay->H * lay->C;
+  hipLaunchKernelGGL(moc::varlen_guard_kernel, dim3(1), dim3(1), 0, st, vl->bucket_off + nb,
+                     vl->routed_cap, lay->check, vl->status);
+  return hipGetLastError();
+}
 
 hipError_t launch_varlen(const moc_layout* lay, const VarlenParams& p, const int32_t* sel,
                          const int32_t* nsel, int32_t* counts, int32_t* totals,

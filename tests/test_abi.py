@@ -363,3 +363,20 @@ def test_route_noalloc_rejects_requests_beyond_its_static_buffer(L):
     assert lib.moc_workspace_bytes(ctypes.byref(ok), ctypes.byref(cfg), L.MOC_OP_ROUTE) <= 16 << 20
     # the usual argument checks still run first
     assert lib.moc_route_noalloc(None, ctypes.byref(cfg), p(1), p(2), p(3), p(4), None) == 1
+
+
+def test_varlen_set_capacity_bounds(L):
+    """The routed-row capacity of the attention workspaces lies in [0, routed_max]; a struct that
+    moc_build_varlen did not fill is refused."""
+    lib = L.load()
+    vl = L.MocVarlen()
+    assert lib.moc_varlen_set_capacity(ctypes.byref(vl), 10) == L.MOC_EINVAL  # not filled
+    vl.status = 0x1000
+    vl.routed_max = 1000
+    vl.routed_cap = 1000
+    assert lib.moc_varlen_set_capacity(ctypes.byref(vl), -1) == L.MOC_EINVAL
+    assert lib.moc_varlen_set_capacity(ctypes.byref(vl), 1001) == L.MOC_EINVAL
+    assert vl.routed_cap == 1000
+    assert lib.moc_varlen_set_capacity(ctypes.byref(vl), 0) == 0 and vl.routed_cap == 0
+    assert lib.moc_varlen_set_capacity(ctypes.byref(vl), 1000) == 0 and vl.routed_cap == 1000
+    assert lib.moc_varlen_set_capacity(None, 5) == L.MOC_EINVAL
