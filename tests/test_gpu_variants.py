@@ -96,13 +96,14 @@ def test_dense_layout_8_shot_length_sampled():
     _attend_rows(run, rows, TOL[w.dtype])
 
 
-def test_shots24_sampled():
-    """The 24-shot layout of the length sweep (512 text + 24 shots x 14 frames x 1,560 tokens =
-    524,672 tokens, C = 337, top-k 2): pooled means bit-exact for every head and chunk, every
-    selection against the oracle (tie exemption, legality), pair counts exact, and attention on
-    sampled rows and chunk edges of every head."""
-    w = mi.shots(n_shots=24)
-    assert w.L == 524_672 and w.C == 337
+@pytest.mark.parametrize("n_shots,L,C", [(16, 349_952, 225), (24, 524_672, 337)])
+def test_shots_sweep_sampled(n_shots, L, C):
+    """The two longest layouts of the length sweep (512 text + n shots x 14 frames x 1,560
+    tokens: 349,952 tokens at 16 shots, 524,672 at 24; top-k 2): pooled means bit-exact for every
+    head and chunk, every selection against the oracle (tie exemption, legality), pair counts
+    exact, and attention on sampled rows and chunk edges of every head."""
+    w = mi.shots(n_shots=n_shots)
+    assert w.L == L and w.C == C
     run = Run(w)
     kb = mo.pool_keys(run.K, w.layout)
     assert np.array_equal(run.h_kbar.view(np.uint32), kb.view(np.uint32))
@@ -112,4 +113,4 @@ def test_shots24_sampled():
     pc.check_legal(w.layout, run.h_sel, run.h_nsel, w.top_k, w.causal)
     assert np.array_equal(run.h_pairs, mo.pair_counts(w.layout, run.h_sel))
     _say(f"pairs {int(run.h_pairs.sum())} exact")
-    _attend_rows(run, _sample_rows(w, 8, seed=24), TOL[w.dtype])
+    _attend_rows(run, _sample_rows(w, 8, seed=n_shots), TOL[w.dtype])
