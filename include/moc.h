@@ -187,8 +187,9 @@ size_t moc_workspace_bytes(const moc_layout *lay, const moc_route_cfg *cfg, int3
  * hold one row per routed (query, chunk) pair - partial outputs in the forward, partial dQ rows
  * and gathered query images in the backward - and moc_workspace_bytes sizes them for
  * B*H*L*S rows, which drop-in noise makes several times the rows a routing really has.
- *   moc_varlen_total: the routing's total routed rows, bucket_off[B*H*C]. The one call of this
- *     library that synchronises: it waits for `stream`, then copies the count to the host.
+ *   moc_varlen_total: the routing's total routed rows, bucket_off[B*H*C]. It waits for
+ *     `stream`, then copies the count to the host. With lay->check set it reads the check word
+ *     first and returns MOC_ELAYOUT (no total) when the layout was rejected.
  *   moc_varlen_set_capacity: sets vl->routed_cap (0 <= routed_cap <= vl->routed_max). Host
  *     only; the varlen contents are unchanged. A capacity at least the total (a total from
  *     moc_varlen_total, or a bound the caller trusts for its routing noise) gives the same

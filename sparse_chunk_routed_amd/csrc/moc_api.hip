@@ -609,6 +609,14 @@ moc_status moc_varlen_total(const moc_layout* lay, const moc_varlen* vl, int64_t
     if (!total) return fail(MOC_EINVAL, "total is NULL");
     s = hip_status(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "stream synchronise");
     if (s != MOC_OK) return s;
+    if (lay->check) {
+      // a rejected layout left the inversion unwritten: there is no total to report
+      uint32_t word = 0;
+      s = hip_status(hipMemcpy(&word, lay->check, sizeof(word), hipMemcpyDeviceToHost),
+                     "copy of the layout check word");
+      if (s != MOC_OK) return s;
+      if (word != 0) return moc_layout_status(word);
+    }
     const int64_t nb = static_cast<int64_t>(lay->B) * lay->H * lay->C;
     int32_t v = 0;
     s = hip_status(hipMemcpy(&v, vl->bucket_off + nb, sizeof(v), hipMemcpyDeviceToHost),

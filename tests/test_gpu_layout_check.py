@@ -129,6 +129,11 @@ def test_nonzero_word_skips_every_kernel():
     with pytest.raises(moc.MocError) as e:
         lay.check_status()
     assert e.value.status == L.MOC_ELAYOUT
+    # no routed-row total is reported for a rejected layout
+    total = ctypes.c_int64(-7)
+    assert lib.moc_varlen_total(ctypes.byref(s), ctypes.byref(r.varlen.struct), ctypes.byref(total),
+                                st) == L.MOC_ELAYOUT
+    assert total.value == -7
     _say("a non-zero check word kept every kernel from writing (8 entry points)")
 
 
