@@ -377,6 +377,10 @@ def main(argv=None) -> int:
     S = moc.sel_width(cfg, w.C)
     pool_bytes = BHLd * s_in + w.B * w.H * w.C * w.d * 4
     route_bytes = BHLd * s_in + w.B * w.H * w.C * w.d * 4 + w.B * w.H * w.L * (S + 1) * 4
+    # the index inversion (the gather that lets a query tile read a chunk's K/V once): sel and
+    # nsel read by the count pass and again by the scatter pass, one bucket_q and one slot int32
+    # written per routed row
+    gather_bytes = 2 * w.B * w.H * w.L * (S + 1) * 4 + 2 * cap["rows"] * 4
     peak = PEAK_MX_TFLOPS if mx else PEAK_TFLOPS[w.dtype]
     att_tf = fwd_flops / (stage["attend_fwd"] * 1e-3) / 1e12
     out = {
@@ -415,6 +419,7 @@ def main(argv=None) -> int:
             "routed_rows": cap["rows"], "routed_rows_static_bound": int(vl.struct.routed_max)},
         "pool_gbs": pool_bytes / (stage["pool"] * 1e-3) / 1e9,
         "route_gbs": route_bytes / (stage["route"] * 1e-3) / 1e9,
+        "gather_gbs": gather_bytes / (stage["varlen"] * 1e-3) / 1e9,
         "roofline": {
             "bound": "mfma",
             "kernel": ("attention forward with quantised scores (routed + anchor kernels of "
@@ -439,6 +444,7 @@ def main(argv=None) -> int:
                                                 else None)
     out["pool_hbm_frac"] = out["pool_gbs"] / PEAK_HBM_GBS
     out["route_hbm_frac"] = out["route_gbs"] / PEAK_HBM_GBS
+    out["gather_hbm_frac"] = out["gather_gbs"] / PEAK_HBM_GBS
     out["pool_frac_of_measured_copy"] = out["pool_gbs"] / mp["hbm_copy_gbs"]
     out["route_frac_of_measured_copy"] = out["route_gbs"] / mp["hbm_copy_gbs"]
     if not a.no_cpu_baseline:
