@@ -26,6 +26,10 @@ namespace moc {
 constexpr int kInvTile = 256;          // queries per inversion tile
 constexpr int kInvWords = kInvTile / 32;
 
+// The bitmap lives in dynamic LDS, C * kInvWords words (launches pass that size), so that small
+// layouts leave room for more workgroups per CU.
+extern __shared__ uint32_t inv_bitmap[];
+
 __device__ __forceinline__ void build_bitmap(uint32_t* bm, const int32_t* __restrict__ sel,
                                              const int32_t* __restrict__ nsel, int bh, int tile,
                                              const VarlenParams& p) {
@@ -34,10 +38,19 @@ __device__ __forceinline__ void build_bitmap(uint32_t* bm, const int32_t* __rest
   const int t = tile * kInvTile + threadIdx.x;
   if (t < p.L) {
     const size_t row = static_cast<size_t>(bh) * p.L + t;
+    const int32_t* sr = sel + row * p.S;
     const int n = nsel[row];
-    for (int j = 0; j < n; ++j) {
-      const int c = sel[row * p.S + j];
-      atomicOr(&bm[c * kInvWords + (threadIdx.x >> 5)], 1u << (threadIdx.x & 31));
+    const uint32_t bit = 1u << (threadIdx.x & 31);
+    uint32_t* col = bm + (threadIdx.x >> 5);
+    // the selection row is read four entries at a time whatever n is (all S entries exist),
+    // so the first loads go out together with the load of n
+    for (int j0 = 0; j0 < p.S; j0 += 4) {
+      int c[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) c[u] = j0 + u < p.S ? sr[j0 + u] : 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (j0 + u < n) atomicOr(col + c[u] * kInvWords, bit);
     }
   }
   __syncthreads();
@@ -47,7 +60,7 @@ __global__ __launch_bounds__(256) void inv_count_kernel(const int32_t* __restric
                                                         const int32_t* __restrict__ nsel,
                                                         VarlenParams p,
                                                         int32_t* __restrict__ counts) {
-  __shared__ uint32_t bm[MOC_MAX_C * kInvWords];
+  uint32_t* bm = inv_bitmap;
   if (layout_rejected(p.chk)) return;
   const int tile = blockIdx.x, bh = blockIdx.y;
   build_bitmap(bm, sel, nsel, bh, tile, p);
@@ -89,134 +102,205 @@ __global__ __launch_bounds__(256) void inv_scan_bucket_kernel(int32_t* __restric
   if (threadIdx.x == 255) totals[blockIdx.x] = part[255];
 }
 
-// Block-wide exclusive scan over n values with 1024 threads (values read via `get`).
+// Two running sums scanned together over one workgroup.
+struct Sum2 {
+  long long a, b;
+};
+
+// Block-wide exclusive scan of n pairs: thread t takes the contiguous items [t*per, t*per+per),
+// the threads' sums are scanned in each wave with lane shuffles and across waves through `wsum`
+// (2 * waves entries). get(i) -> Sum2, put(i, exclusive prefix). Returns the totals; every
+// thread must call it.
 template <typename Get, typename Put>
-__device__ int64_t block_exclusive_scan(int n, Get get, Put put, int64_t* part) {
-  const int per = (n + blockDim.x - 1) / blockDim.x;
-  const int a = threadIdx.x * per;
-  const int e = a + per < n ? a + per : n;
-  int64_t s = 0;
-  for (int i = a; i < e; ++i) s += get(i);
-  part[threadIdx.x] = s;
-  __syncthreads();
-  for (int off = 1; off < static_cast<int>(blockDim.x); off <<= 1) {
-    int64_t v = static_cast<int>(threadIdx.x) >= off ? part[threadIdx.x - off] : 0;
-    __syncthreads();
-    part[threadIdx.x] += v;
-    __syncthreads();
+__device__ Sum2 block_scan2(int n, Get get, Put put, long long* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nw = static_cast<int>(blockDim.x) >> 6;
+  const int per = (n + static_cast<int>(blockDim.x) - 1) / static_cast<int>(blockDim.x);
+  const int i0 = tid * per;
+  const int i1 = i0 + per < n ? i0 + per : n;
+  long long sa = 0, sb = 0;
+  for (int i = i0; i < i1; ++i) {
+    const Sum2 v = get(i);
+    sa += v.a;
+    sb += v.b;
   }
-  int64_t run = threadIdx.x > 0 ? part[threadIdx.x - 1] : 0;
-  for (int i = a; i < e; ++i) {
-    int64_t v = get(i);
-    put(i, run);
-    run += v;
+  long long ia = sa, ib = sb;  // inclusive scan inside the wave
+  for (int d = 1; d < 64; d <<= 1) {
+    const long long ta = __shfl_up(ia, d), tb = __shfl_up(ib, d);
+    if (lane >= d) {
+      ia += ta;
+      ib += tb;
+    }
   }
-  int64_t total = part[blockDim.x - 1];
+  if (lane == 63) {
+    wsum[2 * wave] = ia;
+    wsum[2 * wave + 1] = ib;
+  }
   __syncthreads();
-  return total;
+  long long pa = 0, pb = 0, tot_a = 0, tot_b = 0;
+  for (int w = 0; w < nw; ++w) {
+    const long long xa = wsum[2 * w], xb = wsum[2 * w + 1];
+    if (w < wave) {
+      pa += xa;
+      pb += xb;
+    }
+    tot_a += xa;
+    tot_b += xb;
+  }
+  long long ra = pa + ia - sa, rb = pb + ib - sb;
+  for (int i = i0; i < i1; ++i) {
+    const Sum2 v = get(i);
+    put(i, Sum2{ra, rb});
+    ra += v.a;
+    rb += v.b;
+  }
+  __syncthreads();  // wsum is reused by the next scan
+  return Sum2{tot_a, tot_b};
 }
 
+// Writes the tiles of nseg segments (segment s: `cnt` tiles from index `base`, seg(s, base,
+// cnt)). Groups of kSegLanes lanes take one segment each and write its tiles on consecutive
+// lanes: emit(s, k, base + k). Segments hold a few tiles each (a bucket's rows or a chunk's
+// keys), so narrow groups keep most of the workgroup's lanes busy.
+constexpr int kSegLanes = 8;
+
+template <typename Seg, typename Emit>
+__device__ void emit_segments(int nseg, Seg seg, Emit emit) {
+  const int sub = threadIdx.x % kSegLanes;
+  const int ngroups = static_cast<int>(blockDim.x) / kSegLanes;
+  for (int s = threadIdx.x / kSegLanes; s < nseg; s += ngroups) {
+    int base = 0, cnt = 0;
+    seg(s, base, cnt);
+    for (int k = sub; k < cnt; k += kSegLanes) emit(s, k, base + k);
+  }
+}
+
+// One workgroup of 1024 threads: bucket offsets, routed tiles, anchor tiles, backward key tiles
+// and pair counts. Every step is a block scan or a parallel write; the layout walk (which chunks
+// start and end a shot, where each group's tiles begin) is one scan over the chunks.
 __global__ __launch_bounds__(1024) void inv_global_kernel(
     const int32_t* __restrict__ totals, const int32_t* __restrict__ off_g,
     const int32_t* __restrict__ shot_g, VarlenParams p, int32_t* __restrict__ bucket_off,
     int32_t* __restrict__ tile_base, int32_t* __restrict__ rtiles, int32_t* __restrict__ n_rtiles,
     int32_t* __restrict__ atiles, int32_t* __restrict__ n_atiles, int32_t* __restrict__ ktiles,
     int32_t* __restrict__ n_ktiles, int64_t* __restrict__ pair_count) {
-  __shared__ int64_t part[1024];
-  __shared__ int64_t s_anchor;
+  __shared__ long long wsum[32];
   __shared__ int32_t off[MOC_MAX_C + 1];
   __shared__ int32_t shot[MOC_MAX_C];
-  // tile emission tables: anchor groups (text, shots) and per-chunk key tile starts
+  __shared__ int32_t grp[MOC_MAX_C];     // anchor group of each shot chunk
+  __shared__ int32_t k_base[MOC_MAX_C];  // first backward key tile of each chunk
+  // anchor groups: the text, then every run of chunks with one shot id
   __shared__ int32_t g_q0[MOC_MAX_C + 1], g_q1[MOC_MAX_C + 1], g_base[MOC_MAX_C + 1];
-  __shared__ int32_t g_text[MOC_MAX_C + 1];
-  __shared__ int32_t k_base[MOC_MAX_C], k_q0[MOC_MAX_C], k_q1[MOC_MAX_C];
-  __shared__ int32_t s_ng, s_nsp, s_ntxt_k;
   if (layout_rejected(p.chk)) return;
-  // the serial tile emission below walks the layout: keep it in LDS, not in global memory
   for (int i = threadIdx.x; i <= p.C; i += blockDim.x) off[i] = off_g[i];
   for (int i = threadIdx.x; i < p.C; i += blockDim.x) shot[i] = shot_g[i];
   __syncthreads();
   const int NB = p.B * p.H * p.C;
   const int BM = p.tile_rows;
-  // bucket offsets
-  int64_t tot = block_exclusive_scan(
-      NB, [&](int i) -> int64_t { return totals[i]; },
-      [&](int i, int64_t v) { bucket_off[i] = static_cast<int32_t>(v); }, part);
-  if (threadIdx.x == 0) bucket_off[NB] = static_cast<int32_t>(tot);
-  // routed tiles: ceil(total / BM) per bucket
-  int64_t ntile = block_exclusive_scan(
-      NB, [&](int i) -> int64_t { return (totals[i] + BM - 1) / BM; },
-      [&](int i, int64_t v) { tile_base[i] = static_cast<int32_t>(v); }, part);
-  __syncthreads();
-  for (int i = threadIdx.x; i < NB; i += blockDim.x) {
-    const int nt = (totals[i] + BM - 1) / BM;
-    const int base = tile_base[i];
-    for (int k = 0; k < nt; ++k) {
-      rtiles[2 * (base + k) + 0] = i;
-      rtiles[2 * (base + k) + 1] = k * BM;
-    }
-  }
-  if (threadIdx.x == 0) n_rtiles[0] = static_cast<int32_t>(ntile);
-  // Anchor tiles (shared by all (b,h)) and backward key tiles. Thread 0 lays out where each
-  // group's tiles start (the text, then every shot; the text keys, then every video chunk);
-  // all threads then write the tiles, in the same order a serial walk would.
+  const int KR = p.key_rows;
   const int tb = p.text_begin, te = p.text_end;
   const int nt_txt = te - tb;
-  const int KR = p.key_rows;
+  const int has_text = nt_txt > 0 ? 1 : 0;
+
+  // bucket offsets and the first routed tile of each bucket (ceil(rows / BM) tiles per bucket)
+  const Sum2 rt = block_scan2(
+      NB,
+      [&](int i) -> Sum2 {
+        const int t = totals[i];
+        return Sum2{t, (t + BM - 1) / BM};
+      },
+      [&](int i, Sum2 v) {
+        bucket_off[i] = static_cast<int32_t>(v.a);
+        tile_base[i] = static_cast<int32_t>(v.b);
+      },
+      wsum);
   if (threadIdx.x == 0) {
-    int ng = 0, n = 0;
-    int64_t anchor = 0;
-    if (nt_txt > 0) {
-      g_q0[ng] = tb; g_q1[ng] = te; g_base[ng] = n; g_text[ng] = 1; ++ng;
-      n += (nt_txt + BM - 1) / BM;
-      anchor += static_cast<int64_t>(nt_txt) * nt_txt;
+    bucket_off[NB] = static_cast<int32_t>(rt.a);
+    n_rtiles[0] = static_cast<int32_t>(rt.b);
+  }
+
+  // The layout walk. A chunk starts a group when its shot id differs from the previous chunk's
+  // (text chunks, shot -1, belong to no group); its backward key tiles are ceil(size / KR).
+  auto starts = [&](int c) { return shot[c] >= 0 && (c == 0 || shot[c - 1] != shot[c]); };
+  auto ends = [&](int c) { return shot[c] >= 0 && (c == p.C - 1 || shot[c + 1] != shot[c]); };
+  int nsp = 0, nk_txt = 0;  // text key tiles: key blocks x the non-empty query splits
+  if (has_text) {
+    const int qs = (p.L + p.n_text_split - 1) / p.n_text_split;
+    nsp = (p.L + qs - 1) / qs;
+    if (nsp > p.n_text_split) nsp = p.n_text_split;
+    nk_txt = ((nt_txt + KR - 1) / KR) * nsp;
+  }
+  const Sum2 wk = block_scan2(
+      p.C,
+      [&](int c) -> Sum2 {
+        return Sum2{starts(c) ? 1 : 0,
+                    shot[c] >= 0 ? (off[c + 1] - off[c] + KR - 1) / KR : 0};
+      },
+      [&](int c, Sum2 v) {
+        // a shot chunk belongs to the last group started at or before it
+        grp[c] = has_text + static_cast<int>(v.a) + (starts(c) ? 1 : 0) - 1;
+        k_base[c] = nk_txt + static_cast<int>(v.b);
+      },
+      wsum);
+  const int ng = has_text + static_cast<int>(wk.a);
+  if (threadIdx.x == 0) {
+    n_ktiles[0] = nk_txt + static_cast<int>(wk.b);
+    if (has_text) {
+      g_q0[0] = tb;
+      g_q1[0] = te;
     }
-    int c = 0;
-    while (c < p.C) {
-      const int sh = shot[c];
-      if (sh < 0) { k_q0[c] = 0; k_q1[c] = 0; ++c; continue; }
-      const int c0 = c;
-      while (c < p.C && shot[c] == sh) ++c;
-      const int q0 = off[c0], q1 = off[c];
-      for (int cc = c0; cc < c; ++cc) { k_q0[cc] = q0; k_q1[cc] = q1; }
-      g_q0[ng] = q0; g_q1[ng] = q1; g_base[ng] = n; g_text[ng] = 0; ++ng;
-      n += (q1 - q0 + BM - 1) / BM;
-      anchor += static_cast<int64_t>(q1 - q0) * (nt_txt + (q1 - q0));
-    }
-    s_ng = ng;
-    n_atiles[0] = n;
-    s_anchor = anchor;
-    // text key tiles: key blocks x the query splits that are not empty (a prefix of them)
-    int nk = 0, nsp = 0;
-    if (nt_txt > 0) {
-      const int qs = (p.L + p.n_text_split - 1) / p.n_text_split;
-      while (nsp < p.n_text_split && nsp * qs < p.L) ++nsp;
-      nk = ((nt_txt + KR - 1) / KR) * nsp;
-    }
-    s_nsp = nsp;
-    s_ntxt_k = nk;
-    for (int cc = 0; cc < p.C; ++cc) {
-      k_base[cc] = nk;
-      if (shot[cc] >= 0) nk += (off[cc + 1] - off[cc] + KR - 1) / KR;
-    }
-    n_ktiles[0] = nk;
+  }
+  for (int c = threadIdx.x; c < p.C; c += blockDim.x) {
+    if (starts(c)) g_q0[grp[c]] = off[c];
+    if (ends(c)) g_q1[grp[c]] = off[c + 1];
   }
   __syncthreads();
-  for (int gi = 0; gi < s_ng; ++gi) {
-    const int q0 = g_q0[gi], q1 = g_q1[gi];
-    const int nt = (q1 - q0 + BM - 1) / BM;
-    for (int k = threadIdx.x; k < nt; k += blockDim.x) {
-      const int q = q0 + k * BM;
-      int32_t* a = atiles + 6 * (g_base[gi] + k);
-      a[0] = q; a[1] = q + BM < q1 ? q + BM : q1;
-      a[2] = tb; a[3] = te;
-      a[4] = g_text[gi] ? 0 : q0; a[5] = g_text[gi] ? 0 : q1;
-    }
-  }
-  if (nt_txt > 0) {
+
+  // anchor tiles per group, and the anchor pairs of one (b, h): text^2, plus every shot query
+  // against the text and its own shot
+  const Sum2 an = block_scan2(
+      ng,
+      [&](int g) -> Sum2 {
+        const long long n = g_q1[g] - g_q0[g];
+        return Sum2{(n + BM - 1) / BM,
+                    (has_text && g == 0) ? n * n : n * (nt_txt + n)};
+      },
+      [&](int g, Sum2 v) { g_base[g] = static_cast<int32_t>(v.a); }, wsum);
+  if (threadIdx.x == 0) n_atiles[0] = static_cast<int32_t>(an.a);
+  const long long anchor_pairs = an.b;
+
+  // routed tiles: (bucket, first position)
+  emit_segments(
+      NB,
+      [&](int i, int& base, int& cnt) {
+        base = tile_base[i];
+        cnt = (totals[i] + BM - 1) / BM;
+      },
+      [&](int i, int k, int t) {
+        rtiles[2 * t + 0] = i;
+        rtiles[2 * t + 1] = k * BM;
+      });
+  // anchor tiles: query range, text range, own-shot range (empty for the text group)
+  emit_segments(
+      ng,
+      [&](int g, int& base, int& cnt) {
+        base = g_base[g];
+        cnt = (g_q1[g] - g_q0[g] + BM - 1) / BM;
+      },
+      [&](int g, int k, int t) {
+        const int q0 = g_q0[g], q1 = g_q1[g];
+        const bool text = has_text && g == 0;
+        const int q = q0 + k * BM;
+        int32_t* a = atiles + 6 * t;
+        a[0] = q; a[1] = q + BM < q1 ? q + BM : q1;
+        a[2] = tb; a[3] = te;
+        a[4] = text ? 0 : q0; a[5] = text ? 0 : q1;
+      });
+  // backward key tiles: the text keys against each query split, then every shot chunk's keys
+  if (has_text) {
     const int qs = (p.L + p.n_text_split - 1) / p.n_text_split;
-    for (int i = threadIdx.x; i < s_ntxt_k; i += blockDim.x) {
-      const int k0 = tb + (i / s_nsp) * KR, sp = i % s_nsp;
+    for (int i = threadIdx.x; i < nk_txt; i += blockDim.x) {
+      const int k0 = tb + (i / nsp) * KR, sp = i % nsp;
       const int qa = sp * qs;
       const int qb = qa + qs < p.L ? qa + qs : p.L;
       int32_t* a = ktiles + 6 * i;
@@ -224,18 +308,20 @@ __global__ __launch_bounds__(1024) void inv_global_kernel(
       a[2] = -1; a[3] = qa; a[4] = qb; a[5] = sp;
     }
   }
-  for (int cc = 0; cc < p.C; ++cc) {
-    if (shot[cc] < 0) continue;
-    const int a0 = off[cc], a1 = off[cc + 1];
-    const int nt = (a1 - a0 + KR - 1) / KR;
-    for (int k = threadIdx.x; k < nt; k += blockDim.x) {
-      const int k0 = a0 + k * KR;
-      int32_t* a = ktiles + 6 * (k_base[cc] + k);
-      a[0] = k0; a[1] = k0 + KR < a1 ? k0 + KR : a1;
-      a[2] = cc; a[3] = k_q0[cc]; a[4] = k_q1[cc]; a[5] = -1;
-    }
-  }
-  __syncthreads();
+  emit_segments(
+      p.C,
+      [&](int c, int& base, int& cnt) {
+        base = k_base[c];
+        cnt = shot[c] >= 0 ? (off[c + 1] - off[c] + KR - 1) / KR : 0;
+      },
+      [&](int c, int k, int t) {
+        const int a0 = off[c], a1 = off[c + 1];
+        const int k0 = a0 + k * KR;
+        int32_t* a = ktiles + 6 * t;
+        a[0] = k0; a[1] = k0 + KR < a1 ? k0 + KR : a1;
+        a[2] = c; a[3] = g_q0[grp[c]]; a[4] = g_q1[grp[c]]; a[5] = -1;
+      });
+
   // pair counts: anchor pairs + routed chunk sizes, one wave per (b, h) (integer sums: exact in
   // any order)
   const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
@@ -244,7 +330,7 @@ __global__ __launch_bounds__(1024) void inv_global_kernel(
     for (int c = lane; c < p.C; c += 64)
       s += static_cast<long long>(totals[bh * p.C + c]) * (off[c + 1] - off[c]);
     for (int w = 32; w > 0; w >>= 1) s += __shfl_xor(s, w);
-    if (lane == 0) pair_count[bh] = s_anchor + s;
+    if (lane == 0) pair_count[bh] = anchor_pairs + s;
   }
 }
 
@@ -255,7 +341,7 @@ __global__ __launch_bounds__(256) void inv_scatter_kernel(const int32_t* __restr
                                                           VarlenParams p,
                                                           int32_t* __restrict__ bucket_q,
                                                           int32_t* __restrict__ slot) {
-  __shared__ uint32_t bm[MOC_MAX_C * kInvWords];
+  uint32_t* bm = inv_bitmap;
   if (layout_rejected(p.chk)) return;
   const int tile = blockIdx.x, bh = blockIdx.y;
   build_bitmap(bm, sel, nsel, bh, tile, p);
@@ -310,8 +396,9 @@ hipError_t launch_varlen(const moc_layout* lay, const VarlenParams& p, const int
   const int BH = lay->B * lay->H;
   const int NB = BH * lay->C;
   // with S == 0 every nsel is 0: the counts, totals and tiles simply come out empty
-  hipLaunchKernelGGL(moc::inv_count_kernel, dim3(p.nqt, BH), dim3(256), 0, st, sel, nsel, p,
-                     counts);
+  const size_t bm_bytes = sizeof(uint32_t) * lay->C * moc::kInvWords;
+  hipLaunchKernelGGL(moc::inv_count_kernel, dim3(p.nqt, BH), dim3(256), bm_bytes, st, sel, nsel,
+                     p, counts);
   hipLaunchKernelGGL(moc::inv_scan_bucket_kernel, dim3(NB), dim3(256), 0, st, counts, totals,
                      p.nqt, p.chk);
   hipError_t e = hipGetLastError();
@@ -322,7 +409,7 @@ hipError_t launch_varlen(const moc_layout* lay, const VarlenParams& p, const int
                      out->n_ktiles, pair_count);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(moc::inv_scatter_kernel, dim3(p.nqt, BH), dim3(256), 0, st, sel, nsel,
+  hipLaunchKernelGGL(moc::inv_scatter_kernel, dim3(p.nqt, BH), dim3(256), bm_bytes, st, sel, nsel,
                      counts, out->bucket_off, p, out->bucket_q, out->slot);
   return hipGetLastError();
 }
