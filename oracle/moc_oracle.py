@@ -39,6 +39,10 @@ What is computed (per batch element b and head h; routing is independent per hea
      among the directions for faster kernels, without fixing a format): Q and K in the OCP
      microscaling MXFP8 format (e4m3 elements, one power-of-two scale per 32 elements along d),
      attention (8) over the dequantised values. See mx_quantize().
+ 13. Quantised values (the same pages: quantisation and the key/value layout as directions):
+     V in MXFP8 with its blocks of 32 along the key axis (per head and dim), attention (8) over
+     dequantised Q, K and V (attend_mxv), and the bound on what rounding the softmax weights to
+     e4m3 can add (pv_fp8_bound). See mx_quantize_keys().
 """
 from __future__ import annotations
 
@@ -836,6 +840,75 @@ def attend_mx(Q, K, V, layout, sel, scale: Optional[float] = None,
     for b, h, t in rows:
         Qd[b, h, t] = mx_dequantize(*mx_quantize(Q[b, h, t]))
     return attend(Qd, Kd, V, layout, sel, scale=scale, rows=rows)
+
+
+# ---------------------------------------------------------------------------------------------
+# 13. Quantised values: MXFP8 V along the key axis
+# ---------------------------------------------------------------------------------------------
+# Readings. In P.V the sum runs over keys, so a shared scale can only be factored out of the sum
+# if it is shared along the keys: V is quantised with the rule of section 12 applied to each
+# (b, h, dim) column, in blocks of 32 consecutive keys starting at key 0 (keys 32j .. 32j+31;
+# the last block of a column is padded with zeros, which do not change its largest magnitude).
+# The weights P are not part of the format: a kernel that rounds them to e4m3 before the
+# product adds an error that pv_fp8_bound() bounds; attend_mxv() is the exact attention of the
+# dequantised tensors.
+
+def mx_quantize_keys(V) -> Tuple[np.ndarray, np.ndarray]:
+    """MXFP8 of V [..., L, d] along the key axis: codes uint8 [..., d, L32] and E8M0 scale codes
+    uint8 [..., d, L32/32], L32 = L rounded up to a multiple of 32 (padding keys are zero)."""
+    V = _as_f64(V)
+    L = V.shape[-2]
+    L32 = -(-L // MX_BLOCK) * MX_BLOCK
+    cols = np.zeros(V.shape[:-2] + (V.shape[-1], L32))
+    cols[..., :L] = np.swapaxes(V, -1, -2)
+    return mx_quantize(cols)
+
+
+def mx_dequantize_keys(codes, scales, L: int) -> np.ndarray:
+    """float64 V' [..., L, d] from the column codes and scales of mx_quantize_keys."""
+    cols = mx_dequantize(codes, scales)
+    return np.swapaxes(cols[..., :L], -1, -2)
+
+
+def attend_mxv(Q, K, V, layout, sel, scale: Optional[float] = None,
+               rows: Optional[Sequence[Tuple[int, int, int]]] = None):
+    """Attention (8) over the dequantised Q', K' (rows along d, section 12) and V' (columns along
+    the keys), in exact arithmetic."""
+    V = _as_f64(V)
+    Vd = mx_dequantize_keys(*mx_quantize_keys(V), V.shape[-2])
+    return attend_mx(Q, K, Vd, layout, sel, scale=scale, rows=rows)
+
+
+def pv_fp8_bound(Q, K, V, layout, sel, rows: Sequence[Tuple[int, int, int]],
+                 scale: Optional[float] = None) -> np.ndarray:
+    """Bound [n, d] on |o - o'| for the listed rows, where o is the attention (8) of Q, K, V
+    (pass the dequantised tensors) and o' the same sum with every softmax weight rounded to
+    e4m3 before it multiplies V.
+
+    Derivation. With x_j the scaled scores of Omega(t), m = max x_j and p_j = exp(x_j - m), a
+    kernel holds the weights as w_j = 2^delta p_j for some delta >= 0 of its own (a running
+    maximum that trails the true one; delta <= 8 keeps w_j below the e4m3 maximum) and divides
+    by its row sum 2^delta sum_j p_j of the unrounded weights. Rounding to nearest e4m3 moves a
+    normal value (w >= 2^-6) by at most 2^-4 w, and a subnormal one by at most 2^-10 and at most
+    w itself. The row error is therefore at most
+        2^-4 sum_j p_j |v_j| / l  +  sum_j min(2^-10, p_j) |v_j| / l,    l = sum_j p_j,
+    since 2^-delta min(2^-10, 2^delta p_j) <= min(2^-10, p_j). A row split into parts that are
+    normalised separately and merged with their softmax weights obeys the same bound (each part's
+    maximum is at most m, which only lowers its terms)."""
+    D = derive(layout)
+    Q, K, V = _as_f64(Q), _as_f64(K), _as_f64(V)
+    d = Q.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    sel = np.asarray(sel)
+    out = np.zeros((len(rows), d))
+    for i, (b, h, t) in enumerate(rows):
+        keys = key_set(D, t, sel[b, h, t])
+        x = (K[b, h][keys] @ Q[b, h, t]) * scale
+        p = np.exp(x - np.max(x))
+        av = np.abs(V[b, h][keys])
+        out[i] = (2.0 ** -4 * (p @ av) + np.minimum(2.0 ** -10, p) @ av) / np.sum(p)
+    return out
 
 
 def _as_f64(x) -> np.ndarray:
