@@ -26,6 +26,7 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}  # MI355X dense MFMA (bf16), fp32
 # quantised scores: per attended pair 2d FLOPs of S on fp8 (2 x the bf16 rate) and 2d of P.V
 # on bf16, so the time-weighted dense peak of the pair is 4 / (2 / 5033.2 + 2 / 2516.6)
 PEAK_MX_TFLOPS = 4.0 / (2.0 / (2 * 2516.6) + 2.0 / 2516.6)
+PEAK_FP8_TFLOPS = 2 * 2516.6  # quantised scores and values: both products on fp8
 PEAK_HBM_GBS = 8000.0
 
 
@@ -38,7 +39,7 @@ def parse(argv=None):
                     choices=["headline", "mid", "short", "tiny", "train", "headline_uniform",
                              "single_shot_c64", "single_shot_c128", "single_shot_c256",
                              "single_shot_c512", "single_shot_c1024", "headline_outer",
-                             "headline_mx", "headline_h3"])
+                             "headline_mx", "headline_mxv", "headline_h3"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=768,
@@ -171,7 +172,7 @@ def cpu_baseline(w, Q, K, V, rows_n: int):
     flat = np.sort(rng.choice(w.B * w.H * w.L, size=n, replace=False))
     rows = [(int(i // (w.H * w.L)), int(i // w.L % w.H), int(i % w.L)) for i in flat]
     t0 = time.perf_counter()
-    att = mo.attend_mx if w.mx_scores else mo.attend
+    att = mo.attend_mxv if w.mx_values else mo.attend_mx if w.mx_scores else mo.attend
     att(Q, K, V, w.layout, r.sel, rows=rows)
     t_att = time.perf_counter() - t0
     measured = t_pool + t_route + t_att
@@ -292,13 +293,14 @@ def main(argv=None) -> int:
     outer = w.segments is not None
     segs = moc.DeviceSegments(w.segments, lay) if outer else None
     mx = w.mx_scores
-    qm = km = None
+    mxv = w.mx_values
+    qm = km = vq = None
     names = (["pool"] + (["route_outer"] if outer else []) + ["route", "varlen"]
              + (["mx_quantize"] if mx else []) + ["attend_fwd"]
              + (["attend_bwd"] if with_bwd else []))
 
     def step(ev=None):
-        nonlocal qm, km
+        nonlocal qm, km, vq
         i = 0
 
         def mark():
@@ -322,8 +324,13 @@ def main(argv=None) -> int:
         if mx:
             qm = moc.mx_quantize(Qd, lay, out=qm)
             km = moc.mx_quantize(Kd, lay, out=km)
+            if mxv:
+                vq = moc.mx_quantize_v(Vd, lay, out=vq)
             mark()
-            O, lse = moc.attend_fwd_mx(qm, km, Vd, lay, vl, ws=fwd_ws)
+            if mxv:
+                O, lse = moc.attend_fwd_mxv(qm, km, vq, lay, vl, ws=fwd_ws)
+            else:
+                O, lse = moc.attend_fwd_mx(qm, km, Vd, lay, vl, ws=fwd_ws)
         else:
             O, lse = moc.attend_fwd(Qd, Kd, Vd, lay, vl, ws=fwd_ws)
         mark()
@@ -381,7 +388,7 @@ def main(argv=None) -> int:
     # nsel read by the count pass and again by the scatter pass, one bucket_q and one slot int32
     # written per routed row
     gather_bytes = 2 * w.B * w.H * w.L * (S + 1) * 4 + 2 * cap["rows"] * 4
-    peak = PEAK_MX_TFLOPS if mx else PEAK_TFLOPS[w.dtype]
+    peak = PEAK_FP8_TFLOPS if mxv else PEAK_MX_TFLOPS if mx else PEAK_TFLOPS[w.dtype]
     att_tf = fwd_flops / (stage["attend_fwd"] * 1e-3) / 1e12
     out = {
         "metric": METRIC,
@@ -394,14 +401,17 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8 scores + bf16 P.V" if mx else w.dtype,
+        "dtype": ("mxfp8 scores + mxfp8 V, e4m3 P" if mxv else
+                  "mxfp8 scores + bf16 P.V" if mx else w.dtype),
         "data": "synthetic (seeded normal Q/V, chunk-clustered K; no trained activations)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "C": w.C,
                    "top_k": w.top_k, "causal": w.causal, "p_max": w.p_max, "lambda": w.lam,
                    "seed": w.seed, "layout": w.description,
                    **({"outer_segments": len(w.segments) - 1, "outer_M": w.outer_M}
                       if w.segments is not None else {}),
-                   **({"scores": "MXFP8 Q and K (e4m3, 32-element E8M0 blocks)"} if mx else {})},
+                   **({"scores": "MXFP8 Q and K (e4m3, 32-element E8M0 blocks)"} if mx else {}),
+                   **({"values": "MXFP8 V (32-key E8M0 blocks), softmax weights rounded to "
+                                 "e4m3"} if mxv else {})},
         "layer_ms": ms,
         "step_ms_median": step_ms[len(step_ms) // 2],
         "step_ms_min": step_ms[0],
@@ -422,13 +432,16 @@ def main(argv=None) -> int:
         "gather_gbs": gather_bytes / (stage["varlen"] * 1e-3) / 1e9,
         "roofline": {
             "bound": "mfma",
-            "kernel": ("attention forward with quantised scores (routed + anchor kernels of "
+            "kernel": ("attention forward with quantised scores and values (routed + anchor "
+                       "kernels of moc_attend_fwd_mxv; both products on fp8)" if mxv else
+                       "attention forward with quantised scores (routed + anchor kernels of "
                        "moc_attend_fwd_mx; peak weighted 2d fp8 + 2d bf16 FLOPs per pair)"
                        if mx else "attention forward (routed + anchor kernels of moc_attend_fwd)"),
             "achieved": att_tf, "peak": peak, "unit": "TFLOP/s", "frac": att_tf / peak,
             "traffic": recorded_traffic(a.workload if a.seed == 0 else ""),
-            "traffic_unit": ("HBM bytes per attention-forward call: V transpose + routed + "
-                             "anchor kernels (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)"),
+            "traffic_unit": ("HBM bytes per attention-forward call: "
+                             + ("" if mxv else "V transpose + ") + "routed + anchor kernels "
+                             "(rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)"),
         },
         "cpu_baseline": None,
     }
@@ -436,7 +449,8 @@ def main(argv=None) -> int:
         out["backward_tflops"] = bwd_flops / (stage["attend_bwd"] * 1e-3) / 1e12
     # the same fractions against ceilings re-measured on this GPU
     mp = measured_peaks(dev)
-    mpeak = (4.0 / (2.0 / mp["mfma_fp8_tflops"] + 2.0 / mp["mfma_bf16_tflops"]) if mx
+    mpeak = (mp["mfma_fp8_tflops"] if mxv else
+             4.0 / (2.0 / mp["mfma_fp8_tflops"] + 2.0 / mp["mfma_bf16_tflops"]) if mx
              else mp["mfma_bf16_tflops"])
     out["measured_peaks"] = mp
     # the probe loops are bf16 and fp8 MFMAs: an fp32 path has no measured ceiling here

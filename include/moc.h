@@ -342,6 +342,40 @@ moc_status moc_attend_fwd_mx(const moc_layout *lay, const moc_varlen *vl, const 
                              size_t ws_bytes, void *stream);
 
 /*
+ * MXFP8 quantisation of V along the key axis, for the quantised-values forward (the same pages
+ * name quantisation and the key/value layout as directions for faster kernels). In P.V the
+ * sum runs over keys, so the blocks that share a scale run along the keys: for every (b, h, dim)
+ * column, blocks of 32 consecutive keys from key 0, each coded with the rule of moc_mx_quantize
+ * (E8M0 scale, E4M3 elements, ties to even, saturation at +-448). The output is the attention's
+ * tile layout, so that the forward copies each 64-key tile verbatim:
+ *   vq: device uint8 [B,H,Lp/64,d,80], Lp = L rounded up to a multiple of 64, of
+ *       moc_mx_quantize_v_bytes(lay) bytes. Row (tile j, dim e) holds, at byte 32 b + p
+ *       (block b = 0, 1; p = 0..31), the code of key 64 j + 32 b + s(p), where s swaps bits 3
+ *       and 4 of p; at bytes 64 and 65 the scale codes of blocks 0 and 1; bytes 66-79 zero.
+ *       Keys >= L are coded as zero. Fully overwritten.
+ *   V: device bf16 [B,H,L,d] (the layout's dtype must be MOC_BF16); inputs must be finite.
+ */
+size_t moc_mx_quantize_v_bytes(const moc_layout *lay);
+moc_status moc_mx_quantize_v(const moc_layout *lay, const void *V, uint8_t *vq, void *stream);
+
+/*
+ * Attention forward with quantised scores and values: moc_attend_fwd_mx with V given as the
+ * tiles of moc_mx_quantize_v, and P.V on the block-scaled fp8 matrix cores as well. The
+ * softmax weights are rounded to E4M3 (ties to even) before they multiply V, and the row sums
+ * use the unrounded weights: against the attention of the dequantised Q', K', V' the output
+ * moves by at most 2^-4 sum_j p_j |v'_j| / l + sum_j min(2^-10, p_j) |v'_j| / l per element
+ * (p_j = exp of the scaled score minus the row maximum, l = sum_j p_j), plus fp32 and bf16
+ * output rounding; lse is computed from the unrounded weights.
+ *   Qc, Qs, Kc, Ks: as for moc_attend_fwd_mx; Vq: the output of moc_mx_quantize_v.
+ *   O: bf16 [B,H,L,d]; lse: float [B,H,L]; ws: as for moc_attend_fwd (the transposed V copy
+ *   of that workspace is not used). O and lse must not alias an input.
+ */
+moc_status moc_attend_fwd_mxv(const moc_layout *lay, const moc_varlen *vl, const uint8_t *Qc,
+                              const uint8_t *Qs, const uint8_t *Kc, const uint8_t *Ks,
+                              const uint8_t *Vq, float softmax_scale, void *O, float *lse,
+                              void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Attention backward with the routed sets held fixed (summary §3.1 and Appendix A: top-k is
  * not differentiable; gradients reach the selected keys and values only).
  *   Inputs: Q, K, V, O, lse from moc_attend_fwd, dO. Outputs dQ, dK, dV [B,H,L,d] in the

@@ -70,6 +70,7 @@ class Workload:
     segments: Optional[Tuple[int, ...]] = None  # outer-loop routing: segment chunk offsets
     outer_M: int = 0
     mx_scores: bool = False  # quantised scores: Q and K as MXFP8 in the attention
+    mx_values: bool = False  # quantised values: V as MXFP8 along the keys, P.V on fp8 as well
 
     @property
     def L(self) -> int:
@@ -312,10 +313,20 @@ def headline_mx(seed: int = 0, **kw) -> Workload:
     return replace(w, **kw)
 
 
+def headline_mxv(seed: int = 0, **kw) -> Workload:
+    """Headline workload with quantised scores and values: Q, K and V quantised to MXFP8 for the
+    attention (V in 32-key blocks), P.V on fp8 with the softmax weights rounded to e4m3."""
+    w = headline(seed)
+    w = replace(w, name="headline_mxv", mx_scores=True, mx_values=True,
+                description=w.description + "; attention from MXFP8 Q, K and V")
+    return replace(w, **kw)
+
+
 WORKLOADS = {"tiny": tiny, "mid": mid, "headline": headline, "short": short, "train": train,
              "slice": grad_slice, "headline_uniform": headline_uniform,
              "single_shot": single_shot, "headline_outer": headline_outer,
-             "headline_mx": headline_mx, "headline_h3": headline_h3}
+             "headline_mx": headline_mx, "headline_mxv": headline_mxv,
+             "headline_h3": headline_h3}
 for _c in (64, 128, 256, 512, 1024):
     WORKLOADS[f"single_shot_c{_c}"] = (lambda c: lambda seed=0, **kw: single_shot(seed, c, **kw))(_c)
 

@@ -28,7 +28,8 @@ EXPORTS = (
     "moc_mx_quantize", "moc_attend_fwd_mx", "moc_poisson_thresholds", "moc_status_string",
     "moc_last_error", "moc_check_layout", "moc_layout_check_host", "moc_layout_status",
     "moc_route_noalloc", "moc_varlen_total", "moc_varlen_set_capacity",
-    "moc_attend_workspace_bytes", "moc_varlen_status",
+    "moc_attend_workspace_bytes", "moc_varlen_status", "moc_mx_quantize_v_bytes",
+    "moc_mx_quantize_v", "moc_attend_fwd_mxv",
 )
 
 
@@ -109,6 +110,14 @@ def load() -> ctypes.CDLL:
                                       c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_void_p,
                                       c_size_t, c_void_p]
     lib.moc_attend_fwd_mx.restype = c_int32
+    lib.moc_mx_quantize_v_bytes.argtypes = [P(MocLayout)]
+    lib.moc_mx_quantize_v_bytes.restype = c_size_t
+    lib.moc_mx_quantize_v.argtypes = [P(MocLayout), c_void_p, c_void_p, c_void_p]
+    lib.moc_mx_quantize_v.restype = c_int32
+    lib.moc_attend_fwd_mxv.argtypes = [P(MocLayout), P(MocVarlen), c_void_p, c_void_p, c_void_p,
+                                       c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_void_p,
+                                       c_size_t, c_void_p]
+    lib.moc_attend_fwd_mxv.restype = c_int32
     lib.moc_poisson_thresholds.argtypes = [c_float, c_int32, P(c_uint64)]
     lib.moc_poisson_thresholds.restype = c_int32
     lib.moc_check_layout.argtypes = [P(MocLayout), c_void_p]

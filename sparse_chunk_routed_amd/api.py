@@ -424,6 +424,55 @@ def attend_fwd_mx(Qm: MxTensor, Km: MxTensor, V: torch.Tensor, lay: DeviceLayout
     return O, lse
 
 
+VQ_ROW = 80  # bytes per (64-key tile, dim) row of the quantised V tiles
+
+
+def mx_quantize_v(V: torch.Tensor, lay: DeviceLayout,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """MXFP8 quantisation of a bf16 [B,H,L,d] V along the key axis into the attention's tile
+    layout (moc_mx_quantize_v): uint8 [B,H,Lp/64,d,80]."""
+    _check_qkv(V)
+    if V.dtype != torch.bfloat16:
+        raise ValueError("MXFP8 quantisation takes bf16 input")
+    B, H, Lq, d = V.shape
+    Lp = (Lq + 63) // 64 * 64
+    shape = (B, H, Lp // 64, d, VQ_ROW)
+    s = lay.struct(B, H, d, V.dtype)
+    n = int(L.load().moc_mx_quantize_v_bytes(ctypes.byref(s)))
+    if n != math.prod(shape):
+        raise L.MocError(L.MOC_EINVAL, "quantised V size does not match the tile layout")
+    if out is None or tuple(out.shape) != shape:
+        out = torch.empty(shape, dtype=torch.uint8, device=V.device)
+    L.check(L.load().moc_mx_quantize_v(ctypes.byref(s), _ptr(V), _ptr(out), _stream(V.device)))
+    return out
+
+
+def attend_fwd_mxv(Qm: MxTensor, Km: MxTensor, Vq: torch.Tensor, lay: DeviceLayout, vl: Varlen,
+                   scale: Optional[float] = None, ws: Optional[torch.Tensor] = None):
+    """Forward with quantised scores and values (moc_attend_fwd_mxv): (O [B,H,L,d] bf16,
+    lse [B,H,L])."""
+    B, H, Lp, d = Qm.codes.shape
+    Lq = Qm.L
+    for m in (Qm, Km):
+        if m.codes.shape != (B, H, Lp, d) or m.scales.shape != (B, H, Lp, d // 32):
+            raise ValueError("MXFP8 operands do not match")
+    if tuple(Vq.shape) != (B, H, Lp // 64, d, VQ_ROW) or Vq.dtype != torch.uint8:
+        raise ValueError("quantised V does not match the MXFP8 operands")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    O = torch.empty((B, H, Lq, d), dtype=torch.bfloat16, device=Vq.device)
+    lse = torch.empty((B, H, Lq), dtype=torch.float32, device=Vq.device)
+    need = vl.workspace_bytes(L.MOC_OP_FWD)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=Vq.device)
+    s = lay.struct(B, H, d, torch.bfloat16)
+    L.check(L.load().moc_attend_fwd_mxv(ctypes.byref(s), ctypes.byref(vl.struct), _ptr(Qm.codes),
+                                        _ptr(Qm.scales), _ptr(Km.codes), _ptr(Km.scales),
+                                        _ptr(Vq), float(scale), _ptr(O), _ptr(lse), _ptr(ws),
+                                        ws.numel(), _stream(Vq.device)))
+    return O, lse
+
+
 def attend_bwd(Q, K, V, O, lse, dO, lay: DeviceLayout, vl: Varlen, scale: Optional[float] = None,
                ws: Optional[torch.Tensor] = None):
     """(dQ, dK, dV) in the input dtype."""

@@ -291,14 +291,20 @@ __global__ __launch_bounds__(kNT) void attn_fwd_kernel(
 }
 
 
+// Operand formats of the LDS-staged forward: bf16 Q, K, V; MXFP8 Q and K (quantised scores);
+// MXFP8 Q, K and V (quantised scores and values).
+enum { QNT_NONE = 0, QNT_SCORES = 1, QNT_VALUES = 2 };
+
 // bf16 attention forward: same work decomposition and epilogue as attn_fwd_kernel; two wave
 // groups half a tile apart, K and V^T tiles staged by direct-to-LDS copies into padded
 // 64-key-aligned tiles (four rotating stages) and the permuted key order of attn_fwd_lds.h.
-// MX: Q and K are MXFP8 codes and scales (rows padded to Lp), S on the block-scaled fp8 MFMA.
-template <int D, int MODE, bool MX>
-__global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
+// QNT_SCORES: Q and K are MXFP8 codes and scales (rows padded to Lp), S on the block-scaled fp8
+// MFMA. QNT_VALUES: also V, as the quantised tiles of moc_mx_quantize_v (Vt points at them),
+// and P.V on the block-scaled fp8 MFMA with P^T rounded to e4m3.
+template <int D, int MODE, int QNT>
+__device__ __forceinline__ void attn_fwd_lds_body(
     const void* __restrict__ Qv, const void* __restrict__ Kv, const uint8_t* __restrict__ Qs,
-    const uint8_t* __restrict__ Ks, const bf16_t* __restrict__ Vt, int Lp,
+    const uint8_t* __restrict__ Ks, const void* __restrict__ Vt, int Lp,
     const int32_t* __restrict__ off, AttnParams p, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ bucket_off,
     const int32_t* __restrict__ bucket_q, const int32_t* __restrict__ slot,
@@ -306,9 +312,12 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
     float* __restrict__ lse) {
   using LT = LdsTiles<D>;
   using MT = MxTiles<D>;
+  constexpr bool MX = QNT != QNT_NONE;
+  constexpr bool QV = QNT == QNT_VALUES;
   static_assert(kNW == 8, "two groups of four waves");
-  constexpr int STAGE = MX ? MT::STAGE : LT::STAGE;
-  constexpr int VOFF = MX ? MT::KBYTES : LT::KBYTES;  // V^T tile within a stage
+  constexpr int STAGE = QV ? MxvTiles<D>::STAGE : MX ? MT::STAGE : LT::STAGE;
+  // V tile within a stage
+  constexpr int VOFF = QV ? MxvTiles<D>::VOFF : MX ? MT::KBYTES : LT::KBYTES;
   // four stage buffers as distinct objects, so that the compiler can tell the LDS written by
   // the in-flight direct-to-LDS copies from the stage being read (no forced wait between them)
   __shared__ __attribute__((aligned(1024))) char st0[STAGE];
@@ -355,11 +364,11 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
   }
   // s_waitcnt vmcnt(n) lgkmcnt(0), n = this wave's copies of one stage: all but the newest
   // stage's copies have landed
-  std::conditional_t<MX, MxStageCopier<D, kNW>, StageCopier<D, kNW>> cp;
+  std::conditional_t<MX, MxStageCopier<D, kNW, QV>, StageCopier<D, kNW>> cp;
   cp.init(wv, lane, Lp);
   const int ncopy = cp.count();
   auto wait_but_newest = [&]() __attribute__((always_inline)) {
-    constexpr int NB = MX ? MxStageCopier<D, kNW>::NBASE : LT::KBLK / kNW + LT::VBLK / kNW;
+    constexpr int NB = MX ? MxStageCopier<D, kNW, QV>::NBASE : LT::KBLK / kNW + LT::VBLK / kNW;
     if (ncopy == NB) __builtin_amdgcn_s_waitcnt(0x0070 | NB);
     else if (ncopy == NB + 1) __builtin_amdgcn_s_waitcnt(0x0070 | (NB + 1));
     else __builtin_amdgcn_s_waitcnt(0x0070 | (NB + 2));
@@ -369,7 +378,9 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
   const bf16_t* Kbh = static_cast<const bf16_t*>(Kv) + bh_off;
   const uint8_t* Kcbh = static_cast<const uint8_t*>(Kv) + bhp * D;
   const uint8_t* Ksbh = Ks + bhp * MT::NB;
-  const bf16_t* Vtbh = Vt + static_cast<size_t>(bh) * D * Lp;
+  const bf16_t* Vtbh = static_cast<const bf16_t*>(Vt) + static_cast<size_t>(bh) * D * Lp;
+  // quantised V tiles of this (b, h): Lp / 64 tiles of D rows
+  const uint8_t* Vqbh = static_cast<const uint8_t*>(Vt) + static_cast<size_t>(bh) * Lp * D * kVqRow / kBN;
   std::conditional_t<MX, MxQFrag<D>, QFrag<bf16_t, D>> qf;
   if constexpr (MX)
     qf.load(static_cast<const uint8_t*>(Qv) + (bhp + tok) * D, Qs + (bhp + tok) * MT::NB, g);
@@ -402,7 +413,8 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
   auto issue = [&](int j, uint32_t lds) __attribute__((always_inline)) {
     if (j >= ntot) return;
     const int base = tile_base(j);
-    if constexpr (MX) cp.issue(lds, Kcbh, Ksbh, base, Vtbh, base);
+    if constexpr (QV) cp.issue(lds, Kcbh, Ksbh, base, Vqbh + static_cast<size_t>(base / kBN) * D * kVqRow, base);
+    else if constexpr (MX) cp.issue(lds, Kcbh, Ksbh, base, Vtbh, base);
     else cp.issue(lds, Kbh, base, kmax, Vtbh, base);
   };
 
@@ -419,22 +431,29 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
   // waited for at the end of half-step 2j-1.
   f32x16 s[2];
   bf16x8 pb[4];  // P^T of the previous tile, packed for the four 16-key MFMA steps
+  i32x8 pb8;     // QNT_VALUES: P^T of the previous tile as e4m3 codes (one 64-key MFMA step)
   auto scores = [&](const char* st) __attribute__((always_inline)) {
     if constexpr (MX) score_tile_mx<D>(st, qf, s, ql, g);
     else score_tile_swz<D>(st, qf, s, ql, g);
   };
   bf16x8 pre[kPre > 0 ? kPre : 1];  // V^T operands read ahead for the next P.V
   auto preload = [&](const char* st) __attribute__((always_inline)) {
-    if constexpr (kPre > 0) pv_preload<D, VOFF, kPre>(st, pre, ql, g);
+    if constexpr (kPre > 0 && !QV) pv_preload<D, VOFF, kPre>(st, pre, ql, g);
   };
   // steady MFMA half-step: O += V P of tile j-1 (stage stp), then S of tile j (stage stc)
   auto mfma_full = [&](const char* stp, const char* stc) __attribute__((always_inline)) {
-    pv_swz_packed<D, VOFF, kPre>(stp, pb, acc, ql, g, pre);
+    if constexpr (QV) pv_mxv<D, VOFF>(stp, pb8, acc, ql, g);
+    else pv_swz_packed<D, VOFF, kPre>(stp, pb, acc, ql, g, pre);
     scores(stc);
     // operand reads run kReadAhead ahead of the MFMAs that use them, all the way to the last
     // MFMA (bounded registers; an even spread of the reads over the MFMAs fell behind the
     // last ones, which then each waited for their operand)
-    if constexpr (MX) {
+    if constexpr (QV) {
+      // P.V: three reads per MFMA (two code halves and the scale word); S as below
+      constexpr int NM = D / 32 + 2 * (D / 64);
+      constexpr int NR = 3 * (D / 32) + 4 * (D / 64) + 2;
+      sched_lead_reads<NM, NR, kReadAhead, D / 32, 0, 2, 2, 3>();
+    } else if constexpr (MX) {
       // P.V: one read per MFMA (less the preloaded ones); S: two code reads per MFMA and two
       // scale reads per tile
       constexpr int NM = 4 * (D / 32) + 2 * (D / 64);
@@ -449,10 +468,15 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
   // last MFMA half-step: O += V P of the last tile
   auto mfma_last = [&]() __attribute__((always_inline)) {
     const int r = (ntot - 1) & 3;
-    if (r == 0) pv_swz_packed<D, VOFF, kPre>(st0, pb, acc, ql, g, pre);
-    else if (r == 1) pv_swz_packed<D, VOFF, kPre>(st1, pb, acc, ql, g, pre);
-    else if (r == 2) pv_swz_packed<D, VOFF, kPre>(st2, pb, acc, ql, g, pre);
-    else pv_swz_packed<D, VOFF, kPre>(st3, pb, acc, ql, g, pre);
+    const char* st = r == 0 ? st0 : r == 1 ? st1 : r == 2 ? st2 : st3;
+    if constexpr (QV) {
+      pv_mxv<D, VOFF>(st, pb8, acc, ql, g);
+    } else {
+      if (r == 0) pv_swz_packed<D, VOFF, kPre>(st0, pb, acc, ql, g, pre);
+      else if (r == 1) pv_swz_packed<D, VOFF, kPre>(st1, pb, acc, ql, g, pre);
+      else if (r == 2) pv_swz_packed<D, VOFF, kPre>(st2, pb, acc, ql, g, pre);
+      else pv_swz_packed<D, VOFF, kPre>(st3, pb, acc, ql, g, pre);
+    }
   };
   auto valu_half = [&](int j) __attribute__((always_inline)) {
     int base, lo, hi;
@@ -482,14 +506,36 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
     }
     const float neg = -m_ref;
     float l0 = 0.f, l1 = 0.f;
+    if constexpr (QV) {
+      // P^T as e4m3 codes, round to nearest even (values are at most 2^kRescale = 256, below
+      // the e4m3 maximum 448); the row sum keeps the unrounded values
+      int w[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p0 = fast_exp2(__builtin_fmaf(s[0][i], c2, neg));
-      const float p1 = fast_exp2(__builtin_fmaf(s[1][i], c2, neg));
-      pb[i >> 3][i & 7] = static_cast<__bf16>(p0);
-      pb[2 + (i >> 3)][i & 7] = static_cast<__bf16>(p1);
-      l0 += p0;
-      l1 += p1;
+      for (int k = 0; k < 4; ++k) {
+        float a[4], b[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = fast_exp2(__builtin_fmaf(s[0][4 * k + e], c2, neg));
+          b[e] = fast_exp2(__builtin_fmaf(s[1][4 * k + e], c2, neg));
+          l0 += a[e];
+          l1 += b[e];
+        }
+        w[k] = __builtin_amdgcn_cvt_pk_fp8_f32(a[0], a[1], 0, false);
+        w[k] = __builtin_amdgcn_cvt_pk_fp8_f32(a[2], a[3], w[k], true);
+        w[4 + k] = __builtin_amdgcn_cvt_pk_fp8_f32(b[0], b[1], 0, false);
+        w[4 + k] = __builtin_amdgcn_cvt_pk_fp8_f32(b[2], b[3], w[4 + k], true);
+      }
+      pb8 = i32x8{w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7]};
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p0 = fast_exp2(__builtin_fmaf(s[0][i], c2, neg));
+        const float p1 = fast_exp2(__builtin_fmaf(s[1][i], c2, neg));
+        pb[i >> 3][i & 7] = static_cast<__bf16>(p0);
+        pb[2 + (i >> 3)][i & 7] = static_cast<__bf16>(p1);
+        l0 += p0;
+        l1 += p1;
+      }
     }
     lsum += l0 + l1;
   };
@@ -626,6 +672,35 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
   }
 }
 
+// bf16 Q, K, V (MX = false) or MXFP8 Q and K (MX = true)
+template <int D, int MODE, bool MX>
+__global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
+    const void* __restrict__ Qv, const void* __restrict__ Kv, const uint8_t* __restrict__ Qs,
+    const uint8_t* __restrict__ Ks, const void* __restrict__ Vt, int Lp,
+    const int32_t* __restrict__ off, AttnParams p, const int32_t* __restrict__ tiles,
+    const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ bucket_off,
+    const int32_t* __restrict__ bucket_q, const int32_t* __restrict__ slot,
+    float* __restrict__ pO, float* __restrict__ plse, bf16_t* __restrict__ O,
+    float* __restrict__ lse) {
+  attn_fwd_lds_body<D, MODE, MX ? QNT_SCORES : QNT_NONE>(Qv, Kv, Qs, Ks, Vt, Lp, off, p, tiles,
+                                                          n_tiles, bucket_off, bucket_q, slot,
+                                                          pO, plse, O, lse);
+}
+
+// MXFP8 Q, K and V (quantised scores and values)
+template <int D, int MODE>
+__global__ __launch_bounds__(kNT) void attn_fwd_mxv_kernel(
+    const void* __restrict__ Qv, const void* __restrict__ Kv, const uint8_t* __restrict__ Qs,
+    const uint8_t* __restrict__ Ks, const void* __restrict__ Vq, int Lp,
+    const int32_t* __restrict__ off, AttnParams p, const int32_t* __restrict__ tiles,
+    const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ bucket_off,
+    const int32_t* __restrict__ bucket_q, const int32_t* __restrict__ slot,
+    float* __restrict__ pO, float* __restrict__ plse, bf16_t* __restrict__ O,
+    float* __restrict__ lse) {
+  attn_fwd_lds_body<D, MODE, QNT_VALUES>(Qv, Kv, Qs, Ks, Vq, Lp, off, p, tiles, n_tiles,
+                                         bucket_off, bucket_q, slot, pO, plse, O, lse);
+}
+
 }  // namespace moc
 
 namespace moc_host {
@@ -737,6 +812,46 @@ hipError_t launch_attn_fwd(const moc_layout* lay, const moc_varlen* vl, const vo
                : launch_fwd_bf16<64>(lay, vl, Q, K, nullptr, nullptr, V, scale, O, lse, pO, plse, vt_ws, st);
   return lay->d == 128 ? launch_fwd_t<float, 128>(lay, vl, Q, K, V, scale, O, lse, pO, plse, st)
                        : launch_fwd_t<float, 64>(lay, vl, Q, K, V, scale, O, lse, pO, plse, st);
+}
+
+// quantised scores and values: Q and K as MXFP8 codes and scales (rows padded to Lp), V as the
+// quantised tiles of moc_mx_quantize_v
+template <int D>
+static hipError_t launch_fwd_mxv_d(const moc_layout* lay, const moc_varlen* vl, const uint8_t* Qc,
+                                   const uint8_t* Qs, const uint8_t* Kc, const uint8_t* Ks,
+                                   const uint8_t* Vq, float scale, void* O, float* lse, float* pO,
+                                   float* plse, hipStream_t st) {
+  using moc::bf16_t;
+  AttnParams p;
+  p.B = lay->B; p.H = lay->H; p.L = lay->L; p.C = lay->C; p.S = vl->S;
+  p.scale_log2 = scale * moc::kLog2e;
+  p.chk = vl->status;
+  const int Lp = attn_vt_rows(lay->L);
+  hipError_t e;
+  if (vl->S > 0 && vl->max_rtiles > 0) {
+    p.max_tiles = vl->max_rtiles;
+    hipLaunchKernelGGL((moc::attn_fwd_mxv_kernel<D, moc::MODE_ROUTED>), dim3(vl->max_rtiles),
+                       dim3(moc::kNT), 0, st, Qc, Kc, Qs, Ks, Vq, Lp, lay->chunk_offsets, p,
+                       vl->rtiles, vl->n_rtiles, vl->bucket_off, vl->bucket_q, vl->slot, pO,
+                       plse, static_cast<bf16_t*>(O), lse);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  p.max_tiles = vl->max_atiles;
+  hipLaunchKernelGGL((moc::attn_fwd_mxv_kernel<D, moc::MODE_ANCHOR>),
+                     dim3(vl->max_atiles * lay->B * lay->H), dim3(moc::kNT), 0, st, Qc, Kc, Qs,
+                     Ks, Vq, Lp, lay->chunk_offsets, p, vl->atiles, vl->n_atiles,
+                     vl->bucket_off, vl->bucket_q, vl->slot, pO, plse,
+                     static_cast<bf16_t*>(O), lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd_mxv(const moc_layout* lay, const moc_varlen* vl, const uint8_t* Qc,
+                               const uint8_t* Qs, const uint8_t* Kc, const uint8_t* Ks,
+                               const uint8_t* Vq, float scale, void* O, float* lse, float* pO,
+                               float* plse, hipStream_t st) {
+  return lay->d == 128
+             ? launch_fwd_mxv_d<128>(lay, vl, Qc, Qs, Kc, Ks, Vq, scale, O, lse, pO, plse, st)
+             : launch_fwd_mxv_d<64>(lay, vl, Qc, Qs, Kc, Ks, Vq, scale, O, lse, pO, plse, st);
 }
 
 // quantised scores: Q and K as MXFP8 codes and scales (rows padded to Lp), V bf16

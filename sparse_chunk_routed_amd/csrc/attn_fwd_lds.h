@@ -249,16 +249,35 @@ struct MxTiles {
   static constexpr int SCH = kBN * NB / 16;               // 16-byte chunks of the tile's scales
 };
 
+// Quantised values: V as MXFP8 along the keys, in the tile layout written by moc_mx_quantize_v:
+// per 64-key tile, D rows of kVqRow bytes - the row's 64 e4m3 codes (position p of each 32-key
+// block holds key p with bits 3 and 4 swapped, so that a lane's 16-byte operand read holds the
+// keys of its P^T values), the E8M0 scales of the tile's two 32-key blocks, zero padding. The
+// stage takes the tile verbatim after the MX K tile: the 80-byte pitch is 5 chunks (odd), so
+// the 16 lanes of a read pass land on distinct bank slots.
+constexpr int kVqRow = 80;
+
+template <int D>
+struct MxvTiles {
+  static constexpr int VOFF = MxTiles<D>::KBYTES;
+  static constexpr int VBLK = D * kVqRow / 1024;   // 1 KB copy blocks of the V tile
+  static constexpr int STAGE = VOFF + VBLK * 1024;
+  static_assert(D * kVqRow % 1024 == 0, "the V tile is a whole number of copy blocks");
+};
+
 // Direct-to-LDS copies of one wave for one MX stage: blocks w, w + NW, ... of the code rows and
-// scale block (KBLK + 1 blocks) and of the V^T tile. Code and scale rows are padded to a
-// multiple of 64 rows in global memory, so no row is clamped.
-template <int D, int NW>
+// scale block (KBLK + 1 blocks) and of the V tile (the bf16 V^T tile, or with QV the quantised
+// V tile, which is contiguous in global memory). Code and scale rows are padded to a multiple
+// of 64 rows in global memory, so no row is clamped.
+template <int D, int NW, bool QV = false>
 struct MxStageCopier {
   using MT = MxTiles<D>;
   static constexpr int KB = MT::KBLK + 1;
+  static constexpr int VB = QV ? MxvTiles<D>::VBLK : MT::VBLK;
+  static constexpr int VO = QV ? MxvTiles<D>::VOFF : MT::KBYTES;
   static constexpr int KI = (KB + NW - 1) / NW;
-  static constexpr int VI = (MT::VBLK + NW - 1) / NW;
-  static constexpr int NBASE = KB / NW + MT::VBLK / NW;  // fewest copies of a wave per stage
+  static constexpr int VI = (VB + NW - 1) / NW;
+  static constexpr int NBASE = KB / NW + VB / NW;  // fewest copies of a wave per stage
   int wv;
   uint32_t koff[KI];   // byte offset within the tile's code rows, or within its scale bytes
   uint32_t voff[VI];
@@ -281,20 +300,25 @@ struct MxStageCopier {
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
       const int pos = (wv + i * NW) * 64 + lane;
-      int d = pos / LdsTiles<D>::VROW, c = pos % LdsTiles<D>::VROW;
-      if (c >= kBN / 8) c = 0;
-      if (d >= D) d = D - 1;
-      voff[i] = static_cast<uint32_t>(d) * Lp * 2 + c * 16;
+      if constexpr (QV) {
+        voff[i] = static_cast<uint32_t>(pos < VB * 64 ? pos : VB * 64 - 1) * 16;
+      } else {
+        int d = pos / LdsTiles<D>::VROW, c = pos % LdsTiles<D>::VROW;
+        if (c >= kBN / 8) c = 0;
+        if (d >= D) d = D - 1;
+        voff[i] = static_cast<uint32_t>(d) * Lp * 2 + c * 16;
+      }
     }
   }
 
   __device__ __forceinline__ int count() const {
-    return KB / NW + (wv < KB % NW) + MT::VBLK / NW + (wv < MT::VBLK % NW);
+    return KB / NW + (wv < KB % NW) + VB / NW + (wv < VB % NW);
   }
 
-  // codes/scales of keys kbase .. kbase+63 and V^T keys vbase .. vbase+63 into the stage at `lds`
+  // codes/scales of keys kbase .. kbase+63, and the V tile of those keys: V^T keys vbase ..
+  // vbase+63 of vsrc (bf16 V^T of this (b, h)), or with QV the tile that starts at vsrc
   __device__ __forceinline__ void issue(uint32_t lds, const uint8_t* Kc, const uint8_t* Ks,
-                                        int kbase, const bf16_t* Vtbh, int vbase) const {
+                                        int kbase, const void* vsrc, int vbase) const {
     const uint8_t* kc = Kc + static_cast<size_t>(kbase) * D;
     const uint8_t* ks = Ks + static_cast<size_t>(kbase) * MT::NB;
 #pragma unroll
@@ -304,11 +328,11 @@ struct MxStageCopier {
       if (blk < MT::KBLK) copy16_to_lds(kc, koff[i], lds + blk * 1024);
       else copy16_to_lds(ks, koff[i], lds + blk * 1024);
     }
-    const bf16_t* vb = Vtbh + vbase;
+    const void* vb = QV ? vsrc : static_cast<const void*>(static_cast<const bf16_t*>(vsrc) + vbase);
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
-      if (i * NW + NW > MT::VBLK && wv + i * NW >= MT::VBLK) break;
-      copy16_to_lds(vb, voff[i], lds + MT::KBYTES + (wv + i * NW) * 1024);
+      if (i * NW + NW > VB && wv + i * NW >= VB) break;
+      copy16_to_lds(vb, voff[i], lds + VO + (wv + i * NW) * 1024);
     }
   }
 };
@@ -380,28 +404,52 @@ __device__ __forceinline__ void score_tile_mx(const char* stage, const MxQFrag<D
   }
 }
 
-// Operand reads consumed up to and including MFMA i of an MFMA half-step: NPV P.V MFMAs, the
-// first NPRE of them on preloaded operands and the others one read each, then the score MFMAs,
-// SFIRST reads before the first of them and SREADS per MFMA.
-constexpr int half_step_reads(int i, int npv, int npre, int sfirst, int sreads) {
-  return i < npv ? (i - npre + 1 > 0 ? i - npre + 1 : 0)
-                 : (npv - npre) + sfirst + sreads * (i - npv + 1);
+// O^T[db] += V^T P^T for one 64-key tile on the block-scaled fp8 MFMA: A = the quantised V tile
+// (row d = 32 db + ql; lane group g reads bytes 16 g .. +15 and 32 + 16 g .. +15, and the scale
+// byte of block g of the row), B = P^T as e4m3 codes (pb bytes 0-15: values 0-15 of S^T block
+// 0, bytes 16-31: of block 1; those are the keys that the swapped positions of the V rows
+// hold), with unit scale. Three LDS reads per MFMA.
+template <int D, int VOFF>
+__device__ __forceinline__ void pv_mxv(const char* stage, const i32x8& pb,
+                                       f32x16 (&acc)[D / 32], int ql, int g) {
+  const char* vrow = stage + VOFF + ql * kVqRow;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const char* r = vrow + db * 32 * kVqRow;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(r + 16 * g);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(r + 32 + 16 * g);
+    const uint32_t sa = *reinterpret_cast<const uint32_t*>(r + 64) >> (8 * g);
+    const i32x8 a = i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]),
+                          static_cast<int>(lo[2]), static_cast<int>(lo[3]),
+                          static_cast<int>(hi[0]), static_cast<int>(hi[1]),
+                          static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+    acc[db] = mfma_mx<0>(a, pb, acc[db], sa, 127u);
+  }
+}
+
+// Operand reads consumed up to and including MFMA i of an MFMA half-step: NPV P.V MFMAs of PVR
+// reads each, the first NPRE reads of them preloaded, then the score MFMAs, SFIRST reads before
+// the first of them and SREADS per MFMA.
+constexpr int half_step_reads(int i, int npv, int npre, int sfirst, int sreads, int pvr = 1) {
+  return i < npv ? ((i + 1) * pvr - npre > 0 ? (i + 1) * pvr - npre : 0)
+                 : (npv * pvr - npre) + sfirst + sreads * (i - npv + 1);
 }
 
 // sched_group_barrier pattern that keeps the reads A ahead of the MFMAs that consume them: before
 // MFMA i, the reads of MFMAs up to i plus A more are issued (all NR at the end).
-template <int NM, int NR, int A, int NPV, int NPRE, int SFIRST, int SREADS, int I = 0>
+template <int NM, int NR, int A, int NPV, int NPRE, int SFIRST, int SREADS, int PVR = 1, int I = 0>
 __device__ __forceinline__ void sched_lead_reads() {
-  static_assert(half_step_reads(NM - 1, NPV, NPRE, SFIRST, SREADS) == NR,
+  static_assert(half_step_reads(NM - 1, NPV, NPRE, SFIRST, SREADS, PVR) == NR,
                 "the read count of the half-step does not match its MFMAs");
   if constexpr (I < NM) {
-    constexpr int want = half_step_reads(I, NPV, NPRE, SFIRST, SREADS) + A;
-    constexpr int prev_want = I == 0 ? 0 : half_step_reads(I - 1, NPV, NPRE, SFIRST, SREADS) + A;
+    constexpr int want = half_step_reads(I, NPV, NPRE, SFIRST, SREADS, PVR) + A;
+    constexpr int prev_want =
+        I == 0 ? 0 : half_step_reads(I - 1, NPV, NPRE, SFIRST, SREADS, PVR) + A;
     constexpr int cur = want < NR ? want : NR;
     constexpr int prev = prev_want < NR ? prev_want : NR;
     if constexpr (cur > prev) __builtin_amdgcn_sched_group_barrier(0x100, cur - prev, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    sched_lead_reads<NM, NR, A, NPV, NPRE, SFIRST, SREADS, I + 1>();
+    sched_lead_reads<NM, NR, A, NPV, NPRE, SFIRST, SREADS, PVR, I + 1>();
   }
 }
 

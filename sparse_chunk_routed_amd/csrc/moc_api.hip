@@ -37,6 +37,13 @@ hipError_t launch_attn_fwd_mx(const moc_layout* lay, const moc_varlen* vl, const
                               float* plse, void* vt_ws, hipStream_t st);
 hipError_t launch_mx_quantize(const moc_layout* lay, const void* X, uint8_t* codes,
                               uint8_t* scales, hipStream_t st);
+size_t mx_quantize_v_bytes(const moc_layout* lay);
+hipError_t launch_mx_quantize_v(const moc_layout* lay, const void* V, uint8_t* out,
+                                hipStream_t st);
+hipError_t launch_attn_fwd_mxv(const moc_layout* lay, const moc_varlen* vl, const uint8_t* Qc,
+                               const uint8_t* Qs, const uint8_t* Kc, const uint8_t* Ks,
+                               const uint8_t* Vq, float scale, void* O, float* lse, float* pO,
+                               float* plse, hipStream_t st);
 hipError_t launch_attn_bwd(const moc_layout* lay, const moc_varlen* vl, const void* Q,
                            const void* K, const void* V, const void* O, const float* lse,
                            const void* dO, float scale, void* dQ, void* dK, void* dV,
@@ -526,6 +533,71 @@ moc_status moc_attend_fwd_mx(const moc_layout* lay, const moc_varlen* vl, const 
                       "quantised-scores attention forward launch");
   } catch (...) {
     return fail(MOC_EINTERNAL, "exception in moc_attend_fwd_mx");
+  }
+}
+
+size_t moc_mx_quantize_v_bytes(const moc_layout* lay) {
+  try {
+    if (check_layout(lay) != MOC_OK) return 0;
+    if (lay->dtype != MOC_BF16) {
+      fail(MOC_EDTYPE, "MXFP8 quantisation takes bf16 input");
+      return 0;
+    }
+    return moc_host::mx_quantize_v_bytes(lay);
+  } catch (...) {
+    fail(MOC_EINTERNAL, "exception in moc_mx_quantize_v_bytes");
+    return 0;
+  }
+}
+
+moc_status moc_mx_quantize_v(const moc_layout* lay, const void* V, uint8_t* vq, void* stream) {
+  try {
+    moc_status s = check_layout(lay);
+    if (s != MOC_OK) return s;
+    if (lay->dtype != MOC_BF16) return fail(MOC_EDTYPE, "MXFP8 quantisation takes bf16 input");
+    if (!V || !vq) return fail(MOC_EINVAL, "NULL tensor argument");
+    if (static_cast<const void*>(vq) == V) return fail(MOC_EINVAL, "output aliases the input");
+    if ((s = run_layout_check(lay, stream)) != MOC_OK) return s;
+    return hip_status(moc_host::launch_mx_quantize_v(lay, V, vq, static_cast<hipStream_t>(stream)),
+                      "MXFP8 value quantisation launch");
+  } catch (...) {
+    return fail(MOC_EINTERNAL, "exception in moc_mx_quantize_v");
+  }
+}
+
+moc_status moc_attend_fwd_mxv(const moc_layout* lay, const moc_varlen* vl, const uint8_t* Qc,
+                              const uint8_t* Qs, const uint8_t* Kc, const uint8_t* Ks,
+                              const uint8_t* Vq, float softmax_scale, void* O, float* lse,
+                              void* ws, size_t ws_bytes, void* stream) {
+  try {
+    moc_status s = check_layout(lay);
+    if (s != MOC_OK) return s;
+    s = check_varlen(lay, vl);
+    if (s != MOC_OK) return s;
+    if (lay->dtype != MOC_BF16) return fail(MOC_EDTYPE, "quantised values need a bf16 layout");
+    if (!Qc || !Qs || !Kc || !Ks || !Vq || !O || !lse)
+      return fail(MOC_EINVAL, "NULL tensor argument");
+    const void* ins[] = {Qc, Qs, Kc, Ks, Vq};
+    for (const void* a : ins)
+      if (a == O || a == static_cast<const void*>(lse)) return fail(MOC_EINVAL, "outputs alias inputs");
+    if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+      return fail(MOC_EINVAL, "softmax_scale must be finite and > 0");
+    const size_t need = fwd_bytes(lay, vl->routed_cap);
+    if (!ws || ws_bytes < need)
+      return fail(MOC_EWORKSPACE, "FWD workspace needs %zu bytes (got %zu)", need,
+                  ws ? ws_bytes : size_t(0));
+    const int64_t rows = vl->routed_cap;
+    char* w = static_cast<char*>(ws);
+    float* pO = reinterpret_cast<float*>(w);
+    w += align_up(sizeof(float) * (rows > 0 ? rows : 1) * lay->d);
+    float* plse = reinterpret_cast<float*>(w);
+    if ((s = run_guards(lay, vl, stream)) != MOC_OK) return s;
+    return hip_status(moc_host::launch_attn_fwd_mxv(lay, vl, Qc, Qs, Kc, Ks, Vq, softmax_scale, O,
+                                                    lse, pO, plse,
+                                                    static_cast<hipStream_t>(stream)),
+                      "quantised-values attention forward launch");
+  } catch (...) {
+    return fail(MOC_EINTERNAL, "exception in moc_attend_fwd_mxv");
   }
 }
 

@@ -71,6 +71,73 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const bf16_t* __restrict_
   scales[row * NB + blk] = static_cast<uint8_t>(sc);
 }
 
+// Quantised values: V [B*H][L][D] bf16 -> tiles [B*H][Lp/64][D][80] bytes. Per 64-key tile and
+// dim d, the row holds the MXFP8 codes of V[key][d] for the tile's keys in two blocks of 32
+// (same rule as above, blocks along the keys, aligned to key 0), position p of a block holding
+// key p with bits 3 and 4 swapped (the order in which the attention's P^T operand holds its
+// keys), then the two E8M0 scale codes at bytes 64 and 65, zeros at 66-79. Keys >= L are zero.
+// One thread per (tile, d); a workgroup stages 256 / D tiles of V in LDS.
+constexpr int kVqRowBytes = 80;
+
+__device__ __forceinline__ int swap_bits34(int p) {
+  return (p & ~24) | ((p & 8) << 1) | ((p & 16) >> 1);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void mx_quant_v_kernel(const bf16_t* __restrict__ V, int L,
+                                                         int ntiles, uint8_t* __restrict__ out,
+                                                         const uint32_t* __restrict__ chk) {
+  constexpr int TPB = 256 / D;   // tiles per workgroup
+  constexpr int PITCH = D + 8;   // bf16 per staged key row
+  __shared__ __attribute__((aligned(16))) bf16_t tile[TPB * 64 * PITCH];
+  if (layout_rejected(chk)) return;
+  const int bh = blockIdx.y;
+  const int t0 = blockIdx.x * TPB;
+  for (int e = threadIdx.x; e < TPB * 64 * (D / 8); e += 256) {
+    const int r = e / (D / 8), c = e % (D / 8);   // r = staged key row over the TPB tiles
+    const int key = t0 * 64 + r;
+    mx_u32x4 v = {0u, 0u, 0u, 0u};
+    if (key < L)
+      v = *reinterpret_cast<const mx_u32x4*>(V + (static_cast<size_t>(bh) * L + key) * D + c * 8);
+    *reinterpret_cast<mx_u32x4*>(tile + r * PITCH + c * 8) = v;
+  }
+  __syncthreads();
+  const int tt = threadIdx.x / D, d = threadIdx.x % D;
+  const int ti = t0 + tt;
+  if (ti >= ntiles) return;
+  uint32_t w[20];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    float f[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+      f[k] = __uint_as_float(static_cast<uint32_t>(tile[(tt * 64 + 32 * b + k) * PITCH + d]) << 16);
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) amax = fmaxf(amax, fabsf(f[k]));
+    int E = static_cast<int>((__float_as_uint(amax) >> 23) & 0xff) - 127 - 8;
+    if (E < -127) E = -127;
+    const float inv = __uint_as_float(static_cast<uint32_t>(127 - E) << 23);  // 2^-E
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[e] = fminf(fmaxf(f[swap_bits34(4 * q + e)] * inv, -448.f), 448.f);
+      int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], pk, true);
+      w[8 * b + q] = static_cast<uint32_t>(pk);
+    }
+    if (b == 0) w[16] = static_cast<uint32_t>(E + 127);
+    else w[16] |= static_cast<uint32_t>(E + 127) << 8;
+  }
+  w[17] = w[18] = w[19] = 0u;
+  mx_u32x4* dst = reinterpret_cast<mx_u32x4*>(
+      out + ((static_cast<size_t>(bh) * ntiles + ti) * D + d) * kVqRowBytes);
+#pragma unroll
+  for (int c = 0; c < 5; ++c) dst[c] = mx_u32x4{w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]};
+}
+
 }  // namespace moc
 
 namespace moc_host {
@@ -89,6 +156,25 @@ hipError_t launch_mx_quantize(const moc_layout* lay, const void* X, uint8_t* cod
   else
     hipLaunchKernelGGL((moc::mx_quant_kernel<64>), dim3(static_cast<unsigned>(grid)), dim3(256),
                        0, st, x, lay->L, Lp, nblk, codes, scales, lay->check);
+  return hipGetLastError();
+}
+
+size_t mx_quantize_v_bytes(const moc_layout* lay) {
+  const int Lp = attn_vt_rows(lay->L);
+  return static_cast<size_t>(lay->B) * lay->H * (Lp / 64) * lay->d * moc::kVqRowBytes;
+}
+
+hipError_t launch_mx_quantize_v(const moc_layout* lay, const void* V, uint8_t* out,
+                                hipStream_t st) {
+  const int ntiles = attn_vt_rows(lay->L) / 64;
+  const int BH = lay->B * lay->H;
+  const moc::bf16_t* v = static_cast<const moc::bf16_t*>(V);
+  if (lay->d == 128)
+    hipLaunchKernelGGL((moc::mx_quant_v_kernel<128>), dim3((ntiles + 1) / 2, BH), dim3(256), 0,
+                       st, v, lay->L, ntiles, out, lay->check);
+  else
+    hipLaunchKernelGGL((moc::mx_quant_v_kernel<64>), dim3((ntiles + 3) / 4, BH), dim3(256), 0,
+                       st, v, lay->L, ntiles, out, lay->check);
   return hipGetLastError();
 }
 
