@@ -135,7 +135,10 @@ typedef struct {
  *   rtiles:     [max_rtiles][2] routed work tiles (bucket id, first position in the bucket),
  *               n_rtiles[0] of them valid; each tile covers up to tile_rows queries.
  *   atiles:     [max_atiles][6] anchor work tiles (q0, q1, key range 1 [a0,a1), key range 2
- *               [b0,b1)), n_atiles[0] valid, shared by every (b, h).
+ *               [b0,b1)), n_atiles[0] valid, shared by every (b, h). n_atiles[1..9] split the
+ *               B*H*n_atiles[0] anchor items (b, h, tile) into 8 contiguous ranges of about
+ *               equal cost (a tile costs its 64-key tiles plus 4), one per XCD: range x is
+ *               [n_atiles[1+x], n_atiles[2+x]), at most ceil(1.25 B*H*max_atiles / 8) items.
  *   ktiles:     [max_ktiles][6] key tiles of the backward (k0, k1, chunk or -1 for text,
  *               anchor query range q0, q1, text split index), n_ktiles[0] valid, shared by every
  *               (b, h). A key tile never straddles a chunk; text keys, which every query

@@ -328,10 +328,12 @@ __device__ __forceinline__ void attn_fwd_lds_body(
 
   int bh, q_lo, nq, r1a, r1b, r2a, r2b, bstart = 0;
   if constexpr (MODE == MODE_ANCHOR) {
+    // the items of this XCD's range (about an eighth of the total cost; n_tiles[1 + x] is the
+    // range start, stored by the index inversion), one per workgroup slot of the XCD
     const int nt = n_tiles[0];
-    const int nwork = nt * p.B * p.H;
-    if (static_cast<int>(blockIdx.x) >= nwork) return;
-    const int lid = xcd_remap(blockIdx.x, nwork);
+    const int x = static_cast<int>(blockIdx.x) % kXcds;
+    const int lid = n_tiles[1 + x] + static_cast<int>(blockIdx.x) / kXcds;
+    if (lid >= n_tiles[2 + x]) return;
     bh = lid / nt;
     const int32_t* a = tiles + 6 * (lid % nt);
     q_lo = a[0];
@@ -789,7 +791,7 @@ static hipError_t launch_fwd_bf16(const moc_layout* lay, const moc_varlen* vl, c
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   p.max_tiles = vl->max_atiles;
-  const int grid = vl->max_atiles * lay->B * lay->H;
+  const int grid = moc::kXcds * moc::anchor_xcd_slots(vl->max_atiles, lay->B * lay->H);
   if (mx)
     hipLaunchKernelGGL((moc::attn_fwd_bf16_kernel<D, moc::MODE_ANCHOR, true>), dim3(grid),
                        dim3(moc::kNT), 0, st, Q, K, Qs, Ks, Vt, Lp, lay->chunk_offsets, p,
@@ -838,7 +840,8 @@ static hipError_t launch_fwd_mxv_d(const moc_layout* lay, const moc_varlen* vl, 
   }
   p.max_tiles = vl->max_atiles;
   hipLaunchKernelGGL((moc::attn_fwd_mxv_kernel<D, moc::MODE_ANCHOR>),
-                     dim3(vl->max_atiles * lay->B * lay->H), dim3(moc::kNT), 0, st, Qc, Kc, Qs,
+                     dim3(moc::kXcds * moc::anchor_xcd_slots(vl->max_atiles, lay->B * lay->H)),
+                     dim3(moc::kNT), 0, st, Qc, Kc, Qs,
                      Ks, Vq, Lp, lay->chunk_offsets, p, vl->atiles, vl->n_atiles,
                      vl->bucket_off, vl->bucket_q, vl->slot, pO, plse,
                      static_cast<bf16_t*>(O), lse);

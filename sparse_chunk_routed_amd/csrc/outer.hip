@@ -6,7 +6,7 @@
 // other segment, and the ordinary chunk router then only looks inside the few best segments
 // (the mandatory context stays attached).
 //
-// Segments are given groups of whole chunks (seg_chunk[nseg+1]); a query's block is its own
+// Segments are given as groups of whole chunks (seg_chunk[nseg+1]); a query's block is its own
 // segment. The pass, without host synchronisation:
 //   (a) segment token offsets and kinds (text / video) from the layout;
 //   (b) qseg / kseg: the segment means of Q and of K: the chunk pooling kernel's double-double

@@ -191,6 +191,7 @@ __global__ __launch_bounds__(1024) void inv_global_kernel(
   __shared__ int32_t k_base[MOC_MAX_C];  // first backward key tile of each chunk
   // anchor groups: the text, then every run of chunks with one shot id
   __shared__ int32_t g_q0[MOC_MAX_C + 1], g_q1[MOC_MAX_C + 1], g_base[MOC_MAX_C + 1];
+  __shared__ long long g_cost[MOC_MAX_C + 2];  // exclusive prefix of the groups' tile costs
   if (layout_rejected(p.chk)) return;
   for (int i = threadIdx.x; i <= p.C; i += blockDim.x) off[i] = off_g[i];
   for (int i = threadIdx.x; i < p.C; i += blockDim.x) shot[i] = shot_g[i];
@@ -268,6 +269,63 @@ __global__ __launch_bounds__(1024) void inv_global_kernel(
       [&](int g, Sum2 v) { g_base[g] = static_cast<int32_t>(v.a); }, wsum);
   if (threadIdx.x == 0) n_atiles[0] = static_cast<int32_t>(an.a);
   const long long anchor_pairs = an.b;
+
+  // The anchor items (b, h, tile) in kXcds contiguous ranges of about equal cost, a tile
+  // costing its 64-key tiles (text range, then own shot) plus kAnchorTileFixed; range x starts
+  // at the first item whose cost prefix reaches x / kXcds of the total, kept within the
+  // anchor_xcd_slots workgroups of an XCD. Stored at n_atiles[1 + x], x = 0..kXcds.
+  auto ktiles64 = [](int a, int b) { return b > a ? ((b - 1) >> 6) - (a >> 6) + 1 : 0; };
+  const Sum2 gc = block_scan2(
+      ng,
+      [&](int g) -> Sum2 {
+        const long long n = (g_q1[g] - g_q0[g] + BM - 1) / BM;
+        const bool text = has_text && g == 0;
+        const long long per = ktiles64(tb, te) + (text ? 0 : ktiles64(g_q0[g], g_q1[g])) +
+                              kAnchorTileFixed;
+        return Sum2{n * per, 0};
+      },
+      [&](int g, Sum2 v) { g_cost[g] = v.a; }, wsum);
+  __shared__ long long raw_lo[kXcds];
+  const int nt_all = static_cast<int>(an.a);
+  const long long Ch = gc.a;  // cost of one (b, h)
+  const long long nwork = static_cast<long long>(nt_all) * p.B * p.H;
+  if (threadIdx.x == 0) g_cost[ng] = Ch;
+  __syncthreads();
+  if (threadIdx.x >= 1 && threadIdx.x < kXcds) {
+    const int x = threadIdx.x;
+    long long lo = nwork;
+    if (Ch > 0) {
+      const long long target = Ch * p.B * p.H * x / kXcds;
+      const long long bh = target / Ch, r = target - bh * Ch;
+      int a = 0, b = ng - 1;  // last group whose cost prefix is at most r (g_cost[0] = 0)
+      while (a < b) {
+        const int m = (a + b + 1) >> 1;
+        if (g_cost[m] <= r) a = m;
+        else b = m - 1;
+      }
+      const int nt_g = (g_q1[a] - g_q0[a] + BM - 1) / BM;
+      const long long per = (g_cost[a + 1] - g_cost[a]) / nt_g;
+      lo = bh * nt_all + g_base[a] + (r - g_cost[a] + per - 1) / per;
+    }
+    raw_lo[x] = lo;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const long long slots = anchor_xcd_slots(p.max_atiles, p.B * p.H);
+    long long prev = 0;
+    n_atiles[1] = 0;
+    for (int x = 1; x < kXcds; ++x) {
+      long long lo = raw_lo[x];
+      const long long lo_min = nwork - (kXcds - x) * slots;
+      if (lo < prev) lo = prev;
+      if (lo < lo_min) lo = lo_min;
+      if (lo > prev + slots) lo = prev + slots;
+      if (lo > nwork) lo = nwork;
+      n_atiles[1 + x] = static_cast<int32_t>(lo);
+      prev = lo;
+    }
+    n_atiles[1 + kXcds] = static_cast<int32_t>(nwork);
+  }
 
   // routed tiles: (bucket, first position)
   emit_segments(

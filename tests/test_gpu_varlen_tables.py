@@ -39,6 +39,7 @@ def _gpu_tables(w: mi.Workload):
     n_r, n_a = vl.n_rtiles(), vl.n_atiles()
     n_k = int(vl._view(s.n_ktiles, 1).item())
     return dict(
+        xcd_lo=vl._view(s.n_atiles, 10).cpu().numpy()[1:].astype(np.int64),
         sel=sel.cpu().numpy(), nsel=nsel.cpu().numpy(), BM=int(s.tile_rows),
         n_split=int(s.n_text_split), bucket_off=vl.bucket_off().cpu().numpy(),
         rtiles=vl._view(s.rtiles, 2 * n_r).cpu().numpy().reshape(-1, 2),
@@ -104,6 +105,28 @@ def _expected(w: mi.Workload, g, KR: int):
         np.array(atiles, np.int64).reshape(-1, 6), np.array(ktiles, np.int64).reshape(-1, 6)
 
 
+def _xcd_ranges(atiles: np.ndarray, B: int, H: int, max_atiles: int) -> np.ndarray:
+    """The 9 starts of the 8 anchor ranges, from their definition: item (b, h, tile) costs the
+    tile's 64-key tiles (over its text range and its own-shot range) plus 4; range x starts at
+    the first item whose cost prefix reaches x / 8 of the total, then kept monotone and within
+    ceil(1.25 B H max_atiles / 8) items per range (and so that the later ranges can hold the
+    rest)."""
+    def k64(a, b):
+        return ((b - 1) >> 6) - (a >> 6) + 1 if b > a else 0
+    cost = np.array([k64(t[2], t[3]) + k64(t[4], t[5]) + 4 for t in atiles], np.int64)
+    items = np.tile(cost, B * H)
+    n = len(items)
+    pref = np.concatenate([[0], np.cumsum(items)])
+    slots = (B * H * max_atiles * 5 // 4 + 7) // 8
+    lo = [0]
+    for x in range(1, 8):
+        v = int(np.searchsorted(pref, pref[-1] * x // 8, side="left")) if n else 0
+        v = min(max(v, lo[-1], n - (8 - x) * slots), lo[-1] + slots, n)
+        lo.append(v)
+    lo.append(n)
+    return np.array(lo, np.int64)
+
+
 def _check(w: mi.Workload):
     g = _gpu_tables(w)
     kt = g["ktiles"]
@@ -120,6 +143,9 @@ def _check(w: mi.Workload):
     assert np.array_equal(g["ktiles"], kt_exp)
     assert len(rt) <= g["max"][0] and len(at) <= g["max"][1] and len(kt_exp) <= g["max"][2]
     assert np.array_equal(g["pairs"], mo.pair_counts(w.layout, g["sel"]))
+    xr = _xcd_ranges(at, w.B, w.H, g["max"][1])
+    assert np.array_equal(g["xcd_lo"], xr), (g["xcd_lo"], xr)
+    _say(f"anchor items per XCD range: {np.diff(xr).tolist()}")
 
 
 @pytest.mark.parametrize("seed", range(6))
