@@ -108,14 +108,15 @@ __global__ __launch_bounds__(kBwdQNT) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) char st2[KI::BYTES];
   if (layout_rejected(p.chk)) return;
 
-  // upper-bound grid: blocks past the device-side work count exit; the rest are remapped so
-  // each XCD takes a contiguous range of the real work items
+  // upper-bound grid: blocks past the device-side work count exit; the rest take contiguous
+  // ranges of the real work items per XCD (anchor items: the cost-balanced ranges that the
+  // index inversion stores after the anchor tile count)
   int bh, q_lo, nq, r1a, r1b, r2a, r2b, bstart = 0;
   if constexpr (MODE == BMODE_ANCHOR) {
     const int nt = n_tiles[0];
-    const int nwork = nt * p.B * p.H;
-    if (static_cast<int>(blockIdx.x) >= nwork) return;
-    const int lid = xcd_remap(blockIdx.x, nwork);
+    const int x = static_cast<int>(blockIdx.x) % kXcds;
+    const int lid = n_tiles[1 + x] + static_cast<int>(blockIdx.x) / kXcds;
+    if (lid >= n_tiles[2 + x]) return;
     bh = lid / nt;
     const int32_t* a = tiles + 6 * (lid % nt);
     q_lo = a[0]; nq = a[1] - a[0];
@@ -358,18 +359,20 @@ __global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_kernel(
     const bf16_t* __restrict__ K, const bf16_t* __restrict__ V, BwdParams p,
     const int32_t* __restrict__ ktiles, const int32_t* __restrict__ n_ktiles,
     const char* __restrict__ qblocks, const char* __restrict__ gblocks,
-    const int32_t* __restrict__ gstart, float* __restrict__ textK, float* __restrict__ textV,
-    bf16_t* __restrict__ dK, bf16_t* __restrict__ dV) {
+    const int32_t* __restrict__ gstart, const int32_t* __restrict__ kranges,
+    float* __restrict__ textK, float* __restrict__ textV, bf16_t* __restrict__ dK,
+    bf16_t* __restrict__ dV) {
   using QTl = QTiles<D>;
   using CP = QTileCopier<D, kBwdKNW>;
   __shared__ __attribute__((aligned(1024))) char st0[QTl::BYTES];
   __shared__ __attribute__((aligned(1024))) char st1[QTl::BYTES];
   if (layout_rejected(p.chk)) return;
 
+  // this XCD's range of (b, h, key tile) items (bwd_key_split_kernel), one per workgroup slot
   const int nt = n_ktiles[0];
-  const int nwork = nt * p.B * p.H;
-  if (static_cast<int>(blockIdx.x) >= nwork) return;
-  const int lid = xcd_remap(blockIdx.x, nwork);
+  const int xr = static_cast<int>(blockIdx.x) % kXcds;
+  const int lid = kranges[xr] + static_cast<int>(blockIdx.x) / kXcds;
+  if (lid >= kranges[xr + 1]) return;
   const int bh = lid / nt;
   const int32_t* kt6 = ktiles + 6 * (lid % nt);
   const int k0 = kt6[0], k1 = kt6[1], c = kt6[2], qa = kt6[3], qb = kt6[4], sp = kt6[5];
@@ -658,6 +661,82 @@ __global__ __launch_bounds__(1024) void bwd_gather_scan_kernel(const int32_t* __
   if (threadIdx.x == 1023) gstart[NB] = part[1023];
 }
 
+// The key-centric kernel's (b, h, key tile) items in kXcds contiguous ranges of about equal
+// cost: an item costs its 32-query blocks (the anchor query range's, plus the gathered blocks
+// of its chunk's bucket, known once gstart is) and kKeyTileFixed. Range x starts at the first
+// item whose cost prefix reaches x / kXcds of the total, kept within xcd_slots(max_ktiles, BH)
+// items. One workgroup of 1024: per-thread sums over contiguous items, a block scan, then the
+// thread whose items hold a range start finds it. out[x], x = 0..kXcds.
+__global__ __launch_bounds__(1024) void bwd_key_split_kernel(
+    const int32_t* __restrict__ ktiles, const int32_t* __restrict__ n_ktiles,
+    const int32_t* __restrict__ gstart, int C, int BH, int max_ktiles,
+    int32_t* __restrict__ out, const uint32_t* __restrict__ chk) {
+  __shared__ long long part[1024];
+  __shared__ long long raw[kXcds];
+  if (layout_rejected(chk)) return;
+  const int nkt = n_ktiles[0];
+  const long long nwork = static_cast<long long>(nkt) * BH;
+  auto cost = [&](long long lid) -> long long {
+    const int bh = static_cast<int>(lid / nkt);
+    const int32_t* kt = ktiles + 6 * (lid % nkt);
+    const int c = kt[2], qa = kt[3], qb = kt[4];
+    long long n = qb > qa ? ((qb - 1) >> 5) - (qa >> 5) + 1 : 0;
+    if (c >= 0) {
+      const int b = bh * C + c;
+      n += (gstart[b + 1] - gstart[b]) >> 5;
+    }
+    return n + kKeyTileFixed;
+  };
+  const long long per = (nwork + 1023) / 1024;
+  const long long a = threadIdx.x * per;
+  const long long e = a + per < nwork ? a + per : nwork;
+  long long sum = 0;
+  for (long long i = a; i < e; ++i) sum += cost(i);
+  part[threadIdx.x] = sum;
+  if (threadIdx.x < kXcds) raw[threadIdx.x] = nwork;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const long long v = static_cast<int>(threadIdx.x) >= o ? part[threadIdx.x - o] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  const long long total = part[1023];
+  const long long incl = part[threadIdx.x], excl = incl - sum;
+  for (int x = 1; x < kXcds; ++x) {
+    const long long target = total * x / kXcds;
+    if (target <= 0) {
+      if (threadIdx.x == 0) raw[x] = 0;
+    } else if (excl < target && target <= incl) {
+      long long run = excl;
+      for (long long i = a; i < e; ++i) {
+        run += cost(i);
+        if (run >= target) {
+          raw[x] = i + 1;
+          break;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const long long slots = xcd_slots(max_ktiles, BH);
+    long long prev = 0;
+    out[0] = 0;
+    for (int x = 1; x < kXcds; ++x) {
+      long long lo = raw[x];
+      const long long lo_min = nwork - (kXcds - x) * slots;
+      if (lo < prev) lo = prev;
+      if (lo < lo_min) lo = lo_min;
+      if (lo > prev + slots) lo = prev + slots;
+      if (lo > nwork) lo = nwork;
+      out[x] = static_cast<int32_t>(lo);
+      prev = lo;
+    }
+    out[kXcds] = static_cast<int32_t>(nwork);
+  }
+}
+
 // Query tile images (QTiles layout) for the key-centric kernel: 32 queries' Q and dO rows, their
 // transposes and lse2, D, padded exactly as the kernel stages them. tok[r] is the query of row
 // r, or -1 for a pad (zero rows, lse2 = +inf so that P = 0, D = 0); padding bytes are zero.
@@ -854,7 +933,7 @@ BwdSizes bwd_sizes(const moc_layout* lay, size_t sel) {
   const size_t gtile = lay->d == 128 ? moc::QTiles<128>::BYTES : moc::QTiles<64>::BYTES;
   z.qb = al(static_cast<size_t>(lay->B) * lay->H * (kt_rows(lay->L) / 32) * gtile);
   z.gb = al(gather_rows(lay, sel) / 32 * gtile);
-  z.gstart = al((nb + 1) * sizeof(int32_t));
+  z.gstart = al((nb + 1 + 16) * sizeof(int32_t));  // + the key-tile ranges per XCD
   return z;
 }
 }  // namespace
@@ -881,6 +960,7 @@ static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   char* gblocks = w; w += z.gb;
   int32_t* gstart = reinterpret_cast<int32_t*>(w); w += z.gstart;
   const int Lp = kt_rows(lay->L);
+  int32_t* kranges = gstart + static_cast<size_t>(lay->B) * lay->H * lay->C + 1;
 
   const bf16_t* q = static_cast<const bf16_t*>(Q);
   const bf16_t* k = static_cast<const bf16_t*>(K);
@@ -911,6 +991,9 @@ static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   hipLaunchKernelGGL(moc::bwd_gather_scan_kernel, dim3(1), dim3(1024), 0, st, vl->bucket_off, NB,
                      gstart, vl->status);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(moc::bwd_key_split_kernel, dim3(1), dim3(1024), 0, st, vl->ktiles,
+                     vl->n_ktiles, gstart, lay->C, BH, vl->max_ktiles, kranges, vl->status);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((moc::bwd_qblock_kernel<D, moc::QB_SEQ>),
                      dim3((Lp + moc::kBwdQBM - 1) / moc::kBwdQBM, BH), dim3(256), 0, st, q, g, Dq,
                      l2, p, vl->rtiles, vl->n_rtiles, vl->bucket_off, vl->bucket_q, gstart,
@@ -932,14 +1015,16 @@ static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, cons
   }
   p.max_tiles = vl->max_atiles;
   hipLaunchKernelGGL((moc::bwd_dq_kernel<D, moc::BMODE_ANCHOR>),
-                     dim3(vl->max_atiles * lay->B * lay->H), dim3(moc::kBwdQNT), 0, st, q, kvimg,
+                     dim3(moc::kXcds * moc::xcd_slots(vl->max_atiles, lay->B * lay->H)),
+                     dim3(moc::kBwdQNT), 0, st, q, kvimg,
                      g, Dq, l2, lay->chunk_offsets, p, vl->atiles, vl->n_atiles,
                      vl->bucket_off, vl->bucket_q, vl->slot, dqp, static_cast<bf16_t*>(dQ));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   p.max_tiles = vl->max_ktiles;
-  hipLaunchKernelGGL((moc::bwd_dkdv_kernel<D>), dim3(vl->max_ktiles * lay->B * lay->H),
+  hipLaunchKernelGGL((moc::bwd_dkdv_kernel<D>),
+                     dim3(moc::kXcds * moc::xcd_slots(vl->max_ktiles, lay->B * lay->H)),
                      dim3(moc::kBwdKNT), 0, st, k, v, p, vl->ktiles, vl->n_ktiles, qblocks,
-                     gblocks, gstart, textK, textV, static_cast<bf16_t*>(dK),
+                     gblocks, gstart, kranges, textK, textV, static_cast<bf16_t*>(dK),
                      static_cast<bf16_t*>(dV));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.text_len > 0) {

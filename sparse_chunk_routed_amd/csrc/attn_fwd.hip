@@ -791,7 +791,7 @@ static hipError_t launch_fwd_bf16(const moc_layout* lay, const moc_varlen* vl, c
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   p.max_tiles = vl->max_atiles;
-  const int grid = moc::kXcds * moc::anchor_xcd_slots(vl->max_atiles, lay->B * lay->H);
+  const int grid = moc::kXcds * moc::xcd_slots(vl->max_atiles, lay->B * lay->H);
   if (mx)
     hipLaunchKernelGGL((moc::attn_fwd_bf16_kernel<D, moc::MODE_ANCHOR, true>), dim3(grid),
                        dim3(moc::kNT), 0, st, Q, K, Qs, Ks, Vt, Lp, lay->chunk_offsets, p,
@@ -840,7 +840,7 @@ static hipError_t launch_fwd_mxv_d(const moc_layout* lay, const moc_varlen* vl, 
   }
   p.max_tiles = vl->max_atiles;
   hipLaunchKernelGGL((moc::attn_fwd_mxv_kernel<D, moc::MODE_ANCHOR>),
-                     dim3(moc::kXcds * moc::anchor_xcd_slots(vl->max_atiles, lay->B * lay->H)),
+                     dim3(moc::kXcds * moc::xcd_slots(vl->max_atiles, lay->B * lay->H)),
                      dim3(moc::kNT), 0, st, Qc, Kc, Qs,
                      Ks, Vq, Lp, lay->chunk_offsets, p, vl->atiles, vl->n_atiles,
                      vl->bucket_off, vl->bucket_q, vl->slot, pO, plse,

@@ -55,16 +55,19 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
 
 __device__ __forceinline__ int popc(uint32_t x) { return __builtin_popcount(x); }
 
-// Anchor attention work split over the XCDs: the (b, h, anchor tile) items are cut into kXcds
-// contiguous ranges of about equal cost (the index inversion stores the range starts after
-// the anchor tile count), and each XCD runs its range with this many workgroup slots: a
-// quarter more than an equal split by count, so that ranges of cheaper tiles still fit.
-__host__ __device__ inline int anchor_xcd_slots(int max_atiles, int BH) {
-  const long long n = static_cast<long long>(max_atiles) * BH;
+// Work split over the XCDs: the (b, h, tile) items of the anchor attention kernels and of the
+// key-centric backward are cut into kXcds contiguous ranges of about equal cost (range starts
+// computed on the device before the launch), and each XCD runs its range with this many
+// workgroup slots: a quarter more than an equal split by count, so that ranges of cheaper
+// items still fit. max_tiles bounds the tiles of one (b, h).
+__host__ __device__ inline int xcd_slots(int max_tiles, int BH) {
+  const long long n = static_cast<long long>(max_tiles) * BH;
   return static_cast<int>((n * 5 / 4 + kXcds - 1) / kXcds);
 }
 // cost of one anchor tile: its 64-key tiles plus a fixed start-up and epilogue share
 constexpr int kAnchorTileFixed = 4;
+// cost of one backward key tile: its 32-query blocks plus a fixed start-up and epilogue share
+constexpr int kKeyTileFixed = 2;
 
 // The layout check word of the call (moc_layout.check, NULL when the check is off): a kernel
 // whose call's layout failed the device check returns at its start, before reading anything the

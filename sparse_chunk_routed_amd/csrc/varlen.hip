@@ -273,7 +273,7 @@ __global__ __launch_bounds__(1024) void inv_global_kernel(
   // The anchor items (b, h, tile) in kXcds contiguous ranges of about equal cost, a tile
   // costing its 64-key tiles (text range, then own shot) plus kAnchorTileFixed; range x starts
   // at the first item whose cost prefix reaches x / kXcds of the total, kept within the
-  // anchor_xcd_slots workgroups of an XCD. Stored at n_atiles[1 + x], x = 0..kXcds.
+  // xcd_slots workgroups of an XCD. Stored at n_atiles[1 + x], x = 0..kXcds.
   auto ktiles64 = [](int a, int b) { return b > a ? ((b - 1) >> 6) - (a >> 6) + 1 : 0; };
   const Sum2 gc = block_scan2(
       ng,
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(1024) void inv_global_kernel(
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    const long long slots = anchor_xcd_slots(p.max_atiles, p.B * p.H);
+    const long long slots = xcd_slots(p.max_atiles, p.B * p.H);
     long long prev = 0;
     n_atiles[1] = 0;
     for (int x = 1; x < kXcds; ++x) {
