@@ -96,9 +96,9 @@ __global__ __launch_bounds__(kBwdQNT) void bwd_dq_kernel(
     const bf16_t* __restrict__ Q, const char* __restrict__ kvimg, const bf16_t* __restrict__ dO,
     const float* __restrict__ Dq, const float* __restrict__ lse2,
     const int32_t* __restrict__ off, BwdParams p, const int32_t* __restrict__ tiles,
-    const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ bucket_off,
-    const int32_t* __restrict__ bucket_q, const int32_t* __restrict__ slot,
-    float* __restrict__ dQp, bf16_t* __restrict__ dQ) {
+    const int32_t* __restrict__ n_tiles, int32_t* __restrict__ ctr,
+    const int32_t* __restrict__ bucket_off, const int32_t* __restrict__ bucket_q,
+    const int32_t* __restrict__ slot, float* __restrict__ dQp, bf16_t* __restrict__ dQ) {
   static_assert(kBwdQNW == 8, "two groups of four waves");
   using LT = LdsTiles<D>;
   using KI = KvImage<D>;
@@ -108,15 +108,18 @@ __global__ __launch_bounds__(kBwdQNT) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) char st2[KI::BYTES];
   if (layout_rejected(p.chk)) return;
 
-  // upper-bound grid: blocks past the device-side work count exit; the rest take contiguous
-  // ranges of the real work items per XCD (anchor items: the cost-balanced ranges that the
-  // index inversion stores after the anchor tile count)
+  // upper-bound grid: blocks past the device-side work count exit; the rest take the real work
+  // items per XCD (anchor items: claimed from the cost-balanced ranges that the index inversion
+  // stores after the anchor tile count, from other XCDs' ranges once this XCD's is used up)
   int bh, q_lo, nq, r1a, r1b, r2a, r2b, bstart = 0;
   if constexpr (MODE == BMODE_ANCHOR) {
+    __shared__ int s_item;
+    if (threadIdx.x == 0)
+      s_item = claim_item(n_tiles + 1, ctr, static_cast<int>(blockIdx.x) % kXcds);
+    __syncthreads();
+    const int lid = s_item;
+    if (lid < 0) return;
     const int nt = n_tiles[0];
-    const int x = static_cast<int>(blockIdx.x) % kXcds;
-    const int lid = n_tiles[1 + x] + static_cast<int>(blockIdx.x) / kXcds;
-    if (lid >= n_tiles[2 + x]) return;
     bh = lid / nt;
     const int32_t* a = tiles + 6 * (lid % nt);
     q_lo = a[0]; nq = a[1] - a[0];
@@ -360,19 +363,23 @@ __global__ __launch_bounds__(kBwdKNT, 2) void bwd_dkdv_kernel(
     const int32_t* __restrict__ ktiles, const int32_t* __restrict__ n_ktiles,
     const char* __restrict__ qblocks, const char* __restrict__ gblocks,
     const int32_t* __restrict__ gstart, const int32_t* __restrict__ kranges,
-    float* __restrict__ textK, float* __restrict__ textV, bf16_t* __restrict__ dK,
-    bf16_t* __restrict__ dV) {
+    int32_t* __restrict__ ctr, float* __restrict__ textK, float* __restrict__ textV,
+    bf16_t* __restrict__ dK, bf16_t* __restrict__ dV) {
   using QTl = QTiles<D>;
   using CP = QTileCopier<D, kBwdKNW>;
   __shared__ __attribute__((aligned(1024))) char st0[QTl::BYTES];
   __shared__ __attribute__((aligned(1024))) char st1[QTl::BYTES];
   if (layout_rejected(p.chk)) return;
 
-  // this XCD's range of (b, h, key tile) items (bwd_key_split_kernel), one per workgroup slot
+  // an item of this XCD's range of (b, h, key tile) items (bwd_key_split_kernel), or of another
+  // XCD's once this one's is used up; one item per workgroup
+  __shared__ int s_item;
+  if (threadIdx.x == 0)
+    s_item = claim_item(kranges, ctr, static_cast<int>(blockIdx.x) % kXcds);
+  __syncthreads();
+  const int lid = s_item;
+  if (lid < 0) return;
   const int nt = n_ktiles[0];
-  const int xr = static_cast<int>(blockIdx.x) % kXcds;
-  const int lid = kranges[xr] + static_cast<int>(blockIdx.x) / kXcds;
-  if (lid >= kranges[xr + 1]) return;
   const int bh = lid / nt;
   const int32_t* kt6 = ktiles + 6 * (lid % nt);
   const int k0 = kt6[0], k1 = kt6[1], c = kt6[2], qa = kt6[3], qb = kt6[4], sp = kt6[5];
@@ -1009,8 +1016,8 @@ static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, cons
     p.max_tiles = vl->max_rtiles;
     hipLaunchKernelGGL((moc::bwd_dq_kernel<D, moc::BMODE_ROUTED>), dim3(vl->max_rtiles),
                        dim3(moc::kBwdQNT), 0, st, q, kvimg, g, Dq, l2, lay->chunk_offsets,
-                       p, vl->rtiles, vl->n_rtiles, vl->bucket_off, vl->bucket_q, vl->slot, dqp,
-                       static_cast<bf16_t*>(dQ));
+                       p, vl->rtiles, vl->n_rtiles, nullptr, vl->bucket_off, vl->bucket_q,
+                       vl->slot, dqp, static_cast<bf16_t*>(dQ));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   p.max_tiles = vl->max_atiles;
@@ -1018,14 +1025,15 @@ static hipError_t launch_bwd_t(const moc_layout* lay, const moc_varlen* vl, cons
                      dim3(moc::kXcds * moc::xcd_slots(vl->max_atiles, lay->B * lay->H)),
                      dim3(moc::kBwdQNT), 0, st, q, kvimg,
                      g, Dq, l2, lay->chunk_offsets, p, vl->atiles, vl->n_atiles,
-                     vl->bucket_off, vl->bucket_q, vl->slot, dqp, static_cast<bf16_t*>(dQ));
+                     vl->n_atiles + moc::kCtrDq, vl->bucket_off, vl->bucket_q, vl->slot, dqp,
+                     static_cast<bf16_t*>(dQ));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   p.max_tiles = vl->max_ktiles;
   hipLaunchKernelGGL((moc::bwd_dkdv_kernel<D>),
                      dim3(moc::kXcds * moc::xcd_slots(vl->max_ktiles, lay->B * lay->H)),
                      dim3(moc::kBwdKNT), 0, st, k, v, p, vl->ktiles, vl->n_ktiles, qblocks,
-                     gblocks, gstart, kranges, textK, textV, static_cast<bf16_t*>(dK),
-                     static_cast<bf16_t*>(dV));
+                     gblocks, gstart, kranges, vl->n_atiles + moc::kCtrDkdv, textK, textV,
+                     static_cast<bf16_t*>(dK), static_cast<bf16_t*>(dV));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.text_len > 0) {
     const int64_t n = static_cast<int64_t>(lay->B) * lay->H * p.text_len * D;

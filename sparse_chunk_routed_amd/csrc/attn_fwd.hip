@@ -306,10 +306,10 @@ __device__ __forceinline__ void attn_fwd_lds_body(
     const void* __restrict__ Qv, const void* __restrict__ Kv, const uint8_t* __restrict__ Qs,
     const uint8_t* __restrict__ Ks, const void* __restrict__ Vt, int Lp,
     const int32_t* __restrict__ off, AttnParams p, const int32_t* __restrict__ tiles,
-    const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ bucket_off,
-    const int32_t* __restrict__ bucket_q, const int32_t* __restrict__ slot,
-    float* __restrict__ pO, float* __restrict__ plse, bf16_t* __restrict__ O,
-    float* __restrict__ lse) {
+    const int32_t* __restrict__ n_tiles, int32_t* __restrict__ ctr,
+    const int32_t* __restrict__ bucket_off, const int32_t* __restrict__ bucket_q,
+    const int32_t* __restrict__ slot, float* __restrict__ pO, float* __restrict__ plse,
+    bf16_t* __restrict__ O, float* __restrict__ lse) {
   using LT = LdsTiles<D>;
   using MT = MxTiles<D>;
   constexpr bool MX = QNT != QNT_NONE;
@@ -328,12 +328,16 @@ __device__ __forceinline__ void attn_fwd_lds_body(
 
   int bh, q_lo, nq, r1a, r1b, r2a, r2b, bstart = 0;
   if constexpr (MODE == MODE_ANCHOR) {
-    // the items of this XCD's range (about an eighth of the total cost; n_tiles[1 + x] is the
-    // range start, stored by the index inversion), one per workgroup slot of the XCD
+    // an item of this XCD's range (about an eighth of the total cost; the range starts are at
+    // n_tiles[1 ..], stored by the index inversion), or of another XCD's once this one's is
+    // used up; one item per workgroup
+    __shared__ int s_item;
+    if (threadIdx.x == 0)
+      s_item = claim_item(n_tiles + 1, ctr, static_cast<int>(blockIdx.x) % kXcds);
+    __syncthreads();
+    const int lid = s_item;
+    if (lid < 0) return;
     const int nt = n_tiles[0];
-    const int x = static_cast<int>(blockIdx.x) % kXcds;
-    const int lid = n_tiles[1 + x] + static_cast<int>(blockIdx.x) / kXcds;
-    if (lid >= n_tiles[2 + x]) return;
     bh = lid / nt;
     const int32_t* a = tiles + 6 * (lid % nt);
     q_lo = a[0];
@@ -680,13 +684,13 @@ __global__ __launch_bounds__(kNT) void attn_fwd_bf16_kernel(
     const void* __restrict__ Qv, const void* __restrict__ Kv, const uint8_t* __restrict__ Qs,
     const uint8_t* __restrict__ Ks, const void* __restrict__ Vt, int Lp,
     const int32_t* __restrict__ off, AttnParams p, const int32_t* __restrict__ tiles,
-    const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ bucket_off,
-    const int32_t* __restrict__ bucket_q, const int32_t* __restrict__ slot,
-    float* __restrict__ pO, float* __restrict__ plse, bf16_t* __restrict__ O,
-    float* __restrict__ lse) {
+    const int32_t* __restrict__ n_tiles, int32_t* __restrict__ ctr,
+    const int32_t* __restrict__ bucket_off, const int32_t* __restrict__ bucket_q,
+    const int32_t* __restrict__ slot, float* __restrict__ pO, float* __restrict__ plse,
+    bf16_t* __restrict__ O, float* __restrict__ lse) {
   attn_fwd_lds_body<D, MODE, MX ? QNT_SCORES : QNT_NONE>(Qv, Kv, Qs, Ks, Vt, Lp, off, p, tiles,
-                                                          n_tiles, bucket_off, bucket_q, slot,
-                                                          pO, plse, O, lse);
+                                                          n_tiles, ctr, bucket_off, bucket_q,
+                                                          slot, pO, plse, O, lse);
 }
 
 // MXFP8 Q, K and V (quantised scores and values)
@@ -695,11 +699,11 @@ __global__ __launch_bounds__(kNT) void attn_fwd_mxv_kernel(
     const void* __restrict__ Qv, const void* __restrict__ Kv, const uint8_t* __restrict__ Qs,
     const uint8_t* __restrict__ Ks, const void* __restrict__ Vq, int Lp,
     const int32_t* __restrict__ off, AttnParams p, const int32_t* __restrict__ tiles,
-    const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ bucket_off,
-    const int32_t* __restrict__ bucket_q, const int32_t* __restrict__ slot,
-    float* __restrict__ pO, float* __restrict__ plse, bf16_t* __restrict__ O,
-    float* __restrict__ lse) {
-  attn_fwd_lds_body<D, MODE, QNT_VALUES>(Qv, Kv, Qs, Ks, Vq, Lp, off, p, tiles, n_tiles,
+    const int32_t* __restrict__ n_tiles, int32_t* __restrict__ ctr,
+    const int32_t* __restrict__ bucket_off, const int32_t* __restrict__ bucket_q,
+    const int32_t* __restrict__ slot, float* __restrict__ pO, float* __restrict__ plse,
+    bf16_t* __restrict__ O, float* __restrict__ lse) {
+  attn_fwd_lds_body<D, MODE, QNT_VALUES>(Qv, Kv, Qs, Ks, Vq, Lp, off, p, tiles, n_tiles, ctr,
                                          bucket_off, bucket_q, slot, pO, plse, O, lse);
 }
 
@@ -781,12 +785,12 @@ static hipError_t launch_fwd_bf16(const moc_layout* lay, const moc_varlen* vl, c
     if (mx)
       hipLaunchKernelGGL((moc::attn_fwd_bf16_kernel<D, moc::MODE_ROUTED, true>),
                          dim3(vl->max_rtiles), dim3(moc::kNT), 0, st, Q, K, Qs, Ks, Vt, Lp,
-                         lay->chunk_offsets, p, vl->rtiles, vl->n_rtiles, vl->bucket_off,
+                         lay->chunk_offsets, p, vl->rtiles, vl->n_rtiles, nullptr, vl->bucket_off,
                          vl->bucket_q, vl->slot, pO, plse, static_cast<bf16_t*>(O), lse);
     else
       hipLaunchKernelGGL((moc::attn_fwd_bf16_kernel<D, moc::MODE_ROUTED, false>),
                          dim3(vl->max_rtiles), dim3(moc::kNT), 0, st, Q, K, Qs, Ks, Vt, Lp,
-                         lay->chunk_offsets, p, vl->rtiles, vl->n_rtiles, vl->bucket_off,
+                         lay->chunk_offsets, p, vl->rtiles, vl->n_rtiles, nullptr, vl->bucket_off,
                          vl->bucket_q, vl->slot, pO, plse, static_cast<bf16_t*>(O), lse);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -795,12 +799,14 @@ static hipError_t launch_fwd_bf16(const moc_layout* lay, const moc_varlen* vl, c
   if (mx)
     hipLaunchKernelGGL((moc::attn_fwd_bf16_kernel<D, moc::MODE_ANCHOR, true>), dim3(grid),
                        dim3(moc::kNT), 0, st, Q, K, Qs, Ks, Vt, Lp, lay->chunk_offsets, p,
-                       vl->atiles, vl->n_atiles, vl->bucket_off, vl->bucket_q, vl->slot, pO,
+                       vl->atiles, vl->n_atiles, vl->n_atiles + moc::kCtrFwd, vl->bucket_off,
+                       vl->bucket_q, vl->slot, pO,
                        plse, static_cast<bf16_t*>(O), lse);
   else
     hipLaunchKernelGGL((moc::attn_fwd_bf16_kernel<D, moc::MODE_ANCHOR, false>), dim3(grid),
                        dim3(moc::kNT), 0, st, Q, K, Qs, Ks, Vt, Lp, lay->chunk_offsets, p,
-                       vl->atiles, vl->n_atiles, vl->bucket_off, vl->bucket_q, vl->slot, pO,
+                       vl->atiles, vl->n_atiles, vl->n_atiles + moc::kCtrFwd, vl->bucket_off,
+                       vl->bucket_q, vl->slot, pO,
                        plse, static_cast<bf16_t*>(O), lse);
   return hipGetLastError();
 }
@@ -834,7 +840,7 @@ static hipError_t launch_fwd_mxv_d(const moc_layout* lay, const moc_varlen* vl, 
     p.max_tiles = vl->max_rtiles;
     hipLaunchKernelGGL((moc::attn_fwd_mxv_kernel<D, moc::MODE_ROUTED>), dim3(vl->max_rtiles),
                        dim3(moc::kNT), 0, st, Qc, Kc, Qs, Ks, Vq, Lp, lay->chunk_offsets, p,
-                       vl->rtiles, vl->n_rtiles, vl->bucket_off, vl->bucket_q, vl->slot, pO,
+                       vl->rtiles, vl->n_rtiles, nullptr, vl->bucket_off, vl->bucket_q, vl->slot, pO,
                        plse, static_cast<bf16_t*>(O), lse);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -843,7 +849,7 @@ static hipError_t launch_fwd_mxv_d(const moc_layout* lay, const moc_varlen* vl, 
                      dim3(moc::kXcds * moc::xcd_slots(vl->max_atiles, lay->B * lay->H)),
                      dim3(moc::kNT), 0, st, Qc, Kc, Qs,
                      Ks, Vq, Lp, lay->chunk_offsets, p, vl->atiles, vl->n_atiles,
-                     vl->bucket_off, vl->bucket_q, vl->slot, pO, plse,
+                     vl->n_atiles + moc::kCtrFwd, vl->bucket_off, vl->bucket_q, vl->slot, pO, plse,
                      static_cast<bf16_t*>(O), lse);
   return hipGetLastError();
 }

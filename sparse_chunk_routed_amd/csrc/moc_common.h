@@ -66,6 +66,26 @@ __host__ __device__ inline int xcd_slots(int max_tiles, int BH) {
 }
 // cost of one anchor tile: its 64-key tiles plus a fixed start-up and epilogue share
 constexpr int kAnchorTileFixed = 4;
+
+// Claim counters of the XCD ranges, in the VARLEN workspace after the anchor tile count and its
+// range starts (n_atiles[kCtrFwd + y] etc.); every attention call's guard kernel zeroes them.
+constexpr int kCtrFwd = 16, kCtrDq = 24, kCtrDkdv = 32, kCtrEnd = 40;
+
+// The work item of a workgroup of a range-split kernel: the next unclaimed item of its own XCD's
+// range (ranges[x] .. ranges[x + 1]), else of the other ranges in turn, so that an XCD whose
+// range runs out early takes over the rest of a slower one. ctr[y] counts the claims on range
+// y and only grows. Returns -1 when every range is used up. Called by one thread.
+__device__ inline int claim_item(const int32_t* ranges, int32_t* ctr, int x) {
+  for (int k = 0; k < kXcds; ++k) {
+    const int y = (x + k) % kXcds;
+    const int n = ranges[y + 1] - ranges[y];
+    if (k > 0 && __hip_atomic_load(ctr + y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n)
+      continue;
+    const int i = atomicAdd(ctr + y, 1);
+    if (i < n) return ranges[y] + i;
+  }
+  return -1;
+}
 // cost of one backward key tile: its 32-query blocks plus a fixed start-up and epilogue share
 constexpr int kKeyTileFixed = 2;
 

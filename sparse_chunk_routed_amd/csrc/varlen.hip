@@ -427,7 +427,9 @@ __global__ __launch_bounds__(256) void inv_scatter_kernel(const int32_t* __restr
 // kernel of the call reads first (layout_rejected).
 __global__ void varlen_guard_kernel(const int32_t* __restrict__ total, int64_t cap,
                                     const uint32_t* __restrict__ layout_word,
-                                    uint32_t* __restrict__ status) {
+                                    uint32_t* __restrict__ status, int32_t* __restrict__ ctr) {
+  // the claim counters of the call's range-split kernels start from zero
+  for (int i = kCtrFwd; i < kCtrEnd; ++i) ctr[i] = 0;
   uint32_t st = 0u;
   if (static_cast<int64_t>(total[0]) > cap) st |= MOC_VARLEN_OVER_CAPACITY;
   if (layout_word != nullptr && layout_word[0] != 0u) st |= MOC_VARLEN_BAD_LAYOUT;
@@ -443,7 +445,7 @@ using moc::VarlenParams;
 hipError_t launch_varlen_guard(const moc_layout* lay, const moc_varlen* vl, hipStream_t st) {
   const int64_t nb = static_cast<int64_t>(lay->B) * lay->H * lay->C;
   hipLaunchKernelGGL(moc::varlen_guard_kernel, dim3(1), dim3(1), 0, st, vl->bucket_off + nb,
-                     vl->routed_cap, lay->check, vl->status);
+                     vl->routed_cap, lay->check, vl->status, vl->n_atiles);
   return hipGetLastError();
 }
 
