@@ -139,6 +139,9 @@ typedef struct {
  *               B*H*n_atiles[0] anchor items (b, h, tile) into 8 contiguous ranges of about
  *               equal cost (a tile costs its 64-key tiles plus 4), one per XCD: range x is
  *               [n_atiles[1+x], n_atiles[2+x]), at most ceil(1.25 B*H*max_atiles / 8) items.
+ *               n_atiles[16..39] are claim counters of the attention kernels' work items,
+ *               zeroed at the start of every attention call: attention calls that share one
+ *               moc_varlen must not run at the same time.
  *   ktiles:     [max_ktiles][6] key tiles of the backward (k0, k1, chunk or -1 for text,
  *               anchor query range q0, q1, text split index), n_ktiles[0] valid, shared by every
  *               (b, h). A key tile never straddles a chunk; text keys, which every query
