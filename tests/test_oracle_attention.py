@@ -131,7 +131,7 @@ def test_masked_sdpa_equivalence_random_layouts(seed):
     lhs = np.einsum("bhtd,bhtd->bh", Q, dQ)
     rhs = np.einsum("bhtd,bhtd->bh", K, dK)
     assert np.max(np.abs(lhs - rhs)) < 1e-11
-    # anchors are always inside Omega (spec: text + own shot always present)
+    # anchors are always inside Omega (the text tokens and the own shot are mandatory)
     D = mo.derive(lay)
     for t in range(lay.L):
         ks = set(mo.key_set(D, t, r.sel[0, 0, t]).tolist())
